@@ -1,0 +1,414 @@
+/*
+ * entmax_oracle.c -- plain fp64 CPU oracle for 1.5-entmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the independent reference that the
+ * GPU path is checked against.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it; the product library never
+ * does, and it shares no code, header or constant with the HIP sources.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  - 1.5-entmax of a score vector s:  p_j = [(s_j - tau)/2]_+^2 with tau the
+ *    unique value making sum_j p_j = 1.  ("GPT-2 with AdaSplash Attention via
+ *    NeuralOps", Mathematical Formulation item 2; "DistilBERT MNLI with
+ *    AdaSplash Attention via NeuralOps", Mathematical Formulation item 2;
+ *    "AdaSplash-2: Faster Differentiable Sparse Attention", sec. 2.3 and the
+ *    normaliser f(tau) of sec. 2.4, written there with tau' = tau/2.)
+ *    Entries equal to -inf are masked out and take no part in the row.
+ *
+ *  - tau is found exactly, with no iteration, by the sorting method that
+ *    AdaSplash-2 sec. 2.4 ("Sorting-based solvers") names for alpha = 1.5:
+ *    the support is a top-k set of the sorted scores, and for a fixed support
+ *    the normaliser is a quadratic in tau whose coefficients are the count,
+ *    sum and sum of squares of the support (the S0, S1, S2 of AdaSplash-2
+ *    appendix C.3).  The smaller root is the one below the support scores.
+ *
+ *  - Attention: S = scale * Q K^T over the active keys of each query row,
+ *    O = A V with A the row-wise 1.5-entmax of S (AdaSplash-2 sec. 2.2).
+ *    Active keys per mask mode (0-indexed positions):
+ *       0 none:                 every key
+ *       1 causal:               j <= i
+ *       2 causal window + sink: j <= i and (j == 0 or i - j <= window)
+ *    Mode 2 is the causal "splash" mask of the GPT-2 model card (item 1 of
+ *    its Mathematical Formulation): key 0 always active plus the keys no more
+ *    than W positions behind the query.
+ *
+ *  - Backward, by implicit differentiation of the normaliser (gradients live
+ *    on the support only, AdaSplash-2 sec. 3.3 "Backward pass"):
+ *       g_ij  = [(s_ij - tau_i)/2]_+          (so A_ij = g_ij^2)
+ *       dA_ij = dO_i . V_j
+ *       delta_i = sum_j g_ij dA_ij / sum_j g_ij
+ *       dS_ij = g_ij (dA_ij - delta_i)
+ *       dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i,
+ *       dV_j = sum_i A_ij dO_i.
+ *
+ *  - Block mask: M[I][J] = 1 iff some query of row block I has a key of
+ *    column block J with A > 0 (AdaSplash-2 sec. 3.3 Phase 3, appendix C.4),
+ *    packed 32 column blocks per uint32, bit (J mod 32) of word J / 32.
+ *
+ * All arithmetic is fp64; inputs arrive as fp32 arrays (bf16 and fp32 values
+ * are both exactly representable there).  Sums run in index order.  Exact
+ * zeros of A are skipped in the products, which changes no result.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int cmp_desc(const void* a, const void* b) {
+    double x = *(const double*)a, y = *(const double*)b;
+    return (x < y) - (x > y);
+}
+
+/*
+ * Exact tau of one row.  s[0..n) with -INFINITY marking inactive entries.
+ * work must hold n doubles.  Returns tau (-INFINITY for a row with no active
+ * entry) and writes the support size to *k_out when k_out is not NULL.
+ *
+ * Sorted descending x_1 >= ... >= x_n, shifted by the max m (y = x - m, so
+ * y_1 = 0).  For the top-k set the normaliser sum_t ((y_t - t)/2)^2 = 1 reads
+ * k t^2 - 2 a_k t + (b_k - 4) = 0 with a_k = sum y_t and b_k = sum y_t^2.
+ * Its smaller root t_k = (a_k - sqrt(a_k^2 - k (b_k - 4))) / k is the
+ * threshold of that support; the true support is the largest k whose root
+ * lies at or below its own k-th score (t_k <= y_k).  k = 1 always qualifies
+ * (t_1 = -2), which is the lower bracket end tau >= max - 2.
+ */
+double orc_entmax15_tau(const double* s, int64_t n, double* work, int64_t* k_out) {
+    int64_t na = 0;
+    for (int64_t j = 0; j < n; ++j)
+        if (s[j] != -INFINITY) work[na++] = s[j];
+    if (na == 0) {
+        if (k_out) *k_out = 0;
+        return -INFINITY;
+    }
+    qsort(work, (size_t)na, sizeof(double), cmp_desc);
+    const double m = work[0];
+    double a = 0.0, b = 0.0, best = -2.0;
+    int64_t kbest = 1;
+    for (int64_t k = 1; k <= na; ++k) {
+        const double y = work[k - 1] - m;
+        a += y;
+        b += y * y;
+        const double disc = a * a - (double)k * (b - 4.0);
+        if (disc < 0.0) continue;
+        const double t = (a - sqrt(disc)) / (double)k;
+        if (t <= y) {
+            best = t;
+            kbest = k;
+        }
+    }
+    if (k_out) *k_out = kbest;
+    return m + best;
+}
+
+/* p_j = [(s_j - tau)/2]_+^2 for one row; returns tau. */
+double orc_entmax15(const double* s, int64_t n, double* p, int64_t* k_out) {
+    double* work = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    const double tau = orc_entmax15_tau(s, n, work, k_out);
+    for (int64_t j = 0; j < n; ++j) {
+        const double g = (s[j] > tau) ? 0.5 * (s[j] - tau) : 0.0;
+        p[j] = g * g;
+    }
+    free(work);
+    return tau;
+}
+
+/*
+ * Row-wise entmax of a materialised fp32 score matrix S[rows][ld] (cols used
+ * per row).  tau[rows]; P[rows][cols] (row stride cols) may be NULL.
+ */
+void orc_tau_rows(const float* S, int64_t rows, int64_t cols, int64_t ld,
+                  double* tau, double* P) {
+#pragma omp parallel
+    {
+        double* row = (double*)malloc((size_t)(cols > 0 ? cols : 1) * sizeof(double));
+        double* work = (double*)malloc((size_t)(cols > 0 ? cols : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; ++r) {
+            for (int64_t c = 0; c < cols; ++c) row[c] = (double)S[r * ld + c];
+            const double t = orc_entmax15_tau(row, cols, work, NULL);
+            tau[r] = t;
+            if (P) {
+                for (int64_t c = 0; c < cols; ++c) {
+                    const double g = (row[c] > t) ? 0.5 * (row[c] - t) : 0.0;
+                    P[r * cols + c] = g * g;
+                }
+            }
+        }
+        free(row);
+        free(work);
+    }
+}
+
+/* Active-key predicate of the three mask modes (0-indexed positions). */
+int orc_key_active(int mask, int64_t window, int64_t i, int64_t j) {
+    if (mask == 0) return 1;
+    if (j > i) return 0;
+    if (mask == 1) return 1;
+    return (j == 0) || (i - j <= window);
+}
+
+/* Scores of query row i of one head: s[j] = scale * Q_i . K_j, -inf if masked. */
+static void head_row_scores(const float* Q, const float* K, int64_t L, int64_t d,
+                            double scale, int mask, int64_t window, int64_t i,
+                            double* s) {
+    const float* q = Q + i * d;
+    for (int64_t j = 0; j < L; ++j) {
+        if (!orc_key_active(mask, window, i, j)) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        const float* k = K + j * d;
+        double acc = 0.0;
+        for (int64_t c = 0; c < d; ++c) acc += (double)q[c] * (double)k[c];
+        s[j] = scale * acc;
+    }
+}
+
+/*
+ * Attention forward for a list of query rows.  Q, K, V are [BH][L][d].
+ * rows[r] indexes the flattened [BH*L] query rows; rows == NULL means all
+ * BH*L rows in order (nrows must then equal BH*L).  Outputs per listed row:
+ * O[r][d], tau[r], and (optional) support size nsup[r] and the sum of g,
+ * gsum[r] = sum_j [(s_j - tau)/2]_+.
+ */
+void orc_attn_fwd(const float* Q, const float* K, const float* V,
+                  int64_t BH, int64_t L, int64_t d, double scale, int mask,
+                  int64_t window, const int64_t* rows, int64_t nrows,
+                  double* O, double* tau, int64_t* nsup, double* gsum) {
+    (void)BH;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+        double* work = (double*)malloc((size_t)L * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t flat = rows ? rows[r] : r;
+            const int64_t bh = flat / L, i = flat % L;
+            const float* Qh = Q + bh * L * d;
+            const float* Kh = K + bh * L * d;
+            const float* Vh = V + bh * L * d;
+            head_row_scores(Qh, Kh, L, d, scale, mask, window, i, s);
+            int64_t k = 0;
+            const double t = orc_entmax15_tau(s, L, work, &k);
+            tau[r] = t;
+            if (nsup) nsup[r] = k;
+            double* o = O + r * d;
+            for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+            double gs = 0.0;
+            for (int64_t j = 0; j < L; ++j) {
+                if (!(s[j] > t)) continue; /* A_ij = 0 exactly */
+                const double g = 0.5 * (s[j] - t);
+                const double a = g * g;
+                gs += g;
+                const float* v = Vh + j * d;
+                for (int64_t c = 0; c < d; ++c) o[c] += a * (double)v[c];
+            }
+            if (gsum) gsum[r] = gs;
+        }
+        free(s);
+        free(work);
+    }
+}
+
+/*
+ * Block masks of one head at tile br x bc.  Three masks, each
+ * [ceil(L/br)][ceil(ceil(L/bc)/32)] words:
+ *   m_exact: tile has an entry with s > tau            (the definition)
+ *   m_lo:    tile has an entry with s - tau >  tol     (must be set)
+ *   m_hi:    tile has an entry with s - tau > -tol     (may be set)
+ * tau_out[L] receives the row thresholds when not NULL.
+ */
+void orc_block_mask_head(const float* Q, const float* K, int64_t L, int64_t d,
+                         double scale, int mask, int64_t window, int64_t br,
+                         int64_t bc, double tol, uint32_t* m_exact,
+                         uint32_t* m_lo, uint32_t* m_hi, double* tau_out) {
+    const int64_t Tr = (L + br - 1) / br, Tc = (L + bc - 1) / bc;
+    const int64_t Wd = (Tc + 31) / 32;
+    memset(m_exact, 0, (size_t)(Tr * Wd) * sizeof(uint32_t));
+    memset(m_lo, 0, (size_t)(Tr * Wd) * sizeof(uint32_t));
+    memset(m_hi, 0, (size_t)(Tr * Wd) * sizeof(uint32_t));
+    /* one row block per iteration: no two threads write the same words */
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+        double* work = (double*)malloc((size_t)L * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t I = 0; I < Tr; ++I) {
+            for (int64_t i = I * br; i < L && i < (I + 1) * br; ++i) {
+                head_row_scores(Q, K, L, d, scale, mask, window, i, s);
+                const double t = orc_entmax15_tau(s, L, work, NULL);
+                if (tau_out) tau_out[i] = t;
+                for (int64_t j = 0; j < L; ++j) {
+                    if (s[j] == -INFINITY) continue;
+                    const int64_t J = j / bc;
+                    const uint32_t bit = 1u << (J % 32);
+                    if (s[j] > t) m_exact[I * Wd + J / 32] |= bit;
+                    if (s[j] - t > tol) m_lo[I * Wd + J / 32] |= bit;
+                    if (s[j] - t > -tol) m_hi[I * Wd + J / 32] |= bit;
+                }
+            }
+        }
+        free(s);
+        free(work);
+    }
+}
+
+/*
+ * Full backward of one head.  Q, K, V, dO are [L][d]; outputs dQ, dK, dV are
+ * [L][d]; tau[L], delta[L] optional.  Row pass (parallel over queries): tau,
+ * the support, delta, dQ_i, and the support's (j, A_ij, dS_ij).  Column pass
+ * (serial in query order per key): dK_j and dV_j from those entries.
+ */
+void orc_attn_bwd_head(const float* Q, const float* K, const float* V,
+                       const float* dO, int64_t L, int64_t d, double scale,
+                       int mask, int64_t window, double* dQ, double* dK,
+                       double* dV, double* tau_out, double* delta_out) {
+    int64_t* sup_off = (int64_t*)calloc((size_t)L + 1, sizeof(int64_t));
+    int64_t** sup_j = (int64_t**)calloc((size_t)L, sizeof(int64_t*));
+    double** sup_a = (double**)calloc((size_t)L, sizeof(double*));
+    double** sup_ds = (double**)calloc((size_t)L, sizeof(double*));
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+        double* work = (double*)malloc((size_t)L * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < L; ++i) {
+            head_row_scores(Q, K, L, d, scale, mask, window, i, s);
+            int64_t k = 0;
+            const double t = orc_entmax15_tau(s, L, work, &k);
+            if (tau_out) tau_out[i] = t;
+            int64_t cnt = 0;
+            for (int64_t j = 0; j < L; ++j) cnt += (s[j] > t);
+            sup_off[i + 1] = cnt;
+            int64_t* jj = (int64_t*)malloc((size_t)(cnt > 0 ? cnt : 1) * sizeof(int64_t));
+            double* aa = (double*)malloc((size_t)(cnt > 0 ? cnt : 1) * sizeof(double));
+            double* dd = (double*)malloc((size_t)(cnt > 0 ? cnt : 1) * sizeof(double));
+            double* gg = (double*)malloc((size_t)(cnt > 0 ? cnt : 1) * sizeof(double));
+            double* da = (double*)malloc((size_t)(cnt > 0 ? cnt : 1) * sizeof(double));
+            const float* go = dO + i * d;
+            double num = 0.0, den = 0.0;
+            int64_t c = 0;
+            for (int64_t j = 0; j < L; ++j) {
+                if (!(s[j] > t)) continue;
+                const double g = 0.5 * (s[j] - t);
+                const float* v = V + j * d;
+                double dot = 0.0;
+                for (int64_t e = 0; e < d; ++e) dot += (double)go[e] * (double)v[e];
+                jj[c] = j;
+                gg[c] = g;
+                aa[c] = g * g;
+                da[c] = dot;
+                num += g * dot;
+                den += g;
+                ++c;
+            }
+            const double delta = (den > 0.0) ? num / den : 0.0;
+            if (delta_out) delta_out[i] = delta;
+            double* dq = dQ + i * d;
+            for (int64_t e = 0; e < d; ++e) dq[e] = 0.0;
+            for (int64_t q = 0; q < cnt; ++q) {
+                const double ds = gg[q] * (da[q] - delta);
+                dd[q] = ds;
+                const float* kk = K + jj[q] * d;
+                for (int64_t e = 0; e < d; ++e) dq[e] += scale * ds * (double)kk[e];
+            }
+            sup_j[i] = jj;
+            sup_a[i] = aa;
+            sup_ds[i] = dd;
+            free(gg);
+            free(da);
+        }
+        free(s);
+        free(work);
+    }
+    memset(dK, 0, (size_t)(L * d) * sizeof(double));
+    memset(dV, 0, (size_t)(L * d) * sizeof(double));
+    for (int64_t i = 0; i < L; ++i) {
+        const float* qi = Q + i * d;
+        const float* go = dO + i * d;
+        for (int64_t q = 0; q < sup_off[i + 1]; ++q) {
+            const int64_t j = sup_j[i][q];
+            const double a = sup_a[i][q], ds = sup_ds[i][q];
+            double* dk = dK + j * d;
+            double* dv = dV + j * d;
+            for (int64_t e = 0; e < d; ++e) {
+                dk[e] += scale * ds * (double)qi[e];
+                dv[e] += a * (double)go[e];
+            }
+        }
+        free(sup_j[i]);
+        free(sup_a[i]);
+        free(sup_ds[i]);
+    }
+    free(sup_off);
+    free(sup_j);
+    free(sup_a);
+    free(sup_ds);
+}
+
+/*
+ * dQ and delta for a list of query rows of a [BH][L][d] batch (no dK/dV):
+ * cheap enough to sample at any size.  dQ[r][d], delta[r], tau[r].
+ */
+void orc_attn_bwd_rows(const float* Q, const float* K, const float* V,
+                       const float* dO, int64_t BH, int64_t L, int64_t d,
+                       double scale, int mask, int64_t window,
+                       const int64_t* rows, int64_t nrows, double* dQ,
+                       double* delta_out, double* tau_out) {
+    (void)BH;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+        double* work = (double*)malloc((size_t)L * sizeof(double));
+        double* da = (double*)malloc((size_t)L * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t flat = rows[r];
+            const int64_t bh = flat / L, i = flat % L;
+            const float* Qh = Q + bh * L * d;
+            const float* Kh = K + bh * L * d;
+            const float* Vh = V + bh * L * d;
+            const float* go = dO + flat * d;
+            head_row_scores(Qh, Kh, L, d, scale, mask, window, i, s);
+            const double t = orc_entmax15_tau(s, L, work, NULL);
+            if (tau_out) tau_out[r] = t;
+            double num = 0.0, den = 0.0;
+            for (int64_t j = 0; j < L; ++j) {
+                if (!(s[j] > t)) continue;
+                const double g = 0.5 * (s[j] - t);
+                const float* v = Vh + j * d;
+                double dot = 0.0;
+                for (int64_t e = 0; e < d; ++e) dot += (double)go[e] * (double)v[e];
+                da[j] = dot;
+                num += g * dot;
+                den += g;
+            }
+            const double delta = (den > 0.0) ? num / den : 0.0;
+            if (delta_out) delta_out[r] = delta;
+            double* dq = dQ + r * d;
+            for (int64_t e = 0; e < d; ++e) dq[e] = 0.0;
+            for (int64_t j = 0; j < L; ++j) {
+                if (!(s[j] > t)) continue;
+                const double g = 0.5 * (s[j] - t);
+                const double ds = g * (da[j] - delta);
+                const float* kk = Kh + j * d;
+                for (int64_t e = 0; e < d; ++e) dq[e] += scale * ds * (double)kk[e];
+            }
+        }
+        free(s);
+        free(work);
+        free(da);
+    }
+}
