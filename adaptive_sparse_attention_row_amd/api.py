@@ -1,0 +1,180 @@
+"""Thin ctypes binding over libentmax.so (the C ABI of include/entmax.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback -- a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libentmax.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALPHA, ERR_DTYPE, ERR_MASK, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_ARG = range(10)
+MASK_NONE, MASK_CAUSAL, MASK_WINDOW_SINK = 0, 1, 2
+F32, BF16 = 0, 1
+OPT_CANDIDATE_CAP = 1
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class EntmaxError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: status {status} ({status_str(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libentmax.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m adaptive_sparse_attention_row_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                            ctypes.c_float, ctypes.c_size_t)
+    L.entmax_status_str.restype = ctypes.c_char_p
+    L.entmax_status_str.argtypes = [i32]
+    L.entmax_version.restype = i32
+    L.entmax_version.argtypes = []
+    L.entmax_tile_shape.restype = i32
+    L.entmax_tile_shape.argtypes = [i32, i32, P, P]
+    L.entmax_tau_rows.restype = i32
+    L.entmax_tau_rows.argtypes = [P, P, P, i64, i64, i64, f32, P]
+    L.entmax_attn_fwd_workspace.restype = sz
+    L.entmax_attn_fwd_workspace.argtypes = [i32] * 7
+    L.entmax_attn_fwd.restype = i32
+    L.entmax_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, i32,
+                                  i32, i32, P, sz, P]
+    L.entmax_attn_bwd_workspace.restype = sz
+    L.entmax_attn_bwd_workspace.argtypes = [i32] * 7
+    L.entmax_attn_bwd.restype = i32
+    L.entmax_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, f32, f32,
+                                  i32, i32, i32, P, sz, P]
+    L.entmax_set_option.restype = i32
+    L.entmax_set_option.argtypes = [i32, i32]
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().entmax_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise EntmaxError(fn, status)
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev_ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def tile_shape(d: int, dtype: int = BF16) -> tuple[int, int]:
+    br, bc = ctypes.c_int(0), ctypes.c_int(0)
+    _check("entmax_tile_shape", lib().entmax_tile_shape(d, dtype, ctypes.byref(br), ctypes.byref(bc)))
+    return br.value, bc.value
+
+
+def set_option(option: int, value: int) -> int:
+    r = lib().entmax_set_option(option, value)
+    if r < 0:
+        raise EntmaxError("entmax_set_option", -r)
+    return r
+
+
+def tau_rows(S, want_p: bool = True, P=None, tau=None):
+    """Row-wise 1.5-entmax of a [rows, cols] fp32 CUDA tensor (row stride may
+    exceed cols).  Returns (tau [rows], P [rows, cols] or None)."""
+    import torch
+    if not S.is_cuda or S.dtype != torch.float32 or S.dim() != 2 or S.stride(1) != 1:
+        raise ValueError("S must be a 2-D fp32 CUDA tensor with unit column stride")
+    rows, cols = S.shape
+    ld = S.stride(0) if rows > 1 else cols
+    if want_p and P is None:
+        P = torch.empty_strided((rows, cols), (ld, 1), device=S.device, dtype=torch.float32)
+    if tau is None:
+        tau = torch.empty(rows, device=S.device, dtype=torch.float32)
+    if P is not None and P.stride() != (ld, 1) and rows > 1:
+        raise ValueError("P must share S's row stride")
+    st = lib().entmax_tau_rows(S.data_ptr(), _dev_ptr(P), tau.data_ptr(), rows, cols, ld,
+                               1.5, _stream(S.device))
+    _check("entmax_tau_rows", st)
+    return tau, P
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def mask_shape(B: int, H: int, L: int, d: int, dtype: int = BF16) -> tuple[int, int, int, int]:
+    br, bc = tile_shape(d, dtype)
+    tr, tc = -(-L // br), -(-L // bc)
+    return (B, H, tr, -(-tc // 32))
+
+
+def attn_fwd(q, k, v, scale: Optional[float] = None, mask: int = MASK_NONE, window: int = 0,
+             want_block_mask: bool = True, out=None):
+    """1.5-entmax attention forward.  q, k, v: [B, H, L, d] CUDA tensors
+    (bf16 or fp32, contiguous).  Returns (O fp32, tau fp32 [B, H, L],
+    block_mask int32 view of the packed uint32 mask, or None)."""
+    import torch
+    B, H, L, d = q.shape
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous CUDA tensors of one shape and dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = out if out is not None else torch.empty(B, H, L, d, device=q.device, dtype=torch.float32)
+    tau = torch.empty(B, H, L, device=q.device, dtype=torch.float32)
+    bm = None
+    if want_block_mask:
+        bm = torch.empty(mask_shape(B, H, L, d, dt), device=q.device, dtype=torch.int32)
+    ws_bytes = lib().entmax_attn_fwd_workspace(B, H, L, d, dt, mask, window)
+    ws = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8) if ws_bytes else None
+    st = lib().entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(),
+                               tau.data_ptr(), _dev_ptr(bm), B, H, L, d, float(scale), 1.5, dt,
+                               mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
+    _check("entmax_attn_fwd", st)
+    return O, tau, bm
+
+
+def attn_bwd(q, k, v, do, tau, block_mask, scale: Optional[float] = None,
+             mask: int = MASK_NONE, window: int = 0):
+    """Backward of attn_fwd.  Returns (dQ, dK, dV), fp32 [B, H, L, d]."""
+    import torch
+    B, H, L, d = q.shape
+    for t in (q, k, v, do):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, do must be contiguous CUDA tensors of one shape and dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty(B, H, L, d, device=q.device, dtype=torch.float32)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    ws_bytes = lib().entmax_attn_bwd_workspace(B, H, L, d, dt, mask, window)
+    ws = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8) if ws_bytes else None
+    st = lib().entmax_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                               tau.data_ptr(), block_mask.data_ptr(), dq.data_ptr(),
+                               dk.data_ptr(), dv.data_ptr(), B, H, L, d, float(scale), 1.5, dt,
+                               mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
+    _check("entmax_attn_bwd", st)
+    return dq, dk, dv

@@ -1,0 +1,328 @@
+// attn_common.hpp -- tiles, MFMA score blocks and masks shared by the
+// attention kernels (gfx950, wave64).
+//
+// A workgroup owns 128 query rows of one (batch, head) and runs 4 waves:
+// wave w has row half qh = w & 1 (64 rows) and key parity kh = w >> 1 (it
+// takes every other 64-key tile of a tile list).  Scores are computed
+// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (or the fp32
+// 32x32x2 form), so that lane l of a 32x32 block holds query column l % 32
+// and 16 keys: register r of a block holds key 8*(r/4) + 4*(l/32) + r%4.
+// Per-query reductions are then lane-local plus one exchange with lane l^32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace entmax {
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBR = 128;      // query rows per workgroup
+constexpr int kBC = 64;       // keys per tile
+constexpr int kNT = 256;      // threads per workgroup
+constexpr int kMaxTc = 1024;  // key tiles per row (L <= 65536)
+constexpr int kMaxL = kMaxTc * kBC;
+
+enum TileClass { kSkip = 0, kFull = 1, kPartial = 2 };
+
+struct Geom {
+    int L, mode, W;
+};
+
+// Classify the 64x64 tile (rows [i0, i0+64), keys of tile J) under the mask.
+__device__ __forceinline__ int tile_class(int J, int i0, const Geom& g) {
+    const int c0 = J * kBC, c1 = c0 + kBC - 1, i1 = i0 + 63;
+    if (c0 >= g.L || i0 >= g.L) return kSkip;
+    if (g.mode >= 1 && c0 > i1) return kSkip;
+    if (g.mode == 2 && J != 0 && i0 - c1 > g.W) return kSkip;
+    bool full = (c1 < g.L) && (i1 < g.L);
+    if (g.mode >= 1) full = full && (c1 <= i0);
+    if (g.mode == 2) full = full && (i1 - c0 <= g.W);
+    return full ? kFull : kPartial;
+}
+
+// Active-key predicate, branch-free (it is evaluated per score element).
+__device__ __forceinline__ bool key_active(int i, int j, const Geom& g) {
+    const bool in_range = (i < g.L) & (j < g.L);
+    const bool causal_ok = (j <= i);
+    const bool window_ok = (j == 0) | (i - j <= g.W);
+    const bool mode_ok = (g.mode == 0) | (causal_ok & ((g.mode == 1) | window_ok));
+    return in_range & mode_ok;
+}
+
+// Key index (within a 32-key block) held by register r of lane half h.
+__device__ __forceinline__ int key_of_reg(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Element-type dependent pieces.
+template <typename T, int D>
+struct Ops;
+
+// ------------------------------------------------------------------ bf16
+template <int D>
+struct Ops<__bf16, D> {
+    static constexpr int kEsz = 2;
+    static constexpr int kKRow = D + 8;        // K row stride in LDS (elements)
+    static constexpr int kVRow = kBC + 4;      // V^T row stride in LDS (elements)
+    static constexpr int kKTile = kBC * kKRow; // elements per K tile
+    static constexpr int kVTile = D * kVRow;   // elements per V^T tile
+    static constexpr int kNS = D / 16;         // k-slices of a score block
+    static constexpr int kChunks = kBC * D * kEsz / 16;  // 16-byte chunks per tile
+
+    struct QOp {
+        bf16x8 q[2][kNS];
+    };
+
+    // Q operand for the wave's 64 rows starting at R0 (zero beyond L).
+    __device__ __forceinline__ static void load_q(QOp& op, const __bf16* Qh, int R0, int L) {
+        const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = R0 + qb * 32 + m;
+#pragma unroll
+            for (int s = 0; s < kNS; ++s) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (row < L) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)row * D + s * 16 + h * 8);
+                op.q[qb][s] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+    }
+
+    // acc[kb][qb] = K_tile[kb*32 + .., :] . Q[qb*32 + .., :]  (raw dot products)
+    __device__ __forceinline__ static void scores(f32x16 (&acc)[2][2], const __bf16* Kt, const QOp& op) {
+        const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[kb][qb][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kNS; ++s) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 k = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(Kt + (kb * 32 + m) * kKRow + s * 16 + h * 8));
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    acc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, op.q[qb][s], acc[kb][qb], 0, 0, 0);
+            }
+        }
+    }
+
+    // Global -> registers: chunk c of the tile starting at key c0 (zero past L).
+    __device__ __forceinline__ static u32x4 load_k_chunk(const __bf16* Kh, int c0, int L, int c) {
+        const int key = c / (D / 8), ch = c % (D / 8);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (c0 + key < L) v = *reinterpret_cast<const u32x4*>(Kh + (size_t)(c0 + key) * D + ch * 8);
+        return v;
+    }
+    __device__ __forceinline__ static void store_k_chunk(__bf16* Kt, int c, u32x4 v) {
+        const int key = c / (D / 8), ch = c % (D / 8);
+        *reinterpret_cast<u32x4*>(Kt + key * kKRow + ch * 8) = v;
+    }
+
+    // V tile transposed into LDS: V^T[d][key].  Unit u covers 4 keys x 8 d.
+    static constexpr int kVUnits = (kBC / 4) * (D / 8);
+    struct VRegs {
+        u32x4 r[4];
+    };
+    __device__ __forceinline__ static VRegs load_v_unit(const __bf16* Vh, int c0, int L, int u) {
+        const int kg = u % (kBC / 4), dg = u / (kBC / 4);
+        VRegs x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = c0 + 4 * kg + i;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (key < L) v = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dg * 8);
+            x.r[i] = v;
+        }
+        return x;
+    }
+    __device__ __forceinline__ static void store_v_unit(__bf16* Vt, int u, const VRegs& x) {
+        const int kg = u % (kBC / 4), dg = u / (kBC / 4);
+        // x.r[i] holds d = 8dg..8dg+7 of key 4kg+i; write 4 keys per d row.
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (x.r[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+            u32x2 pk;
+            pk[0] = w[0] | (w[1] << 16);
+            pk[1] = w[2] | (w[3] << 16);
+            *reinterpret_cast<u32x2*>(Vt + (dg * 8 + e) * kVRow + 4 * kg) = pk;
+        }
+    }
+
+    struct OAcc {
+        f32x16 o[D / 32][2];
+    };
+
+    // O^T[d][q] += V^T[d][keys of block kb] . A^T, A given as 4*A per
+    // register (a4[kb][qb][r]), split into bf16 hi + lo.
+    __device__ __forceinline__ static void pv(OAcc& oa, const __bf16* Vt, const f32x16 (&a4)[2][2], const bool (&on)[2]) {
+        const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (!on[kb]) continue;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 bh[2], bl[2];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) {
+                        const float a = a4[kb][qb][8 * t + p];
+                        const __bf16 hi = (__bf16)a;
+                        bh[qb][p] = hi;
+                        bl[qb][p] = (__bf16)(a - (float)hi);
+                    }
+                }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const __bf16* row = Vt + (db * 32 + m) * kVRow + kb * 32 + 16 * t + 4 * h;
+                    const u32x2 lo4 = *reinterpret_cast<const u32x2*>(row);
+                    const u32x2 hi4 = *reinterpret_cast<const u32x2*>(row + 8);
+                    u32x4 vv;
+                    vv[0] = lo4[0]; vv[1] = lo4[1]; vv[2] = hi4[0]; vv[3] = hi4[1];
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        oa.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bh[qb], oa.o[db][qb], 0, 0, 0);
+                        oa.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bl[qb], oa.o[db][qb], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+};
+
+// ------------------------------------------------------------------ fp32
+template <int D>
+struct Ops<float, D> {
+    static constexpr int kEsz = 4;
+    static constexpr int kKRow = D + 4;
+    static constexpr int kVRow = D + 4;          // V kept in natural [key][d] layout
+    static constexpr int kKTile = kBC * kKRow;
+    static constexpr int kVTile = kBC * kVRow;
+    static constexpr int kChunks = kBC * D * kEsz / 16;
+
+    struct QOp {
+        float q[2][D / 2];
+    };
+
+    __device__ __forceinline__ static void load_q(QOp& op, const float* Qh, int R0, int L) {
+        const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = R0 + qb * 32 + m;
+#pragma unroll
+            for (int s = 0; s < D / 2; ++s) op.q[qb][s] = (row < L) ? Qh[(size_t)row * D + 2 * s + h] : 0.0f;
+        }
+    }
+
+    __device__ __forceinline__ static void scores(f32x16 (&acc)[2][2], const float* Kt, const QOp& op) {
+        const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[kb][qb][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < D / 2; ++s) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const float k = Kt[(kb * 32 + m) * kKRow + 2 * s + h];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    acc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k, op.q[qb][s], acc[kb][qb], 0, 0, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ static u32x4 load_k_chunk(const float* Kh, int c0, int L, int c) {
+        const int key = c / (D / 4), ch = c % (D / 4);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (c0 + key < L) v = *reinterpret_cast<const u32x4*>(Kh + (size_t)(c0 + key) * D + ch * 4);
+        return v;
+    }
+    __device__ __forceinline__ static void store_k_chunk(float* Kt, int c, u32x4 v) {
+        const int key = c / (D / 4), ch = c % (D / 4);
+        *reinterpret_cast<u32x4*>(Kt + key * kKRow + ch * 4) = v;
+    }
+
+    // V stays in natural layout: a unit is one 16-byte chunk.
+    static constexpr int kVUnits = kChunks;
+    struct VRegs {
+        u32x4 r;
+    };
+    __device__ __forceinline__ static VRegs load_v_unit(const float* Vh, int c0, int L, int u) {
+        VRegs x;
+        x.r = load_k_chunk(Vh, c0, L, u);
+        return x;
+    }
+    __device__ __forceinline__ static void store_v_unit(float* Vt, int u, const VRegs& x) {
+        const int key = u / (D / 4), ch = u % (D / 4);
+        *reinterpret_cast<u32x4*>(Vt + key * kVRow + ch * 4) = x.r;
+    }
+
+    struct OAcc {
+        f32x16 o[D / 32][2];
+    };
+
+    __device__ __forceinline__ static void pv(OAcc& oa, const float* Vt, const f32x16 (&a4)[2][2], const bool (&on)[2]) {
+        const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (!on[kb]) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kb * 32 + key_of_reg(r, h);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const float va = Vt[key * kVRow + db * 32 + m];
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        oa.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, a4[kb][qb][r], oa.o[db][qb], 0, 0, 0);
+                }
+            }
+        }
+    }
+};
+
+// Set masked elements of a partial tile to -inf (select, no branches).
+__device__ __forceinline__ void apply_mask(f32x16 (&acc)[2][2], int J, int R0, const Geom& g) {
+    const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int i = R0 + qb * 32 + m;
+            f32x16 a = acc[kb][qb];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = J * kBC + kb * 32 + key_of_reg(r, h);
+                a[r] = key_active(i, j, g) ? a[r] : neg_inf();
+            }
+            acc[kb][qb] = a;
+        }
+}
+
+// Work item -> (bh, first row).  Items of one q-block rank are consecutive
+// across heads, so the 8 XCDs (blocks dealt round-robin) each see a few
+// heads; causal runs take the longest rows first.
+__device__ __forceinline__ void decode_item(int item, int BH, int nQ, bool heavy_first, int& bh, int& r0) {
+    bh = item % BH;
+    const int qi = item / BH;
+    r0 = (heavy_first ? (nQ - 1 - qi) : qi) * kBR;
+}
+
+}  // namespace attn
+}  // namespace entmax

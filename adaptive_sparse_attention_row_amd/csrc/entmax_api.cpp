@@ -1,0 +1,147 @@
+// entmax_api.cpp -- the exported C ABI: argument validation, then launches.
+// Declarations and the contract of every entry point are in include/entmax.h.
+#include "../../include/entmax.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ENTMAX_OK : ENTMAX_ERR_HIP; }
+
+int g_cand_cap = 0;  // 0: the compiled default
+
+// Shared checks of the attention entry points (everything except pointers).
+int check_attn_shape(int B, int H, int L, int d, float alpha, int dtype, int mask, int window) {
+    if (alpha != 1.5f) return ENTMAX_ERR_ALPHA;
+    if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return ENTMAX_ERR_DTYPE;
+    if (mask != ENTMAX_MASK_NONE && mask != ENTMAX_MASK_CAUSAL &&
+        mask != ENTMAX_MASK_CAUSAL_WINDOW_SINK)
+        return ENTMAX_ERR_MASK;
+    if (mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK && window < 0) return ENTMAX_ERR_MASK;
+    if (B < 1 || H < 1 || L < 1 || (d != 64 && d != 128)) return ENTMAX_ERR_SHAPE;
+    if ((int64_t)B * H > 0x7fffffffLL || L > (1 << 16) ||
+        (int64_t)B * H * L * d > (int64_t)1 << 40)
+        return ENTMAX_ERR_SHAPE;
+    return ENTMAX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* entmax_status_str(int status) {
+    switch (status) {
+        case ENTMAX_OK: return "ok";
+        case ENTMAX_ERR_NULL: return "null pointer argument";
+        case ENTMAX_ERR_SHAPE: return "unsupported or inconsistent shape";
+        case ENTMAX_ERR_ALPHA: return "alpha must be 1.5";
+        case ENTMAX_ERR_DTYPE: return "unknown dtype";
+        case ENTMAX_ERR_MASK: return "unknown mask mode or negative window";
+        case ENTMAX_ERR_WORKSPACE: return "workspace missing or too small";
+        case ENTMAX_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case ENTMAX_ERR_HIP: return "HIP launch failed";
+        case ENTMAX_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+int entmax_version(void) { return (1 << 16) | 0; }
+
+int entmax_tile_shape(int d, int dtype, int* block_rows, int* block_cols) {
+    if (block_rows == nullptr || block_cols == nullptr) return ENTMAX_ERR_NULL;
+    if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return ENTMAX_ERR_DTYPE;
+    if (d != 64 && d != 128) return ENTMAX_ERR_SHAPE;
+    *block_rows = entmax::kMaskBr;
+    *block_cols = entmax::kMaskBc;
+    return ENTMAX_OK;
+}
+
+int entmax_set_option(int option, int value) {
+    if (option != ENTMAX_OPT_CANDIDATE_CAP) return -ENTMAX_ERR_ARG;
+    const int maxcap = entmax::attn_max_candidate_cap(64, ENTMAX_BF16);
+    if (value > maxcap) return -ENTMAX_ERR_ARG;
+    const int prev = g_cand_cap;
+    g_cand_cap = value > 0 ? value : 0;
+    return prev;
+}
+
+int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
+                    int64_t ld, float alpha, void* stream) {
+    if (alpha != 1.5f) return ENTMAX_ERR_ALPHA;
+    if (rows < 0 || cols < 1 || ld < cols || rows > 0x7fffffffLL || cols > 0x7fffffffLL)
+        return ENTMAX_ERR_SHAPE;
+    if (rows == 0) return ENTMAX_OK;
+    if (S == nullptr || tau == nullptr) return ENTMAX_ERR_NULL;
+    (void)hipGetLastError();
+    return hip_status(entmax::launch_tau_rows(S, P, tau, rows, cols, ld, (hipStream_t)stream));
+}
+
+size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask, int window) {
+    if (check_attn_shape(B, H, L, d, 1.5f, dtype, mask, window) != ENTMAX_OK) return 0;
+    return entmax::attn_fwd_workspace_bytes(B, H, L, d, dtype);
+}
+
+int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float* tau,
+                    uint32_t* block_mask, int B, int H, int L, int d, float scale, float alpha,
+                    int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr || tau == nullptr)
+        return ENTMAX_ERR_NULL;
+    int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
+    if (st != ENTMAX_OK) return st;
+    if (!(scale > 0.0f) || !isfinite(scale)) return ENTMAX_ERR_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ENTMAX_ERR_ALIGN;
+    if (((uintptr_t)tau & 3u) || ((uintptr_t)block_mask & 3u)) return ENTMAX_ERR_ALIGN;
+    const size_t need = entmax::attn_fwd_workspace_bytes(B, H, L, d, dtype);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ENTMAX_ERR_WORKSPACE;
+    entmax::AttnArgs a = {};
+    a.q = Q; a.k = K; a.v = V; a.o = O; a.tau = tau; a.block_mask = block_mask;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
+    a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
+    const int maxcap = entmax::attn_max_candidate_cap(d, dtype);
+    a.cand_cap = (g_cand_cap > 0 && g_cand_cap < maxcap) ? g_cand_cap : maxcap;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    (void)hipGetLastError();
+    return hip_status(entmax::launch_attn_fwd(a, (hipStream_t)stream));
+}
+
+size_t entmax_attn_bwd_workspace(int B, int H, int L, int d, int dtype, int mask, int window) {
+    if (check_attn_shape(B, H, L, d, 1.5f, dtype, mask, window) != ENTMAX_OK) return 0;
+    return entmax::attn_bwd_workspace_bytes(B, H, L, d, dtype);
+}
+
+int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
+                    const float* tau, const uint32_t* block_mask, float* dQ, float* dK,
+                    float* dV, int B, int H, int L, int d, float scale, float alpha, int dtype,
+                    int mask, int window, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    if (Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || tau == nullptr ||
+        block_mask == nullptr || dQ == nullptr || dK == nullptr || dV == nullptr)
+        return ENTMAX_ERR_NULL;
+    int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
+    if (st != ENTMAX_OK) return st;
+    if (!(scale > 0.0f) || !isfinite(scale)) return ENTMAX_ERR_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) ||
+        !aligned16(dK) || !aligned16(dV))
+        return ENTMAX_ERR_ALIGN;
+    if (((uintptr_t)tau & 3u) || ((uintptr_t)block_mask & 3u)) return ENTMAX_ERR_ALIGN;
+    const size_t need = entmax::attn_bwd_workspace_bytes(B, H, L, d, dtype);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ENTMAX_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return ENTMAX_ERR_ALIGN;
+    entmax::AttnArgs a = {};
+    a.q = Q; a.k = K; a.v = V; a.dout = dO; a.tau = const_cast<float*>(tau);
+    a.block_mask = const_cast<uint32_t*>(block_mask);
+    a.dq = dQ; a.dk = dK; a.dv = dV;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
+    a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    (void)hipGetLastError();
+    return hip_status(entmax::launch_attn_bwd(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// launch.hpp -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace entmax {
+
+hipError_t launch_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
+                           int64_t ld, hipStream_t stream);
+
+// Arguments of one attention call after validation.
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;      // backward only
+    float* o;              // forward only
+    float* tau;            // forward writes, backward reads
+    uint32_t* block_mask;  // forward writes (may be null); backward reads
+    float* dq;
+    float* dk;
+    float* dv;
+    int B, H, L, d;
+    float scale;
+    int dtype;  // 0 fp32, 1 bf16
+    int mask;   // 0 none, 1 causal, 2 causal window + sink
+    int window;
+    int cand_cap;  // forward candidate capacity per row
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+// Block-mask tile (rows x cols) of the forward.
+constexpr int kMaskBr = 64;
+constexpr int kMaskBc = 64;
+
+size_t attn_fwd_workspace_bytes(int B, int H, int L, int d, int dtype);
+size_t attn_bwd_workspace_bytes(int B, int H, int L, int d, int dtype);
+int attn_max_candidate_cap(int d, int dtype);
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace entmax

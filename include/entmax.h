@@ -1,0 +1,168 @@
+/*
+ * entmax.h -- C ABI of libentmax.so: 1.5-entmax attention with a per-row
+ * threshold on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (score units throughout):
+ *   S_ij  = scale * Q_i . K_j                  for active keys j of row i
+ *   tau_i : sum_j [(S_ij - tau_i)/2]_+^2 = 1    (unique; the row normaliser)
+ *   A_ij  = [(S_ij - tau_i)/2]_+^2              (exact zeros where S_ij <= tau_i)
+ *   O_i   = sum_j A_ij V_j
+ * Sources: "GPT-2 with AdaSplash Attention via NeuralOps", Mathematical
+ * Formulation items 1-2 (threshold equation, masking); "AdaSplash-2: Faster
+ * Differentiable Sparse Attention", sec. 2.2 (S = QK^T/sqrt(d), O = pi(S)V),
+ * sec. 2.3-2.4 (alpha-entmax and its normaliser; written there as
+ * [(alpha-1)s - tau']_+^(1/(alpha-1)), which is this map with tau = 2 tau'
+ * for alpha = 1.5), sec. 3.3 (block mask, output over non-null blocks,
+ * backward on the support).
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument is DEVICE memory owned by the caller; the library
+ *    never allocates, frees, or reads device data on the host.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *    is the null stream).  Nothing synchronises.
+ *  - Arguments are validated before any launch; on any error nothing is
+ *    launched and no output is touched.  A failed launch returns
+ *    ENTMAX_ERR_HIP (the HIP error is consumed).
+ *  - alpha must be 1.5f; other values return ENTMAX_ERR_ALPHA.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - The library keeps no per-call state; concurrent calls on different
+ *    streams are safe when their outputs and workspaces are disjoint.
+ */
+#ifndef ENTMAX_H
+#define ENTMAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    ENTMAX_OK = 0,
+    ENTMAX_ERR_NULL = 1,      /* a required pointer is NULL */
+    ENTMAX_ERR_SHAPE = 2,     /* unsupported or inconsistent size */
+    ENTMAX_ERR_ALPHA = 3,     /* alpha != 1.5 */
+    ENTMAX_ERR_DTYPE = 4,     /* unknown dtype code */
+    ENTMAX_ERR_MASK = 5,      /* unknown mask mode, or window < 0 in mode 2 */
+    ENTMAX_ERR_WORKSPACE = 6, /* workspace missing or too small */
+    ENTMAX_ERR_ALIGN = 7,     /* a pointer is not 16-byte aligned */
+    ENTMAX_ERR_HIP = 8,       /* a HIP launch failed */
+    ENTMAX_ERR_ARG = 9        /* other invalid argument (scale, option) */
+};
+
+/* Mask modes (0-indexed positions i = query, j = key).
+ *  ENTMAX_MASK_NONE:  every key.
+ *  ENTMAX_MASK_CAUSAL: j <= i.
+ *  ENTMAX_MASK_CAUSAL_WINDOW_SINK: j <= i and (j == 0 or i - j <= window):
+ *    the sink token 0 plus the keys at most `window` positions behind the
+ *    query ("GPT-2 with AdaSplash Attention via NeuralOps", Mathematical
+ *    Formulation item 1, active set {0} U [max(1, i - W), i]). */
+enum { ENTMAX_MASK_NONE = 0, ENTMAX_MASK_CAUSAL = 1, ENTMAX_MASK_CAUSAL_WINDOW_SINK = 2 };
+
+/* Element type of Q, K, V and dO.  O, tau and all gradients are fp32. */
+enum { ENTMAX_F32 = 0, ENTMAX_BF16 = 1 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* entmax_status_str(int status);
+
+/* ABI version, (major << 16) | minor. */
+int entmax_version(void);
+
+/*
+ * Granularity of the block mask written by entmax_attn_fwd: row blocks of
+ * *block_rows queries by column blocks of *block_cols keys (the B_r x B_c
+ * tiles of AdaSplash-2 appendix C.1).  Returns ENTMAX_ERR_SHAPE for an
+ * unsupported d, ENTMAX_ERR_DTYPE for an unknown dtype, ENTMAX_ERR_NULL for
+ * NULL outputs.
+ */
+int entmax_tile_shape(int d, int dtype, int* block_rows, int* block_cols);
+
+/*
+ * Row-wise 1.5-entmax of a materialised fp32 score matrix.
+ *   S    [rows][ld] fp32, row r's scores are S[r*ld + 0 .. cols-1]; -inf
+ *        entries are inactive (p = 0, not counted in the row).
+ *   P    [rows][ld] fp32 output (same layout as S) or NULL for tau only.
+ *        P may not overlap S.
+ *   tau  [rows] fp32 output, score units; -inf for a row with no finite
+ *        entry (its P row is all zero).
+ * Requires rows >= 0, 1 <= cols <= ld.  rows == 0 is a no-op (any pointer
+ * may then be NULL); otherwise S and tau must be non-NULL.
+ * The threshold solve is the hybrid Halley-bisection of "AdaSplash: Adaptive
+ * Sparse Flash Attention" (summary, Approach) on the bracket
+ * [max - 2, max - 2/sqrt(n)] of AdaSplash-2 sec. 2.4 (scaled to score units),
+ * restricted to the scores above max - 2, with an exact finish once the
+ * support is known.  NaN inputs give unspecified results.
+ */
+int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
+                    int64_t ld, float alpha, void* stream);
+
+/*
+ * Workspace bytes entmax_attn_fwd needs for this problem (0 if none).
+ * Returns 0 for invalid arguments too; entmax_attn_fwd reports those.
+ */
+size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask,
+                                 int window);
+
+/*
+ * 1.5-entmax attention forward (AdaSplash-2 sec. 3.3, phases: score sweep,
+ * threshold, block mask, output over non-null blocks only).
+ *   Q, K, V    [B][H][L][d] of `dtype`, contiguous, 16-byte aligned.
+ *   O          [B][H][L][d] fp32 output.
+ *   tau        [B][H][L] fp32 output, score units.
+ *   block_mask optional output (NULL to skip): uint32
+ *              [B][H][ceil(L/br)][ceil(ceil(L/bc)/32)] with (br, bc) from
+ *              entmax_tile_shape; bit (J % 32) of word J/32 of row block I is
+ *              set iff some query of block I has a key of block J with
+ *              A > 0 (AdaSplash-2 appendix C.4 packing).
+ *   scale > 0 multiplies Q.K (e.g. 1/sqrt(d)).
+ *   d in {64, 128}; B, H >= 1; 1 <= L <= 65536 (per-row tile tables are
+ *   kept on chip); otherwise ENTMAX_ERR_SHAPE.
+ *   workspace  at least entmax_attn_fwd_workspace(...) bytes; it holds the
+ *              block mask when block_mask is NULL.
+ */
+int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float* tau,
+                    uint32_t* block_mask, int B, int H, int L, int d, float scale,
+                    float alpha, int dtype, int mask, int window, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes entmax_attn_bwd needs (per-row statistics).
+ */
+size_t entmax_attn_bwd_workspace(int B, int H, int L, int d, int dtype, int mask,
+                                 int window);
+
+/*
+ * 1.5-entmax attention backward, restricted to the support (AdaSplash-2
+ * sec. 3.3 "Backward pass" and appendix C.6): with g = [(S - tau)/2]_+,
+ *   dA_ij = dO_i . V_j,  delta_i = sum_j g_ij dA_ij / sum_j g_ij,
+ *   dS_ij = g_ij (dA_ij - delta_i),
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = A^T dO.
+ *   Q, K, V, dO  [B][H][L][d] of `dtype`; tau and block_mask exactly as
+ *   written by entmax_attn_fwd for the same Q, K, V, scale, mask, window.
+ *   dQ, dK, dV   [B][H][L][d] fp32 outputs (overwritten).
+ *   workspace    at least entmax_attn_bwd_workspace(...) bytes.
+ */
+int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
+                    const float* tau, const uint32_t* block_mask, float* dQ, float* dK,
+                    float* dV, int B, int H, int L, int d, float scale, float alpha,
+                    int dtype, int mask, int window, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Process-wide tuning / testing options (not thread-safe; set before use).
+ *  ENTMAX_OPT_CANDIDATE_CAP: per-row capacity of the forward's candidate
+ *    buffer, 1 .. the compiled maximum (value <= 0 restores the default).
+ *    Rows with more candidates take the iterative full-sweep path; tests use
+ *    a tiny cap to force that path.
+ * Returns the previous value, or -ENTMAX_ERR_ARG for an unknown option or an
+ * out-of-range value.
+ */
+enum { ENTMAX_OPT_CANDIDATE_CAP = 1 };
+int entmax_set_option(int option, int value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTMAX_H */

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/entmax.h declares, and rejects bad arguments before any launch (the
+pointers used here are never dereferenced: validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "entmax.h")
+LIB = os.path.join(ROOT, "adaptive_sparse_attention_row_amd", "libentmax.so")
+
+FAKE = 4096  # non-null, 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(entmax_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not os.path.exists(LIB):
+        pytest.fail("libentmax.so is not built (run __graft_entry__.build())")
+    from adaptive_sparse_attention_row_amd import api as a
+    a.lib()
+    return a
+
+
+def test_header_symbols_exported(api):
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(api):
+    for s in range(10):
+        assert api.status_str(s) and api.status_str(s) != "unknown status"
+    assert api.status_str(99) == "unknown status"
+
+
+def test_tile_shape(api):
+    assert api.tile_shape(64, api.BF16) == (64, 64)
+    assert api.tile_shape(128, api.F32) == (64, 64)
+    L = api.lib()
+    br, bc = ctypes.c_int(), ctypes.c_int()
+    assert L.entmax_tile_shape(96, 1, ctypes.byref(br), ctypes.byref(bc)) == api.ERR_SHAPE
+    assert L.entmax_tile_shape(64, 7, ctypes.byref(br), ctypes.byref(bc)) == api.ERR_DTYPE
+    assert L.entmax_tile_shape(64, 1, None, ctypes.byref(bc)) == api.ERR_NULL
+
+
+def test_tau_rows_validation(api):
+    L = api.lib()
+    f = L.entmax_tau_rows
+    assert f(None, None, FAKE, 4, 8, 8, 1.5, None) == api.ERR_NULL
+    assert f(FAKE, None, None, 4, 8, 8, 1.5, None) == api.ERR_NULL
+    assert f(FAKE, None, FAKE, 4, 8, 8, 2.0, None) == api.ERR_ALPHA
+    assert f(FAKE, None, FAKE, -1, 8, 8, 1.5, None) == api.ERR_SHAPE
+    assert f(FAKE, None, FAKE, 4, 0, 8, 1.5, None) == api.ERR_SHAPE
+    assert f(FAKE, None, FAKE, 4, 9, 8, 1.5, None) == api.ERR_SHAPE
+    assert f(None, None, None, 0, 8, 8, 1.5, None) == api.OK   # empty: no-op
+
+
+def fwd(L, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, tau=FAKE, bm=FAKE, B=1, H=1, Ls=128, d=64,
+             scale=0.125, alpha=1.5, dtype=1, mask=0, window=0, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return L.entmax_attn_fwd(a["Q"], a["K"], a["V"], a["O"], a["tau"], a["bm"], a["B"], a["H"],
+                             a["Ls"], a["d"], a["scale"], a["alpha"], a["dtype"], a["mask"],
+                             a["window"], a["ws"], a["wsb"], None)
+
+
+def test_attn_fwd_validation(api):
+    L = api.lib()
+    assert fwd(L, Q=None) == api.ERR_NULL
+    assert fwd(L, tau=None) == api.ERR_NULL
+    assert fwd(L, alpha=2.0) == api.ERR_ALPHA
+    assert fwd(L, dtype=5) == api.ERR_DTYPE
+    assert fwd(L, mask=3) == api.ERR_MASK
+    assert fwd(L, mask=2, window=-1) == api.ERR_MASK
+    assert fwd(L, d=96) == api.ERR_SHAPE
+    assert fwd(L, Ls=0) == api.ERR_SHAPE
+    assert fwd(L, Ls=65537) == api.ERR_SHAPE
+    assert fwd(L, B=0) == api.ERR_SHAPE
+    assert fwd(L, scale=0.0) == api.ERR_ARG
+    assert fwd(L, scale=float("nan")) == api.ERR_ARG
+    assert fwd(L, Q=FAKE + 4) == api.ERR_ALIGN
+    assert fwd(L, O=FAKE + 8) == api.ERR_ALIGN
+    need = L.entmax_attn_fwd_workspace(1, 1, 128, 64, 1, 0, 0)
+    assert need > 0
+    assert fwd(L, ws=None) == api.ERR_WORKSPACE
+    assert fwd(L, wsb=need - 1) == api.ERR_WORKSPACE
+    assert L.entmax_attn_fwd_workspace(1, 1, 128, 96, 1, 0, 0) == 0
+
+
+def test_attn_bwd_validation(api):
+    L = api.lib()
+    f = L.entmax_attn_bwd
+    need = L.entmax_attn_bwd_workspace(1, 2, 100, 64, 1, 1, 0)
+    assert need >= 2 * 100 * 4
+    base = [FAKE] * 9 + [1, 2, 100, 64, 0.125, 1.5, 1, 1, 0, FAKE, need, None]
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == api.ERR_NULL      # Q
+    assert call(5, None) == api.ERR_NULL      # block mask
+    assert call(8, None) == api.ERR_NULL      # dV
+    assert call(14, 1.0) == api.ERR_ALPHA
+    assert call(15, 9) == api.ERR_DTYPE
+    assert call(16, 4) == api.ERR_MASK
+    assert call(12, 32) == api.ERR_SHAPE
+    assert call(13, -1.0) == api.ERR_ARG
+    assert call(18, None) == api.ERR_WORKSPACE
+    assert call(19, need - 1) == api.ERR_WORKSPACE
+    assert call(6, FAKE + 4) == api.ERR_ALIGN
+
+
+def test_set_option(api):
+    prev = api.set_option(api.OPT_CANDIDATE_CAP, 5)
+    assert api.set_option(api.OPT_CANDIDATE_CAP, 0) == 5
+    assert api.set_option(api.OPT_CANDIDATE_CAP, prev) == 0
+    with pytest.raises(api.EntmaxError):
+        api.set_option(99, 1)
+    with pytest.raises(api.EntmaxError):
+        api.set_option(api.OPT_CANDIDATE_CAP, 1 << 20)

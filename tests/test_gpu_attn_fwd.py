@@ -1,0 +1,227 @@
+"""GPU parity of entmax_attn_fwd against the fp64 oracle.
+
+Acceptance: |dtau| <= 1e-4 * max(1, |tau|); max |dO| <= 2e-3 for bf16 inputs
+and <= 1e-5 for fp32 inputs; the block mask contains every 64x64 tile with a
+weight clearly above zero (s - tau > 1e-4) and no tile whose scores all lie
+at or below tau - 1e-4 (ties inside the band may go either way).
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+TAU_TOL = 1e-4
+O_TOL = {"bf16": 2e-3, "f32": 1e-5}
+BAND = 1e-4
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from adaptive_sparse_attention_row_amd import api
+    assert torch.cuda.is_available()
+    api.lib()
+    return api, torch
+
+
+def run_gpu(api, torch, inp, scale, mode, W, want_mask=True):
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    O, tau, bm = api.attn_fwd(q, k, v, scale=scale, mask=mode, window=W, want_block_mask=want_mask)
+    torch.cuda.synchronize()
+    return O.cpu().numpy(), tau.cpu().numpy(), (bm.cpu().numpy().view(np.uint32) if bm is not None else None)
+
+
+def np32(t):
+    return t.float().numpy()
+
+
+def check_rows(orc, inp, scale, mode, W, O, tau, dtype, rows=None, label=""):
+    Q, K, V = np32(inp["q"]), np32(inp["k"]), np32(inp["v"])
+    B, H, L, d = Q.shape
+    O_ref, tau_ref, _, _ = orc.attn_fwd(Q, K, V, scale, mode, W, rows=rows)
+    Of = O.reshape(-1, d)
+    tf = tau.reshape(-1)
+    if rows is not None:
+        Of, tf = Of[rows], tf[rows]
+    dt = np.abs(tf - tau_ref)
+    assert np.all(dt <= TAU_TOL * np.maximum(1.0, np.abs(tau_ref))), f"{label} tau max err {dt.max()}"
+    err = np.abs(Of - O_ref).max()
+    assert err <= O_TOL[dtype], f"{label} O max err {err}"
+    return err
+
+
+def check_mask(orc, inp, scale, mode, W, bm, heads, label=""):
+    Q, K = np32(inp["q"]), np32(inp["k"])
+    B, H, L, d = Q.shape
+    Qf, Kf = Q.reshape(B * H, L, d), K.reshape(B * H, L, d)
+    bmf = bm.reshape(B * H, bm.shape[2], bm.shape[3])
+    for bh in heads:
+        ex, lo, hi, _ = orc.block_mask_head(Qf[bh], Kf[bh], scale, mode, W, 64, 64, tol=BAND)
+        g = bmf[bh]
+        assert np.all((lo & ~g) == 0), f"{label} head {bh}: missing non-null tiles"
+        assert np.all((g & ~hi) == 0), f"{label} head {bh}: extra tiles"
+
+
+def gen(B, H, L, d, dtype, seed, clusters=0, q_std=1.0):
+    from adaptive_sparse_attention_row_amd.workloads import gen_attn
+    return gen_attn(B, H, L, d, dtype, seed, clusters=clusters, q_std=q_std)
+
+
+SHAPES = [
+    # (B, H, L, d, dtype)
+    (1, 2, 1, 64, "bf16"),
+    (1, 2, 2, 64, "bf16"),
+    (2, 1, 63, 64, "bf16"),
+    (1, 2, 65, 128, "bf16"),
+    (1, 1, 127, 64, "f32"),
+    (1, 2, 129, 64, "bf16"),
+    (1, 1, 200, 128, "f32"),
+    (2, 2, 257, 64, "bf16"),
+    (1, 2, 1000, 128, "bf16"),
+    (1, 1, 640, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dH%dL%dd%d%s" % s)
+@pytest.mark.parametrize("mode,W", [(0, 0), (1, 0), (2, 5), (2, 32)], ids=["none", "causal", "win5", "win32"])
+def test_shapes_and_masks(env, orc, shape, mode, W):
+    api, torch = env
+    B, H, L, d, dtype = shape
+    inp = gen(B, H, L, d, dtype, seed=L * 7 + d + mode)
+    scale = 1.0 / math.sqrt(d)
+    print(f"shape={shape} mode={mode} W={W}", flush=True)
+    O, tau, bm = run_gpu(api, torch, inp, scale, mode, W)
+    check_rows(orc, inp, scale, mode, W, O, tau, dtype, label=str(shape))
+    check_mask(orc, inp, scale, mode, W, bm, range(B * H), label=str(shape))
+
+
+def test_c1_full(env, orc):
+    """L = 256, d = 64, fp32, non-causal, every row."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C1, gen_config
+    inp = gen_config(C1)
+    O, tau, bm = run_gpu(api, torch, inp, C1.scale, C1.mask, C1.window)
+    err = check_rows(orc, inp, C1.scale, C1.mask, C1.window, O, tau, "f32", label="c1")
+    check_mask(orc, inp, C1.scale, C1.mask, C1.window, bm, [0], label="c1")
+    print(f"c1 max |dO| = {err:.3e}")
+
+
+@pytest.mark.parametrize("cfgname", ["c3a", "c3b"])
+def test_c3_full(env, orc, cfgname):
+    """B8 H12 L1024 d64 bf16, causal and window 32 + sink, every row."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C3A, C3B, gen_config
+    cfg = C3A if cfgname == "c3a" else C3B
+    inp = gen_config(cfg)
+    O, tau, bm = run_gpu(api, torch, inp, cfg.scale, cfg.mask, cfg.window)
+    err = check_rows(orc, inp, cfg.scale, cfg.mask, cfg.window, O, tau, "bf16", label=cfgname)
+    check_mask(orc, inp, cfg.scale, cfg.mask, cfg.window, bm, [0, 17, 95], label=cfgname)
+    print(f"{cfgname} max |dO| = {err:.3e}")
+
+
+def test_c4_two_heads_full(env, orc):
+    """Clustered L = 8192 (two of the twelve heads): every row, full mask."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C4, gen_config
+    inp = gen_config(C4, H=2)
+    O, tau, bm = run_gpu(api, torch, inp, C4.scale, C4.mask, C4.window)
+    err = check_rows(orc, inp, C4.scale, C4.mask, C4.window, O, tau, "bf16", label="c4h2")
+    check_mask(orc, inp, C4.scale, C4.mask, C4.window, bm, [0, 1], label="c4h2")
+    nnz = sum(bin(int(x)).count("1") for x in bm.reshape(-1))
+    print(f"c4 (2 heads) max |dO| = {err:.3e}, block sparsity {1 - nnz / (2 * 128 * 128):.4f}")
+
+
+def test_c4_full_size_sampled(env, orc):
+    """All twelve heads of the clustered L = 8192 workload; sampled rows."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C4, gen_config
+    inp = gen_config(C4)
+    O, tau, bm = run_gpu(api, torch, inp, C4.scale, C4.mask, C4.window)
+    L = C4.L
+    rng = np.random.default_rng(0)
+    rows = []
+    for bh in range(C4.B * C4.H):
+        pick = np.concatenate([[0, 1, 127, 128, L - 1], rng.integers(0, L, 60)])
+        rows.extend(bh * L + pick)
+    rows = np.array(rows)
+    err = check_rows(orc, inp, C4.scale, C4.mask, C4.window, O, tau, "bf16", rows=rows, label="c4")
+    check_mask(orc, inp, C4.scale, C4.mask, C4.window, bm, [5], label="c4")
+    print(f"c4 sampled max |dO| = {err:.3e}")
+
+
+def test_c5_forward_sampled(env, orc):
+    """B1 H16 L16384 d128 causal: sampled rows of every head."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C5, gen_config
+    inp = gen_config(C5)
+    O, tau, bm = run_gpu(api, torch, inp, C5.scale, C5.mask, C5.window)
+    L = C5.L
+    rng = np.random.default_rng(1)
+    rows = []
+    for bh in range(C5.B * C5.H):
+        pick = np.concatenate([[0, 1, 63, 64, 127, 128, L - 1], rng.integers(0, L, 24)])
+        rows.extend(bh * L + pick)
+    rows = np.array(rows)
+    err = check_rows(orc, inp, C5.scale, C5.mask, C5.window, O, tau, "bf16", rows=rows, label="c5")
+    print(f"c5 sampled max |dO| = {err:.3e}")
+
+
+def test_degenerate_rows(env, orc):
+    """All-equal scores (every key in the support, so the candidate lists
+    overflow and the fallback sweeps run), and one-hot rows."""
+    api, torch = env
+    import torch as T
+    B, H, L, d = 1, 2, 700, 64
+    inp = gen(B, H, L, d, "bf16", seed=9)
+    inp["q"][0, 0] = 0            # head 0: all scores 0 -> uniform weights
+    # head 1: each query aligned with its own key far above the rest
+    k1 = T.randn(L, d)
+    inp["k"][0, 1] = k1.to(T.bfloat16)
+    inp["q"][0, 1] = (8.0 * k1).to(T.bfloat16)
+    for mode, W in ((0, 0), (1, 0), (2, 3)):
+        O, tau, bm = run_gpu(api, torch, inp, 1.0 / 8, mode, W)
+        check_rows(orc, inp, 1.0 / 8, mode, W, O, tau, "bf16", label=f"degenerate mode {mode}")
+        check_mask(orc, inp, 1.0 / 8, mode, W, bm, [0, 1], label=f"degenerate mode {mode}")
+
+
+@pytest.mark.parametrize("cap", [1, 3])
+def test_forced_fallback(env, orc, cap):
+    """A tiny candidate capacity sends every row with more candidates than
+    `cap` through the iterative full-sweep path."""
+    api, torch = env
+    prev = api.set_option(api.OPT_CANDIDATE_CAP, cap)
+    try:
+        for (B, H, L, d, dtype, mode, W) in ((1, 2, 300, 64, "bf16", 1, 0), (1, 1, 200, 128, "bf16", 0, 0),
+                                            (1, 1, 130, 64, "f32", 2, 7)):
+            inp = gen(B, H, L, d, dtype, seed=cap * 100 + L)
+            O, tau, bm = run_gpu(api, torch, inp, 1.0 / math.sqrt(d), mode, W)
+            check_rows(orc, inp, 1.0 / math.sqrt(d), mode, W, O, tau, dtype, label=f"fallback cap={cap}")
+            check_mask(orc, inp, 1.0 / math.sqrt(d), mode, W, bm, range(B * H), label=f"fallback cap={cap}")
+    finally:
+        api.set_option(api.OPT_CANDIDATE_CAP, prev)
+
+
+def test_no_mask_output_and_window_extremes(env, orc):
+    api, torch = env
+    inp = gen(1, 2, 300, 64, "bf16", seed=11)
+    # block_mask = NULL (the library keeps it in the workspace)
+    O, tau, bm = run_gpu(api, torch, inp, 0.125, 1, 0, want_mask=False)
+    assert bm is None
+    check_rows(orc, inp, 0.125, 1, 0, O, tau, "bf16", label="no mask")
+    # W = 0: sink + self only; W >= L: plain causal
+    for W in (0, 1, 299, 10 ** 6):
+        O, tau, bm = run_gpu(api, torch, inp, 0.125, 2, W)
+        check_rows(orc, inp, 0.125, 2, W, O, tau, "bf16", label=f"W={W}")
+        check_mask(orc, inp, 0.125, 2, W, bm, [0, 1], label=f"W={W}")
+
+
+def test_scale_and_query_spread(env, orc):
+    """Large and small score spreads (very sparse and nearly dense rows)."""
+    api, torch = env
+    for q_std, scale in ((4.0, 0.125), (0.05, 0.125), (1.0, 1.0)):
+        inp = gen(1, 2, 513, 64, "bf16", seed=int(q_std * 100), q_std=q_std)
+        O, tau, bm = run_gpu(api, torch, inp, scale, 0, 0)
+        check_rows(orc, inp, scale, 0, 0, O, tau, "bf16", label=f"q_std={q_std}")
+        check_mask(orc, inp, scale, 0, 0, bm, [0, 1], label=f"q_std={q_std}")

@@ -1,0 +1,135 @@
+"""GPU parity of entmax_tau_rows against the fp64 oracle.
+
+Tolerances (from the acceptance bar on tau and the support): |dtau| <=
+1e-4 * max(1, |tau|); the support {P > 0} equals {S > tau_ref} except where
+|S - tau_ref| < 1e-4; |dP| <= 1e-4 (|dp/dtau| = sqrt(p) <= 1, so the tau bound
+carries over) and every row of P sums to 1 within 1e-4.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+TAU_TOL = 1e-4
+P_TOL = 1e-4
+BAND = 1e-4
+
+
+def _check(S_np, tau_gpu, P_gpu, orc, label=""):
+    tau_ref, P_ref = orc.tau_rows(S_np, want_p=True)
+    S64 = S_np.astype(np.float64)
+    finite_rows = np.isfinite(tau_ref)
+    assert np.array_equal(np.isfinite(tau_gpu), finite_rows), label
+    dt = np.abs(tau_gpu[finite_rows] - tau_ref[finite_rows])
+    assert np.all(dt <= TAU_TOL * np.maximum(1.0, np.abs(tau_ref[finite_rows]))), \
+        f"{label} max dtau {dt.max()}"
+    if P_gpu is None:
+        return
+    assert np.max(np.abs(P_gpu - P_ref)) <= P_TOL, f"{label} max dP {np.max(np.abs(P_gpu - P_ref))}"
+    sup_ref = S64 > tau_ref[:, None]
+    sup_gpu = P_gpu > 0
+    far = np.abs(S64 - tau_ref[:, None]) >= BAND
+    assert np.array_equal(sup_ref & far, sup_gpu & far), label
+    sums = P_gpu.astype(np.float64).sum(1)
+    assert np.all(np.abs(sums[finite_rows] - 1.0) <= 1e-4), label
+    assert np.all(P_gpu[~finite_rows] == 0), label
+
+
+def _run(api, torch, S_np, want_p=True, ld=None):
+    rows, cols = S_np.shape
+    if ld is None or ld == cols:
+        S = torch.from_numpy(S_np).cuda()
+    else:
+        big = torch.zeros(rows, ld, dtype=torch.float32)
+        big[:, :cols] = torch.from_numpy(S_np)
+        S = big.cuda()[:, :cols]
+    tau, P = api.tau_rows(S, want_p=want_p)
+    torch.cuda.synchronize()
+    return tau.cpu().numpy(), (P.cpu().numpy() if P is not None else None)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from adaptive_sparse_attention_row_amd import api
+    assert torch.cuda.is_available()
+    api.lib()
+    return api, torch
+
+
+@pytest.mark.parametrize("cols", [1, 2, 3, 63, 64, 65, 257, 1000, 1024, 1025, 4096, 8191,
+                                  8192, 8193, 20000])
+def test_widths(env, orc, cols):
+    api, torch = env
+    rng = np.random.default_rng(cols)
+    S = rng.normal(size=(37, cols)).astype(np.float32) * rng.uniform(0.2, 3.0)
+    tau, P = _run(api, torch, S)
+    print(f"cols={cols}", flush=True)
+    _check(S, tau, P, orc, f"cols={cols}")
+
+
+@pytest.mark.parametrize("cols,ld", [(100, 104), (100, 101), (5000, 5003), (9000, 9001)])
+def test_row_stride_and_alignment(env, orc, cols, ld):
+    api, torch = env
+    rng = np.random.default_rng(ld)
+    S = rng.normal(size=(19, cols)).astype(np.float32)
+    tau, P = _run(api, torch, S, ld=ld)
+    _check(S, tau, P, orc, f"cols={cols} ld={ld}")
+
+
+def test_tau_only(env, orc):
+    api, torch = env
+    S = np.random.default_rng(5).normal(size=(50, 700)).astype(np.float32)
+    tau, P = _run(api, torch, S, want_p=False)
+    assert P is None
+    _check(S, tau, None, orc, "tau only")
+
+
+def test_degenerate_rows(env, orc):
+    api, torch = env
+    cols = 3000
+    rng = np.random.default_rng(6)
+    S = rng.normal(size=(8, cols)).astype(np.float32)
+    S[0] = 1.25                                  # all equal: p = 1/n
+    S[1] = -np.inf; S[1, 17] = 4.0               # single active entry
+    S[2] = rng.normal(size=cols) - 10; S[2, 5] = 3.0  # one-hot (gap > 2)
+    S[3] = -np.inf                               # no active entry
+    S[4, ::2] = -np.inf                          # half masked
+    S[5] = np.linspace(-1, 1, cols)              # every score a candidate
+    S[6] = 0.0; S[6, :7] = 1e-3                  # near-ties
+    S[7] = rng.normal(size=cols) * 1e-3          # all within 2 of the max
+    tau, P = _run(api, torch, S)
+    _check(S, tau, P, orc, "degenerate")
+    np.testing.assert_allclose(P[0], 1.0 / cols, rtol=1e-4)
+    assert P[1, 17] == 1.0 and np.sum(P[1] > 0) == 1
+    assert P[2, 5] == 1.0 and np.sum(P[2] > 0) == 1
+    assert tau[3] == -np.inf and np.all(P[3] == 0)
+
+
+def test_overflowing_candidates(env, orc):
+    # more than the LDS candidate capacity within 2 of the max, register and
+    # streamed rows both
+    api, torch = env
+    rng = np.random.default_rng(7)
+    for cols in (8192, 12000):
+        S = (rng.normal(size=(6, cols)) * 0.05).astype(np.float32)
+        tau, P = _run(api, torch, S)
+        _check(S, tau, P, orc, f"overflow cols={cols}")
+
+
+def test_zero_rows(env):
+    api, torch = env
+    S = torch.empty(0, 10, device="cuda")
+    tau, P = api.tau_rows(S)
+    assert tau.numel() == 0
+
+
+def test_full_size_c2(env, orc):
+    """The 8192 x 8192 N(0, 1) workload, every row and every element."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C2, gen_rows
+    S = gen_rows(C2.rows, C2.cols, C2.seed)
+    print("c2 generated", flush=True)
+    tau, P = api.tau_rows(S.cuda())
+    torch.cuda.synchronize()
+    _check(S.numpy(), tau.cpu().numpy(), P.cpu().numpy(), orc, "c2")
