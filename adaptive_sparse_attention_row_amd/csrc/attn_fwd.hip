@@ -666,12 +666,17 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
 }
 
 template <typename T, int D>
-hipError_t launch_typed(const FwdParams& fp, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_tau_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fwd_out_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
-    return hipGetLastError();
+hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t stream) {
+    if (phase & 1) {
+        hipLaunchKernelGGL((fwd_tau_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (phase & 2) {
+        hipLaunchKernelGGL((fwd_out_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 size_t mask_bytes(int B, int H, int L) {
@@ -692,7 +697,7 @@ int attn_max_candidate_cap(int d, int dtype) {
     return attn::FwdCfg<__bf16, 128>::kCap;
 }
 
-hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream) {
     using namespace attn;
     if (a.L > kMaxL) return hipErrorInvalidValue;
     FwdParams fp;
@@ -707,11 +712,11 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     fp.cap = a.cand_cap;
     const int grid = fp.nQ * fp.BH;
     if (a.dtype == 1) {
-        if (a.d == 64) return launch_typed<__bf16, 64>(fp, grid, stream);
-        return launch_typed<__bf16, 128>(fp, grid, stream);
+        if (a.d == 64) return launch_typed<__bf16, 64>(fp, grid, phase, stream);
+        return launch_typed<__bf16, 128>(fp, grid, phase, stream);
     }
-    if (a.d == 64) return launch_typed<float, 64>(fp, grid, stream);
-    return launch_typed<float, 128>(fp, grid, stream);
+    if (a.d == 64) return launch_typed<float, 64>(fp, grid, phase, stream);
+    return launch_typed<float, 128>(fp, grid, phase, stream);
 }
 
 }  // namespace entmax

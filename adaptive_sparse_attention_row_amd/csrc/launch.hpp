@@ -39,7 +39,8 @@ constexpr int kMaskBc = 64;
 size_t attn_fwd_workspace_bytes(int B, int H, int L, int d, int dtype);
 size_t attn_bwd_workspace_bytes(int B, int H, int L, int d, int dtype);
 int attn_max_candidate_cap(int d, int dtype);
-hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+// phase: 1 = threshold + mask, 2 = output, 3 = both
+hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace entmax

@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the 1.5-entmax attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A timed step is one full forward (threshold + block mask + sparse output) of
+the long-context workload: B=1, H=12, L=8192, d=64, bf16, 64 clustered
+centroids, no mask.  The metric is its effective (dense-equivalent)
+throughput, 4*d*pairs / time.  The same run also times, each with HIP events
+on the stream the library launches on:
+  * the threshold kernel alone (the dominant kernel: one dense MFMA score
+    sweep, 2*d*pairs FLOP) -> the `roofline` object;
+  * the row-wise tau kernel on the 8192 x 8192 fp32 score matrix (HBM-bound;
+    3 rotating buffer sets so the 256 MB Infinity Cache cannot serve it);
+  * the other forward workloads and the backward, when built;
+and the fp64 CPU oracle on a bounded sample of the same workload
+(`cpu_baseline`).  Rank 0 prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "1.5-entmax attn fwd ms + effective TFLOP/s at L=8192; tau-row kernel GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+THRESH_SOURCES = ["adaptive_sparse_attention_row_amd/csrc/attn_fwd.hip",
+                  "adaptive_sparse_attention_row_amd/csrc/attn_common.hpp",
+                  "adaptive_sparse_attention_row_amd/csrc/device_common.hpp"]
+TAUROWS_SOURCES = ["adaptive_sparse_attention_row_amd/csrc/tau_rows.hip",
+                   "adaptive_sparse_attention_row_amd/csrc/device_common.hpp"]
+
+
+def counter_traffic(name, sources):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, valid
+    only while the kernel sources are unchanged."""
+    path = os.path.join(ROOT, "profiles", f"{name}.counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest(sources):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP-event timing of a callable over K launches on torch's current stream
+    (the stream the library is handed)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per call
+
+
+def pairs_of(cfg):
+    L = cfg.L
+    if cfg.mask == 0:
+        per = L * L
+    elif cfg.mask == 1:
+        per = L * (L + 1) // 2
+    else:
+        W = cfg.window
+        per = sum(min(i + 1, W + 1) + (1 if i > W else 0) for i in range(L))
+    return cfg.B * cfg.H * per
+
+
+def popcount_mask(bm):
+    import numpy as np
+    x = bm.view(np.uint32).reshape(-1)
+    return int(np.unpackbits(x.view(np.uint8)).sum())
+
+
+def structural_tiles(cfg):
+    from adaptive_sparse_attention_row_amd.workloads import MASK_NONE
+    T = -(-cfg.L // 64)
+    n = 0
+    for I in range(T):
+        i0, i1 = I * 64, min(I * 64 + 63, cfg.L - 1)
+        for J in range(T):
+            c0, c1 = J * 64, min(J * 64 + 63, cfg.L - 1)
+            if cfg.mask == MASK_NONE:
+                n += 1
+            elif c0 > i1:
+                continue
+            elif cfg.mask == 1:
+                n += 1
+            elif J == 0 or i0 - c1 <= cfg.window:
+                n += 1
+    return n * cfg.B * cfg.H
+
+
+def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False):
+    """Forward (and backward) timing of one attention workload."""
+    from adaptive_sparse_attention_row_amd.workloads import gen_config
+    inp = gen_config(cfg)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    B, H, L, d = q.shape
+    dt = api._dtype_code(q)
+    O = torch.empty(B, H, L, d, device="cuda", dtype=torch.float32)
+    tau = torch.empty(B, H, L, device="cuda", dtype=torch.float32)
+    bm = torch.empty(api.mask_shape(B, H, L, d, dt), device="cuda", dtype=torch.int32)
+    lib = api.lib()
+    sc, st = float(cfg.scale), api._stream(q.device)
+
+    def fwd():
+        r = lib.entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(), tau.data_ptr(),
+                                bm.data_ptr(), B, H, L, d, sc, 1.5, dt, cfg.mask, cfg.window, None, 0, st)
+        assert r == 0, api.status_str(r)
+
+    def thr():
+        r = lib.entmax_attn_threshold(q.data_ptr(), k.data_ptr(), tau.data_ptr(), bm.data_ptr(), B, H, L, d,
+                                      sc, 1.5, dt, cfg.mask, cfg.window, st)
+        assert r == 0, api.status_str(r)
+
+    def out():
+        r = lib.entmax_attn_output(q.data_ptr(), k.data_ptr(), v.data_ptr(), tau.data_ptr(), bm.data_ptr(),
+                                   O.data_ptr(), B, H, L, d, sc, 1.5, dt, cfg.mask, cfg.window, st)
+        assert r == 0, api.status_str(r)
+
+    t_fwd = timer(fwd, steps, warmup)
+    t_thr = timer(thr, steps, warmup)
+    t_out = timer(out, steps, warmup)
+    torch.cuda.synchronize()
+    nnz = popcount_mask(bm.cpu().numpy())
+    struct = structural_tiles(cfg)
+    pairs = pairs_of(cfg)
+    res = {
+        "fwd_ms": round(t_fwd, 5),
+        "threshold_ms": round(t_thr, 5),
+        "output_ms": round(t_out, 5),
+        "dense_equiv_tflops": round(4 * d * pairs / (t_fwd * 1e-3) / 1e12, 3),
+        "threshold_mfma_tflops": round(2 * d * pairs / (t_thr * 1e-3) / 1e12, 3),
+        "nonnull_tiles_64": nnz,
+        "structural_tiles_64": struct,
+        "block_sparsity_64": round(1.0 - nnz / struct, 5),
+        "pairs": pairs,
+    }
+    if with_bwd:
+        do = inp["do"].cuda()
+        dq = torch.empty_like(O); dk = torch.empty_like(O); dv = torch.empty_like(O)
+        wsb = lib.entmax_attn_bwd_workspace(B, H, L, d, dt, cfg.mask, cfg.window)
+        ws = torch.empty(max(wsb, 1), device="cuda", dtype=torch.uint8)
+        fwd()
+
+        def bwd():
+            r = lib.entmax_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), tau.data_ptr(),
+                                    bm.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d,
+                                    sc, 1.5, dt, cfg.mask, cfg.window, ws.data_ptr(), wsb, st)
+            if r != 0:
+                raise RuntimeError(api.status_str(r))
+
+        try:
+            t_bwd = timer(bwd, max(1, steps // 2), 1)
+            res["bwd_ms"] = round(t_bwd, 5)
+            res["bwd_dense_equiv_tflops"] = round(10 * d * pairs / (t_bwd * 1e-3) / 1e12, 3)
+        except RuntimeError as e:
+            res["bwd"] = f"not available: {e}"
+    del q, k, v, O
+    torch.cuda.empty_cache()
+    return res, (t_fwd, t_thr, t_out)
+
+
+def bench_tau_rows(api, torch, timer, steps, warmup):
+    from adaptive_sparse_attention_row_amd.workloads import C2, gen_rows
+    S0 = gen_rows(C2.rows, C2.cols, C2.seed).cuda()
+    sets = [S0] + [S0.roll(i + 1, 0).contiguous() for i in range(2)]
+    Ps = [torch.empty_like(S0) for _ in range(3)]
+    taus = [torch.empty(C2.rows, device="cuda") for _ in range(3)]
+    lib = api.lib()
+    st = api._stream(S0.device)
+    it = [0]
+
+    def run():
+        i = it[0] % 3
+        it[0] += 1
+        r = lib.entmax_tau_rows(sets[i].data_ptr(), Ps[i].data_ptr(), taus[i].data_ptr(), C2.rows, C2.cols,
+                                C2.cols, 1.5, st)
+        assert r == 0, api.status_str(r)
+
+    t = timer(run, max(steps, 30), warmup)
+    algo_bytes = 4 * C2.rows * C2.cols * 2 + 4 * C2.rows
+    gbs = algo_bytes / (t * 1e-3) / 1e9
+    del sets, Ps, taus, S0
+    torch.cuda.empty_cache()
+    return {
+        "workload": C2.name,
+        "ms": round(t, 5),
+        "algorithmic_bytes": algo_bytes,
+        "GB_per_s": round(gbs, 1),
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": counter_traffic("tau_rows_c2", TAUROWS_SOURCES),
+        },
+    }
+
+
+def cpu_baseline(cfg, target_s=15.0):
+    """The fp64 oracle on evenly spaced query rows of the same workload."""
+    import numpy as np
+    import oracle
+    from adaptive_sparse_attention_row_amd.workloads import gen_config
+    oracle.build(force=False)
+    inp = gen_config(cfg)
+    Q, K, V = (inp[n].float().numpy() for n in ("q", "k", "v"))
+    total = cfg.B * cfg.H * cfg.L
+    probe = np.linspace(0, total - 1, 256).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(Q, K, V, cfg.scale, cfg.mask, cfg.window, rows=probe)
+    per_row = (time.perf_counter() - t0) / probe.size
+    n = int(min(total, max(256, target_s / max(per_row, 1e-9))))
+    rows = np.linspace(0, total - 1, n).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(Q, K, V, cfg.scale, cfg.mask, cfg.window, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4 * cfg.d * n * cfg.L  # dense-equivalent, same accounting as the GPU line
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {total} query rows (evenly spaced over all heads) of {cfg.name}, "
+                  f"fp64 exact tau + dense A.V, {dt:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is described in DESIGN.md, not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from adaptive_sparse_attention_row_amd import api
+    from adaptive_sparse_attention_row_amd.workloads import C3A, C3B, C4, C5
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    api.lib()
+    timer = Timer(torch)
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    t_wall0 = time.perf_counter()
+    head, (t_fwd, t_thr, t_out) = bench_attn(api, torch, timer, C4, args.steps, args.warmup)
+    log(f"c4 fwd {head['fwd_ms']:.4f} ms  threshold {t_thr:.4f} ms  output {t_out:.4f} ms  "
+        f"{head['dense_equiv_tflops']} TFLOP/s dense-eq, block sparsity {head['block_sparsity_64']}")
+
+    d, pairs = C4.d, head["pairs"]
+    achieved = 2 * d * pairs / (t_thr * 1e-3) / 1e12
+    roofline = {
+        "kernel": "fwd_tau (threshold: MFMA score sweep + candidate sweep + exact tau + mask)",
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": counter_traffic("fwd_tau_c4", THRESH_SOURCES),
+        "algorithmic_flop_per_launch": 2 * d * pairs,
+    }
+
+    extras = {}
+    if not args.no_extras:
+        extras["c2_tau_rows"] = bench_tau_rows(api, torch, timer, args.steps, args.warmup)
+        log(f"c2 tau_rows {extras['c2_tau_rows']['ms']} ms {extras['c2_tau_rows']['GB_per_s']} GB/s")
+        for cfg in (C3A, C3B):
+            extras[cfg.name], _ = bench_attn(api, torch, timer, cfg, args.steps, args.warmup)
+            log(f"{cfg.name}: {extras[cfg.name]}")
+        extras[C5.name], _ = bench_attn(api, torch, timer, C5, max(2, args.steps // 4), 2, with_bwd=True)
+        log(f"{C5.name}: {extras[C5.name]}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(C4)
+        log(f"cpu baseline: {cpu}")
+
+    value = head["dense_equiv_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["fwd_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": C4.name, "B": C4.B, "H": C4.H, "L": C4.L, "d": C4.d, "mask": "none",
+                   "scale": C4.scale, "clusters": C4.clusters, "parallelism": "single GPU"},
+        "block_sparsity_64": head["block_sparsity_64"],
+        "c4_fwd": head,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "paths": extras,
+        "bench_wall_s": round(time.perf_counter() - t_wall0, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -98,8 +98,10 @@ int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t 
                     int64_t ld, float alpha, void* stream);
 
 /*
- * Workspace bytes entmax_attn_fwd needs for this problem (0 if none).
- * Returns 0 for invalid arguments too; entmax_attn_fwd reports those.
+ * Workspace bytes entmax_attn_fwd needs when it is called with
+ * block_mask == NULL (the mask is then kept in the workspace); with a
+ * block_mask output no workspace is needed.  Returns 0 for invalid arguments
+ * too; entmax_attn_fwd reports those.
  */
 size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask,
                                  int window);
@@ -118,13 +120,31 @@ size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask
  *   scale > 0 multiplies Q.K (e.g. 1/sqrt(d)).
  *   d in {64, 128}; B, H >= 1; 1 <= L <= 65536 (per-row tile tables are
  *   kept on chip); otherwise ENTMAX_ERR_SHAPE.
- *   workspace  at least entmax_attn_fwd_workspace(...) bytes; it holds the
- *              block mask when block_mask is NULL.
+ *   workspace  when block_mask is NULL: at least
+ *              entmax_attn_fwd_workspace(...) bytes, 4-byte aligned (it holds
+ *              the mask); otherwise ignored (may be NULL).
  */
 int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float* tau,
                     uint32_t* block_mask, int B, int H, int L, int d, float scale,
                     float alpha, int dtype, int mask, int window, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of entmax_attn_fwd, callable on their own (same argument
+ * rules; entmax_attn_fwd is exactly threshold followed by output).
+ *  entmax_attn_threshold: phases 1-3 of AdaSplash-2 sec. 3.3 -- writes tau
+ *    [B][H][L] and the packed block mask (required here, same layout as
+ *    above).  Needs no workspace.
+ *  entmax_attn_output: phase 4 -- given that tau and block mask, writes
+ *    O [B][H][L][d] fp32 from the non-null tiles only.
+ */
+int entmax_attn_threshold(const void* Q, const void* K, float* tau, uint32_t* block_mask,
+                          int B, int H, int L, int d, float scale, float alpha, int dtype,
+                          int mask, int window, void* stream);
+int entmax_attn_output(const void* Q, const void* K, const void* V, const float* tau,
+                       const uint32_t* block_mask, float* O, int B, int H, int L, int d,
+                       float scale, float alpha, int dtype, int mask, int window,
+                       void* stream);
 
 /*
  * Workspace bytes entmax_attn_bwd needs (per-row statistics).

@@ -92,8 +92,8 @@ def test_attn_fwd_validation(api):
     assert fwd(L, O=FAKE + 8) == api.ERR_ALIGN
     need = L.entmax_attn_fwd_workspace(1, 1, 128, 64, 1, 0, 0)
     assert need > 0
-    assert fwd(L, ws=None) == api.ERR_WORKSPACE
-    assert fwd(L, wsb=need - 1) == api.ERR_WORKSPACE
+    assert fwd(L, bm=None, ws=None) == api.ERR_WORKSPACE
+    assert fwd(L, bm=None, wsb=need - 1) == api.ERR_WORKSPACE
     assert L.entmax_attn_fwd_workspace(1, 1, 128, 96, 1, 0, 0) == 0
 
 
