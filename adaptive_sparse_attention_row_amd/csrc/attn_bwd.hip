@@ -1,8 +1,474 @@
-// attn_bwd.hip -- placeholder until the backward kernels land.
+// attn_bwd.hip -- 1.5-entmax attention backward on gfx950.
+//
+// With g = [(S - tau)/2]_+ (so A = g^2), the threshold's implicit derivative
+// gives, on the support only ("AdaSplash-2: Faster Differentiable Sparse
+// Attention", sec. 3.3 "Backward pass", appendix C.6):
+//   dA_ij = dO_i . V_j,   delta_i = sum_j g_ij dA_ij / sum_j g_ij,
+//   dS_ij = g_ij (dA_ij - delta_i),
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = A^T dO.
+// Both kernels walk the forward's block mask, so null 64x64 tiles cost
+// nothing (AdaSplash-2 uses M for dQ and its transpose for dK, dV).
+//
+// bwd_dq    one workgroup per 128 query rows (the forward's layout: lanes
+//           are queries).  Pass 1 over the row's non-null tiles: S^T = K Q^T
+//           and dA^T = V dO^T on MFMA, accumulating sum g dA and sum g per
+//           row -> delta (also written for the other kernel).  Pass 2:
+//           dS, then dQ^T += K^T dS^T on MFMA.
+// bwd_dkdv  one workgroup per 128 (d = 128) or 256 (d = 64) keys; lanes are
+//           keys.  For every query tile of the mask column: S = Q K^T and
+//           dA = dO V^T on MFMA, then dV^T += dO^T A and dK^T += Q^T dS.
+// Weights fed to MFMA (A, dS) are split into bf16 hi + lo; accumulation is
+// fp32; all gradients are written in fp32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_common.hpp"
+#include "device_common.hpp"
 #include "launch.hpp"
+
 namespace entmax {
-size_t attn_bwd_workspace_bytes(int B, int H, int L, int, int) {
-    return ((size_t)B * H * L * 2 * sizeof(float) + 255) & ~(size_t)255;
+namespace attn {
+namespace {
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* tau;
+    const uint32_t* mask;  // [BH][Tr64][Wd]
+    float* dq;
+    float* dk;
+    float* dv;
+    float* delta;  // workspace [BH][L]
+    int BH, L, mode, W, nQ, nKB, Tc, Tr64, Wd;
+    float scale;
+};
+
+// Stage one 64-row tile of X (rows r0 .., zero past L) into LDS, in the
+// score-operand layout or the PV-operand layout.
+template <typename T, int D>
+__device__ __forceinline__ void stage_score(T* dst, const T* Xh, int r0, int L) {
+    using O = Ops<T, D>;
+    constexpr int kIt = (O::kChunks + kNT - 1) / kNT;
+    u32x4 v[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+        const int c = threadIdx.x + i * kNT;
+        if (c < O::kChunks) v[i] = O::load_k_chunk(Xh, r0, L, c);
+    }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+        const int c = threadIdx.x + i * kNT;
+        if (c < O::kChunks) O::store_k_chunk(dst, c, v[i]);
+    }
 }
-hipError_t launch_attn_bwd(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+template <typename T, int D>
+__device__ __forceinline__ void stage_pv(T* dst, const T* Xh, int r0, int L) {
+    using O = Ops<T, D>;
+    constexpr int kIt = (O::kVUnits + kNT - 1) / kNT;
+    typename O::VRegs v[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+        const int u = threadIdx.x + i * kNT;
+        if (u < O::kVUnits) v[i] = O::load_v_unit(Xh, r0, L, u);
+    }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+        const int u = threadIdx.x + i * kNT;
+        if (u < O::kVUnits) O::store_v_unit(dst, u, v[i]);
+    }
+}
+
+template <class FlagsOf>
+__device__ __forceinline__ int build_list16(uint16_t* list, int n_items, FlagsOf flags_of) {
+    const int l = lane_id();
+    int n = 0;
+    for (int base = 0; base < n_items; base += kWave) {
+        const int J = base + l;
+        const int f = (J < n_items) ? flags_of(J) : 0;
+        const uint64_t b = __ballot(f != 0);
+        if (f) list[n + lanes_below(b)] = (uint16_t)(J | (f << 12));
+        n += __popcll(b);
+    }
+    return n;
+}
+
+// Tiles staged per step by the dQ kernel: 2 (one per key-parity wave pair),
+// or 1 when LDS cannot hold two (fp32, d = 128).
+template <typename T, int D>
+struct DqCfg {
+    static constexpr int kTps = (sizeof(T) == 4 && D == 128) ? 1 : 2;
+    static constexpr int kBlk = Ops<T, D>::kKTile > Ops<T, D>::kVTile ? Ops<T, D>::kKTile : Ops<T, D>::kVTile;
+};
+
+// ------------------------------------------------------------ dQ kernel
+template <typename T, int D>
+__global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
+    using O = Ops<T, D>;
+    constexpr int TPS = DqCfg<T, D>::kTps;
+    constexpr int BLK = DqCfg<T, D>::kBlk;
+    constexpr int kRed = 2 * 64 * (D + 4);
+    constexpr int kStage = TPS * 3 * BLK * (int)sizeof(T);
+    constexpr int kBytes = kStage > kRed * 4 ? kStage : kRed * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kBytes];
+    __shared__ uint16_t list[kMaxTc];
+    __shared__ uint32_t mw[2][kMaxTc / 32];
+    __shared__ float part[2][kBR][2];
+    __shared__ int nlist_s;
+    T* lds = reinterpret_cast<T*>(smem);
+
+    const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
+    const int l = lane_id(), m = l & 31, h = l >> 5;
+    int bh, r0;
+    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    const int R0 = r0 + 64 * qh;
+    const Geom g = {p.L, p.mode, p.W};
+    const size_t head_off = (size_t)bh * p.L * D;
+    const T* Qh = reinterpret_cast<const T*>(p.q) + head_off;
+    const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
+    const T* Vh = reinterpret_cast<const T*>(p.v) + head_off;
+    const T* dOh = reinterpret_cast<const T*>(p.dout) + head_off;
+
+    for (int i = t; i < 2 * p.Wd; i += kNT) {
+        const int hh = i / p.Wd, wd = i % p.Wd;
+        const int I = r0 / 64 + hh;
+        mw[hh][wd] = (I < p.Tr64) ? p.mask[((size_t)bh * p.Tr64 + I) * p.Wd + wd] : 0u;
+    }
+    __syncthreads();
+    if (w == 0) {
+        const int n = build_list16(list, p.Tc, [&](int J) {
+            return (int)((mw[0][J >> 5] >> (J & 31)) & 1u) | (int)(((mw[1][J >> 5] >> (J & 31)) & 1u) << 1);
+        });
+        if (l == 0) nlist_s = n;
+    }
+    typename O::template QOp<2> qop, dop;
+    O::load_q(qop, Qh, R0, p.L);
+    O::load_q(dop, dOh, R0, p.L);
+    float tq[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int row = R0 + qb * 32 + m;
+        tq[qb] = (row < p.L) ? p.tau[(size_t)bh * p.L + row] : __builtin_inff();
+    }
+    __syncthreads();
+    const int n = nlist_s;
+
+    // Walk the list; fn(J, Kt, Vt, KPVt) for each tile flagged for this half.
+    auto walk = [&](auto fn) {
+        const int steps = (n + TPS - 1) / TPS;
+        for (int st = 0; st < steps; ++st) {
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < TPS; ++u) {
+                const int e = st * TPS + u;
+                const int J = (e < n) ? (list[e] & 0xfff) : 0;
+                const int c0 = (e < n) ? J * kBC : p.L;
+                T* base = lds + u * 3 * BLK;
+                stage_score<T, D>(base, Kh, c0, p.L);
+                stage_score<T, D>(base + BLK, Vh, c0, p.L);
+                stage_pv<T, D>(base + 2 * BLK, Kh, c0, p.L);
+            }
+            __syncthreads();
+            const int u = (TPS == 2) ? kh : 0;
+            const int e = st * TPS + u;
+            if (e >= n || (TPS == 1 && (st & 1) != kh)) continue;
+            const int ent = list[e];
+            if (!((ent >> (12 + qh)) & 1)) continue;
+            const int J = ent & 0xfff;
+            const int cls = tile_class(J, R0, g);
+            if (cls == kSkip) continue;
+            const T* base = lds + u * 3 * BLK;
+            fn(J, cls, base, base + BLK, base + 2 * BLK);
+        }
+        __syncthreads();
+    };
+
+    // ---- pass 1: delta_i = sum g dA / sum g  (2g used on both sides)
+    float num[2] = {0.f, 0.f}, den[2] = {0.f, 0.f};
+    walk([&](int J, int cls, const T* Kt, const T* Vt, const T*) {
+        f32x16 s[2][2], da[2][2];
+        O::scores(s, Kt, qop);
+        if (cls == kPartial) apply_mask(s, J, R0, g);
+        O::scores(da, Vt, dop);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float dd = fmaxf(s[kb][qb][r] * p.scale - tq[qb], 0.0f);
+                    num[qb] += dd * da[kb][qb][r];
+                    den[qb] += dd;
+                }
+    });
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        num[qb] += __shfl_xor(num[qb], 32, kWave);
+        den[qb] += __shfl_xor(den[qb], 32, kWave);
+        if (h == 0) {
+            part[kh][qh * 64 + qb * 32 + m][0] = num[qb];
+            part[kh][qh * 64 + qb * 32 + m][1] = den[qb];
+        }
+    }
+    __syncthreads();
+    float dl[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int rr = qh * 64 + qb * 32 + m;
+        const float nn = part[0][rr][0] + part[1][rr][0];
+        const float dn = part[0][rr][1] + part[1][rr][1];
+        dl[qb] = dn > 0.f ? nn / dn : 0.f;
+        const int row = r0 + rr;
+        if (kh == 0 && h == 0 && row < p.L) p.delta[(size_t)bh * p.L + row] = dl[qb];
+    }
+
+    // ---- pass 2: dQ^T += K^T (2 dS)^T
+    typename O::template OAcc<2> oa;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oa.o[db][qb][i] = 0.f;
+    walk([&](int J, int cls, const T* Kt, const T* Vt, const T* KPVt) {
+        f32x16 s[2][2], da[2][2];
+        O::scores(s, Kt, qop);
+        if (cls == kPartial) apply_mask(s, J, R0, g);
+        O::scores(da, Vt, dop);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float dd = fmaxf(s[kb][qb][r] * p.scale - tq[qb], 0.0f);
+                    s[kb][qb][r] = dd * (da[kb][qb][r] - dl[qb]);
+                }
+        const bool on[2] = {true, true};
+        O::pv(oa, KPVt, s, on);
+    });
+
+    float* red = reinterpret_cast<float*>(smem);
+    constexpr int kRS = D + 4;
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    f32x4 v4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v4[e] = oa.o[db][qb][4 * r4 + e];
+                    *reinterpret_cast<f32x4*>(red + (qh * 64 + qb * 32 + m) * kRS + db * 32 + 8 * r4 + 4 * h) = v4;
+                }
+    }
+    __syncthreads();
+    if (kh == 0) {
+        const float f = 0.5f * p.scale;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int q = qb * 32 + m;
+                const int row = R0 + q;
+                if (row >= p.L) continue;
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int d = db * 32 + 8 * r4 + 4 * h;
+                    const f32x4 o2 = *reinterpret_cast<const f32x4*>(red + (qh * 64 + q) * kRS + d);
+                    f32x4 v4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v4[e] = f * (oa.o[db][qb][4 * r4 + e] + o2[e]);
+                    *reinterpret_cast<f32x4*>(p.dq + ((size_t)bh * p.L + row) * D + d) = v4;
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------ dK/dV kernel
+template <typename T, int D>
+struct DkvCfg {
+    static constexpr int kNBK = (D == 64) ? 2 : 1;  // 32-key blocks per wave
+    static constexpr int kKW = 32 * kNBK;            // keys per wave
+    static constexpr int kKeys = 4 * kKW;            // keys per workgroup
+    static constexpr int kBlk = DqCfg<T, D>::kBlk;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
+    using O = Ops<T, D>;
+    constexpr int NBK = DkvCfg<T, D>::kNBK;
+    constexpr int KW = DkvCfg<T, D>::kKW;
+    constexpr int BLK = DkvCfg<T, D>::kBlk;
+    __shared__ __attribute__((aligned(16))) T lds[4 * BLK];
+    __shared__ uint16_t list[kMaxTc];
+    __shared__ float tau_s[64], del_s[64];
+    __shared__ int nlist_s;
+
+    const int t = threadIdx.x, w = t / kWave;
+    const int l = lane_id(), m = l & 31, h = l >> 5;
+    const int bh = blockIdx.x % p.BH;
+    const int c0 = (blockIdx.x / p.BH) * DkvCfg<T, D>::kKeys;
+    const int cw = c0 + w * KW;  // this wave's first key
+    const Geom g = {p.L, p.mode, p.W};
+    const size_t head_off = (size_t)bh * p.L * D;
+    const T* Qh = reinterpret_cast<const T*>(p.q) + head_off;
+    const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
+    const T* Vh = reinterpret_cast<const T*>(p.v) + head_off;
+    const T* dOh = reinterpret_cast<const T*>(p.dout) + head_off;
+    const uint32_t* Mh = p.mask + (size_t)bh * p.Tr64 * p.Wd;
+
+    // query tiles of the mask columns of the four waves' key tiles
+    if (w == 0) {
+        const int n = build_list16(list, p.Tr64, [&](int I) {
+            int f = 0;
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) {
+                const int cww = c0 + ww * KW;
+                if (cww < p.L) {
+                    const int J = cww / kBC;
+                    f |= (int)((Mh[(size_t)I * p.Wd + (J >> 5)] >> (J & 31)) & 1u) << ww;
+                }
+            }
+            return f;
+        });
+        if (l == 0) nlist_s = n;
+    }
+    typename O::template QOp<NBK> kop, vop;
+    O::load_q(kop, Kh, cw, p.L);
+    O::load_q(vop, Vh, cw, p.L);
+    typename O::template OAcc<NBK> dka, dva;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int cb = 0; cb < NBK; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                dka.o[db][cb][i] = 0.f;
+                dva.o[db][cb][i] = 0.f;
+            }
+    __syncthreads();
+    const int n = nlist_s;
+    T* Qt = lds;
+    T* dOt = lds + BLK;
+    T* QPVt = lds + 2 * BLK;
+    T* dOPVt = lds + 3 * BLK;
+
+    for (int e = 0; e < n; ++e) {
+        const int ent = list[e];
+        const int I = ent & 0xfff;
+        const int i0 = I * 64;
+        __syncthreads();
+        stage_score<T, D>(Qt, Qh, i0, p.L);
+        stage_score<T, D>(dOt, dOh, i0, p.L);
+        stage_pv<T, D>(QPVt, Qh, i0, p.L);
+        stage_pv<T, D>(dOPVt, dOh, i0, p.L);
+        if (t < 64) {
+            const int row = i0 + t;
+            tau_s[t] = (row < p.L) ? p.tau[(size_t)bh * p.L + row] : __builtin_inff();
+            del_s[t] = (row < p.L) ? p.delta[(size_t)bh * p.L + row] : 0.f;
+        }
+        __syncthreads();
+        if (!((ent >> (12 + w)) & 1)) continue;
+        const int cls = block_class(i0, 64, cw, KW, g);
+        if (cls == kSkip) continue;
+        f32x16 s[2][NBK], da[2][NBK];
+        O::scores(s, Qt, kop);   // rows: queries (registers), lanes: keys
+        if (cls == kPartial) apply_mask_rows_are_queries(s, i0, cw, g);
+        O::scores(da, dOt, vop);
+        f32x16 a4[2][NBK];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            float tr[16], dr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qi = kb * 32 + key_of_reg(r, h);
+                tr[r] = tau_s[qi];
+                dr[r] = del_s[qi];
+            }
+#pragma unroll
+            for (int cb = 0; cb < NBK; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float dd = fmaxf(s[kb][cb][r] * p.scale - tr[r], 0.0f);
+                    a4[kb][cb][r] = dd * dd;
+                    s[kb][cb][r] = dd * (da[kb][cb][r] - dr[r]);
+                }
+        }
+        const bool on[2] = {true, true};
+        O::pv(dva, dOPVt, a4, on);
+        O::pv(dka, QPVt, s, on);
+    }
+
+    const float fk = 0.5f * p.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int cb = 0; cb < NBK; ++cb) {
+            const int key = cw + cb * 32 + m;
+            if (key >= p.L) continue;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = db * 32 + 8 * r4 + 4 * h;
+                f32x4 k4, v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    k4[e] = fk * dka.o[db][cb][4 * r4 + e];
+                    v4[e] = 0.25f * dva.o[db][cb][4 * r4 + e];
+                }
+                *reinterpret_cast<f32x4*>(p.dk + ((size_t)bh * p.L + key) * D + d) = k4;
+                *reinterpret_cast<f32x4*>(p.dv + ((size_t)bh * p.L + key) * D + d) = v4;
+            }
+        }
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_typed(const BwdParams& bp, hipStream_t stream) {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace attn
+
+size_t attn_bwd_workspace_bytes(int B, int H, int L, int, int) {
+    return ((size_t)B * H * L * sizeof(float) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream) {
+    using namespace attn;
+    if (a.L > kMaxL) return hipErrorInvalidValue;
+    BwdParams bp;
+    bp.q = a.q; bp.k = a.k; bp.v = a.v; bp.dout = a.dout;
+    bp.tau = a.tau; bp.mask = a.block_mask;
+    bp.dq = a.dq; bp.dk = a.dk; bp.dv = a.dv;
+    bp.delta = reinterpret_cast<float*>(a.workspace);
+    bp.BH = a.B * a.H; bp.L = a.L; bp.mode = a.mask; bp.W = a.window;
+    bp.nQ = (a.L + kBR - 1) / kBR;
+    bp.Tc = (a.L + kBC - 1) / kBC;
+    bp.Tr64 = (a.L + 63) / 64;
+    bp.Wd = (bp.Tc + 31) / 32;
+    bp.scale = a.scale;
+    if (a.dtype == 1) {
+        if (a.d == 64) {
+            bp.nKB = (a.L + DkvCfg<__bf16, 64>::kKeys - 1) / DkvCfg<__bf16, 64>::kKeys;
+            return launch_bwd_typed<__bf16, 64>(bp, stream);
+        }
+        bp.nKB = (a.L + DkvCfg<__bf16, 128>::kKeys - 1) / DkvCfg<__bf16, 128>::kKeys;
+        return launch_bwd_typed<__bf16, 128>(bp, stream);
+    }
+    if (a.d == 64) {
+        bp.nKB = (a.L + DkvCfg<float, 64>::kKeys - 1) / DkvCfg<float, 64>::kKeys;
+        return launch_bwd_typed<float, 64>(bp, stream);
+    }
+    bp.nKB = (a.L + DkvCfg<float, 128>::kKeys - 1) / DkvCfg<float, 128>::kKeys;
+    return launch_bwd_typed<float, 128>(bp, stream);
+}
+
 }  // namespace entmax

@@ -75,32 +75,38 @@ struct Ops<__bf16, D> {
     static constexpr int kNS = D / 16;         // k-slices of a score block
     static constexpr int kChunks = kBC * D * kEsz / 16;  // 16-byte chunks per tile
 
+    // Register-resident MFMA operand for NB blocks of 32 rows (the rows
+    // that end up on the lanes of a score block).
+    template <int NB = 2>
     struct QOp {
-        bf16x8 q[2][kNS];
+        bf16x8 q[NB][kNS];
     };
 
-    // Q operand for the wave's 64 rows starting at R0 (zero beyond L).
-    __device__ __forceinline__ static void load_q(QOp& op, const __bf16* Qh, int R0, int L) {
+    // Operand rows R0 .. R0 + 32*NB - 1 of X (zero beyond L).
+    template <int NB>
+    __device__ __forceinline__ static void load_q(QOp<NB>& op, const __bf16* Xh, int R0, int L) {
         const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < NB; ++qb) {
             const int row = R0 + qb * 32 + m;
 #pragma unroll
             for (int s = 0; s < kNS; ++s) {
                 u32x4 v = {0u, 0u, 0u, 0u};
-                if (row < L) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)row * D + s * 16 + h * 8);
+                if (row < L) v = *reinterpret_cast<const u32x4*>(Xh + (size_t)row * D + s * 16 + h * 8);
                 op.q[qb][s] = __builtin_bit_cast(bf16x8, v);
             }
         }
     }
 
-    // acc[kb][qb] = K_tile[kb*32 + .., :] . Q[qb*32 + .., :]  (raw dot products)
-    __device__ __forceinline__ static void scores(f32x16 (&acc)[2][2], const __bf16* Kt, const QOp& op) {
+    // acc[kb][qb] = Tile[kb*32 + .., :] . Op[qb*32 + .., :]  (raw dot
+    // products; tile rows in registers, operand rows on lanes)
+    template <int NB>
+    __device__ __forceinline__ static void scores(f32x16 (&acc)[2][NB], const __bf16* Kt, const QOp<NB>& op) {
         const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[kb][qb][i] = 0.0f;
 #pragma unroll
@@ -110,7 +116,7 @@ struct Ops<__bf16, D> {
                 const bf16x8 k = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(Kt + (kb * 32 + m) * kKRow + s * 16 + h * 8));
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < NB; ++qb)
                     acc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, op.q[qb][s], acc[kb][qb], 0, 0, 0);
             }
         }
@@ -160,22 +166,27 @@ struct Ops<__bf16, D> {
         }
     }
 
+    template <int NB = 2>
     struct OAcc {
-        f32x16 o[D / 32][2];
+        f32x16 o[D / 32][NB];
     };
 
-    // O^T[d][q] += V^T[d][keys of block kb] . A^T, A given as 4*A per
-    // register (a4[kb][qb][r]), split into bf16 hi + lo.
-    __device__ __forceinline__ static void pv(OAcc& oa, const __bf16* Vt, const f32x16 (&a4)[2][2], const bool (&on)[2]) {
+    // O^T[d][c] += Vt^T[d][tile rows of block kb] . W[rows][c] for the NB
+    // operand blocks c: W arrives in score-block layout (tile rows in
+    // registers, columns on lanes) and is split into bf16 hi + lo.  Vt is the
+    // tile in PV layout (transposed, [d][row]).
+    template <int NB>
+    __device__ __forceinline__ static void pv(OAcc<NB>& oa, const __bf16* Vt, const f32x16 (&a4)[2][NB],
+                                              const bool (&on)[2]) {
         const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (!on[kb]) continue;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                bf16x8 bh[2], bl[2];
+                bf16x8 bh[NB], bl[NB];
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
+                for (int qb = 0; qb < NB; ++qb) {
 #pragma unroll
                     for (int p = 0; p < 8; ++p) {
                         const float a = a4[kb][qb][8 * t + p];
@@ -193,7 +204,7 @@ struct Ops<__bf16, D> {
                     vv[0] = lo4[0]; vv[1] = lo4[1]; vv[2] = hi4[0]; vv[3] = hi4[1];
                     const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
+                    for (int qb = 0; qb < NB; ++qb) {
                         oa.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bh[qb], oa.o[db][qb], 0, 0, 0);
                         oa.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bl[qb], oa.o[db][qb], 0, 0, 0);
                     }
@@ -213,26 +224,29 @@ struct Ops<float, D> {
     static constexpr int kVTile = kBC * kVRow;
     static constexpr int kChunks = kBC * D * kEsz / 16;
 
+    template <int NB = 2>
     struct QOp {
-        float q[2][D / 2];
+        float q[NB][D / 2];
     };
 
-    __device__ __forceinline__ static void load_q(QOp& op, const float* Qh, int R0, int L) {
+    template <int NB>
+    __device__ __forceinline__ static void load_q(QOp<NB>& op, const float* Xh, int R0, int L) {
         const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < NB; ++qb) {
             const int row = R0 + qb * 32 + m;
 #pragma unroll
-            for (int s = 0; s < D / 2; ++s) op.q[qb][s] = (row < L) ? Qh[(size_t)row * D + 2 * s + h] : 0.0f;
+            for (int s = 0; s < D / 2; ++s) op.q[qb][s] = (row < L) ? Xh[(size_t)row * D + 2 * s + h] : 0.0f;
         }
     }
 
-    __device__ __forceinline__ static void scores(f32x16 (&acc)[2][2], const float* Kt, const QOp& op) {
+    template <int NB>
+    __device__ __forceinline__ static void scores(f32x16 (&acc)[2][NB], const float* Kt, const QOp<NB>& op) {
         const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[kb][qb][i] = 0.0f;
 #pragma unroll
@@ -241,7 +255,7 @@ struct Ops<float, D> {
             for (int kb = 0; kb < 2; ++kb) {
                 const float k = Kt[(kb * 32 + m) * kKRow + 2 * s + h];
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < NB; ++qb)
                     acc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k, op.q[qb][s], acc[kb][qb], 0, 0, 0);
             }
         }
@@ -273,11 +287,15 @@ struct Ops<float, D> {
         *reinterpret_cast<u32x4*>(Vt + key * kVRow + ch * 4) = x.r;
     }
 
+    template <int NB = 2>
     struct OAcc {
-        f32x16 o[D / 32][2];
+        f32x16 o[D / 32][NB];
     };
 
-    __device__ __forceinline__ static void pv(OAcc& oa, const float* Vt, const f32x16 (&a4)[2][2], const bool (&on)[2]) {
+    // fp32: the PV layout is the natural [row][d] layout.
+    template <int NB>
+    __device__ __forceinline__ static void pv(OAcc<NB>& oa, const float* Vt, const f32x16 (&a4)[2][NB],
+                                              const bool (&on)[2]) {
         const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -289,7 +307,7 @@ struct Ops<float, D> {
                 for (int db = 0; db < D / 32; ++db) {
                     const float va = Vt[key * kVRow + db * 32 + m];
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
+                    for (int qb = 0; qb < NB; ++qb)
                         oa.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, a4[kb][qb][r], oa.o[db][qb], 0, 0, 0);
                 }
             }
@@ -312,6 +330,38 @@ __device__ __forceinline__ void apply_mask(f32x16 (&acc)[2][2], int J, int R0, c
                 a[r] = key_active(i, j, g) ? a[r] : neg_inf();
             }
             acc[kb][qb] = a;
+        }
+}
+
+// Class of the block rows [i0, i0 + ni) x keys [c0, c0 + nc) under the mask.
+__device__ __forceinline__ int block_class(int i0, int ni, int c0, int nc, const Geom& g) {
+    const int i1 = i0 + ni - 1, c1 = c0 + nc - 1;
+    if (c0 >= g.L || i0 >= g.L) return kSkip;
+    if (g.mode >= 1 && c0 > i1) return kSkip;
+    if (g.mode == 2 && c0 != 0 && i0 - c1 > g.W) return kSkip;
+    bool full = (c1 < g.L) && (i1 < g.L);
+    if (g.mode >= 1) full = full && (c1 <= i0);
+    if (g.mode == 2) full = full && (i1 - c0 <= g.W);
+    return full ? kFull : kPartial;
+}
+
+// Masking for score blocks whose tile rows (registers) are QUERIES and whose
+// lanes are KEYS: query = I0 + kb*32 + reg row, key = C0 + cb*32 + lane.
+template <int NB>
+__device__ __forceinline__ void apply_mask_rows_are_queries(f32x16 (&acc)[2][NB], int I0, int C0, const Geom& g) {
+    const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            const int j = C0 + cb * 32 + m;
+            f32x16 a = acc[kb][cb];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = I0 + kb * 32 + key_of_reg(r, h);
+                a[r] = key_active(i, j, g) ? a[r] : neg_inf();
+            }
+            acc[kb][cb] = a;
         }
 }
 

@@ -88,7 +88,7 @@ __device__ __forceinline__ int build_list(uint16_t* list, int Tc, FlagsOf flags_
 // flagged for this wave's row half.
 template <typename T, int D, int NBUF, bool WITH_V, class Fn>
 __device__ __forceinline__ void sweep(const uint16_t* list, int n, const T* Kh, const T* Vh, T* kbuf, T* vbuf,
-                      const typename Ops<T, D>::QOp& qop, int R0, const Geom& g, Fn fn) {
+                      const typename Ops<T, D>::template QOp<2>& qop, int R0, const Geom& g, Fn fn) {
     using O = Ops<T, D>;
     const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
     constexpr int kKPer = 2 * O::kChunks / kNT;                         // K chunks per thread per pair
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_tau_kernel(FwdParams p) {
     const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
     const int cap = p.cap < CAP ? p.cap : CAP;
 
-    typename O::QOp qop;
+    typename O::template QOp<2> qop;
     O::load_q(qop, Qh, R0, p.L);
 
     // ---- structural tile list; init tables
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
         });
         if (l == 0) nlist_s = n;
     }
-    typename O::QOp qop;
+    typename O::template QOp<2> qop;
     O::load_q(qop, Qh, R0, p.L);
     float tq[2];
 #pragma unroll
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
         const int row = R0 + qb * 32 + m;
         tq[qb] = (row < p.L) ? p.tau[(size_t)bh * p.L + row] : __builtin_inff();
     }
-    typename O::OAcc oa;
+    typename O::template OAcc<2> oa;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll

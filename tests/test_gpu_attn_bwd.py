@@ -1,0 +1,156 @@
+"""GPU parity of entmax_attn_bwd against the fp64 oracle.
+
+Acceptance per gradient tensor: max |d| / max |ref| <= 5e-3 (the relative
+bound on gradients); the relative Frobenius error is printed too.  The
+backward consumes the forward's tau and block mask, as its contract says.
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 5e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from adaptive_sparse_attention_row_amd import api
+    assert torch.cuda.is_available()
+    api.lib()
+    return api, torch
+
+
+def gpu_fwd_bwd(api, torch, inp, scale, mode, W):
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    O, tau, bm = api.attn_fwd(q, k, v, scale=scale, mask=mode, window=W)
+    dq, dk, dv = api.attn_bwd(q, k, v, do, tau, bm, scale=scale, mask=mode, window=W)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def rel(a, b):
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30)), \
+        float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def check_heads(orc, inp, scale, mode, W, dq, dk, dv, heads, label):
+    Q, K, V, dO = (inp[n].float().numpy() for n in ("q", "k", "v", "do"))
+    B, H, L, d = Q.shape
+    f = lambda x: x.reshape(B * H, L, d)
+    Q, K, V, dO, dq, dk, dv = map(f, (Q, K, V, dO, dq, dk, dv))
+    worst = 0.0
+    for bh in heads:
+        rq, rk, rv, _, _ = orc.attn_bwd_head(Q[bh], K[bh], V[bh], dO[bh], scale, mode, W)
+        for name, g, r in (("dQ", dq[bh], rq), ("dK", dk[bh], rk), ("dV", dv[bh], rv)):
+            mx, fro = rel(g, r)
+            worst = max(worst, mx)
+            assert mx <= GRAD_TOL, f"{label} head {bh} {name}: max rel {mx:.3e} (fro {fro:.3e})"
+    return worst
+
+
+def gen(B, H, L, d, dtype, seed, q_std=1.0):
+    from adaptive_sparse_attention_row_amd.workloads import gen_attn
+    return gen_attn(B, H, L, d, dtype, seed, with_grad=True, q_std=q_std)
+
+
+SHAPES = [
+    (1, 2, 1, 64, "bf16"),
+    (1, 1, 2, 64, "bf16"),
+    (2, 1, 63, 64, "bf16"),
+    (1, 2, 65, 128, "bf16"),
+    (1, 1, 127, 64, "f32"),
+    (1, 2, 130, 64, "bf16"),
+    (1, 1, 200, 128, "f32"),
+    (2, 2, 257, 64, "bf16"),
+    (1, 2, 700, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dH%dL%dd%d%s" % s)
+@pytest.mark.parametrize("mode,W", [(0, 0), (1, 0), (2, 5)], ids=["none", "causal", "win5"])
+def test_shapes_and_masks(env, orc, shape, mode, W):
+    api, torch = env
+    B, H, L, d, dtype = shape
+    inp = gen(B, H, L, d, dtype, seed=L * 3 + d + mode)
+    scale = 1.0 / math.sqrt(d)
+    print(f"bwd shape={shape} mode={mode}", flush=True)
+    dq, dk, dv = gpu_fwd_bwd(api, torch, inp, scale, mode, W)
+    check_heads(orc, inp, scale, mode, W, dq, dk, dv, range(B * H), str(shape))
+
+
+def test_c1_full(env, orc):
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C1
+    inp = gen(C1.B, C1.H, C1.L, C1.d, "f32", seed=C1.seed)
+    dq, dk, dv = gpu_fwd_bwd(api, torch, inp, C1.scale, C1.mask, C1.window)
+    w = check_heads(orc, inp, C1.scale, C1.mask, C1.window, dq, dk, dv, [0], "c1")
+    print(f"c1 bwd worst max-rel {w:.3e}")
+
+
+@pytest.mark.parametrize("mode,W", [(1, 0), (2, 32)], ids=["c3a", "c3b"])
+def test_c3_full(env, orc, mode, W):
+    """B8 H12 L1024 d64 bf16 with an upstream gradient: every head."""
+    api, torch = env
+    inp = gen(8, 12, 1024, 64, "bf16", seed=3)
+    dq, dk, dv = gpu_fwd_bwd(api, torch, inp, 0.125, mode, W)
+    w = check_heads(orc, inp, 0.125, mode, W, dq, dk, dv, range(96), f"c3 mode {mode}")
+    print(f"c3 mode {mode} bwd worst max-rel {w:.3e}")
+
+
+def test_c4_clustered_two_heads(env, orc):
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import gen_attn
+    inp = gen_attn(1, 2, 8192, 64, "bf16", 4, clusters=64, with_grad=True)
+    dq, dk, dv = gpu_fwd_bwd(api, torch, inp, 0.125, 0, 0)
+    w = check_heads(orc, inp, 0.125, 0, 0, dq, dk, dv, [0, 1], "c4")
+    print(f"c4 bwd worst max-rel {w:.3e}")
+
+
+def test_c5_full_size(env, orc):
+    """B1 H16 L16384 d128 causal: one whole head exactly, sampled dQ rows of
+    every head."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C5, gen_config
+    inp = gen_config(C5)
+    dq, dk, dv = gpu_fwd_bwd(api, torch, inp, C5.scale, C5.mask, C5.window)
+    print("c5 gpu done", flush=True)
+    w = check_heads(orc, inp, C5.scale, C5.mask, C5.window, dq, dk, dv, [7], "c5")
+    Q, K, V, dO = (inp[n].float().numpy() for n in ("q", "k", "v", "do"))
+    L = C5.L
+    rng = np.random.default_rng(2)
+    rows = np.concatenate([bh * L + np.concatenate([[0, 1, 64, L - 1], rng.integers(0, L, 12)])
+                           for bh in range(C5.H)])
+    rdq, _, _ = orc.attn_bwd_rows(Q, K, V, dO, C5.scale, C5.mask, C5.window, rows)
+    g = dq.reshape(-1, C5.d)[rows]
+    mx = np.abs(g - rdq).max() / np.abs(rdq).max()
+    assert mx <= GRAD_TOL, f"c5 sampled dQ max rel {mx:.3e}"
+    print(f"c5 bwd head-7 worst max-rel {w:.3e}, sampled dQ max-rel {mx:.3e}")
+
+
+def test_degenerate_and_fallback(env, orc):
+    """All-equal scores (support = every active key) and a forced fallback in
+    the forward feeding the backward."""
+    api, torch = env
+    import torch as T
+    inp = gen(1, 2, 300, 64, "bf16", seed=21)
+    inp["q"][0, 0] = 0
+    for mode, W in ((0, 0), (1, 0), (2, 4)):
+        dq, dk, dv = gpu_fwd_bwd(api, torch, inp, 0.125, mode, W)
+        check_heads(orc, inp, 0.125, mode, W, dq, dk, dv, [0, 1], f"degenerate mode {mode}")
+    prev = api.set_option(api.OPT_CANDIDATE_CAP, 2)
+    try:
+        dq, dk, dv = gpu_fwd_bwd(api, torch, inp, 0.125, 1, 0)
+        check_heads(orc, inp, 0.125, 1, 0, dq, dk, dv, [0, 1], "fallback")
+    finally:
+        api.set_option(api.OPT_CANDIDATE_CAP, prev)
+
+
+def test_sparse_rows(env, orc):
+    """Large score spread: very sparse supports (many null tiles)."""
+    api, torch = env
+    inp = gen(1, 2, 513, 64, "bf16", seed=31, q_std=4.0)
+    dq, dk, dv = gpu_fwd_bwd(api, torch, inp, 0.125, 0, 0)
+    check_heads(orc, inp, 0.125, 0, 0, dq, dk, dv, [0, 1], "sparse")
