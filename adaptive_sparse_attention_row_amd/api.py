@@ -58,7 +58,11 @@ def lib() -> ctypes.CDLL:
     L.entmax_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, f32, f32,
                                   i32, i32, i32, P, sz, P]
     L.entmax_attn_threshold.restype = i32
-    L.entmax_attn_threshold.argtypes = [P, P, P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P]
+    L.entmax_attn_threshold.argtypes = [P, P, P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P, sz, P]
+    L.entmax_attn_threshold_workspace.restype = sz
+    L.entmax_attn_threshold_workspace.argtypes = [i32] * 7
+    L.entmax_attn_score_stats.restype = i32
+    L.entmax_attn_score_stats.argtypes = [P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P, sz, P]
     L.entmax_attn_output.restype = i32
     L.entmax_attn_output.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P]
     L.entmax_set_option.restype = i32
@@ -151,8 +155,8 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, mask: int = MASK_NONE, wind
     bm = None
     if want_block_mask:
         bm = torch.empty(mask_shape(B, H, L, d, dt), device=q.device, dtype=torch.int32)
-    ws_bytes = 0 if want_block_mask else lib().entmax_attn_fwd_workspace(B, H, L, d, dt, mask, window)
-    ws = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8) if ws_bytes else None
+    ws_bytes = lib().entmax_attn_fwd_workspace(B, H, L, d, dt, mask, window)
+    ws = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
     st = lib().entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(),
                                tau.data_ptr(), _dev_ptr(bm), B, H, L, d, float(scale), 1.5, dt,
                                mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
@@ -161,7 +165,7 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, mask: int = MASK_NONE, wind
 
 
 def attn_threshold(q, k, scale: Optional[float] = None, mask: int = MASK_NONE, window: int = 0,
-                   tau=None, block_mask=None):
+                   tau=None, block_mask=None, workspace=None):
     """Phases 1-3 only: returns (tau fp32 [B, H, L], packed block mask)."""
     import torch
     B, H, L, d = q.shape
@@ -172,8 +176,12 @@ def attn_threshold(q, k, scale: Optional[float] = None, mask: int = MASK_NONE, w
         tau = torch.empty(B, H, L, device=q.device, dtype=torch.float32)
     if block_mask is None:
         block_mask = torch.empty(mask_shape(B, H, L, d, dt), device=q.device, dtype=torch.int32)
+    ws_bytes = lib().entmax_attn_threshold_workspace(B, H, L, d, dt, mask, window)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
     st = lib().entmax_attn_threshold(q.data_ptr(), k.data_ptr(), tau.data_ptr(), block_mask.data_ptr(),
-                                     B, H, L, d, float(scale), 1.5, dt, mask, window, _stream(q.device))
+                                     B, H, L, d, float(scale), 1.5, dt, mask, window,
+                                     workspace.data_ptr(), workspace.numel(), _stream(q.device))
     _check("entmax_attn_threshold", st)
     return tau, block_mask
 

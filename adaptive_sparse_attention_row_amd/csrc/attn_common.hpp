@@ -60,6 +60,19 @@ __device__ __forceinline__ bool key_active(int i, int j, const Geom& g) {
 // Key index (within a 32-key block) held by register r of lane half h.
 __device__ __forceinline__ int key_of_reg(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Natural-layout tiles in LDS are stored unpadded with the 16-byte chunks of
+// each row XOR-swizzled: chunk c of row r sits at position c ^ f(r).  With 8
+// chunks per row (bf16, d = 64) f(r) = (r & 7) ^ ((r >> 3) & 1); with 16 or
+// more, f(r) = r & 15.  Either way the 16-byte operand reads of 16
+// consecutive rows at one chunk hit distinct bank groups (32 or 64 banks),
+// and the layout can be filled by direct global->LDS loads, which write 64
+// consecutive 16-byte chunks per instruction.
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+    if constexpr (CPR == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
+    else return c ^ (r & 15);
+}
+
 // Element-type dependent pieces.
 template <typename T, int D>
 struct Ops;
@@ -68,7 +81,8 @@ struct Ops;
 template <int D>
 struct Ops<__bf16, D> {
     static constexpr int kEsz = 2;
-    static constexpr int kKRow = D + 8;        // K row stride in LDS (elements)
+    static constexpr int kCPR = D / 8;         // 16-byte chunks per row
+    static constexpr int kKRow = D;            // natural tile row stride (swizzled chunks)
     static constexpr int kVRow = kBC + 4;      // V^T row stride in LDS (elements)
     static constexpr int kKTile = kBC * kKRow; // elements per K tile
     static constexpr int kVTile = D * kVRow;   // elements per V^T tile
@@ -113,8 +127,9 @@ struct Ops<__bf16, D> {
         for (int s = 0; s < kNS; ++s) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
+                const int row = kb * 32 + m;
                 const bf16x8 k = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(Kt + (kb * 32 + m) * kKRow + s * 16 + h * 8));
+                    bf16x8, *reinterpret_cast<const u32x4*>(Kt + row * kKRow + swz<kCPR>(row, 2 * s + h) * 8));
 #pragma unroll
                 for (int qb = 0; qb < NB; ++qb)
                     acc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, op.q[qb][s], acc[kb][qb], 0, 0, 0);
@@ -131,7 +146,7 @@ struct Ops<__bf16, D> {
     }
     __device__ __forceinline__ static void store_k_chunk(__bf16* Kt, int c, u32x4 v) {
         const int key = c / (D / 8), ch = c % (D / 8);
-        *reinterpret_cast<u32x4*>(Kt + key * kKRow + ch * 8) = v;
+        *reinterpret_cast<u32x4*>(Kt + key * kKRow + swz<kCPR>(key, ch) * 8) = v;
     }
 
     // V tile transposed into LDS: V^T[d][key].  Unit u covers 4 keys x 8 d.
@@ -218,7 +233,8 @@ struct Ops<__bf16, D> {
 template <int D>
 struct Ops<float, D> {
     static constexpr int kEsz = 4;
-    static constexpr int kKRow = D + 4;
+    static constexpr int kCPR = D / 4;
+    static constexpr int kKRow = D;
     static constexpr int kVRow = D + 4;          // V kept in natural [key][d] layout
     static constexpr int kKTile = kBC * kKRow;
     static constexpr int kVTile = kBC * kVRow;
@@ -253,7 +269,8 @@ struct Ops<float, D> {
         for (int s = 0; s < D / 2; ++s) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const float k = Kt[(kb * 32 + m) * kKRow + 2 * s + h];
+                const int row = kb * 32 + m, e = 2 * s + h;
+                const float k = Kt[row * kKRow + swz<kCPR>(row, e >> 2) * 4 + (e & 3)];
 #pragma unroll
                 for (int qb = 0; qb < NB; ++qb)
                     acc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k, op.q[qb][s], acc[kb][qb], 0, 0, 0);
@@ -269,7 +286,7 @@ struct Ops<float, D> {
     }
     __device__ __forceinline__ static void store_k_chunk(float* Kt, int c, u32x4 v) {
         const int key = c / (D / 4), ch = c % (D / 4);
-        *reinterpret_cast<u32x4*>(Kt + key * kKRow + ch * 4) = v;
+        *reinterpret_cast<u32x4*>(Kt + key * kKRow + swz<kCPR>(key, ch) * 4) = v;
     }
 
     // V stays in natural layout: a unit is one 16-byte chunk.

@@ -36,12 +36,12 @@
 #include "attn_common.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "tile_dma.hpp"
 
 namespace entmax {
 namespace attn {
 namespace {
 
-constexpr int kTop = 8;        // tile maxima kept per row for tau_lo
 constexpr int kMaxIter = 40;   // solver iterations
 constexpr int kFbMaxIter = 60; // fallback sweeps
 
@@ -51,7 +51,9 @@ struct FwdParams {
     const void* v;
     float* o;
     float* tau;
-    uint32_t* mask;  // [BH][Tr64][Wd]
+    uint32_t* mask;   // [BH][Tr64][Wd]
+    float* rowstat;   // workspace [BH][L][2]: row max, tau_lo (score units)
+    float* umax;      // workspace [BH][Tr64][Tc]: largest raw score per (64-row block, tile)
     int BH, L, mode, W, nQ, Tc, Tr64, Wd;
     float scale;
     int cap;
@@ -175,6 +177,80 @@ __device__ __forceinline__ void sweep(const uint16_t* list, int n, const T* Kh, 
     __syncthreads();
 }
 
+// --------------------------------------------------------- DMA ring sweep
+// Stream the tiles of `list` in pairs (wave kh takes entry 2p + kh) through
+// an S-stage ring filled by direct global->LDS loads, keeping S - 1 pairs in
+// flight, and call fn(J, cls, acc) for every tile flagged for this wave's row
+// half.  One barrier per pair; the global loads stay outstanding across it.
+template <typename T, int D, int S, class Fn>
+__device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T* Kh, T* ring,
+                                           const typename Ops<T, D>::template QOp<2>& qop, int R0,
+                                           const Geom& g, Fn fn) {
+    using O = Ops<T, D>;
+    using DMA = TileDMA<T, D>;
+    constexpr int kIpp = DMA::template instrs<2>();
+    constexpr int kStage = 2 * DMA::kTileElems;
+    const int w = threadIdx.x / kWave, qh = w & 1, kh = w >> 1;
+    const int npairs = (n + 1) / 2;
+    if (npairs == 0) return;
+    auto issue = [&](int pp) {
+        int r0[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = 2 * pp + u;
+            r0[u] = (e < n) ? (list[e] & 0xfff) * kBC : 0;
+        }
+        DMA::template issue<2>(ring + (pp % S) * kStage, Kh, r0, g.L);
+    };
+#pragma unroll
+    for (int pp = 0; pp < S - 1; ++pp)
+        if (pp < npairs) issue(pp);
+    for (int pp = 0; pp < npairs; ++pp) {
+        if constexpr (S == 1) {
+            // single stage: wait for the previous tile's readers, then load
+            barrier_keep_vm();
+            issue(pp);
+            wait_vmcnt<0>();
+        } else {
+            if (npairs - 1 - pp >= S - 2) wait_vmcnt<(S - 2) * kIpp>();
+            else wait_vmcnt<0>();
+        }
+        barrier_keep_vm();
+        if (S > 1 && pp + S - 1 < npairs) issue(pp + S - 1);
+        const int e = 2 * pp + kh;
+        if (e < n) {
+            const int ent = list[e];
+            const int J = ent & 0xfff;
+            if ((ent >> (12 + qh)) & 1) {
+                const int cls = tile_class(J, R0, g);
+                if (cls != kSkip) {
+                    f32x16 acc[2][2];
+                    O::scores(acc, ring + (pp % S) * kStage + kh * DMA::kTileElems, qop);
+                    if (cls == kPartial) apply_mask(acc, J, R0, g);
+                    fn(J, cls, acc);
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Maximum over the 64 lanes of a wave, by DPP row shifts and broadcasts
+// (VALU only), returned to every lane.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+#define ENTMAX_DPP_MAX(ctrl, rmask)                                                              \
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                          \
+                     __builtin_bit_cast(int, x), __builtin_bit_cast(int, x), ctrl, rmask, 0xf, false)))
+    ENTMAX_DPP_MAX(0x111, 0xf);  // row_shr:1
+    ENTMAX_DPP_MAX(0x112, 0xf);  // row_shr:2
+    ENTMAX_DPP_MAX(0x114, 0xf);  // row_shr:4
+    ENTMAX_DPP_MAX(0x118, 0xf);  // row_shr:8  -> lane 15 of each row holds the row max
+    ENTMAX_DPP_MAX(0x142, 0xa);  // row_bcast:15
+    ENTMAX_DPP_MAX(0x143, 0xc);  // row_bcast:31 -> lane 63 holds the wave max
+#undef ENTMAX_DPP_MAX
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // --------------------------------------------------------- small solvers
 // Exact threshold of N sorted-descending values (score units, -inf entries
 // absent): scan of the top-k prefixes, each a quadratic in tau.
@@ -196,17 +272,220 @@ __device__ __forceinline__ float tau_of_sorted(const float (&x)[N]) {
     return m + best;
 }
 
-// ------------------------------------------------------------ kernel 1
+// Sort N (a power of two) values descending in registers (bitonic network).
+template <int N>
+__device__ __forceinline__ void sort_desc(float (&x)[N]) {
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const bool desc = (i & k) == 0;
+                    const float a = x[i], b = x[l];
+                    const float hi = fmaxf(a, b), lo = fminf(a, b);
+                    x[i] = desc ? hi : lo;
+                    x[l] = desc ? lo : hi;
+                }
+            }
+}
+
+// Threshold of a row from its candidate list cv[0..n): every entry is above
+// `lo`, and none of the row's other scores is.  Two lanes share a row (h = 0
+// and 1 take alternate entries; sums are combined with lane l ^ 32).
+// Newton steps from below: f(t) = sum [(x - t)/2]_+^2 - 1 is convex and
+// decreasing, so a step from a point with f >= 0 stays at or below the root
+// (bisection takes over if rounding lands above it).  Exact finish: when the
+// closed-form root of {x > t} lies below the set's smallest member, that set
+// is the support and the root is tau.  Sums in fp64.  Returns tau; lanes with
+// active == false only take part in the exchanges.
+__device__ double solve_candidates(const float* cv, int n, double mx, double lo, double hi,
+                                   bool active, int h) {
+    double t = lo, result = lo;
+    bool done = !active;
+    for (int it = 0; it < kMaxIter; ++it) {
+        if (__ballot(!done) == 0) break;
+        double C = 0, S1 = 0, S2 = 0, F = 0, F1 = 0;
+        float mn = __builtin_inff();
+        if (!done) {
+            for (int i = h; i < n; i += 2) {
+                const float x = cv[i];
+                if ((double)x > t) {
+                    const double y = (double)x - mx;
+                    const double gg = 0.5 * ((double)x - t);
+                    C += 1.0; S1 += y; S2 += y * y; F += gg * gg; F1 += gg;
+                    mn = fminf(mn, x);
+                }
+            }
+        }
+        C += __shfl_xor(C, 32, kWave);
+        S1 += __shfl_xor(S1, 32, kWave);
+        S2 += __shfl_xor(S2, 32, kWave);
+        F += __shfl_xor(F, 32, kWave);
+        F1 += __shfl_xor(F1, 32, kWave);
+        mn = fminf(mn, __shfl_xor(mn, 32, kWave));
+        if (done) continue;
+        const double f = F - 1.0;
+        if (f >= 0.0 && C > 0.0) {
+            lo = t;
+            const double disc = fmax(S1 * S1 - C * (S2 - 4.0), 0.0);
+            const double ts = mx + (S1 - sqrt(disc)) / C;
+            if (ts < (double)mn) {
+                result = fmax(ts, t);
+                done = true;
+                continue;
+            }
+            double tn = t + f / F1;
+            if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
+            t = tn;
+        } else {
+            hi = t;
+            t = 0.5 * (lo + hi);
+        }
+        if (hi - lo <= 1e-12 * fmax(1.0, fabs(t))) {
+            result = 0.5 * (lo + hi);
+            done = true;
+        }
+    }
+    if (!done) result = 0.5 * (lo + hi);
+    return result;
+}
+
+// Largest entry of a candidate list (two lanes per row).
+__device__ __forceinline__ float list_max(const float* cv, int n, int h) {
+    float mx = neg_inf();
+    for (int i = h; i < n; i += 2) mx = fmaxf(mx, cv[i]);
+    return fmaxf(mx, __shfl_xor(mx, 32, kWave));
+}
+
+constexpr int kRounds = 3;  // candidate collections before the sweep fallback
+
 template <typename T, int D>
-__global__ __launch_bounds__(kNT, 1) void fwd_tau_kernel(FwdParams p) {
+struct StatsCfg {
+    // ring stages (pairs of tiles in flight + 1)
+    static constexpr int kS = (sizeof(T) == 4 && D == 128) ? 2 : 3;
+};
+template <typename T, int D>
+struct SolveCfg {
+    static constexpr int kS = (sizeof(T) == 2 && D == 64) ? 3 : ((sizeof(T) == 4 && D == 128) ? 1 : 2);
+};
+
+constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
+
+// ------------------------------------------------------------ kernel 1a
+// Dense sweep: per row the top tile maxima (-> tau_lo and the maximum) and
+// per (64-row half, tile) the largest raw score.
+template <typename T, int D>
+__global__ __launch_bounds__(kNT, 2) void fwd_stats_kernel(FwdParams p) {
+    using O = Ops<T, D>;
+    constexpr int S = StatsCfg<T, D>::kS;
+    __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
+    __shared__ uint16_t list[kMaxTc];
+    __shared__ float umax[2][kMaxTc];
+    __shared__ int nlist_s;
+    // the per-row lists are merged through the ring once the sweep is over
+    typedef float StRow[kBR][2 * kTop4];
+    static_assert(sizeof(float) * 2 * kBR * 2 * kTop4 <= sizeof(T) * S * 2 * 64 * D, "merge space");
+    StRow* st = reinterpret_cast<StRow*>(ring);
+
+    const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
+    const int l = lane_id(), m = l & 31, h = l >> 5;
+    int bh, r0;
+    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    const int R0 = r0 + 64 * qh;
+    const Geom g = {p.L, p.mode, p.W};
+    const size_t head_off = (size_t)bh * p.L * D;
+    const T* Qh = reinterpret_cast<const T*>(p.q) + head_off;
+    const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
+
+    typename O::template QOp<2> qop;
+    O::load_q(qop, Qh, R0, p.L);
+    for (int i = t; i < 2 * kMaxTc; i += kNT) (&umax[0][0])[i] = neg_inf();
+    if (w == 0) {
+        const int n = build_list(list, p.Tc, [&](int J) {
+            return (tile_class(J, r0, g) != kSkip ? 1 : 0) | (tile_class(J, r0 + 64, g) != kSkip ? 2 : 0);
+        });
+        if (l == 0) nlist_s = n;
+    }
+    __syncthreads();
+
+    float top[2][kTop4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < kTop4; ++i) top[qb][i] = neg_inf();
+
+    ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
+        float wm = neg_inf();
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float tm = neg_inf();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tm = fmaxf(tm, acc[kb][qb][r]);
+            float x = tm;
+#pragma unroll
+            for (int i = 0; i < kTop4; ++i) {
+                const float hi = fmaxf(top[qb][i], x);
+                x = fminf(top[qb][i], x);
+                top[qb][i] = hi;
+            }
+            wm = fmaxf(wm, tm);
+        }
+        wm = wave_max_dpp(wm);
+        if (l == 0) umax[qh][J] = wm;
+    });
+
+    // merge the four lists of each row (two lane halves x two key parities)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float other[kTop4];
+#pragma unroll
+        for (int i = 0; i < kTop4; ++i) other[i] = __shfl_xor(top[qb][i], 32, kWave);
+        if (h == 0) {
+            float* e = &st[kh][qh * 64 + qb * 32 + m][0];
+#pragma unroll
+            for (int i = 0; i < kTop4; ++i) {
+                e[i] = top[qb][i];
+                e[kTop4 + i] = other[i];
+            }
+        }
+    }
+    __syncthreads();
+    const int srow = qh * 64 + kh * 32 + m;
+    const int grow = r0 + srow;
+    if (h == 0 && grow < p.L) {
+        float v[4 * kTop4];
+#pragma unroll
+        for (int i = 0; i < 2 * kTop4; ++i) {
+            v[i] = st[0][srow][i] * p.scale;
+            v[2 * kTop4 + i] = st[1][srow][i] * p.scale;
+        }
+        sort_desc(v);
+        const float lo = tau_of_sorted(v);
+        reinterpret_cast<float2*>(p.rowstat)[(size_t)bh * p.L + grow] = make_float2(v[0], lo);
+    }
+    for (int i = t; i < 2 * p.Tc; i += kNT) {
+        const int hh = i / p.Tc, J = i % p.Tc;
+        const int I = r0 / 64 + hh;
+        if (I < p.Tr64) p.umax[((size_t)bh * p.Tr64 + I) * p.Tc + J] = umax[hh][J];
+    }
+}
+
+// ------------------------------------------------------------ kernel 1b
+// Candidate sweep, exact per-row tau, block mask, fallback.
+template <typename T, int D>
+__global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
     using O = Ops<T, D>;
     constexpr int CAP = FwdCfg<T, D>::kCap;
-    constexpr int NBUF = FwdCfg<T, D>::kNBuf;
+    constexpr int S = SolveCfg<T, D>::kS;
 
-    __shared__ __attribute__((aligned(16))) T kbuf[NBUF * 2 * O::kKTile];
+    __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
     __shared__ __attribute__((aligned(16))) float cval[kBR * CAP];
     __shared__ uint16_t cjt[kBR * CAP];
-    __shared__ float umax[2][kMaxTc];
     __shared__ uint16_t list[kMaxTc];
     __shared__ int cnt[kBR];
     __shared__ float row_m[kBR], row_lo[kBR], row_tau[kBR];
@@ -227,97 +506,31 @@ __global__ __launch_bounds__(kNT, 1) void fwd_tau_kernel(FwdParams p) {
 
     typename O::template QOp<2> qop;
     O::load_q(qop, Qh, R0, p.L);
-
-    // ---- structural tile list; init tables
-    for (int i = t; i < 2 * kMaxTc; i += kNT) (&umax[0][0])[i] = neg_inf();
+    if (t < kBR) {
+        const int grow = r0 + t;
+        float2 rs = make_float2(neg_inf(), __builtin_inff());
+        if (grow < p.L) rs = reinterpret_cast<const float2*>(p.rowstat)[(size_t)bh * p.L + grow];
+        row_m[t] = rs.x;
+        row_lo[t] = rs.y;
+        cnt[t] = 0;
+    }
     for (int i = t; i < 2 * (kMaxTc / 32); i += kNT) (&maskw[0][0])[i] = 0u;
-    if (w == 0) {
-        const int n = build_list(list, p.Tc, [&](int J) {
-            return (tile_class(J, r0, g) != kSkip ? 1 : 0) | (tile_class(J, r0 + 64, g) != kSkip ? 2 : 0);
-        });
-        if (l == 0) nlist_s = n;
-    }
     __syncthreads();
 
-    // ---- sweep 1: row max, top tile maxima, per-(half, tile) max
-    float rmax[2] = {neg_inf(), neg_inf()};
-    float top[2][kTop];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < kTop; ++i) top[qb][i] = neg_inf();
-
-    sweep<T, D, NBUF, false>(list, nlist_s, Kh, nullptr, kbuf, nullptr, qop, R0, g,
-                             [&](int J, int, f32x16(&acc)[2][2], const T*) {
-        float wm = neg_inf();
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float tm = neg_inf();
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tm = fmaxf(tm, acc[kb][qb][r]);
-            tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
-            rmax[qb] = fmaxf(rmax[qb], tm);
-            float x = tm;
-#pragma unroll
-            for (int i = 0; i < kTop; ++i) {
-                const float hi = fmaxf(top[qb][i], x);
-                x = fminf(top[qb][i], x);
-                top[qb][i] = hi;
-            }
-            wm = fmaxf(wm, tm);
-        }
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, kWave));
-        if (l == 0) umax[qh][J] = wm;
-    });
-
-    // ---- merge the two key-parity halves of each row; tau_lo
-    float* st = cval;  // [kh][row][1 + kTop] (candidate space is free here)
-    constexpr int kSt = 1 + kTop;
-    if (h == 0) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float* e = st + (kh * kBR + qh * 64 + qb * 32 + m) * kSt;
-            e[0] = rmax[qb];
-#pragma unroll
-            for (int i = 0; i < kTop; ++i) e[1 + i] = top[qb][i];
-        }
-    }
-    __syncthreads();
-    const int srow = qh * 64 + kh * 32 + m;  // the row this lane solves
-    const bool svalid = (r0 + srow) < p.L;
-    if (h == 0) {
-        const float* a = st + srow * kSt;
-        const float* b = st + (kBR + srow) * kSt;
-        float merged[2 * kTop];
-        int ia = 0, ib = 0;
-#pragma unroll
-        for (int i = 0; i < 2 * kTop; ++i) {
-            const float va = (ia < kTop) ? a[1 + ia] : neg_inf();
-            const float vb = (ib < kTop) ? b[1 + ib] : neg_inf();
-            const bool ta = va >= vb;
-            merged[i] = (ta ? va : vb) * p.scale;
-            ia += ta ? 1 : 0;
-            ib += ta ? 0 : 1;
-        }
-        const float mx = fmaxf(a[0], b[0]) * p.scale;
-        float lo = __builtin_inff();
-        if (svalid) lo = tau_of_sorted(merged);
-        row_m[srow] = svalid ? mx : neg_inf();
-        row_lo[srow] = lo;
-        cnt[srow] = 0;
-    }
-    __syncthreads();
-
-    // ---- sweep-2 tile list: tiles whose best score beats some row's tau_lo
+    // tiles whose best score beats the smallest tau_lo of the row half
     if (w == 0) {
         float th[2];
+        const float* um[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) th[hh] = wave_min(row_lo[hh * 64 + l]);
+        for (int hh = 0; hh < 2; ++hh) {
+            th[hh] = wave_min(row_lo[hh * 64 + l]);
+            const int I = r0 / 64 + hh;
+            um[hh] = (I < p.Tr64) ? p.umax + ((size_t)bh * p.Tr64 + I) * p.Tc : nullptr;
+        }
         const int n = build_list(list, p.Tc, [&](int J) {
-            return (umax[0][J] * p.scale > th[0] ? 1 : 0) | (umax[1][J] * p.scale > th[1] ? 2 : 0);
+            const int f0 = (um[0] && um[0][J] * p.scale > th[0]) ? 1 : 0;
+            const int f1 = (um[1] && um[1][J] * p.scale > th[1]) ? 2 : 0;
+            return f0 | f1;
         });
         if (l == 0) {
             nlist_s = n;
@@ -326,115 +539,97 @@ __global__ __launch_bounds__(kNT, 1) void fwd_tau_kernel(FwdParams p) {
     }
     __syncthreads();
 
-    // ---- sweep 2: collect candidates s > tau_lo
-    float lo_q[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) lo_q[qb] = row_lo[qh * 64 + qb * 32 + m];
-    sweep<T, D, NBUF, false>(list, nlist_s, Kh, nullptr, kbuf, nullptr, qop, R0, g,
-                             [&](int J, int, f32x16(&acc)[2][2], const T*) {
+    const int srow = qh * 64 + kh * 32 + m;  // the row this lane solves (with lane l ^ 32)
+    const bool svalid = (r0 + srow) < p.L;
+    // per-row state: 1 = to be (re)collected and solved, 0 = solved, 2 = overflowing
+    __shared__ int rstate[kBR];
+    if (t < kBR) rstate[t] = (r0 + t) < p.L ? 1 : 0;
+    __syncthreads();
+
+    for (int round = 0; round < kRounds; ++round) {
+        // ---- collect candidates s > tau_lo of the rows still open
+        float lo_q[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            float bm = neg_inf();
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[kb][qb][r]);
-            if (__ballot(bm * p.scale > lo_q[qb]) == 0) continue;
             const int row = qh * 64 + qb * 32 + m;
+            lo_q[qb] = rstate[row] == 1 ? row_lo[row] : __builtin_inff();
+        }
+        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int qb = 0; qb < 2; ++qb) {
+                float bm = neg_inf();
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float s = acc[kb][qb][r] * p.scale;
-                    if (s > lo_q[qb]) {
-                        const int slot = atomicAdd(&cnt[row], 1);
-                        if (slot < cap) {
-                            cval[row * CAP + slot] = s;
-                            cjt[row * CAP + slot] = (uint16_t)J;
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[kb][qb][r]);
+                if (__ballot(bm * p.scale > lo_q[qb]) == 0) continue;
+                const int row = qh * 64 + qb * 32 + m;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float sv = acc[kb][qb][r] * p.scale;
+                        if (sv > lo_q[qb]) {
+                            const int slot = atomicAdd(&cnt[row], 1);
+                            if (slot < cap) {
+                                cval[row * CAP + slot] = sv;
+                                cjt[row * CAP + slot] = (uint16_t)J;
+                            }
                         }
                     }
-                }
-        }
-    });
+            }
+        });
 
-    // ---- exact threshold per row from its candidates (two lanes per row)
-    {
+        // ---- solve the open rows whose lists are complete; for overflowing
+        // rows, the threshold of the candidates they kept is a better bound
+        const int st0 = rstate[srow];
         const int nc = cnt[srow];
-        const bool ovf = svalid && nc > cap;
+        const bool open = st0 == 1;
+        const bool complete = open && nc <= cap;
         const int n = nc < cap ? nc : cap;
-        const float mx = row_m[srow];
-        bool done = !svalid || ovf;
-        float lo = row_lo[srow];
-        float hi = mx - 2.0f / sqrtf((float)(nc > 0 ? nc : 1));
-        float tcur = lo, result = lo;
         const float* cv = cval + srow * CAP;
-        for (int it = 0; it < kMaxIter; ++it) {
-            if (__ballot(!done) == 0) break;
-            double C = 0, S1 = 0, S2 = 0, F = 0, F1 = 0;
-            float mn = __builtin_inff();
-            if (!done) {
-                for (int i = h; i < n; i += 2) {
-                    const float x = cv[i];
-                    if (x > tcur) {
-                        const double y = (double)x - (double)mx;
-                        const double gg = 0.5 * ((double)x - (double)tcur);
-                        C += 1.0; S1 += y; S2 += y * y; F += gg * gg; F1 += gg;
-                        mn = fminf(mn, x);
-                    }
+        const double mx = row_m[srow];
+        const double tau_row = solve_candidates(cv, n, mx, row_lo[srow],
+                                                mx - 2.0 / sqrt((double)(nc > 0 ? nc : 1)), complete, h);
+        // subset threshold (a lower bound on the row's tau) for overflowing rows
+        const bool over = open && nc > cap;
+        const float smax = list_max(cv, n, h);
+        const double tau_sub = solve_candidates(cv, n, smax, (double)smax - 2.0,
+                                                (double)smax - 2.0 / sqrt((double)(n > 0 ? n : 1)), over, h);
+        if (complete) {
+            const float tr = (float)tau_row;
+            for (int i = h; i < n; i += 2)
+                if (cv[i] > tr) {
+                    const int J = cjt[srow * CAP + i];
+                    atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
                 }
-            }
-            C += __shfl_xor(C, 32, kWave);
-            S1 += __shfl_xor(S1, 32, kWave);
-            S2 += __shfl_xor(S2, 32, kWave);
-            F += __shfl_xor(F, 32, kWave);
-            F1 += __shfl_xor(F1, 32, kWave);
-            mn = fminf(mn, __shfl_xor(mn, 32, kWave));
-            if (!done) {
-                const double f = F - 1.0;
-                if (f >= 0.0) {
-                    const double disc = fmax(S1 * S1 - C * (S2 - 4.0), 0.0);
-                    const double ts = (double)mx + (S1 - sqrt(disc)) / C;
-                    if (ts < (double)mn) {
-                        result = fmaxf((float)ts, tcur);
-                        done = true;
-                    } else {
-                        lo = tcur;
-                    }
-                } else {
-                    hi = tcur;
-                }
-                if (!done) {
-                    if (hi - lo <= 1e-7f * fmaxf(1.0f, fabsf(tcur))) {
-                        result = 0.5f * (lo + hi);
-                        done = true;
-                    } else {
-                        const double fp = -F1, fpp = 0.5 * C;
-                        const double den = 2.0 * fp * fp - f * fpp;
-                        double tn = (double)tcur - 2.0 * f * fp / den;
-                        if (!(den > 0.0) || !(tn > lo && tn < hi)) tn = 0.5 * ((double)lo + (double)hi);
-                        tcur = (float)tn;
-                        if (!(tcur > lo && tcur < hi)) tcur = 0.5f * (lo + hi);
-                    }
-                }
-            }
         }
-        if (svalid && !ovf && !done) result = 0.5f * (lo + hi);
+        __syncthreads();  // every lane is done reading the lists
         if (h == 0) {
-            row_tau[srow] = (svalid && !ovf) ? result : __builtin_inff();
-            if (ovf) atomicOr(&ovf_s, 1);
-        }
-        // mask bits from candidates above tau
-        const float tr = (svalid && !ovf) ? result : __builtin_inff();
-        for (int i = h; i < n; i += 2)
-            if (cv[i] > tr) {
-                const int J = cjt[srow * CAP + i];
-                atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
+            if (complete) {
+                row_tau[srow] = (float)tau_row;
+                rstate[srow] = 0;
+            } else if (over) {
+                // upper bracket from this round's count of scores above tau_lo
+                fb_part[srow][0][1] = (float)(mx - 2.0 / sqrt((double)nc));
+                const float nl = fmaxf(row_lo[srow], (float)tau_sub);
+                // no progress possible: leave the row to the sweep fallback
+                if (round == kRounds - 1 || !(nl > row_lo[srow])) rstate[srow] = 2;
+                row_lo[srow] = nl;
+                cnt[srow] = 0;
             }
-        // overflow rows: carry their bracket to the fallback
-        if (h == 0 && ovf) {
-            fb_part[srow][0][0] = row_lo[srow];
-            fb_part[srow][0][1] = mx - 2.0f / sqrtf((float)nc);
         }
+        if (t == 0) ovf_s = 0;
+        __syncthreads();
+        if (h == 0 && rstate[srow] == 1) atomicOr(&ovf_s, 1);
+        __syncthreads();
+        if (!ovf_s) break;
+    }
+    if (t == 0) ovf_s = 0;
+    __syncthreads();
+    if (h == 0 && rstate[srow] == 2) {
+        atomicOr(&ovf_s, 1);
+        fb_part[srow][0][0] = row_lo[srow];
     }
     __syncthreads();
 
@@ -445,7 +640,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_tau_kernel(FwdParams p) {
         __shared__ int fb_active[kBR];
         __shared__ int fb_any;
         if (h == 0) {
-            const bool ovf = svalid && cnt[srow] > cap;
+            const bool ovf = svalid && rstate[srow] == 2;
             fb_active[srow] = ovf ? 1 : 0;
             fb_lo[srow] = ovf ? fb_part[srow][0][0] : 0.f;
             fb_hi[srow] = ovf ? fb_part[srow][0][1] : 0.f;
@@ -462,8 +657,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_tau_kernel(FwdParams p) {
                 tq[qb] = fb_t[row];
             }
             float sc[2] = {0.f, 0.f}, sf[2] = {0.f, 0.f}, sf1[2] = {0.f, 0.f};
-            sweep<T, D, NBUF, false>(list, nlist_s, Kh, nullptr, kbuf, nullptr, qop, R0, g,
-                                     [&](int, int, f32x16(&acc)[2][2], const T*) {
+            ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
                     if (!aq[qb]) continue;
@@ -502,7 +696,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_tau_kernel(FwdParams p) {
                 const float F1 = fb_part[srow][0][2] + fb_part[srow][1][2];
                 float lo = fb_lo[srow], hi = fb_hi[srow], tc = fb_t[srow];
                 if (F - 1.0f >= 0.0f) lo = tc; else hi = tc;
-                if (hi - lo <= 1e-7f * fmaxf(1.0f, fabsf(tc))) {
+                if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
                     fb_active[srow] = 0;
                     row_tau[srow] = 0.5f * (lo + hi);
                 } else {
@@ -524,11 +718,10 @@ __global__ __launch_bounds__(kNT, 1) void fwd_tau_kernel(FwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = qh * 64 + qb * 32 + m;
-            aq[qb] = (r0 + row) < p.L && cnt[row] > cap;
+            aq[qb] = (r0 + row) < p.L && rstate[row] == 2;
             tq[qb] = row_tau[row];
         }
-        sweep<T, D, NBUF, false>(list, nlist_s, Kh, nullptr, kbuf, nullptr, qop, R0, g,
-                                 [&](int J, int, f32x16(&acc)[2][2], const T*) {
+        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
             bool any = false;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
@@ -668,28 +861,44 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
 template <typename T, int D>
 hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t stream) {
     if (phase & 1) {
-        hipLaunchKernelGGL((fwd_tau_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        hipLaunchKernelGGL((fwd_stats_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (phase & 2) {
+        hipLaunchKernelGGL((fwd_solve_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (phase & 4) {
         hipLaunchKernelGGL((fwd_out_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
         return hipGetLastError();
     }
     return hipSuccess;
 }
 
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 size_t mask_bytes(int B, int H, int L) {
     const size_t tr = (L + 63) / 64, tc = (L + 63) / 64, wd = (tc + 31) / 32;
     return (size_t)B * H * tr * wd * sizeof(uint32_t);
+}
+size_t rowstat_bytes(int B, int H, int L) { return (size_t)B * H * L * 2 * sizeof(float); }
+size_t umax_bytes(int B, int H, int L) {
+    const size_t tr = (L + 63) / 64, tc = (L + 63) / 64;
+    return (size_t)B * H * tr * tc * sizeof(float);
 }
 
 }  // namespace
 }  // namespace attn
 
+size_t attn_threshold_workspace_bytes(int B, int H, int L) {
+    return attn::round256(attn::rowstat_bytes(B, H, L)) + attn::round256(attn::umax_bytes(B, H, L));
+}
+
 size_t attn_fwd_workspace_bytes(int B, int H, int L, int, int) {
-    // room for the block mask when the caller does not want it
-    return (attn::mask_bytes(B, H, L) + 255) & ~(size_t)255;
+    // threshold scratch, then room for the block mask when the caller does not keep it
+    return attn_threshold_workspace_bytes(B, H, L) + attn::round256(attn::mask_bytes(B, H, L));
 }
 
 int attn_max_candidate_cap(int d, int dtype) {
@@ -702,7 +911,11 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream) {
     if (a.L > kMaxL) return hipErrorInvalidValue;
     FwdParams fp;
     fp.q = a.q; fp.k = a.k; fp.v = a.v; fp.o = a.o; fp.tau = a.tau;
-    fp.mask = a.block_mask ? a.block_mask : reinterpret_cast<uint32_t*>(a.workspace);
+    char* ws = reinterpret_cast<char*>(a.workspace);
+    fp.rowstat = reinterpret_cast<float*>(ws);
+    fp.umax = reinterpret_cast<float*>(ws + round256(rowstat_bytes(a.B, a.H, a.L)));
+    fp.mask = a.block_mask ? a.block_mask
+                           : reinterpret_cast<uint32_t*>(ws + attn_threshold_workspace_bytes(a.B, a.H, a.L));
     fp.BH = a.B * a.H; fp.L = a.L; fp.mode = a.mask; fp.W = a.window;
     fp.nQ = (a.L + kBR - 1) / kBR;
     fp.Tc = (a.L + kBC - 1) / kBC;

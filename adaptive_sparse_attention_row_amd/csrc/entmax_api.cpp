@@ -81,6 +81,12 @@ int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t 
     return hip_status(entmax::launch_tau_rows(S, P, tau, rows, cols, ld, (hipStream_t)stream));
 }
 
+size_t entmax_attn_threshold_workspace(int B, int H, int L, int d, int dtype, int mask,
+                                       int window) {
+    if (check_attn_shape(B, H, L, d, 1.5f, dtype, mask, window) != ENTMAX_OK) return 0;
+    return entmax::attn_threshold_workspace_bytes(B, H, L);
+}
+
 size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask, int window) {
     if (check_attn_shape(B, H, L, d, 1.5f, dtype, mask, window) != ENTMAX_OK) return 0;
     return entmax::attn_fwd_workspace_bytes(B, H, L, d, dtype);
@@ -97,10 +103,10 @@ int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float
     if (!(scale > 0.0f) || !isfinite(scale)) return ENTMAX_ERR_ARG;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ENTMAX_ERR_ALIGN;
     if (((uintptr_t)tau & 3u) || ((uintptr_t)block_mask & 3u)) return ENTMAX_ERR_ALIGN;
-    // the workspace only stands in for a block mask the caller does not keep
-    const size_t need = block_mask ? 0 : entmax::attn_fwd_workspace_bytes(B, H, L, d, dtype);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ENTMAX_ERR_WORKSPACE;
-    if (need > 0 && ((uintptr_t)workspace & 3u)) return ENTMAX_ERR_ALIGN;
+    const size_t need = block_mask ? entmax::attn_threshold_workspace_bytes(B, H, L)
+                                   : entmax::attn_fwd_workspace_bytes(B, H, L, d, dtype);
+    if (workspace == nullptr || workspace_bytes < need) return ENTMAX_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ENTMAX_ERR_ALIGN;
     entmax::AttnArgs a = {};
     a.q = Q; a.k = K; a.v = V; a.o = O; a.tau = tau; a.block_mask = block_mask;
     a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
@@ -109,12 +115,13 @@ int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float
     a.cand_cap = (g_cand_cap > 0 && g_cand_cap < maxcap) ? g_cand_cap : maxcap;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     (void)hipGetLastError();
-    return hip_status(entmax::launch_attn_fwd(a, 3, (hipStream_t)stream));
+    return hip_status(entmax::launch_attn_fwd(a, 7, (hipStream_t)stream));
 }
 
 int entmax_attn_threshold(const void* Q, const void* K, float* tau, uint32_t* block_mask,
                           int B, int H, int L, int d, float scale, float alpha, int dtype,
-                          int mask, int window, void* stream) {
+                          int mask, int window, void* workspace, size_t workspace_bytes,
+                          void* stream) {
     if (Q == nullptr || K == nullptr || tau == nullptr || block_mask == nullptr)
         return ENTMAX_ERR_NULL;
     int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
@@ -122,12 +129,36 @@ int entmax_attn_threshold(const void* Q, const void* K, float* tau, uint32_t* bl
     if (!(scale > 0.0f) || !isfinite(scale)) return ENTMAX_ERR_ARG;
     if (!aligned16(Q) || !aligned16(K)) return ENTMAX_ERR_ALIGN;
     if (((uintptr_t)tau & 3u) || ((uintptr_t)block_mask & 3u)) return ENTMAX_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < entmax::attn_threshold_workspace_bytes(B, H, L))
+        return ENTMAX_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ENTMAX_ERR_ALIGN;
     entmax::AttnArgs a = {};
     a.q = Q; a.k = K; a.tau = tau; a.block_mask = block_mask;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     const int maxcap = entmax::attn_max_candidate_cap(d, dtype);
     a.cand_cap = (g_cand_cap > 0 && g_cand_cap < maxcap) ? g_cand_cap : maxcap;
+    (void)hipGetLastError();
+    return hip_status(entmax::launch_attn_fwd(a, 3, (hipStream_t)stream));
+}
+
+int entmax_attn_score_stats(const void* Q, const void* K, int B, int H, int L, int d, float scale,
+                            float alpha, int dtype, int mask, int window, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (Q == nullptr || K == nullptr) return ENTMAX_ERR_NULL;
+    int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
+    if (st != ENTMAX_OK) return st;
+    if (!(scale > 0.0f) || !isfinite(scale)) return ENTMAX_ERR_ARG;
+    if (!aligned16(Q) || !aligned16(K)) return ENTMAX_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < entmax::attn_threshold_workspace_bytes(B, H, L))
+        return ENTMAX_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ENTMAX_ERR_ALIGN;
+    entmax::AttnArgs a = {};
+    a.q = Q; a.k = K;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
+    a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     (void)hipGetLastError();
     return hip_status(entmax::launch_attn_fwd(a, 1, (hipStream_t)stream));
 }
@@ -150,7 +181,7 @@ int entmax_attn_output(const void* Q, const void* K, const void* V, const float*
     a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     (void)hipGetLastError();
-    return hip_status(entmax::launch_attn_fwd(a, 2, (hipStream_t)stream));
+    return hip_status(entmax::launch_attn_fwd(a, 4, (hipStream_t)stream));
 }
 
 size_t entmax_attn_bwd_workspace(int B, int H, int L, int d, int dtype, int mask, int window) {

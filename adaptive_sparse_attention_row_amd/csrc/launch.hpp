@@ -36,10 +36,11 @@ struct AttnArgs {
 constexpr int kMaskBr = 64;
 constexpr int kMaskBc = 64;
 
+size_t attn_threshold_workspace_bytes(int B, int H, int L);
 size_t attn_fwd_workspace_bytes(int B, int H, int L, int d, int dtype);
 size_t attn_bwd_workspace_bytes(int B, int H, int L, int d, int dtype);
 int attn_max_candidate_cap(int d, int dtype);
-// phase: 1 = threshold + mask, 2 = output, 3 = both
+// phase bits: 1 = score statistics, 2 = threshold solve + mask, 4 = output
 hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream);
 

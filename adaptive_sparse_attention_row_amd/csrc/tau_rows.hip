@@ -109,7 +109,7 @@ __device__ float refine_tau(float m, float total, Visit visit, float (*red)[kWav
         } else {
             hi = t;
         }
-        if (hi - lo <= 1e-7f * fmaxf(1.0f, fabsf(t))) break;
+        if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) break;
         t = halley_or_bisect(t, s.F, s.F1, s.C, lo, hi);
     }
     return 0.5f * (lo + hi);

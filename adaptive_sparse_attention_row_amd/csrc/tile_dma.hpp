@@ -1,0 +1,73 @@
+// tile_dma.hpp -- direct global -> LDS staging of 64-row tiles (gfx950
+// global_load_lds_dwordx4) into a ring of stages, with explicit counter waits.
+//
+// Each DMA instruction writes the 16 bytes of each of the 64 lanes to 64
+// consecutive 16-byte LDS slots starting at a wave-uniform base; the global
+// address of each lane is free.  A tile's slot (row r, position p) is filled
+// from chunk swz(r, p) of that row, which produces the swizzled natural
+// layout the score reads expect (swz is its own inverse).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_common.hpp"
+
+namespace entmax {
+namespace attn {
+
+// s_waitcnt with vmcnt <= N and no wait on the other counters (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that first drains this wave's LDS operations but leaves
+// outstanding global loads (the prefetch ring) in flight.
+__device__ __forceinline__ void barrier_keep_vm() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <typename T, int D>
+struct TileDMA {
+    static constexpr int kCPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+    static constexpr int kTileCh = 64 * kCPR;             // chunks per tile
+    static constexpr int kTileElems = 64 * D;
+
+    // Number of DMA instructions each thread issues for NT tiles.
+    template <int NT>
+    static constexpr int instrs() {
+        return NT * kTileCh / kNT;
+    }
+
+    // Stage NT tiles (rows r0[k] .. r0[k] + 63 of X, clamped to L - 1; rows
+    // past L hold junk that the masks discard) into dst (NT tiles back to back).
+    template <int NT>
+    __device__ __forceinline__ static void issue(T* dst, const T* Xh, const int (&r0)[NT], int L) {
+        const int t = threadIdx.x, w = t / kWave, lane = t & (kWave - 1);
+        constexpr int kPerWave = NT * kTileCh / 4;
+        constexpr int kIpw = kPerWave / kWave;
+        static_assert(kIpw * kWave * 4 == NT * kTileCh, "tile chunks must split evenly");
+#pragma unroll
+        for (int k = 0; k < kIpw; ++k) {
+            const int q0 = w * kPerWave + k * kWave;  // first slot of this instruction
+            const int q = q0 + lane;
+            const int tile = q / kTileCh, qt = q % kTileCh;
+            const int r = qt / kCPR, pos = qt % kCPR;
+            int row = r0[tile] + r;
+            row = row < L ? row : L - 1;
+            const T* src = Xh + (size_t)row * D + swz<kCPR>(r, pos) * (16 / (int)sizeof(T));
+            T* base = dst + q0 * (16 / (int)sizeof(T));
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                             (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
+        }
+    }
+};
+
+}  // namespace attn
+}  // namespace entmax

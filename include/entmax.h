@@ -98,11 +98,15 @@ int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t 
                     int64_t ld, float alpha, void* stream);
 
 /*
- * Workspace bytes entmax_attn_fwd needs when it is called with
- * block_mask == NULL (the mask is then kept in the workspace); with a
- * block_mask output no workspace is needed.  Returns 0 for invalid arguments
- * too; entmax_attn_fwd reports those.
+ * Workspace bytes entmax_attn_fwd needs: per-row statistics of the score
+ * sweep (8 bytes per query row) and the largest score of every (64-row
+ * block, 64-key tile) (4 bytes each), plus room for the block mask (used only
+ * when block_mask == NULL).  entmax_attn_threshold needs the same minus the
+ * mask part: entmax_attn_threshold_workspace.  Both return 0 for invalid
+ * arguments; the calls report those.
  */
+size_t entmax_attn_threshold_workspace(int B, int H, int L, int d, int dtype, int mask,
+                                       int window);
 size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask,
                                  int window);
 
@@ -120,9 +124,9 @@ size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask
  *   scale > 0 multiplies Q.K (e.g. 1/sqrt(d)).
  *   d in {64, 128}; B, H >= 1; 1 <= L <= 65536 (per-row tile tables are
  *   kept on chip); otherwise ENTMAX_ERR_SHAPE.
- *   workspace  when block_mask is NULL: at least
- *              entmax_attn_fwd_workspace(...) bytes, 4-byte aligned (it holds
- *              the mask); otherwise ignored (may be NULL).
+ *   workspace  16-byte aligned, at least entmax_attn_fwd_workspace(...) bytes
+ *              (entmax_attn_threshold_workspace(...) suffices when block_mask
+ *              is not NULL).  Contents on entry are ignored.
  */
 int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float* tau,
                     uint32_t* block_mask, int B, int H, int L, int d, float scale,
@@ -134,13 +138,28 @@ int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float
  * rules; entmax_attn_fwd is exactly threshold followed by output).
  *  entmax_attn_threshold: phases 1-3 of AdaSplash-2 sec. 3.3 -- writes tau
  *    [B][H][L] and the packed block mask (required here, same layout as
- *    above).  Needs no workspace.
+ *    above).  Needs entmax_attn_threshold_workspace(...) bytes of workspace.
  *  entmax_attn_output: phase 4 -- given that tau and block mask, writes
  *    O [B][H][L][d] fp32 from the non-null tiles only.
  */
 int entmax_attn_threshold(const void* Q, const void* K, float* tau, uint32_t* block_mask,
                           int B, int H, int L, int d, float scale, float alpha, int dtype,
-                          int mask, int window, void* stream);
+                          int mask, int window, void* workspace, size_t workspace_bytes,
+                          void* stream);
+/*
+ * Phase 1 alone (AdaSplash-2 sec. 3.3 "Phase 1 (maximum)", extended): one
+ * dense MFMA sweep of S = scale Q K^T over the keys the mask allows.  Writes
+ * into the workspace, for each query row, its maximum score and a lower
+ * bound on tau (the exact threshold of its largest tile maxima; adding scores
+ * to a row only raises its threshold), as float2 [B][H][L] at offset 0, and
+ * the largest raw dot product of every (64-row block, 64-key tile) as float
+ * [B][H][ceil(L/64)][ceil(L/64)] at the next 256-byte boundary.
+ * entmax_attn_threshold runs this and then the solve.  Workspace as for
+ * entmax_attn_threshold.
+ */
+int entmax_attn_score_stats(const void* Q, const void* K, int B, int H, int L, int d, float scale,
+                            float alpha, int dtype, int mask, int window, void* workspace,
+                            size_t workspace_bytes, void* stream);
 int entmax_attn_output(const void* Q, const void* K, const void* V, const float* tau,
                        const uint32_t* block_mask, float* O, int B, int H, int L, int d,
                        float scale, float alpha, int dtype, int mask, int window,

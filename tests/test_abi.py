@@ -91,10 +91,26 @@ def test_attn_fwd_validation(api):
     assert fwd(L, Q=FAKE + 4) == api.ERR_ALIGN
     assert fwd(L, O=FAKE + 8) == api.ERR_ALIGN
     need = L.entmax_attn_fwd_workspace(1, 1, 128, 64, 1, 0, 0)
-    assert need > 0
-    assert fwd(L, bm=None, ws=None) == api.ERR_WORKSPACE
+    need_thr = L.entmax_attn_threshold_workspace(1, 1, 128, 64, 1, 0, 0)
+    assert need > need_thr > 0
+    assert fwd(L, ws=None) == api.ERR_WORKSPACE
     assert fwd(L, bm=None, wsb=need - 1) == api.ERR_WORKSPACE
+    assert fwd(L, wsb=need_thr - 1) == api.ERR_WORKSPACE
+    assert fwd(L, ws=FAKE + 8) == api.ERR_ALIGN
     assert L.entmax_attn_fwd_workspace(1, 1, 128, 96, 1, 0, 0) == 0
+    thr = L.entmax_attn_threshold
+    base = [FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 64, 0.125, 1.5, 1, 0, 0, FAKE, need_thr, None]
+    def tcall(i, v):
+        a = list(base)
+        a[i] = v
+        return thr(*a)
+    assert tcall(3, None) == api.ERR_NULL
+    assert tcall(9, 1.0) == api.ERR_ALPHA
+    assert tcall(13, None) == api.ERR_WORKSPACE
+    assert tcall(14, need_thr - 1) == api.ERR_WORKSPACE
+    out = L.entmax_attn_output
+    assert out(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 128, 64, 0.125, 1.5, 1, 0, 0, None) == api.ERR_NULL
+    assert out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 64, 0.125, 1.5, 1, 3, 0, None) == api.ERR_MASK
 
 
 def test_attn_bwd_validation(api):

@@ -225,3 +225,51 @@ def test_scale_and_query_spread(env, orc):
         O, tau, bm = run_gpu(api, torch, inp, scale, 0, 0)
         check_rows(orc, inp, scale, 0, 0, O, tau, "bf16", label=f"q_std={q_std}")
         check_mask(orc, inp, scale, 0, 0, bm, [0, 1], label=f"q_std={q_std}")
+
+
+def _score_stats(api, torch, inp, scale, mode, W):
+    q, k = inp["q"].cuda(), inp["k"].cuda()
+    B, H, L, d = q.shape
+    dt = api._dtype_code(q)
+    lib = api.lib()
+    wsb = lib.entmax_attn_threshold_workspace(B, H, L, d, dt, mode, W)
+    ws = torch.zeros(wsb, device="cuda", dtype=torch.uint8)
+    st = lib.entmax_attn_score_stats(q.data_ptr(), k.data_ptr(), B, H, L, d, float(scale), 1.5, dt, mode, W,
+                                     ws.data_ptr(), wsb, api._stream(q.device))
+    assert st == 0, api.status_str(st)
+    torch.cuda.synchronize()
+    rs = ws[: B * H * L * 8].view(torch.float32).view(B * H, L, 2).cpu().numpy()
+    return rs[..., 0], rs[..., 1]
+
+
+@pytest.mark.parametrize("cfgname", ["c3a", "c5_two_heads", "c4_two_heads"])
+def test_score_stats_bounds(env, orc, cfgname):
+    """Phase 1 alone: each row's maximum equals the oracle's (up to fp32
+    rounding of the dot products), tau_lo never exceeds the exact tau, and
+    the candidates above tau_lo stay well inside the per-row list capacity."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C3A, C4, C5, gen_config
+    cfg = {"c3a": C3A, "c5_two_heads": C5, "c4_two_heads": C4}[cfgname]
+    inp = gen_config(cfg, B=1, H=2)
+    mx, lo = _score_stats(api, torch, inp, cfg.scale, cfg.mask, cfg.window)
+    Q, K = np32(inp["q"]), np32(inp["k"])
+    L = cfg.L
+    rng = np.random.default_rng(3)
+    cap = 128 if cfg.d == 64 else 96
+    counts = []
+    for bh in range(2):
+        for i in np.concatenate([[0, 1, L - 1], rng.integers(0, L, 40)]):
+            s = cfg.scale * (K[0, bh].astype(np.float64) @ Q[0, bh, i].astype(np.float64))
+            if cfg.mask >= 1:
+                act = np.arange(L) <= i
+                if cfg.mask == 2:
+                    act &= (np.arange(L) == 0) | (i - np.arange(L) <= cfg.window)
+                s = np.where(act, s, -np.inf)
+            _, tau, _ = orc.entmax15(s)
+            assert abs(mx[bh, i] - s.max()) <= 1e-5 * max(1, abs(s.max())), (bh, i)
+            assert lo[bh, i] <= tau + 1e-5 * max(1, abs(tau)), (bh, i, lo[bh, i], tau)
+            assert lo[bh, i] >= s.max() - 2 - 1e-5 * max(1, abs(s.max()))
+            counts.append(int(np.sum(s > lo[bh, i])))
+    counts = np.array(counts)
+    print(f"{cfgname}: candidates above tau_lo mean {counts.mean():.1f} max {counts.max()} (capacity {cap})")
+    assert counts.max() <= cap
