@@ -193,6 +193,7 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
     const int w = threadIdx.x / kWave, qh = w & 1, kh = w >> 1;
     const int npairs = (n + 1) / 2;
     if (npairs == 0) return;
+    const auto ln = DMA::template lanes<2>();
     auto issue = [&](int pp) {
         int r0[2];
 #pragma unroll
@@ -200,7 +201,7 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
             const int e = 2 * pp + u;
             r0[u] = (e < n) ? (list[e] & 0xfff) * kBC : 0;
         }
-        DMA::template issue<2>(ring + (pp % S) * kStage, Kh, r0, g.L);
+        DMA::template issue<2>(ring + (pp % S) * kStage, Kh, r0, g.L, ln);
     };
 #pragma unroll
     for (int pp = 0; pp < S - 1; ++pp)
@@ -238,9 +239,12 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
 // Maximum over the 64 lanes of a wave, by DPP row shifts and broadcasts
 // (VALU only), returned to every lane.
 __device__ __forceinline__ float wave_max_dpp(float x) {
+// lanes without a source read -inf (the identity of max), so no copy of x
+// is needed per step
 #define ENTMAX_DPP_MAX(ctrl, rmask)                                                              \
     x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                          \
-                     __builtin_bit_cast(int, x), __builtin_bit_cast(int, x), ctrl, rmask, 0xf, false)))
+                     __builtin_bit_cast(int, neg_inf()), __builtin_bit_cast(int, x), ctrl, rmask, \
+                     0xf, false)))
     ENTMAX_DPP_MAX(0x111, 0xf);  // row_shr:1
     ENTMAX_DPP_MAX(0x112, 0xf);  // row_shr:2
     ENTMAX_DPP_MAX(0x114, 0xf);  // row_shr:4
@@ -362,10 +366,23 @@ __device__ __forceinline__ float list_max(const float* cv, int n, int h) {
 
 constexpr int kRounds = 3;  // candidate collections before the sweep fallback
 
+#ifndef ENTMAX_STATS_STAGES_BF16_64
+#define ENTMAX_STATS_STAGES_BF16_64 3
+#endif
+#ifndef ENTMAX_STATS_STAGES_BF16_128
+#define ENTMAX_STATS_STAGES_BF16_128 2
+#endif
+#ifndef ENTMAX_STATS_OCCUPANCY
+#define ENTMAX_STATS_OCCUPANCY 3
+#endif
+// Ring stages (pairs of tiles in flight + 1) of the score-statistics sweep,
+// and the number of key tiles per row its on-chip tables are sized for
+// (TCMAX * 64 >= L): small tables leave room for three workgroups per CU.
 template <typename T, int D>
 struct StatsCfg {
-    // ring stages (pairs of tiles in flight + 1)
-    static constexpr int kS = (sizeof(T) == 4 && D == 128) ? 2 : 3;
+    static constexpr int kS = (sizeof(T) == 2 && D == 64) ? ENTMAX_STATS_STAGES_BF16_64
+                              : (sizeof(T) == 2) ? ENTMAX_STATS_STAGES_BF16_128
+                              : ((D == 128) ? 2 : 3);
 };
 template <typename T, int D>
 struct SolveCfg {
@@ -377,13 +394,13 @@ constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
 // ------------------------------------------------------------ kernel 1a
 // Dense sweep: per row the top tile maxima (-> tau_lo and the maximum) and
 // per (64-row half, tile) the largest raw score.
-template <typename T, int D>
-__global__ __launch_bounds__(kNT, 2) void fwd_stats_kernel(FwdParams p) {
+template <typename T, int D, int TCMAX>
+__global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(FwdParams p) {
     using O = Ops<T, D>;
     constexpr int S = StatsCfg<T, D>::kS;
     __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
-    __shared__ uint16_t list[kMaxTc];
-    __shared__ float umax[2][kMaxTc];
+    __shared__ uint16_t list[TCMAX];
+    __shared__ float umax[2][TCMAX];
     __shared__ int nlist_s;
     // the per-row lists are merged through the ring once the sweep is over
     typedef float StRow[kBR][2 * kTop4];
@@ -402,7 +419,7 @@ __global__ __launch_bounds__(kNT, 2) void fwd_stats_kernel(FwdParams p) {
 
     typename O::template QOp<2> qop;
     O::load_q(qop, Qh, R0, p.L);
-    for (int i = t; i < 2 * kMaxTc; i += kNT) (&umax[0][0])[i] = neg_inf();
+    for (int i = t; i < 2 * TCMAX; i += kNT) (&umax[0][0])[i] = neg_inf();
     if (w == 0) {
         const int n = build_list(list, p.Tc, [&](int J) {
             return (tile_class(J, r0, g) != kSkip ? 1 : 0) | (tile_class(J, r0 + 64, g) != kSkip ? 2 : 0);
@@ -484,8 +501,11 @@ __global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
     constexpr int S = SolveCfg<T, D>::kS;
 
     __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
-    __shared__ __attribute__((aligned(16))) float cval[kBR * CAP];
-    __shared__ uint16_t cjt[kBR * CAP];
+    // odd row stride: the lanes of a wave read the same slot of 32 different
+    // rows at once, which must fall in different banks
+    constexpr int CST = CAP + 1;
+    __shared__ __attribute__((aligned(16))) float cval[kBR * CST];
+    __shared__ uint16_t cjt[kBR * CST];
     __shared__ uint16_t list[kMaxTc];
     __shared__ int cnt[kBR];
     __shared__ float row_m[kBR], row_lo[kBR], row_tau[kBR];
@@ -572,8 +592,8 @@ __global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
                         if (sv > lo_q[qb]) {
                             const int slot = atomicAdd(&cnt[row], 1);
                             if (slot < cap) {
-                                cval[row * CAP + slot] = sv;
-                                cjt[row * CAP + slot] = (uint16_t)J;
+                                cval[row * CST + slot] = sv;
+                                cjt[row * CST + slot] = (uint16_t)J;
                             }
                         }
                     }
@@ -587,7 +607,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
         const bool open = st0 == 1;
         const bool complete = open && nc <= cap;
         const int n = nc < cap ? nc : cap;
-        const float* cv = cval + srow * CAP;
+        const float* cv = cval + srow * CST;
         const double mx = row_m[srow];
         const double tau_row = solve_candidates(cv, n, mx, row_lo[srow],
                                                 mx - 2.0 / sqrt((double)(nc > 0 ? nc : 1)), complete, h);
@@ -600,7 +620,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
             const float tr = (float)tau_row;
             for (int i = h; i < n; i += 2)
                 if (cv[i] > tr) {
-                    const int J = cjt[srow * CAP + i];
+                    const int J = cjt[srow * CST + i];
                     atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
                 }
         }
@@ -861,7 +881,12 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
 template <typename T, int D>
 hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t stream) {
     if (phase & 1) {
-        hipLaunchKernelGGL((fwd_stats_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        if (fp.Tc <= 128)
+            hipLaunchKernelGGL((fwd_stats_kernel<T, D, 128>), dim3(grid), dim3(kNT), 0, stream, fp);
+        else if (fp.Tc <= 256)
+            hipLaunchKernelGGL((fwd_stats_kernel<T, D, 256>), dim3(grid), dim3(kNT), 0, stream, fp);
+        else
+            hipLaunchKernelGGL((fwd_stats_kernel<T, D, kMaxTc>), dim3(grid), dim3(kNT), 0, stream, fp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -45,23 +45,49 @@ struct TileDMA {
         return NT * kTileCh / kNT;
     }
 
-    // Stage NT tiles (rows r0[k] .. r0[k] + 63 of X, clamped to L - 1; rows
-    // past L hold junk that the masks discard) into dst (NT tiles back to back).
+    // Per-lane parts of the DMA addresses, fixed for a kernel: for each of a
+    // thread's instructions, the row within its tile, the tile index and the
+    // element offset of the (swizzled) source chunk within that row.
     template <int NT>
-    __device__ __forceinline__ static void issue(T* dst, const T* Xh, const int (&r0)[NT], int L) {
+    struct Lanes {
+        static constexpr int kIpw = NT * kTileCh / 4 / kWave;
+        int row[kIpw];
+        int tile[kIpw];
+        int col[kIpw];
+    };
+
+    template <int NT>
+    __device__ __forceinline__ static Lanes<NT> lanes() {
         const int t = threadIdx.x, w = t / kWave, lane = t & (kWave - 1);
         constexpr int kPerWave = NT * kTileCh / 4;
-        constexpr int kIpw = kPerWave / kWave;
+        Lanes<NT> ln;
+#pragma unroll
+        for (int k = 0; k < Lanes<NT>::kIpw; ++k) {
+            const int q = w * kPerWave + k * kWave + lane;
+            const int qt = q % kTileCh;
+            ln.tile[k] = q / kTileCh;
+            ln.row[k] = qt / kCPR;
+            ln.col[k] = swz<kCPR>(ln.row[k], qt % kCPR) * (16 / (int)sizeof(T));
+        }
+        return ln;
+    }
+
+    // Stage NT tiles (rows r0[k] .. r0[k] + 63 of X; rows past L read row
+    // L - 1, junk that the masks discard) into dst (NT tiles back to back).
+    template <int NT>
+    __device__ __forceinline__ static void issue(T* dst, const T* Xh, const int (&r0)[NT], int L,
+                                                 const Lanes<NT>& ln) {
+        const int w = threadIdx.x / kWave;
+        constexpr int kPerWave = NT * kTileCh / 4;
+        constexpr int kIpw = Lanes<NT>::kIpw;
         static_assert(kIpw * kWave * 4 == NT * kTileCh, "tile chunks must split evenly");
 #pragma unroll
         for (int k = 0; k < kIpw; ++k) {
-            const int q0 = w * kPerWave + k * kWave;  // first slot of this instruction
-            const int q = q0 + lane;
-            const int tile = q / kTileCh, qt = q % kTileCh;
-            const int r = qt / kCPR, pos = qt % kCPR;
-            int row = r0[tile] + r;
+            const int q0 = w * kPerWave + k * kWave;  // first slot of this instruction (uniform)
+            const int tr0 = r0[ln.tile[k]];
+            int row = tr0 + ln.row[k];
             row = row < L ? row : L - 1;
-            const T* src = Xh + (size_t)row * D + swz<kCPR>(r, pos) * (16 / (int)sizeof(T));
+            const T* src = Xh + (size_t)row * D + ln.col[k];
             T* base = dst + q0 * (16 / (int)sizeof(T));
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                              (__attribute__((address_space(3))) void*)(base), 16, 0, 0);

@@ -280,6 +280,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5"], default=None,
+                    help="run one workload only (for profiler passes); prints its record")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -295,6 +297,18 @@ def main():
     api.lib()
     timer = Timer(torch)
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.only is not None:
+        if args.only == "c2":
+            rec = bench_tau_rows(api, torch, timer, args.steps, args.warmup)
+        elif args.only == "c3":
+            rec = {C3A.name: bench_attn(api, torch, timer, C3A, args.steps, args.warmup)[0],
+                   C3B.name: bench_attn(api, torch, timer, C3B, args.steps, args.warmup)[0]}
+        elif args.only == "c4":
+            rec = bench_attn(api, torch, timer, C4, args.steps, args.warmup)[0]
+        else:
+            rec = bench_attn(api, torch, timer, C5, args.steps, args.warmup, with_bwd=True)[0]
+        print(json.dumps({"only": args.only, "record": rec}), flush=True)
+        return
 
     t_wall0 = time.perf_counter()
     head, (t_fwd, t_stats, t_out) = bench_attn(api, torch, timer, C4, args.steps, args.warmup)
