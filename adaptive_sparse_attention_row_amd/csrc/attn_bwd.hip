@@ -449,7 +449,8 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream) {
     bp.tau = a.tau; bp.mask = a.block_mask;
     bp.dq = a.dq; bp.dk = a.dk; bp.dv = a.dv;
     bp.delta = reinterpret_cast<float*>(a.workspace);
-    bp.BH = a.B * a.H; bp.L = a.L; bp.mode = a.mask; bp.W = a.window;
+    bp.BH = a.B * a.H; bp.L = a.L; bp.mode = a.mask;
+    bp.W = a.window < a.L ? a.window : a.L;  // a window of L or more is plain causal
     bp.nQ = (a.L + kBR - 1) / kBR;
     bp.Tc = (a.L + kBC - 1) / kBC;
     bp.Tr64 = (a.L + 63) / 64;

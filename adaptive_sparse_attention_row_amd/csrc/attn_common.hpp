@@ -12,6 +12,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
 
 #include "device_common.hpp"
 
@@ -332,22 +333,34 @@ struct Ops<float, D> {
     }
 };
 
-// Set masked elements of a partial tile to -inf (select, no branches).
+// Set masked elements of a partial tile to -inf.  Register r of lane half h
+// holds key jb + c(r) of the lane's query, c(r) = 8 (r / 4) + r % 4 a
+// compile-time offset, so every condition of key_active reduces to one
+// interval lo <= c(r) <= hi per lane and 32-key block (plus key 0 under the
+// sink): two compares with constants and a select per element.
 __device__ __forceinline__ void apply_mask(f32x16 (&acc)[2][2], int J, int R0, const Geom& g) {
     const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+        const int jb = J * kBC + kb * 32 + 4 * h;
+        const bool sink = (g.mode == 2) & (jb == 0);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int i = R0 + qb * 32 + m;
+            int hi = g.L - 1 - jb;                        // key < L
+            if (g.mode >= 1) hi = min(hi, i - jb);        // key <= query
+            if (i >= g.L) hi = -1;                        // query < L
+            const int lo = (g.mode == 2) ? i - jb - g.W : INT_MIN;  // query - key <= W
             f32x16 a = acc[kb][qb];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = J * kBC + kb * 32 + key_of_reg(r, h);
-                a[r] = key_active(i, j, g) ? a[r] : neg_inf();
+                const int c = 8 * (r >> 2) + (r & 3);
+                const bool act = (c <= hi) & ((c >= lo) | ((r == 0) & sink));
+                a[r] = act ? a[r] : neg_inf();
             }
             acc[kb][qb] = a;
         }
+    }
 }
 
 // Class of the block rows [i0, i0 + ni) x keys [c0, c0 + nc) under the mask.
@@ -363,23 +376,31 @@ __device__ __forceinline__ int block_class(int i0, int ni, int c0, int nc, const
 }
 
 // Masking for score blocks whose tile rows (registers) are QUERIES and whose
-// lanes are KEYS: query = I0 + kb*32 + reg row, key = C0 + cb*32 + lane.
+// lanes are KEYS (the backward's dK/dV orientation): register r of lane half
+// h holds query ib + c(r), so the conditions again reduce to one interval of
+// c(r) per lane (the sink column, key 0, drops the window bound).
 template <int NB>
 __device__ __forceinline__ void apply_mask_rows_are_queries(f32x16 (&acc)[2][NB], int I0, int C0, const Geom& g) {
     const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+        const int ib = I0 + kb * 32 + 4 * h;
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
             const int j = C0 + cb * 32 + m;
+            int hi = g.L - 1 - ib;                                       // query < L
+            if ((g.mode == 2) & (j != 0)) hi = min(hi, j - ib + g.W);    // query - key <= W
+            if (j >= g.L) hi = -1;                                       // key < L
+            const int lo = (g.mode >= 1) ? j - ib : INT_MIN;             // key <= query
             f32x16 a = acc[kb][cb];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int i = I0 + kb * 32 + key_of_reg(r, h);
-                a[r] = key_active(i, j, g) ? a[r] : neg_inf();
+                const int c = 8 * (r >> 2) + (r & 3);
+                a[r] = ((c <= hi) & (c >= lo)) ? a[r] : neg_inf();
             }
             acc[kb][cb] = a;
         }
+    }
 }
 
 // Work item -> (bh, first row).  Items of one q-block rank are consecutive

@@ -54,17 +54,15 @@ struct FwdParams {
     uint32_t* mask;   // [BH][Tr64][Wd]
     float* rowstat;   // workspace [BH][L][2]: row max, tau_lo (score units)
     float* umax;      // workspace [BH][Tr64][Tc]: largest raw score per (64-row block, tile)
+    float* cval;      // workspace [BH * nQ][kCandCap][128]: candidate scores, slot-major per row block
+    uint16_t* cjt;    // workspace, same shape: position of each candidate's tile in the tile list
     int BH, L, mode, W, nQ, Tc, Tr64, Wd;
     float scale;
     int cap;
 };
 
-// Candidate capacity per row (LDS-limited) and K buffering per variant.
-template <typename T, int D>
-struct FwdCfg {
-    static constexpr int kCap = (sizeof(T) == 2 && D == 64) ? 128 : 96;
-    static constexpr int kNBuf = (sizeof(T) == 4 && D == 128) ? 1 : 2;
-};
+// Candidate slots per row in the workspace lists.
+constexpr int kCandCap = 128;
 
 // ------------------------------------------------------------ tile lists
 // Build a list of tile indices with per-row-half flags (bit 0: qh 0,
@@ -180,8 +178,8 @@ __device__ __forceinline__ void sweep(const uint16_t* list, int n, const T* Kh, 
 // --------------------------------------------------------- DMA ring sweep
 // Stream the tiles of `list` in pairs (wave kh takes entry 2p + kh) through
 // an S-stage ring filled by direct global->LDS loads, keeping S - 1 pairs in
-// flight, and call fn(J, cls, acc) for every tile flagged for this wave's row
-// half.  One barrier per pair; the global loads stay outstanding across it.
+// flight, and call fn(J, e, acc) for every tile flagged for this wave's row
+// half (e: the tile's position in the list).  One barrier per pair; the global loads stay outstanding across it.
 template <typename T, int D, int S, class Fn>
 __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T* Kh, T* ring,
                                            const typename Ops<T, D>::template QOp<2>& qop, int R0,
@@ -228,7 +226,7 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
                     f32x16 acc[2][2];
                     O::scores(acc, ring + (pp % S) * kStage + kh * DMA::kTileElems, qop);
                     if (cls == kPartial) apply_mask(acc, J, R0, g);
-                    fn(J, cls, acc);
+                    fn(J, e, acc);
                 }
             }
         }
@@ -296,43 +294,94 @@ __device__ __forceinline__ void sort_desc(float (&x)[N]) {
             }
 }
 
-// Threshold of a row from its candidate list cv[0..n): every entry is above
-// `lo`, and none of the row's other scores is.  Two lanes share a row (h = 0
-// and 1 take alternate entries; sums are combined with lane l ^ 32).
-// Newton steps from below: f(t) = sum [(x - t)/2]_+^2 - 1 is convex and
-// decreasing, so a step from a point with f >= 0 stays at or below the root
-// (bisection takes over if rounding lands above it).  Exact finish: when the
-// closed-form root of {x > t} lies below the set's smallest member, that set
-// is the support and the root is tau.  Sums in fp64.  Returns tau; lanes with
-// active == false only take part in the exchanges.
-__device__ double solve_candidates(const float* cv, int n, double mx, double lo, double hi,
-                                   bool active, int h) {
+// Candidate slots per row kept in LDS; further slots live in the workspace.
+constexpr int kLdsCand = 48;
+
+// A row's candidate list: entry i at lds[i * kBR] for i < kLdsCand, else at
+// glob[i * kBR] (both slot-major over the 128 rows of a workgroup, so the
+// lanes of a wave touch consecutive words).  Two lanes share a row: the lane
+// with parity h takes entries start, start + 2, ... (start = h at first).
+struct CandSrc {
+    const float* lds;
+    const float* glob;
+    int n, start;
+    __device__ __forceinline__ float at(int i) const {
+        return i < kLdsCand ? lds[i * kBR] : glob[(size_t)i * kBR];
+    }
+    template <class F>
+    __device__ __forceinline__ void each(F f) const {
+        const int nl = n < kLdsCand ? n : kLdsCand;
+#pragma unroll 4
+        for (int i = start; i < nl; i += 2) f(lds[i * kBR]);
+#pragma unroll 4
+        for (int i = start > kLdsCand ? start : kLdsCand + (start & 1); i < n; i += 2) f(glob[(size_t)i * kBR]);
+    }
+};
+
+// The same list with the lane's first KR entries held in registers; missing
+// entries read -inf, which no threshold test passes.
+template <int KR>
+struct RegSrc {
+    float v[KR];
+    CandSrc tail;  // the lane's entries from start + 2 * KR on
+    static_assert(2 * KR <= kLdsCand, "register entries come from LDS");
+    __device__ __forceinline__ void load(const CandSrc& src) {
+#pragma unroll
+        for (int k = 0; k < KR; ++k) {
+            const int i = src.start + 2 * k;
+            v[k] = (i < src.n) ? src.lds[i * kBR] : neg_inf();
+        }
+        tail = src;
+        tail.start = src.start + 2 * KR;
+    }
+    template <class F>
+    __device__ __forceinline__ void each(F f) const {
+#pragma unroll
+        for (int k = 0; k < KR; ++k) f(v[k]);
+        tail.each(f);
+    }
+};
+
+// Threshold of a row from its candidates: every entry is above `lo`, and
+// none of the row's other scores is.  Two lanes share a row (sums are
+// combined with lane l ^ 32).  Newton steps from below: f(t) = sum
+// [(x - t)/2]_+^2 - 1 is convex and decreasing, so a step from a point with
+// f >= 0 stays at or below the root (bisection takes over if rounding lands
+// above it).  Exact finish: when the closed-form root of {x > t} lies below
+// the set's smallest member, that set is the support and the root is tau.
+// Sums in fp64.  Returns tau; lanes with active == false only take part in
+// the exchanges.
+template <class Src>
+__device__ __forceinline__ double solve_candidates(const Src& src, double mx, double lo, double hi,
+                                                   bool active) {
     double t = lo, result = lo;
     bool done = !active;
     for (int it = 0; it < kMaxIter; ++it) {
         if (__ballot(!done) == 0) break;
-        double C = 0, S1 = 0, S2 = 0, F = 0, F1 = 0;
+        // over {x > t}, with y = x - mx: count, sum y, sum y^2, smallest x
+        int c = 0;
+        double S1 = 0, S2 = 0;
         float mn = __builtin_inff();
         if (!done) {
-            for (int i = h; i < n; i += 2) {
-                const float x = cv[i];
-                if ((double)x > t) {
-                    const double y = (double)x - mx;
-                    const double gg = 0.5 * ((double)x - t);
-                    C += 1.0; S1 += y; S2 += y * y; F += gg * gg; F1 += gg;
-                    mn = fminf(mn, x);
-                }
-            }
+            src.each([&](float x) {
+                const bool on = (double)x > t;
+                const double y = on ? (double)x - mx : 0.0;
+                c += on ? 1 : 0;
+                S1 += y;
+                S2 = fma(y, y, S2);
+                mn = fminf(mn, on ? x : __builtin_inff());
+            });
         }
-        C += __shfl_xor(C, 32, kWave);
+        c += __shfl_xor(c, 32, kWave);
         S1 += __shfl_xor(S1, 32, kWave);
         S2 += __shfl_xor(S2, 32, kWave);
-        F += __shfl_xor(F, 32, kWave);
-        F1 += __shfl_xor(F1, 32, kWave);
         mn = fminf(mn, __shfl_xor(mn, 32, kWave));
         if (done) continue;
-        const double f = F - 1.0;
-        if (f >= 0.0 && C > 0.0) {
+        const double C = (double)c, u = t - mx;
+        // f(t) = sum ((y - u)/2)^2 - 1 and -f'(t) = sum (y - u)/2 over the set
+        const double f = 0.25 * (S2 - 2.0 * u * S1 + C * u * u) - 1.0;
+        const double F1 = 0.5 * (S1 - C * u);
+        if (f >= 0.0 && c > 0) {
             lo = t;
             const double disc = fmax(S1 * S1 - C * (S2 - 4.0), 0.0);
             const double ts = mx + (S1 - sqrt(disc)) / C;
@@ -358,9 +407,10 @@ __device__ double solve_candidates(const float* cv, int n, double mx, double lo,
 }
 
 // Largest entry of a candidate list (two lanes per row).
-__device__ __forceinline__ float list_max(const float* cv, int n, int h) {
+template <class Src>
+__device__ __forceinline__ float list_max(const Src& src) {
     float mx = neg_inf();
-    for (int i = h; i < n; i += 2) mx = fmaxf(mx, cv[i]);
+    src.each([&](float x) { mx = fmaxf(mx, x); });
     return fmaxf(mx, __shfl_xor(mx, 32, kWave));
 }
 
@@ -384,9 +434,17 @@ struct StatsCfg {
                               : (sizeof(T) == 2) ? ENTMAX_STATS_STAGES_BF16_128
                               : ((D == 128) ? 2 : 3);
 };
+#ifndef ENTMAX_COLLECT_STAGES
+#define ENTMAX_COLLECT_STAGES 2
+#endif
+#ifndef ENTMAX_COLLECT_OCCUPANCY
+#define ENTMAX_COLLECT_OCCUPANCY 2
+#endif
+// Ring stages and workgroups per CU of the candidate sweep.
 template <typename T, int D>
-struct SolveCfg {
-    static constexpr int kS = (sizeof(T) == 2 && D == 64) ? 3 : ((sizeof(T) == 4 && D == 128) ? 1 : 2);
+struct CollectCfg {
+    static constexpr int kS = (sizeof(T) == 4 && D == 128) ? 1 : ENTMAX_COLLECT_STAGES;
+    static constexpr int kOcc = (sizeof(T) == 2 && D == 64) ? ENTMAX_COLLECT_OCCUPANCY : 1;
 };
 
 constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
@@ -493,88 +551,91 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
 }
 
 // ------------------------------------------------------------ kernel 1b
-// Candidate sweep, exact per-row tau, block mask, fallback.
-template <typename T, int D>
-__global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
-    using O = Ops<T, D>;
-    constexpr int CAP = FwdCfg<T, D>::kCap;
-    constexpr int S = SolveCfg<T, D>::kS;
+// Candidate sweep over the tiles whose best score beats tau_lo: every score
+// above its row's tau_lo goes to the row's list (global memory, so the
+// workgroup's LDS stays small).  Rows whose list overflows get a tighter
+// bound (the threshold of the candidates they kept, a lower bound on tau
+// since tau only grows with the set) and are collected again; rows still
+// overflowing after kRounds are solved by Halley-bisection sweeps.  Then the
+// exact tau of every complete list (two lanes per row, the first
+// 2 * kSolveRegs candidates in registers), its non-null tiles (those holding
+// a candidate above tau), and tau and the mask words of both 64-row blocks.
+#ifndef ENTMAX_SOLVE_REGS
+#define ENTMAX_SOLVE_REGS 16
+#endif
+constexpr int kSolveRegs = ENTMAX_SOLVE_REGS;
 
+template <typename T, int D, int TCMAX>
+__global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kernel(FwdParams p) {
+    using O = Ops<T, D>;
+    constexpr int S = CollectCfg<T, D>::kS;
+    constexpr int WD = TCMAX / 32;
     __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
-    // odd row stride: the lanes of a wave read the same slot of 32 different
-    // rows at once, which must fall in different banks
-    constexpr int CST = CAP + 1;
-    __shared__ __attribute__((aligned(16))) float cval[kBR * CST];
-    __shared__ uint16_t cjt[kBR * CST];
-    __shared__ uint16_t list[kMaxTc];
-    __shared__ int cnt[kBR];
-    __shared__ float row_m[kBR], row_lo[kBR], row_tau[kBR];
-    __shared__ uint32_t maskw[2][kMaxTc / 32];
-    __shared__ int nlist_s, ovf_s;
-    __shared__ float fb_part[kBR][2][3];
+    // candidate slots [slot][row], then one spare word per thread
+    __shared__ float lval[kLdsCand * kBR + kNT];
+    __shared__ uint16_t lpos[kLdsCand * kBR + kNT];
+    __shared__ uint16_t list[TCMAX];
+    __shared__ float um_s[2][TCMAX];
+    __shared__ int cnt[kBR], rstate[kBR];
+    __shared__ float row_m[kBR], row_lo[kBR], row_hi[kBR], row_tau[kBR];
+    __shared__ uint32_t maskw[2][WD];
+    __shared__ int nlist_s, flag_s;
 
     const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    const size_t blk = (size_t)bh * p.nQ + r0 / kBR;
     const int R0 = r0 + 64 * qh;
     const Geom g = {p.L, p.mode, p.W};
     const size_t head_off = (size_t)bh * p.L * D;
     const T* Qh = reinterpret_cast<const T*>(p.q) + head_off;
     const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
-    const int cap = p.cap < CAP ? p.cap : CAP;
+    const int cap = p.cap < kCandCap ? p.cap : kCandCap;
+    float* cval = p.cval + blk * kCandCap * kBR;
+    uint16_t* cjt = p.cjt + blk * kCandCap * kBR;
+    const float2* rowstat = reinterpret_cast<const float2*>(p.rowstat) + (size_t)bh * p.L;
 
     typename O::template QOp<2> qop;
     O::load_q(qop, Qh, R0, p.L);
+    // row statistics and the tile maxima of both row blocks, loaded together
     if (t < kBR) {
-        const int grow = r0 + t;
-        float2 rs = make_float2(neg_inf(), __builtin_inff());
-        if (grow < p.L) rs = reinterpret_cast<const float2*>(p.rowstat)[(size_t)bh * p.L + grow];
+        const bool valid = (r0 + t) < p.L;
+        const float2 rs = valid ? rowstat[r0 + t] : make_float2(neg_inf(), __builtin_inff());
         row_m[t] = rs.x;
         row_lo[t] = rs.y;
         cnt[t] = 0;
+        rstate[t] = valid ? 1 : 0;  // 1: to collect, 3: list complete, 2: sweep fallback, 0: no row
     }
-    for (int i = t; i < 2 * (kMaxTc / 32); i += kNT) (&maskw[0][0])[i] = 0u;
+    for (int i = t; i < 2 * p.Tc; i += kNT) {
+        const int hh = i / p.Tc, J = i - hh * p.Tc;
+        const int I = r0 / 64 + hh;
+        um_s[hh][J] = (I < p.Tr64) ? p.umax[((size_t)bh * p.Tr64 + I) * p.Tc + J] * p.scale : neg_inf();
+    }
+    for (int i = t; i < 2 * WD; i += kNT) (&maskw[0][0])[i] = 0u;
     __syncthreads();
 
     // tiles whose best score beats the smallest tau_lo of the row half
     if (w == 0) {
-        float th[2];
-        const float* um[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            th[hh] = wave_min(row_lo[hh * 64 + l]);
-            const int I = r0 / 64 + hh;
-            um[hh] = (I < p.Tr64) ? p.umax + ((size_t)bh * p.Tr64 + I) * p.Tc : nullptr;
-        }
+        const float th0 = wave_min(row_lo[l]), th1 = wave_min(row_lo[64 + l]);
         const int n = build_list(list, p.Tc, [&](int J) {
-            const int f0 = (um[0] && um[0][J] * p.scale > th[0]) ? 1 : 0;
-            const int f1 = (um[1] && um[1][J] * p.scale > th[1]) ? 2 : 0;
-            return f0 | f1;
+            return (um_s[0][J] > th0 ? 1 : 0) | (um_s[1][J] > th1 ? 2 : 0);
         });
-        if (l == 0) {
-            nlist_s = n;
-            ovf_s = 0;
-        }
+        if (l == 0) nlist_s = n;
     }
     __syncthreads();
 
-    const int srow = qh * 64 + kh * 32 + m;  // the row this lane solves (with lane l ^ 32)
-    const bool svalid = (r0 + srow) < p.L;
-    // per-row state: 1 = to be (re)collected and solved, 0 = solved, 2 = overflowing
-    __shared__ int rstate[kBR];
-    if (t < kBR) rstate[t] = (r0 + t) < p.L ? 1 : 0;
-    __syncthreads();
-
+    const int srow = qh * 64 + kh * 32 + m;  // the row this lane handles (with lane l ^ 32)
+    const int lds_lim = cap < kLdsCand ? cap : kLdsCand;
+    const int spare = kLdsCand * kBR + t;
     for (int round = 0; round < kRounds; ++round) {
-        // ---- collect candidates s > tau_lo of the rows still open
         float lo_q[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = qh * 64 + qb * 32 + m;
             lo_q[qb] = rstate[row] == 1 ? row_lo[row] : __builtin_inff();
         }
-        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
+        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int e, f32x16(&acc)[2][2]) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 float bm = neg_inf();
@@ -583,88 +644,102 @@ __global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[kb][qb][r]);
                 if (__ballot(bm * p.scale > lo_q[qb]) == 0) continue;
-                const int row = qh * 64 + qb * 32 + m;
+                const float lo = lo_q[qb];
+                int nb = 0;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float sv = acc[kb][qb][r] * p.scale;
-                        if (sv > lo_q[qb]) {
-                            const int slot = atomicAdd(&cnt[row], 1);
-                            if (slot < cap) {
-                                cval[row * CST + slot] = sv;
-                                cjt[row * CST + slot] = (uint16_t)J;
-                            }
-                        }
+                        acc[kb][qb][r] *= p.scale;
+                        nb += acc[kb][qb][r] > lo ? 1 : 0;
                     }
+                const int row = qh * 64 + qb * 32 + m;
+                int base = 0;
+                if (nb) base = atomicAdd(&cnt[row], nb);
+                if (__ballot(base + nb > lds_lim) == 0) {
+                    // all in LDS: the lane's candidates take consecutive slots from
+                    // base in register order; other elements write the spare word
+                    int slot = base;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const bool on = acc[kb][qb][r] > lo;
+                            const int a = on ? slot * kBR + row : spare;
+                            lval[a] = acc[kb][qb][r];
+                            lpos[a] = (uint16_t)e;
+                            slot += on ? 1 : 0;
+                        }
+                } else {
+                    uint32_t bits = 0;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            bits |= (acc[kb][qb][r] > lo) ? (1u << (kb * 16 + r)) : 0u;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if ((bits >> (kb * 16 + r)) & 1u) {
+                                const int slot = base + __popc(bits & ((1u << (kb * 16 + r)) - 1u));
+                                const float sv = acc[kb][qb][r];
+                                if (slot < kLdsCand && slot < cap) {
+                                    lval[slot * kBR + row] = sv;
+                                    lpos[slot * kBR + row] = (uint16_t)e;
+                                } else if (slot < cap) {
+                                    cval[(size_t)slot * kBR + row] = sv;
+                                    cjt[(size_t)slot * kBR + row] = (uint16_t)e;
+                                }
+                            }
+                }
             }
         });
 
-        // ---- solve the open rows whose lists are complete; for overflowing
-        // rows, the threshold of the candidates they kept is a better bound
-        const int st0 = rstate[srow];
+        const bool open = rstate[srow] == 1;
         const int nc = cnt[srow];
-        const bool open = st0 == 1;
-        const bool complete = open && nc <= cap;
-        const int n = nc < cap ? nc : cap;
-        const float* cv = cval + srow * CST;
-        const double mx = row_m[srow];
-        const double tau_row = solve_candidates(cv, n, mx, row_lo[srow],
-                                                mx - 2.0 / sqrt((double)(nc > 0 ? nc : 1)), complete, h);
-        // subset threshold (a lower bound on the row's tau) for overflowing rows
         const bool over = open && nc > cap;
-        const float smax = list_max(cv, n, h);
-        const double tau_sub = solve_candidates(cv, n, smax, (double)smax - 2.0,
-                                                (double)smax - 2.0 / sqrt((double)(n > 0 ? n : 1)), over, h);
-        if (complete) {
-            const float tr = (float)tau_row;
-            for (int i = h; i < n; i += 2)
-                if (cv[i] > tr) {
-                    const int J = cjt[srow * CST + i];
-                    atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
-                }
+        float lo_new = neg_inf();
+        if (__ballot(over) != 0) {
+            // threshold of the kept candidates: a lower bound on the row's tau
+            const CandSrc src = {lval + srow, cval + srow, over ? cap : 0, h};
+            const float smax = list_max(src);
+            const double ts = solve_candidates(src, smax, (double)smax - 2.0,
+                                               (double)smax - 2.0 / sqrt((double)cap), over);
+            lo_new = __double2float_rd(ts);
         }
-        __syncthreads();  // every lane is done reading the lists
-        if (h == 0) {
-            if (complete) {
-                row_tau[srow] = (float)tau_row;
-                rstate[srow] = 0;
-            } else if (over) {
-                // upper bracket from this round's count of scores above tau_lo
-                fb_part[srow][0][1] = (float)(mx - 2.0 / sqrt((double)nc));
-                const float nl = fmaxf(row_lo[srow], (float)tau_sub);
-                // no progress possible: leave the row to the sweep fallback
+        if (h == 0 && open) {
+            if (!over) {
+                rstate[srow] = 3;  // list complete, nc entries
+            } else {
+                // every score above tau is above lo, so at most nc of them
+                row_hi[srow] = (float)((double)row_m[srow] - 2.0 / sqrt((double)nc));
+                const float nl = fmaxf(row_lo[srow], lo_new);
                 if (round == kRounds - 1 || !(nl > row_lo[srow])) rstate[srow] = 2;
                 row_lo[srow] = nl;
                 cnt[srow] = 0;
             }
         }
-        if (t == 0) ovf_s = 0;
+        if (t == 0) flag_s = 0;
         __syncthreads();
-        if (h == 0 && rstate[srow] == 1) atomicOr(&ovf_s, 1);
+        if (h == 0 && rstate[srow] == 1) atomicOr(&flag_s, 1);
         __syncthreads();
-        if (!ovf_s) break;
+        if (!flag_s) break;
     }
-    if (t == 0) ovf_s = 0;
+
+    if (t == 0) flag_s = 0;
     __syncthreads();
-    if (h == 0 && rstate[srow] == 2) {
-        atomicOr(&ovf_s, 1);
-        fb_part[srow][0][0] = row_lo[srow];
-    }
+    if (h == 0 && rstate[srow] == 2) atomicOr(&flag_s, 1);
     __syncthreads();
 
     // ---- fallback: Halley-bisection sweeps for rows whose list overflowed
-    if (ovf_s) {
-        // per-row state in LDS: lo in row_lo, hi in row_m's sibling array
-        __shared__ float fb_lo[kBR], fb_hi[kBR], fb_t[kBR];
+    if (flag_s) {
+        __shared__ float fb_t[kBR];
         __shared__ int fb_active[kBR];
-        __shared__ int fb_any;
+        __shared__ float fb_part[kBR][2][3];
         if (h == 0) {
-            const bool ovf = svalid && rstate[srow] == 2;
-            fb_active[srow] = ovf ? 1 : 0;
-            fb_lo[srow] = ovf ? fb_part[srow][0][0] : 0.f;
-            fb_hi[srow] = ovf ? fb_part[srow][0][1] : 0.f;
-            fb_t[srow] = ovf ? fb_part[srow][0][0] : 0.f;
+            fb_active[srow] = rstate[srow] == 2 ? 1 : 0;
+            fb_t[srow] = row_lo[srow];
         }
         __syncthreads();
         for (int it = 0; it < kFbMaxIter; ++it) {
@@ -708,37 +783,37 @@ __global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
                     fb_part[row][kh][2] = sf1[qb];
                 }
             }
-            if (t == 0) fb_any = 0;
+            if (t == 0) flag_s = 0;
             __syncthreads();
             if (h == 0 && fb_active[srow]) {
                 const float C = fb_part[srow][0][0] + fb_part[srow][1][0];
                 const float F = fb_part[srow][0][1] + fb_part[srow][1][1];
                 const float F1 = fb_part[srow][0][2] + fb_part[srow][1][2];
-                float lo = fb_lo[srow], hi = fb_hi[srow], tc = fb_t[srow];
+                float lo = row_lo[srow], hi = row_hi[srow], tc = fb_t[srow];
                 if (F - 1.0f >= 0.0f) lo = tc; else hi = tc;
                 if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
                     fb_active[srow] = 0;
                     row_tau[srow] = 0.5f * (lo + hi);
                 } else {
                     fb_t[srow] = halley_or_bisect(tc, F, F1, C, lo, hi);
-                    atomicOr(&fb_any, 1);
+                    atomicOr(&flag_s, 1);
                 }
-                fb_lo[srow] = lo;
-                fb_hi[srow] = hi;
+                row_lo[srow] = lo;
+                row_hi[srow] = hi;
             }
             __syncthreads();
-            if (!fb_any) break;
+            if (!flag_s) break;
         }
         // rows still active after the cap take their bracket midpoint
-        if (h == 0 && fb_active[srow]) row_tau[srow] = 0.5f * (fb_lo[srow] + fb_hi[srow]);
+        if (h == 0 && fb_active[srow]) row_tau[srow] = 0.5f * (row_lo[srow] + row_hi[srow]);
         __syncthreads();
-        // mark the tiles of the overflow rows
+        // mark the tiles of the fallback rows
         float tq[2];
         bool aq[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = qh * 64 + qb * 32 + m;
-            aq[qb] = (r0 + row) < p.L && rstate[row] == 2;
+            aq[qb] = rstate[row] == 2;
             tq[qb] = row_tau[row];
         }
         ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
@@ -755,11 +830,56 @@ __global__ __launch_bounds__(kNT, 1) void fwd_solve_kernel(FwdParams p) {
         });
     }
 
-    // ---- outputs: tau and the packed mask of both 64-row blocks
-    if (t < kBR) {
-        const int row = r0 + t;
-        if (row < p.L) p.tau[(size_t)bh * p.L + row] = row_tau[t];
+    // ---- exact tau of the rows with complete lists
+    {
+        const bool act = rstate[srow] == 3;
+        const int n = act ? cnt[srow] : 0;
+        RegSrc<kSolveRegs> src;
+        src.load(CandSrc{lval + srow, cval + srow, n, h});
+        const double mx = row_m[srow];
+        const double tau = solve_candidates(src, mx, row_lo[srow], mx - 2.0 / sqrt((double)(n > 0 ? n : 1)), act);
+        const float tr = (float)tau;
+        const int nl = nlist_s;
+        auto pos_of = [&](int i) -> int {
+            return i < kLdsCand ? lpos[i * kBR + srow] : cjt[(size_t)i * kBR + srow];
+        };
+        if (nl <= 64) {
+            // list positions holding a support entry, OR-ed over the wave, then
+            // one lane per position sets the tile's bit
+            uint64_t lm = 0;
+            if (act) {
+#pragma unroll
+                for (int k = 0; k < kSolveRegs; ++k) {
+                    const uint64_t b = 1ull << (pos_of(h + 2 * k) & 63);
+                    lm |= (src.v[k] > tr) ? b : 0ull;
+                }
+                for (int i = h + 2 * kSolveRegs; i < n; i += 2)
+                    if (src.tail.at(i) > tr) lm |= 1ull << pos_of(i);
+            }
+            uint32_t lo32 = (uint32_t)lm, hi32 = (uint32_t)(lm >> 32);
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                lo32 |= __shfl_xor(lo32, off, kWave);
+                hi32 |= __shfl_xor(hi32, off, kWave);
+            }
+            const uint32_t mine = (l < 32) ? (lo32 >> l) & 1u : (hi32 >> (l - 32)) & 1u;
+            if (l < nl && mine) {
+                const int J = list[l] & 0xfff;
+                atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
+            }
+        } else if (act) {
+            for (int i = h; i < n; i += 2)
+                if (src.tail.at(i) > tr) {
+                    const int J = list[pos_of(i)] & 0xfff;
+                    atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
+                }
+        }
+        if (act && h == 0) row_tau[srow] = tr;
     }
+    __syncthreads();
+
+    // ---- outputs: tau and the packed mask of both 64-row blocks
+    if (t < kBR && r0 + t < p.L) p.tau[(size_t)bh * p.L + r0 + t] = row_tau[t];
     for (int i = t; i < 2 * p.Wd; i += kNT) {
         const int hh = i / p.Wd, wd = i % p.Wd;
         const int I = r0 / 64 + hh;
@@ -891,7 +1011,12 @@ hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t st
         if (e != hipSuccess) return e;
     }
     if (phase & 2) {
-        hipLaunchKernelGGL((fwd_solve_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        if (fp.Tc <= 128)
+            hipLaunchKernelGGL((fwd_solve_kernel<T, D, 128>), dim3(grid), dim3(kNT), 0, stream, fp);
+        else if (fp.Tc <= 256)
+            hipLaunchKernelGGL((fwd_solve_kernel<T, D, 256>), dim3(grid), dim3(kNT), 0, stream, fp);
+        else
+            hipLaunchKernelGGL((fwd_solve_kernel<T, D, kMaxTc>), dim3(grid), dim3(kNT), 0, stream, fp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -913,12 +1038,16 @@ size_t umax_bytes(int B, int H, int L) {
     const size_t tr = (L + 63) / 64, tc = (L + 63) / 64;
     return (size_t)B * H * tr * tc * sizeof(float);
 }
+size_t cand_rows(int B, int H, int L) { return (size_t)B * H * ((L + kBR - 1) / kBR) * kBR; }
 
 }  // namespace
 }  // namespace attn
 
 size_t attn_threshold_workspace_bytes(int B, int H, int L) {
-    return attn::round256(attn::rowstat_bytes(B, H, L)) + attn::round256(attn::umax_bytes(B, H, L));
+    using namespace attn;
+    const size_t rows = cand_rows(B, H, L);
+    return round256(rowstat_bytes(B, H, L)) + round256(umax_bytes(B, H, L)) +
+           round256(rows * kCandCap * sizeof(float)) + round256(rows * kCandCap * sizeof(uint16_t));
 }
 
 size_t attn_fwd_workspace_bytes(int B, int H, int L, int, int) {
@@ -926,10 +1055,7 @@ size_t attn_fwd_workspace_bytes(int B, int H, int L, int, int) {
     return attn_threshold_workspace_bytes(B, H, L) + attn::round256(attn::mask_bytes(B, H, L));
 }
 
-int attn_max_candidate_cap(int d, int dtype) {
-    if (dtype == 1 && d == 64) return attn::FwdCfg<__bf16, 64>::kCap;
-    return attn::FwdCfg<__bf16, 128>::kCap;
-}
+int attn_max_candidate_cap(int, int) { return attn::kCandCap; }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream) {
     using namespace attn;
@@ -938,10 +1064,17 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream) {
     fp.q = a.q; fp.k = a.k; fp.v = a.v; fp.o = a.o; fp.tau = a.tau;
     char* ws = reinterpret_cast<char*>(a.workspace);
     fp.rowstat = reinterpret_cast<float*>(ws);
-    fp.umax = reinterpret_cast<float*>(ws + round256(rowstat_bytes(a.B, a.H, a.L)));
+    size_t off = round256(rowstat_bytes(a.B, a.H, a.L));
+    fp.umax = reinterpret_cast<float*>(ws + off);
+    off += round256(umax_bytes(a.B, a.H, a.L));
+    const size_t rows = cand_rows(a.B, a.H, a.L);
+    fp.cval = reinterpret_cast<float*>(ws + off);
+    off += round256(rows * kCandCap * sizeof(float));
+    fp.cjt = reinterpret_cast<uint16_t*>(ws + off);
     fp.mask = a.block_mask ? a.block_mask
                            : reinterpret_cast<uint32_t*>(ws + attn_threshold_workspace_bytes(a.B, a.H, a.L));
-    fp.BH = a.B * a.H; fp.L = a.L; fp.mode = a.mask; fp.W = a.window;
+    fp.BH = a.B * a.H; fp.L = a.L; fp.mode = a.mask;
+    fp.W = a.window < a.L ? a.window : a.L;  // a window of L or more is plain causal
     fp.nQ = (a.L + kBR - 1) / kBR;
     fp.Tc = (a.L + kBC - 1) / kBC;
     fp.Tr64 = (a.L + 63) / 64;

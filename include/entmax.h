@@ -99,9 +99,11 @@ int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t 
 
 /*
  * Workspace bytes entmax_attn_fwd needs: per-row statistics of the score
- * sweep (8 bytes per query row) and the largest score of every (64-row
- * block, 64-key tile) (4 bytes each), plus room for the block mask (used only
- * when block_mask == NULL).  entmax_attn_threshold needs the same minus the
+ * sweep (8 bytes per query row), the largest score of every (64-row block,
+ * 64-key tile) (4 bytes each), and per query row (L rounded up to 128) a
+ * list of up to 128 candidate scores with their key tiles
+ * (768 bytes per row), plus room for the block mask (used only when
+ * block_mask == NULL).  entmax_attn_threshold needs the same minus the
  * mask part: entmax_attn_threshold_workspace.  Both return 0 for invalid
  * arguments; the calls report those.
  */
@@ -191,9 +193,9 @@ int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
 /*
  * Process-wide tuning / testing options (not thread-safe; set before use).
  *  ENTMAX_OPT_CANDIDATE_CAP: per-row capacity of the forward's candidate
- *    buffer, 1 .. the compiled maximum (value <= 0 restores the default).
- *    Rows with more candidates take the iterative full-sweep path; tests use
- *    a tiny cap to force that path.
+ *    list, 1 .. 128 (value <= 0 restores 128).  Rows with more candidates
+ *    are collected again above a tighter bound, then take the iterative
+ *    full-sweep path; tests use a tiny cap to force those paths.
  * Returns the previous value, or -ENTMAX_ERR_ARG for an unknown option or an
  * out-of-range value.
  */

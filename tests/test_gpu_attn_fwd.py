@@ -255,7 +255,7 @@ def test_score_stats_bounds(env, orc, cfgname):
     Q, K = np32(inp["q"]), np32(inp["k"])
     L = cfg.L
     rng = np.random.default_rng(3)
-    cap = 128 if cfg.d == 64 else 96
+    cap = 128
     counts = []
     for bh in range(2):
         for i in np.concatenate([[0, 1, L - 1], rng.integers(0, L, 40)]):
