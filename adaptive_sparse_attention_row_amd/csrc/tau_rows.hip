@@ -1,19 +1,26 @@
 // tau_rows.hip -- row-wise 1.5-entmax threshold and probabilities on a
 // materialised fp32 score matrix (the HBM-bound row kernel).
 //
-// One 256-thread workgroup per row.  The row is read from HBM once into
-// registers, its maximum m is reduced across the workgroup, and the scores
-// above m - 2 (the lower bracket end of "AdaSplash-2: Faster Differentiable
-// Sparse Attention" sec. 2.4 in score units; no score at or below it can carry
-// weight) are compacted into LDS.  The threshold is then refined on those few
-// candidates only with the hybrid Halley-bisection of "AdaSplash: Adaptive
-// Sparse Flash Attention" (summary, Approach), safeguarded by the bracket
-// [m - 2, m - 2/sqrt(n)], with an exact finish: when tau sits below the
-// support, the support is {s > tau} and the normaliser restricted to it is a
-// quadratic in tau solved in closed form (the S0/S1/S2 form of AdaSplash-2
-// appendix C.3).  P is written from the register copy, so HBM sees one read
-// and one write per element.  Rows wider than the register capacity stream
-// the row three times (max, candidates, output).
+// Rows up to 8192 wide: one single-wave workgroup per row, the row read from
+// HBM once into registers (128 values per lane at 8192 columns, which leaves
+// room for three waves per SIMD, i.e. 12 rows in flight per CU).  Every
+// reduction is a DPP wave reduction; there are no barriers.  Per row:
+//   1. the maximum m;
+//   2. a lower bound on tau: the exact threshold of the 64 lane maxima, a
+//      subset of the row (a threshold only rises as scores are added);
+//   3. the scores above that bound, compacted into LDS (usually little more
+//      than the support);
+//   4. tau from those candidates by the hybrid Halley-bisection of "AdaSplash:
+//      Adaptive Sparse Flash Attention" (summary, Approach), inside the
+//      bracket [lower bound, m - 2/sqrt(n)] of "AdaSplash-2: Faster
+//      Differentiable Sparse Attention" sec. 2.4 (score units), with an exact
+//      finish: once the set {s > t} is the support, the normaliser restricted
+//      to it is a quadratic in tau solved in closed form (the S0/S1/S2 form of
+//      AdaSplash-2 appendix C.3);
+//   5. P from the register copy, so HBM sees one read and one write per
+//      element.
+// Wider rows take a 256-thread streaming kernel that reads the row three
+// times (maximum, candidates above m - 2, output).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -120,42 +127,129 @@ __device__ __forceinline__ float prob(float x, float tau) {
     return g * g;
 }
 
-// Register-resident row: VPT values per thread.  VEC: float4 accesses
-// (ld % 4 == 0 and 16-byte aligned S / P); otherwise scalar accesses.
-template <int VPT, bool VEC>
-__global__ __launch_bounds__(kThreads) void tau_rows_reg(const float* __restrict__ S,
-                                                        float* __restrict__ P,
-                                                        float* __restrict__ tau_out,
-                                                        int cols, int64_t ld) {
-    __shared__ float cand[kCandCap];
-    __shared__ float red[2][kWaves][6];
-    __shared__ float mbuf[kWaves];
-    __shared__ int wcnt[kWaves];
+// prob() with h = -tau/2 precomputed: fma(x, 1/2, h) rounds 0.5x - 0.5tau,
+// and halving is exact, so this equals 0.5 * (x - tau) bit for bit.
+__device__ __forceinline__ float prob_h(float x, float h) {
+    const float g = fmaxf(__builtin_fmaf(x, 0.5f, h), 0.0f);
+    return g * g;
+}
 
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const int64_t row = blockIdx.x;
+// DPP sum / min over the 64 lanes of a wave, result in every lane.  Lanes
+// with no source in a step read the identity (0 or +inf).
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+#define ENTMAX_DPP_STEP(op, idv, ctrl, rmask)                                                  \
+    x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                           \
+                  __builtin_bit_cast(int, idv), __builtin_bit_cast(int, x), ctrl, rmask, 0xf, \
+                  false)))
+#define ENTMAX_ADD(a, b) ((a) + (b))
+    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x111, 0xf);
+    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x112, 0xf);
+    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x114, 0xf);
+    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x118, 0xf);
+    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x142, 0xa);
+    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x143, 0xc);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ __forceinline__ float wave_min_dpp(float x) {
+    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x111, 0xf);
+    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x112, 0xf);
+    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x114, 0xf);
+    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x118, 0xf);
+    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x142, 0xa);
+    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x143, 0xc);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x111, 0xf);
+    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x112, 0xf);
+    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x114, 0xf);
+    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x118, 0xf);
+    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x142, 0xa);
+    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x143, 0xc);
+#undef ENTMAX_ADD
+#undef ENTMAX_DPP_STEP
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// Threshold of a set held by one wave: `each(t, sums)` adds this lane's part
+// of the sums over {x > t}.  Halley-bisection in the bracket [lo, m - 2/sqrt(n)]
+// (lo a lower bound on tau, no smaller than m - 2; n >= the support size)
+// with the exact finish of refine_tau; all sums are wave reductions.  Every
+// lane returns the same tau.
+template <class Each>
+__device__ __forceinline__ float wave_tau(float m, float n, float lo, Each each) {
+    float hi = m - 2.0f / sqrtf(n);
+    float t = lo;
+    for (int it = 0; it < kMaxIter; ++it) {
+        RowSums s = {0.f, 0.f, 0.f, 0.f, 0.f, __builtin_inff()};
+        each(t, s);
+        s.C = wave_sum_dpp(s.C);
+        s.S1 = wave_sum_dpp(s.S1);
+        s.S2 = wave_sum_dpp(s.S2);
+        s.F = wave_sum_dpp(s.F);
+        s.F1 = wave_sum_dpp(s.F1);
+        s.mn = wave_min_dpp(s.mn);
+        if (s.F - 1.0f >= 0.0f) {
+            const float ts = support_root(m, s.C, s.S1, s.S2);
+            if (ts < s.mn) return fmaxf(ts, t);
+            lo = t;
+        } else {
+            hi = t;
+        }
+        if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) break;
+        t = halley_or_bisect(t, s.F, s.F1, s.C, lo, hi);
+    }
+    return 0.5f * (lo + hi);
+}
+
+constexpr int kRowsPerBlock = 1;  // one single-wave workgroup per row
+constexpr int kWaveCand = 2048;                  // LDS candidates per wave
+
+// One single-wave workgroup per row (its slot frees as soon as that row is
+// done), the row register-resident: VPT values per lane (lane l holds columns
+// (64 k + l) * 4 + e for VEC, 64 k + l otherwise).  No barriers.  VEC: float4 accesses
+// (ld % 4 == 0 and 16-byte aligned S / P).
+template <int VPT, bool VEC>
+__global__ __launch_bounds__(kWave, 3) void tau_rows_wave(const float* __restrict__ S,
+                                                         float* __restrict__ P,
+                                                         float* __restrict__ tau_out,
+                                                         int64_t rows, int cols, int64_t ld) {
+    __shared__ float cand_all[kRowsPerBlock][kWaveCand];
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + w;
+    if (row >= rows) return;
+    float* cand = cand_all[w];
     const float* src = S + row * ld;
     float v[VPT];
 
+    // every chunk lies inside the row (wave-uniform): no guards
+    const bool full = cols == VPT * kWave;
     if constexpr (VEC) {
+        if (full) {
 #pragma unroll
-        for (int k = 0; k < VPT / 4; ++k) {
-            const int pos = (t + kThreads * k) * 4;
-            if (pos + 3 < cols) {
-                const f32x4 q = *reinterpret_cast<const f32x4*>(src + pos);
-                v[4 * k + 0] = q[0];
-                v[4 * k + 1] = q[1];
-                v[4 * k + 2] = q[2];
-                v[4 * k + 3] = q[3];
-            } else {
+            for (int k = 0; k < VPT / 4; ++k) {
+                const f32x4 q =
+                    __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (k * kWave + lane) * 4));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * k + e] = (pos + e < cols) ? src[pos + e] : neg_inf();
+                for (int e = 0; e < 4; ++e) v[4 * k + e] = q[e];
+            }
+        } else {
+            // chunks past the end re-read the last chunk that starts inside the
+            // row (ld % 4 == 0, so it lies within the row's ld span); entries at
+            // or past cols read -inf
+            const int last = ((cols - 1) / 4) * 4;
+#pragma unroll
+            for (int k = 0; k < VPT / 4; ++k) {
+                const int pos = (k * kWave + lane) * 4;
+                const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + min(pos, last)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * k + e] = (pos + e < cols) ? q[e] : neg_inf();
             }
         }
     } else {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int pos = t + kThreads * k;
+            const int pos = k * kWave + lane;
             v[k] = (pos < cols) ? src[pos] : neg_inf();
         }
     }
@@ -163,76 +257,69 @@ __global__ __launch_bounds__(kThreads) void tau_rows_reg(const float* __restrict
     float mx = neg_inf();
 #pragma unroll
     for (int k = 0; k < VPT; ++k) mx = fmaxf(mx, v[k]);
-    const float m = block_max(mx, mbuf);
+    const float m = wave_max_dpp(mx);
 
     float tau;
     if (m == neg_inf()) {
         tau = neg_inf();  // no active entry: P = 0
     } else {
-        const float lo0 = m - 2.0f;
-        uint32_t cnt = 0;
+        // Lower bound: the exact threshold of the 64 lane maxima, a subset of
+        // the row (a threshold only rises as scores are added).  The row's
+        // largest scores mostly sit in different lanes, so it is close to tau
+        // and few scores lie above it.
+        const float n1 = wave_sum_dpp(mx > neg_inf() ? 1.0f : 0.0f);
+        const float tlo = wave_tau(m, n1, m - 2.0f, [&](float tt, RowSums& s) { accumulate(s, mx, tt, m); });
+        // the scores above it, compacted in register order (elements where no
+        // lane has one are skipped)
+        int n = 0;
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) cnt += __popcll(__ballot(v[k] > lo0));
-        if (lane == 0) wcnt[w] = (int)cnt;
-        __syncthreads();
-        int base = 0, total = 0;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-            base += (i < w) ? wcnt[i] : 0;
-            total += wcnt[i];
-        }
-        if (total <= kCandCap) {
-            int off = base;
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const bool c = v[k] > lo0;
-                const uint64_t b = __ballot(c);
-                if (c) cand[off + lanes_below(b)] = v[k];
-                off += __popcll(b);
+        for (int k = 0; k < VPT; ++k) {
+            const bool c = v[k] > tlo;
+            const uint64_t b = __ballot(c);
+            if (b != 0) {
+                const int slot = n + lanes_below(b);
+                if (c && slot < kWaveCand) cand[slot] = v[k];
+                n += __popcll(b);
             }
-            __syncthreads();
-            tau = refine_tau(
-                m, (float)total,
-                [&](float tt, RowSums& s) {
-                    for (int i = t; i < total; i += kThreads) accumulate(s, cand[i], tt, m);
-                },
-                red);
+        }
+        if (n <= kWaveCand) {
+            tau = wave_tau(m, (float)n, tlo, [&](float tt, RowSums& s) {
+                for (int i = lane; i < n; i += kWave) accumulate(s, cand[i], tt, m);
+            });
         } else {
-            tau = refine_tau(
-                m, (float)total,
-                [&](float tt, RowSums& s) {
-#pragma unroll
-                    for (int k = 0; k < VPT; ++k) accumulate(s, v[k], tt, m);
-                },
-                red);
+            // more candidates than the LDS buffer (near-constant rows): sweep
+            // the row in memory each iteration (the register copy would be
+            // pinned twice over by the loop)
+            tau = wave_tau(m, (float)n, tlo, [&](float tt, RowSums& s) {
+                for (int pos = lane; pos < cols; pos += kWave) accumulate(s, src[pos], tt, m);
+            });
         }
     }
 
-    if (t == 0) tau_out[row] = tau;
+    if (lane == 0) tau_out[row] = tau;
     if (P == nullptr) return;
     float* dst = P + row * ld;
+    const float h = -0.5f * tau;
     if constexpr (VEC) {
 #pragma unroll
         for (int k = 0; k < VPT / 4; ++k) {
-            const int pos = (t + kThreads * k) * 4;
-            if (pos + 3 < cols) {
-                f32x4 q;
-                q[0] = prob(v[4 * k + 0], tau);
-                q[1] = prob(v[4 * k + 1], tau);
-                q[2] = prob(v[4 * k + 2], tau);
-                q[3] = prob(v[4 * k + 3], tau);
+            const int pos = (k * kWave + lane) * 4;
+            f32x4 q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[e] = prob_h(v[4 * k + e], h);
+            if (full || pos + 3 < cols) {
                 __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(dst + pos));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (pos + e < cols) dst[pos + e] = prob(v[4 * k + e], tau);
+                    if (pos + e < cols) dst[pos + e] = q[e];
             }
         }
     } else {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int pos = t + kThreads * k;
-            if (pos < cols) dst[pos] = prob(v[k], tau);
+            const int pos = k * kWave + lane;
+            if (pos < cols) dst[pos] = prob_h(v[k], h);
         }
     }
 }
@@ -305,10 +392,11 @@ __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restr
 }
 
 template <int VPT, bool VEC>
-hipError_t launch_reg(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
-                      int64_t ld, hipStream_t stream) {
-    hipLaunchKernelGGL((tau_rows_reg<VPT, VEC>), dim3((unsigned)rows), dim3(kThreads), 0,
-                       stream, S, P, tau, (int)cols, ld);
+hipError_t launch_wave(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
+                       int64_t ld, hipStream_t stream) {
+    const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL((tau_rows_wave<VPT, VEC>), dim3((unsigned)blocks), dim3(kWave), 0, stream, S,
+                       P, tau, rows, (int)cols, ld);
     return hipGetLastError();
 }
 
@@ -319,15 +407,16 @@ hipError_t launch_tau_rows(const float* S, float* P, float* tau, int64_t rows, i
     const bool vec = (ld % 4 == 0) && ((uintptr_t)S % 16 == 0) &&
                      (P == nullptr || (uintptr_t)P % 16 == 0);
     if (vec) {
-        if (cols <= 1 * 4 * kThreads) return launch_reg<4, true>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 2 * 4 * kThreads) return launch_reg<8, true>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 4 * 4 * kThreads) return launch_reg<16, true>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 8 * 4 * kThreads) return launch_reg<32, true>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 8 * kWave) return launch_wave<8, true>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 16 * kWave) return launch_wave<16, true>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 32 * kWave) return launch_wave<32, true>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 64 * kWave) return launch_wave<64, true>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 128 * kWave) return launch_wave<128, true>(S, P, tau, rows, cols, ld, stream);
     } else {
-        if (cols <= 4 * kThreads) return launch_reg<4, false>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 8 * kThreads) return launch_reg<8, false>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 16 * kThreads) return launch_reg<16, false>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 32 * kThreads) return launch_reg<32, false>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 8 * kWave) return launch_wave<8, false>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 16 * kWave) return launch_wave<16, false>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 32 * kWave) return launch_wave<32, false>(S, P, tau, rows, cols, ld, stream);
+        if (cols <= 64 * kWave) return launch_wave<64, false>(S, P, tau, rows, cols, ld, stream);
     }
     hipLaunchKernelGGL(tau_rows_stream, dim3((unsigned)rows), dim3(kThreads), 0, stream, S, P,
                        tau, cols, ld);
