@@ -244,6 +244,79 @@ def bench_tau_rows(api, torch, timer, steps, warmup):
     }
 
 
+COPY_BYTES = 256 << 20  # per direction
+
+
+def bench_copy(torch, timer, steps, warmup):
+    """A plain device-to-device copy of COPY_BYTES (3 rotating buffer pairs):
+    the reference for scaling the HBM byte counters of the kernels."""
+    n = COPY_BYTES // 4
+    xs = [torch.randn(n, device="cuda") for _ in range(3)]
+    ys = [torch.empty_like(xs[0]) for _ in range(3)]
+    it = [0]
+
+    def run():
+        i = it[0] % 3
+        it[0] += 1
+        ys[i].copy_(xs[i])
+
+    t = timer(run, steps, warmup)
+    return {"workload": "device copy", "bytes_each_way": COPY_BYTES, "ms": round(t, 5),
+            "GB_per_s": round(2 * COPY_BYTES / (t * 1e-3) / 1e9, 1)}
+
+
+def read_counter_csv(path, kernel_substr, counter):
+    """Mean per-dispatch value of `counter` over the dispatches of kernels
+    whose name contains kernel_substr, from a rocprofv3 counter_collection.csv."""
+    import csv
+    vals = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for kernels matching {kernel_substr!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def counters_summary(args):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a kernel by what the
+    same counters read for the copy of known size, and record the HBM bytes
+    per launch with the digest of the kernel's sources."""
+    sources = {"stats": STATS_SOURCES, "taurows": TAUROWS_SOURCES}[args.sources]
+    kf, nkf = read_counter_csv(args.fetch_csv, args.kernel, "FETCH_SIZE")
+    kw, nkw = read_counter_csv(args.write_csv, args.kernel, "WRITE_SIZE")
+    cf, _ = read_counter_csv(args.copy_fetch_csv, args.copy_kernel, "FETCH_SIZE")
+    cw, _ = read_counter_csv(args.copy_write_csv, args.copy_kernel, "WRITE_SIZE")
+    ff = COPY_BYTES / 1024.0 / cf   # true KiB per counted KiB, reads
+    fw = COPY_BYTES / 1024.0 / cw   # same, writes
+    fetch_b = kf * ff * 1024.0
+    write_b = kw * fw * 1024.0
+    rec = {
+        "kernel": args.kernel,
+        "source_digest": source_digest(sources),
+        "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kw, 1),
+        "dispatches": [nkf, nkw],
+        "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+        "scale_fetch": round(ff, 4), "scale_write": round(fw, 4),
+        "hbm_fetch_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(fetch_b + write_b),
+    }
+    out = os.path.join(ROOT, "profiles", f"{args.counters_summary}.counters.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", f"{args.counters_summary}.counters.md"), "w") as f:
+        f.write(f"# HBM traffic of `{args.kernel}`\n\n")
+        f.write("Commands (from /tmp with TMPDIR=/tmp; R = repository root; one counter per run):\n\n```\n")
+        f.write(args.commands.replace(";;", "\n") + "\n```\n\n")
+        f.write("| | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch |\n|---|---|---|\n")
+        f.write(f"| kernel | {kf:.1f} | {kw:.1f} |\n")
+        f.write(f"| copy of {COPY_BYTES >> 20} MiB each way | {cf:.1f} | {cw:.1f} |\n\n")
+        f.write(f"Scale (true/counted): fetch {ff:.4f}, write {fw:.4f}.  HBM bytes per launch: "
+                f"{int(fetch_b)} read + {int(write_b)} written = {int(fetch_b + write_b)}.\n")
+    print(json.dumps(rec))
+
+
 def cpu_baseline(cfg, target_s=15.0):
     """The fp64 oracle on evenly spaced query rows of the same workload."""
     import numpy as np
@@ -280,9 +353,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "copy"], default=None,
                     help="run one workload only (for profiler passes); prints its record")
+    ap.add_argument("--counters-summary", metavar="NAME", default=None,
+                    help="write profiles/NAME.counters.{json,md} from rocprofv3 counter CSVs (no GPU)")
+    ap.add_argument("--kernel", default=None, help="kernel name substring (with --counters-summary)")
+    ap.add_argument("--sources", choices=["stats", "taurows"], default="stats")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--copy-fetch-csv")
+    ap.add_argument("--copy-write-csv")
+    ap.add_argument("--copy-kernel", default="copyBuffer")
+    ap.add_argument("--commands", default="", help="the profiling commands, ';;'-separated")
     args = ap.parse_args()
+    if args.counters_summary is not None:
+        counters_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is described in DESIGN.md, not implemented)", file=sys.stderr)
@@ -298,7 +384,9 @@ def main():
     timer = Timer(torch)
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.only is not None:
-        if args.only == "c2":
+        if args.only == "copy":
+            rec = bench_copy(torch, timer, args.steps, args.warmup)
+        elif args.only == "c2":
             rec = bench_tau_rows(api, torch, timer, args.steps, args.warmup)
         elif args.only == "c3":
             rec = {C3A.name: bench_attn(api, torch, timer, C3A, args.steps, args.warmup)[0],
