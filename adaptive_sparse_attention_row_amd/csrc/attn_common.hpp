@@ -24,6 +24,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBR = 128;      // query rows per workgroup
 constexpr int kBC = 64;       // keys per tile
@@ -338,14 +339,15 @@ struct Ops<float, D> {
 // compile-time offset, so every condition of key_active reduces to one
 // interval lo <= c(r) <= hi per lane and 32-key block (plus key 0 under the
 // sink): two compares with constants and a select per element.
-__device__ __forceinline__ void apply_mask(f32x16 (&acc)[2][2], int J, int R0, const Geom& g) {
+template <int NB>
+__device__ __forceinline__ void apply_mask(f32x16 (&acc)[2][NB], int J, int R0, const Geom& g) {
     const int l = lane_id(), m = l & 31, h = l >> 5;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const int jb = J * kBC + kb * 32 + 4 * h;
         const bool sink = (g.mode == 2) & (jb == 0);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < NB; ++qb) {
             const int i = R0 + qb * 32 + m;
             int hi = g.L - 1 - jb;                        // key < L
             if (g.mode >= 1) hi = min(hi, i - jb);        // key <= query

@@ -1005,6 +1005,177 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
     }
 }
 
+// ------------------------------------------------------------ kernel 2, bf16
+// Output over the non-null tiles for bf16 inputs.  Each of the four waves
+// owns 32 query rows and every key of a tile, so nothing is reduced across
+// waves.  K (natural, swizzled) and V (transposed to V^T[d][key]) are staged
+// per tile through registers into two LDS buffers.  O^T += V^T A^T runs on
+// fp16 MFMA, the recipe of "AdaSplash-2: Faster Differentiable Sparse
+// Attention" sec. 3.3 phase 4 (A and the V tile cast to fp16): A <= 1 keeps 11
+// significant bits in fp16, and bf16 V converts exactly within fp16 range.  A
+// workgroup that meets a V entry beyond that range redoes its rows with A
+// split into bf16 hi + lo against bf16 V.
+template <int D>
+__global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(FwdParams p) {
+    using O = Ops<__bf16, D>;
+    constexpr int kVRow = O::kVRow;
+    constexpr int kKPer = O::kChunks / kNT;  // K chunks per thread per tile
+    static_assert(O::kChunks % kNT == 0 && O::kVUnits <= kNT, "staging split");
+    __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][O::kKTile];
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][D * kVRow];  // fp16 or bf16 bits
+    __shared__ uint16_t list[kMaxTc];
+    __shared__ uint32_t mw[2][kMaxTc / 32];
+    __shared__ int nlist_s, vover_s;
+
+    const int t = threadIdx.x, w = t / kWave;
+    const int l = lane_id(), m = l & 31, h = l >> 5;
+    int bh, r0;
+    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    const int R0 = r0 + 32 * w;  // this wave's rows
+    const int hh = w >> 1;       // their 64-row block
+    const Geom g = {p.L, p.mode, p.W};
+    const size_t head_off = (size_t)bh * p.L * D;
+    const __bf16* Qh = reinterpret_cast<const __bf16*>(p.q) + head_off;
+    const __bf16* Kh = reinterpret_cast<const __bf16*>(p.k) + head_off;
+    const __bf16* Vh = reinterpret_cast<const __bf16*>(p.v) + head_off;
+
+    for (int i = t; i < 2 * p.Wd; i += kNT) {
+        const int b = i / p.Wd, wd = i % p.Wd;
+        const int I = r0 / 64 + b;
+        mw[b][wd] = (I < p.Tr64) ? p.mask[((size_t)bh * p.Tr64 + I) * p.Wd + wd] : 0u;
+    }
+    if (t == 0) vover_s = 0;
+    __syncthreads();
+    if (w == 0) {
+        const int n = build_list(list, p.Tc, [&](int J) {
+            return (int)((mw[0][J >> 5] >> (J & 31)) & 1u) | (int)(((mw[1][J >> 5] >> (J & 31)) & 1u) << 1);
+        });
+        if (l == 0) nlist_s = n;
+    }
+    typename O::template QOp<1> qop;
+    O::load_q(qop, Qh, R0, p.L);
+    const float tq = (R0 + m < p.L) ? p.tau[(size_t)bh * p.L + R0 + m] : __builtin_inff();
+    __syncthreads();
+    const int n = nlist_s;
+
+    u32x4 kr[kKPer];
+    typename O::VRegs vr;
+    auto load = [&](int e) {
+        const int c0 = (list[e] & 0xfff) * kBC;
+#pragma unroll
+        for (int i = 0; i < kKPer; ++i) kr[i] = O::load_k_chunk(Kh, c0, g.L, t + kNT * i);
+        if (t < O::kVUnits) vr = O::load_v_unit(Vh, c0, g.L, t);
+    };
+    // V^T row d holds keys 4kg .. 4kg + 3 of unit (kg, dg) at 4kg; fp16 when
+    // F16 (returns whether an entry left fp16 range), bf16 otherwise
+    auto store = [&](int buf, bool f16) -> bool {
+#pragma unroll
+        for (int i = 0; i < kKPer; ++i) O::store_k_chunk(kbuf[buf], t + kNT * i, kr[i]);
+        bool over = false;
+        if (t < O::kVUnits) {
+            if (!f16) {
+                O::store_v_unit(reinterpret_cast<__bf16*>(vbuf[buf]), t, vr);
+            } else {
+                const int kg = t % (kBC / 4), dg = t / (kBC / 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t hw[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t bits = (vr.r[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                        const float f = __builtin_bit_cast(float, bits << 16);
+                        over |= fabsf(f) > 65504.0f;
+                        hw[i] = __builtin_bit_cast(uint16_t, (_Float16)f);
+                    }
+                    u32x2 pk;
+                    pk[0] = hw[0] | (hw[1] << 16);
+                    pk[1] = hw[2] | (hw[3] << 16);
+                    *reinterpret_cast<u32x2*>(&vbuf[buf][(dg * 8 + e) * kVRow + 4 * kg]) = pk;
+                }
+            }
+        }
+        return over;
+    };
+
+    typename O::template OAcc<1> oa;
+    auto run = [&](bool f16) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oa.o[db][0][i] = 0.f;
+        if (n == 0) return;
+        bool over = false;
+        load(0);
+        over |= store(0, f16);
+        for (int e = 0; e < n; ++e) {
+            __syncthreads();  // buffer e & 1 is complete; nobody reads the other one any more
+            if (e + 1 < n) load(e + 1);
+            const int ent = list[e];
+            if ((ent >> (12 + hh)) & 1) {
+                const int J = ent & 0xfff;
+                const int cls = block_class(R0, 32, J * kBC, kBC, g);
+                if (cls != kSkip) {
+                    f32x16 acc[2][1];
+                    O::template scores<1>(acc, kbuf[e & 1], qop);
+                    if (cls == kPartial) apply_mask<1>(acc, J, R0, g);
+                    // A = [(s - tau)/2]_+^2 with s = scale * (Q.K); A <= 1, so no
+                    // partial sum of A V exceeds max |V|
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float dd = 0.5f * fmaxf(acc[kb][0][r] * p.scale - tq, 0.0f);
+                            acc[kb][0][r] = dd * dd;
+                        }
+                    if (f16) {
+                        const uint16_t* Vt = vbuf[e & 1];
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int s2 = 0; s2 < 2; ++s2) {
+                                f16x8 b;
+#pragma unroll
+                                for (int q = 0; q < 8; ++q) b[q] = (_Float16)acc[kb][0][8 * s2 + q];
+#pragma unroll
+                                for (int db = 0; db < D / 32; ++db) {
+                                    const uint16_t* row = Vt + (db * 32 + m) * kVRow + kb * 32 + 16 * s2 + 4 * h;
+                                    const u32x2 lo4 = *reinterpret_cast<const u32x2*>(row);
+                                    const u32x2 hi4 = *reinterpret_cast<const u32x2*>(row + 8);
+                                    u32x4 vv;
+                                    vv[0] = lo4[0]; vv[1] = lo4[1]; vv[2] = hi4[0]; vv[3] = hi4[1];
+                                    oa.o[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                        __builtin_bit_cast(f16x8, vv), b, oa.o[db][0], 0, 0, 0);
+                                }
+                            }
+                    } else {
+                        const bool on[2] = {true, true};
+                        O::template pv<1>(oa, reinterpret_cast<const __bf16*>(vbuf[e & 1]), acc, on);
+                    }
+                }
+            }
+            if (e + 1 < n) over |= store((e + 1) & 1, f16);
+        }
+        if (over) atomicOr(&vover_s, 1);
+        __syncthreads();
+    };
+    run(true);
+    if (vover_s) run(false);  // a V entry beyond fp16 range somewhere in this block's tiles
+
+    // O = sum A V; register r of a lane holds d = db*32 + 8(r/4) + 4h + r%4
+    if (R0 + m < p.L) {
+        float* orow = p.o + ((size_t)bh * p.L + R0 + m) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = oa.o[db][0][4 * r4 + e];
+                *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * r4 + 4 * h) = v4;
+            }
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t stream) {
     if (phase & 1) {
@@ -1028,7 +1199,10 @@ hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t st
         if (e != hipSuccess) return e;
     }
     if (phase & 4) {
-        hipLaunchKernelGGL((fwd_out_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        if constexpr (sizeof(T) == 2)
+            hipLaunchKernelGGL((fwd_out_bf16_kernel<D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        else
+            hipLaunchKernelGGL((fwd_out_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
         return hipGetLastError();
     }
     return hipSuccess;

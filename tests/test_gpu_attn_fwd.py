@@ -273,3 +273,26 @@ def test_score_stats_bounds(env, orc, cfgname):
     counts = np.array(counts)
     print(f"{cfgname}: candidates above tau_lo mean {counts.mean():.1f} max {counts.max()} (capacity {cap})")
     assert counts.max() <= cap
+
+
+@pytest.mark.parametrize("vbig", [6.0e4, 2.0e5, 3.0e38], ids=["fp16_range", "beyond_fp16", "bf16_max"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_v(env, orc, vbig, d):
+    """bf16 V entries beyond fp16 range (|v| > 65504) send their workgroup
+    through the bf16 hi + lo product; entries inside it stay on fp16.  Both
+    must match the oracle to the bf16 bound relative to max |V|."""
+    api, torch = env
+    import torch as T
+    inp = gen(1, 2, 300, d, "bf16", seed=77 + d)
+    v = inp["v"].float()
+    v[0, 0, 5] = vbig          # one key row of head 0
+    v[0, 1, 130, : d // 2] = -vbig   # part of a key row of head 1
+    inp["v"] = v.to(T.bfloat16)
+    for mode, W in ((0, 0), (1, 0)):
+        O, tau, _ = run_gpu(api, torch, inp, 1.0 / math.sqrt(d), mode, W, want_mask=False)
+        assert np.all(np.isfinite(O)), f"non-finite O for |v| = {vbig}"
+        Q, K, V = np32(inp["q"]), np32(inp["k"]), np32(inp["v"])
+        O_ref, tau_ref, _, _ = orc.attn_fwd(Q, K, V, 1.0 / math.sqrt(d), mode, W)
+        vmax = float(np.abs(V).max())
+        err = np.abs(O.reshape(-1, d) - O_ref).max()
+        assert err <= O_TOL["bf16"] * max(1.0, vmax), f"|v| = {vbig} mode {mode}: O max err {err}"
