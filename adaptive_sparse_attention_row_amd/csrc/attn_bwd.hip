@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
     __shared__ int nlist_s;
     T* lds = reinterpret_cast<T*>(smem);
 
-    const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
+    const int t = threadIdx.x, w = wave_id(), qh = w & 1, kh = w >> 1;
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
     __shared__ float tau_s[64], del_s[64];
     __shared__ int nlist_s;
 
-    const int t = threadIdx.x, w = t / kWave;
+    const int t = threadIdx.x, w = wave_id();
     const int l = lane_id(), m = l & 31, h = l >> 5;
     const int bh = blockIdx.x % p.BH;
     const int c0 = (blockIdx.x / p.BH) * DkvCfg<T, D>::kKeys;

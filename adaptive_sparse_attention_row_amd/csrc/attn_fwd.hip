@@ -90,7 +90,7 @@ template <typename T, int D, int NBUF, bool WITH_V, class Fn>
 __device__ __forceinline__ void sweep(const uint16_t* list, int n, const T* Kh, const T* Vh, T* kbuf, T* vbuf,
                       const typename Ops<T, D>::template QOp<2>& qop, int R0, const Geom& g, Fn fn) {
     using O = Ops<T, D>;
-    const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
+    const int t = threadIdx.x, w = wave_id(), qh = w & 1, kh = w >> 1;
     constexpr int kKPer = 2 * O::kChunks / kNT;                         // K chunks per thread per pair
     constexpr int kVPer = WITH_V ? (2 * O::kVUnits + kNT - 1) / kNT : 0;  // V units per thread per pair
     const int npairs = (n + 1) / 2;
@@ -192,16 +192,17 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
     using DMA = TileDMA<T, D>;
     constexpr int kIpp = DMA::template instrs<2>();
     constexpr int kStage = 2 * DMA::kTileElems;
-    const int w = threadIdx.x / kWave, qh = w & 1, kh = w >> 1;
+    const int w = wave_id(), qh = w & 1, kh = w >> 1;
     const int npairs = (n + 1) / 2;
     if (npairs == 0) return;
     const auto ln = DMA::template lanes<2>();
+    // list entries are the same for the whole wave: read them into scalars
     auto issue = [&](int pp) {
         int r0[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int e = 2 * pp + u;
-            r0[u] = (e < n) ? (list[e] & 0xfff) * kBC : 0;
+            r0[u] = (e < n) ? (__builtin_amdgcn_readfirstlane(list[e]) & 0xfff) * kBC : 0;
         }
         DMA::template issue<2>(ring + (pp % S) * kStage, Kh, r0, g.L, ln);
     };
@@ -209,7 +210,7 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
     auto tile_of = [&](int pp, int& e, int& J) -> int {
         e = 2 * pp + kh;
         if (e >= n) return kSkip;
-        const int ent = list[e];
+        const int ent = __builtin_amdgcn_readfirstlane(list[e]);
         J = ent & 0xfff;
         if (!((ent >> (12 + qh)) & 1)) return kSkip;
         return tile_class(J, R0, g);
@@ -242,23 +243,26 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
 }
 
 // Maximum over the 64 lanes of a wave, by DPP row shifts and broadcasts
-// (VALU only), returned to every lane.
+// (VALU only), returned to every lane.  Each step is one v_max_f32 with a
+// DPP source; a lane without a source is not written and keeps its value,
+// which is what the max would give.  (The compiler does not fold a DPP move
+// whose fallback value is live into its user, hence the assembly; the
+// s_nop covers the two wait states a DPP read of a VGPR written by the
+// previous VALU instruction needs.)
+#define ENTMAX_DPP_MAX(ctrl)                                                       \
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " ctrl " bank_mask:0xf" : "=v"(y) : "v"(x), "0"(x)); \
+    x = y
 __device__ __forceinline__ float wave_max_dpp(float x) {
-// lanes without a source read -inf (the identity of max), so no copy of x
-// is needed per step
-#define ENTMAX_DPP_MAX(ctrl, rmask)                                                              \
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                          \
-                     __builtin_bit_cast(int, neg_inf()), __builtin_bit_cast(int, x), ctrl, rmask, \
-                     0xf, false)))
-    ENTMAX_DPP_MAX(0x111, 0xf);  // row_shr:1
-    ENTMAX_DPP_MAX(0x112, 0xf);  // row_shr:2
-    ENTMAX_DPP_MAX(0x114, 0xf);  // row_shr:4
-    ENTMAX_DPP_MAX(0x118, 0xf);  // row_shr:8  -> lane 15 of each row holds the row max
-    ENTMAX_DPP_MAX(0x142, 0xa);  // row_bcast:15
-    ENTMAX_DPP_MAX(0x143, 0xc);  // row_bcast:31 -> lane 63 holds the wave max
-#undef ENTMAX_DPP_MAX
+    float y;
+    ENTMAX_DPP_MAX("row_shr:1 row_mask:0xf");
+    ENTMAX_DPP_MAX("row_shr:2 row_mask:0xf");
+    ENTMAX_DPP_MAX("row_shr:4 row_mask:0xf");
+    ENTMAX_DPP_MAX("row_shr:8 row_mask:0xf");     // lane 15 of each row holds the row max
+    ENTMAX_DPP_MAX("row_bcast:15 row_mask:0xa");
+    ENTMAX_DPP_MAX("row_bcast:31 row_mask:0xc");  // lane 63 holds the wave max
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
+#undef ENTMAX_DPP_MAX
 
 // --------------------------------------------------------- small solvers
 // Exact threshold of N sorted-descending values (score units, -inf entries
@@ -448,10 +452,22 @@ struct StatsCfg {
 #define ENTMAX_COLLECT_OCCUPANCY 2
 #endif
 // Ring stages and workgroups per CU of the candidate sweep.
+#ifndef ENTMAX_COLLECT_STAGES_BF16_128
+#define ENTMAX_COLLECT_STAGES_BF16_128 1
+#endif
+#ifndef ENTMAX_COLLECT_OCCUPANCY_BF16_128
+#define ENTMAX_COLLECT_OCCUPANCY_BF16_128 2
+#endif
+// (bf16, d = 128: a one-stage ring leaves room in LDS for two workgroups per
+// CU, whose sweeps then hide each other's loads.)
 template <typename T, int D>
 struct CollectCfg {
-    static constexpr int kS = (sizeof(T) == 4 && D == 128) ? 1 : ENTMAX_COLLECT_STAGES;
-    static constexpr int kOcc = (sizeof(T) == 2 && D == 64) ? ENTMAX_COLLECT_OCCUPANCY : 1;
+    static constexpr int kS = (sizeof(T) == 4 && D == 128) ? 1
+                              : (sizeof(T) == 2 && D == 128) ? ENTMAX_COLLECT_STAGES_BF16_128
+                                                             : ENTMAX_COLLECT_STAGES;
+    static constexpr int kOcc = (sizeof(T) == 2 && D == 64)    ? ENTMAX_COLLECT_OCCUPANCY
+                                : (sizeof(T) == 2 && D == 128) ? ENTMAX_COLLECT_OCCUPANCY_BF16_128
+                                                               : 1;
 };
 
 constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
@@ -472,7 +488,7 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
     static_assert(sizeof(float) * 2 * kBR * 2 * kTop4 <= sizeof(T) * S * 2 * 64 * D, "merge space");
     StRow* st = reinterpret_cast<StRow*>(ring);
 
-    const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
+    const int t = threadIdx.x, w = wave_id(), qh = w & 1, kh = w >> 1;
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
@@ -565,12 +581,18 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
 // since tau only grows with the set) and are collected again; rows still
 // overflowing after kRounds are solved by Halley-bisection sweeps.  Then the
 // exact tau of every complete list (two lanes per row, the first
-// 2 * kSolveRegs candidates in registers), its non-null tiles (those holding
+// 2 * kSolveRegs<D> candidates in registers), its non-null tiles (those holding
 // a candidate above tau), and tau and the mask words of both 64-row blocks.
 #ifndef ENTMAX_SOLVE_REGS
 #define ENTMAX_SOLVE_REGS 16
 #endif
-constexpr int kSolveRegs = ENTMAX_SOLVE_REGS;
+#ifndef ENTMAX_SOLVE_REGS_128
+#define ENTMAX_SOLVE_REGS_128 8
+#endif
+// (d = 128 keeps fewer candidates in registers: its query operand takes twice
+// the registers, and the kernel runs two workgroups per CU.)
+template <int D>
+constexpr int kSolveRegs = D == 128 ? ENTMAX_SOLVE_REGS_128 : ENTMAX_SOLVE_REGS;
 
 template <typename T, int D, int TCMAX>
 __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kernel(FwdParams p) {
@@ -588,7 +610,7 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
     __shared__ uint32_t maskw[2][WD];
     __shared__ int nlist_s, flag_s;
 
-    const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
+    const int t = threadIdx.x, w = wave_id(), qh = w & 1, kh = w >> 1;
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
@@ -841,7 +863,7 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
     {
         const bool act = rstate[srow] == 3;
         const int n = act ? cnt[srow] : 0;
-        RegSrc<kSolveRegs> src;
+        RegSrc<kSolveRegs<D>> src;
         src.load(CandSrc{lval + srow, cval + srow, n, h});
         const double mx = row_m[srow];
         const double tau = solve_candidates(src, mx, row_lo[srow], mx - 2.0 / sqrt((double)(n > 0 ? n : 1)), act);
@@ -856,11 +878,11 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
             uint64_t lm = 0;
             if (act) {
 #pragma unroll
-                for (int k = 0; k < kSolveRegs; ++k) {
+                for (int k = 0; k < kSolveRegs<D>; ++k) {
                     const uint64_t b = 1ull << (pos_of(h + 2 * k) & 63);
                     lm |= (src.v[k] > tr) ? b : 0ull;
                 }
-                for (int i = h + 2 * kSolveRegs; i < n; i += 2)
+                for (int i = h + 2 * kSolveRegs<D>; i < n; i += 2)
                     if (src.tail.at(i) > tr) lm |= 1ull << pos_of(i);
             }
             uint32_t lo32 = (uint32_t)lm, hi32 = (uint32_t)(lm >> 32);
@@ -910,7 +932,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
     T* kbuf = reinterpret_cast<T*>(smem);
     T* vbuf = kbuf + NBUF * 2 * O::kKTile;
 
-    const int t = threadIdx.x, w = t / kWave, qh = w & 1, kh = w >> 1;
+    const int t = threadIdx.x, w = wave_id(), qh = w & 1, kh = w >> 1;
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
@@ -1027,7 +1049,7 @@ __global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(Fw
     __shared__ uint32_t mw[2][kMaxTc / 32];
     __shared__ int nlist_s, vover_s;
 
-    const int t = threadIdx.x, w = t / kWave;
+    const int t = threadIdx.x, w = wave_id();
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);

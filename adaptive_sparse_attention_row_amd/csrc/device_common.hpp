@@ -31,6 +31,10 @@ __device__ __forceinline__ float wave_min(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Index of this wave in its workgroup, as a scalar (it is the same for every
+// lane, and code that depends only on it then stays on the scalar unit).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
 // Number of set bits of `mask` in lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restr
     __shared__ float mbuf[kWaves];
     __shared__ int wcnt[kWaves];
 
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = wave_id();
     const int64_t row = blockIdx.x;
     const float* src = S + row * ld;
 

@@ -46,51 +46,73 @@ struct TileDMA {
     }
 
     // Per-lane parts of the DMA addresses, fixed for a kernel: for each of a
-    // thread's instructions, the row within its tile, the tile index and the
-    // element offset of the (swizzled) source chunk within that row.
+    // thread's instructions, the row within its tile, the tile index (the
+    // same for the whole wave), the element offset of the (swizzled) source
+    // chunk within that row, and row and chunk together as one offset from
+    // the tile's first element.
     template <int NT>
     struct Lanes {
         static constexpr int kIpw = NT * kTileCh / 4 / kWave;
         int row[kIpw];
         int tile[kIpw];
         int col[kIpw];
+        int off[kIpw];
     };
 
     template <int NT>
     __device__ __forceinline__ static Lanes<NT> lanes() {
-        const int t = threadIdx.x, w = t / kWave, lane = t & (kWave - 1);
+        const int t = threadIdx.x, lane = t & (kWave - 1);
+        const int w = wave_id();
         constexpr int kPerWave = NT * kTileCh / 4;
         Lanes<NT> ln;
 #pragma unroll
         for (int k = 0; k < Lanes<NT>::kIpw; ++k) {
             const int q = w * kPerWave + k * kWave + lane;
             const int qt = q % kTileCh;
-            ln.tile[k] = q / kTileCh;
+            ln.tile[k] = __builtin_amdgcn_readfirstlane(q / kTileCh);
             ln.row[k] = qt / kCPR;
             ln.col[k] = swz<kCPR>(ln.row[k], qt % kCPR) * (16 / (int)sizeof(T));
+            ln.off[k] = ln.row[k] * D + ln.col[k];
         }
         return ln;
     }
 
     // Stage NT tiles (rows r0[k] .. r0[k] + 63 of X; rows past L read row
     // L - 1, junk that the masks discard) into dst (NT tiles back to back).
+    // r0 must be wave-uniform: a tile inside [0, L) is then addressed from a
+    // scalar base plus the lane's fixed offset.
     template <int NT>
     __device__ __forceinline__ static void issue(T* dst, const T* Xh, const int (&r0)[NT], int L,
                                                  const Lanes<NT>& ln) {
-        const int w = threadIdx.x / kWave;
+        const int w = wave_id();
         constexpr int kPerWave = NT * kTileCh / 4;
         constexpr int kIpw = Lanes<NT>::kIpw;
         static_assert(kIpw * kWave * 4 == NT * kTileCh, "tile chunks must split evenly");
+        int rmax = r0[0];
 #pragma unroll
-        for (int k = 0; k < kIpw; ++k) {
-            const int q0 = w * kPerWave + k * kWave;  // first slot of this instruction (uniform)
-            const int tr0 = r0[ln.tile[k]];
-            int row = tr0 + ln.row[k];
-            row = row < L ? row : L - 1;
-            const T* src = Xh + (size_t)row * D + ln.col[k];
-            T* base = dst + q0 * (16 / (int)sizeof(T));
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                             (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
+        for (int k = 1; k < NT; ++k) rmax = rmax > r0[k] ? rmax : r0[k];
+        // (with more than four instructions per thread the offset table costs
+        // more registers than it saves instructions: rows are recomputed)
+        if (kIpw <= 4 && rmax + 64 <= L) {
+#pragma unroll
+            for (int k = 0; k < kIpw; ++k) {
+                const int q0 = w * kPerWave + k * kWave;  // first slot of this instruction
+                const T* tb = Xh + (size_t)r0[ln.tile[k]] * D;
+                T* base = dst + q0 * (16 / (int)sizeof(T));
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tb + (uint32_t)ln.off[k]),
+                                                 (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kIpw; ++k) {
+                const int q0 = w * kPerWave + k * kWave;
+                int row = r0[ln.tile[k]] + ln.row[k];
+                if (rmax + 64 > L) row = row < L ? row : L - 1;
+                const T* src = Xh + (size_t)row * D + ln.col[k];
+                T* base = dst + q0 * (16 / (int)sizeof(T));
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                                 (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
+            }
         }
     }
 };
