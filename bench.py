@@ -12,7 +12,9 @@ on the stream the library launches on:
     sweep, 2*d*pairs FLOP) -> the `roofline` object;
   * the row-wise tau kernel on the 8192 x 8192 fp32 score matrix (HBM-bound;
     3 rotating buffer sets so the 256 MB Infinity Cache cannot serve it);
-  * the other forward workloads and the backward, when built;
+  * the other forward workloads and the backward;
+  * the block-sparsity sweep (clustered L = 8192 with 64 ... 1 cluster runs)
+    with a linear fit of forward time against the non-null tile fraction;
 and the fp64 CPU oracle on a bounded sample of the same workload
 (`cpu_baseline`).  Rank 0 prints exactly one JSON line on stdout.
 """
@@ -209,6 +211,31 @@ def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False):
     return res, (t_fwd, t_stats, t_out)
 
 
+def bench_sweep(api, torch, timer, steps, warmup):
+    """Block-sparsity sweep: the clustered L = 8192 generator with 64 ... 1
+    cluster runs per head.  Fits t = t0 + t1 * (non-null tile fraction): t0 is
+    the part every configuration pays (the dense score sweep), t1 the part
+    that scales with the non-null tiles ("AdaSplash-2: Faster Differentiable
+    Sparse Attention", sec. 4.2: runtime falling with block sparsity)."""
+    from adaptive_sparse_attention_row_amd.workloads import sweep_configs
+    pts = []
+    for cfg in sweep_configs():
+        r, _ = bench_attn(api, torch, timer, cfg, steps, warmup)
+        frac = r["nonnull_tiles_64"] / r["structural_tiles_64"]
+        pts.append({"workload": cfg.name, "clusters": cfg.clusters, "nonnull_fraction": round(frac, 5),
+                    "fwd_ms": r["fwd_ms"], "score_stats_ms": r["score_stats_ms"], "solve_ms": r["solve_ms"],
+                    "output_ms": r["output_ms"], "dense_equiv_tflops": r["dense_equiv_tflops"]})
+        log(f"sweep {cfg.name}: non-null {frac:.4f} fwd {r['fwd_ms']:.4f} ms")
+    n = len(pts)
+    xs = [p["nonnull_fraction"] for p in pts]
+    ys = [p["fwd_ms"] for p in pts]
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    t1 = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx if sxx > 0 else 0.0
+    t0 = my - t1 * mx
+    return {"points": pts, "fit_ms": {"t0": round(t0, 5), "t1_per_unit_fraction": round(t1, 5)}}
+
+
 def bench_tau_rows(api, torch, timer, steps, warmup):
     from adaptive_sparse_attention_row_amd.workloads import C2, gen_rows
     S0 = gen_rows(C2.rows, C2.cols, C2.seed).cuda()
@@ -353,7 +380,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "copy"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "sweep", "copy"], default=None,
                     help="run one workload only (for profiler passes); prints its record")
     ap.add_argument("--counters-summary", metavar="NAME", default=None,
                     help="write profiles/NAME.counters.{json,md} from rocprofv3 counter CSVs (no GPU)")
@@ -393,6 +420,8 @@ def main():
                    C3B.name: bench_attn(api, torch, timer, C3B, args.steps, args.warmup)[0]}
         elif args.only == "c4":
             rec = bench_attn(api, torch, timer, C4, args.steps, args.warmup)[0]
+        elif args.only == "sweep":
+            rec = bench_sweep(api, torch, timer, args.steps, args.warmup)
         else:
             rec = bench_attn(api, torch, timer, C5, args.steps, args.warmup, with_bwd=True)[0]
         print(json.dumps({"only": args.only, "record": rec}), flush=True)
@@ -425,6 +454,8 @@ def main():
             log(f"{cfg.name}: {extras[cfg.name]}")
         extras[C5.name], _ = bench_attn(api, torch, timer, C5, max(2, args.steps // 4), 2, with_bwd=True)
         log(f"{C5.name}: {extras[C5.name]}")
+        extras["sparsity_sweep"] = bench_sweep(api, torch, timer, args.steps, args.warmup)
+        log(f"sparsity sweep fit: {extras['sparsity_sweep']['fit_ms']}")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -15,6 +15,9 @@ Definitions followed (see the header of ``entmax_oracle.c`` for the full list):
   * attention S = scale Q K^T, O = A V: AdaSplash-2 sec. 2.2.
   * backward restricted to the support: AdaSplash-2 sec. 3.3 "Backward pass".
   * block mask packing, 32 column blocks per word: AdaSplash-2 appendix C.4.
+  * general alpha in (1, 2] (AdaSplash-2 sec. 2.3): p = [(alpha-1)(s - tau)]_+
+    ^(1/(alpha-1)); exact by sorting at alpha = 2 (sparsemax), by bisection on
+    the bracket of sec. 2.4 for other alpha.
 """
 from __future__ import annotations
 
@@ -76,6 +79,25 @@ def _load() -> ctypes.CDLL:
     lib.orc_attn_bwd_rows.argtypes = [P, P, P, P, i64, i64, i64,
                                       ctypes.c_double, ctypes.c_int, i64, P,
                                       i64, P, P, P]
+    D = ctypes.c_double
+    lib.orc_entmax_tau_bisect.restype = D
+    lib.orc_entmax_tau_bisect.argtypes = [P, i64, D]
+    lib.orc_entmax_alpha.restype = D
+    lib.orc_entmax_alpha.argtypes = [P, i64, D, P, P]
+    lib.orc_tau_rows_alpha.restype = None
+    lib.orc_tau_rows_alpha.argtypes = [P, i64, i64, i64, D, P, P]
+    lib.orc_attn_fwd_alpha.restype = None
+    lib.orc_attn_fwd_alpha.argtypes = [P, P, P, i64, i64, i64, D, ctypes.c_int, i64, D,
+                                       P, i64, P, P, P, P]
+    lib.orc_block_mask_head_alpha.restype = None
+    lib.orc_block_mask_head_alpha.argtypes = [P, P, i64, i64, D, ctypes.c_int, i64, D,
+                                              i64, i64, D, P, P, P, P]
+    lib.orc_attn_bwd_head_alpha.restype = None
+    lib.orc_attn_bwd_head_alpha.argtypes = [P, P, P, P, i64, i64, D, ctypes.c_int, i64, D,
+                                            P, P, P, P, P]
+    lib.orc_attn_bwd_rows_alpha.restype = None
+    lib.orc_attn_bwd_rows_alpha.argtypes = [P, P, P, P, i64, i64, i64, D, ctypes.c_int,
+                                            i64, D, P, i64, P, P, P]
     _lib = lib
     return lib
 
@@ -107,19 +129,37 @@ def key_active(mask: int, window: int, i: int, j: int) -> bool:
     return bool(_load().orc_key_active(mask, window, i, j))
 
 
-def tau_rows(S, want_p: bool = True) -> tuple[np.ndarray, Optional[np.ndarray]]:
+def entmax(s, alpha: float = 1.5) -> tuple[np.ndarray, float, int]:
+    """alpha-entmax of one score vector for alpha in (1, 2] (fp64; -inf
+    entries are inactive): p = [(alpha-1)(s - tau)]_+^(1/(alpha-1)).
+
+    Returns (p, tau, support_size)."""
+    s = np.ascontiguousarray(np.asarray(s, dtype=np.float64))
+    p = np.empty_like(s)
+    k = ctypes.c_int64(0)
+    tau = _load().orc_entmax_alpha(_ptr(s), s.size, float(alpha), _ptr(p), ctypes.byref(k))
+    return p, float(tau), int(k.value)
+
+
+def tau_bisect(s, alpha: float) -> float:
+    """tau by plain bisection on the bracket (any alpha in (1, 2])."""
+    s = np.ascontiguousarray(np.asarray(s, dtype=np.float64))
+    return float(_load().orc_entmax_tau_bisect(_ptr(s), s.size, float(alpha)))
+
+
+def tau_rows(S, want_p: bool = True, alpha: float = 1.5) -> tuple[np.ndarray, Optional[np.ndarray]]:
     """Row-wise tau (and P) of a 2-D fp32 score matrix."""
     S = _f32(S)
     rows, cols = S.shape
     tau = np.empty(rows, dtype=np.float64)
     P = np.empty((rows, cols), dtype=np.float64) if want_p else None
-    _load().orc_tau_rows(_ptr(S), rows, cols, cols, _ptr(tau),
-                         _ptr(P) if P is not None else None)
+    _load().orc_tau_rows_alpha(_ptr(S), rows, cols, cols, float(alpha), _ptr(tau),
+                               _ptr(P) if P is not None else None)
     return tau, P
 
 
 def attn_fwd(Q, K, V, scale: float, mask: int = MASK_NONE, window: int = 0,
-             rows: Optional[np.ndarray] = None):
+             rows: Optional[np.ndarray] = None, alpha: float = 1.5):
     """Forward for the listed flattened query rows (all rows when None).
 
     Q, K, V: [B, H, L, d] (any float dtype holding exact values).
@@ -138,14 +178,14 @@ def attn_fwd(Q, K, V, scale: float, mask: int = MASK_NONE, window: int = 0,
     tau = np.empty(n, dtype=np.float64)
     nsup = np.empty(n, dtype=np.int64)
     gsum = np.empty(n, dtype=np.float64)
-    _load().orc_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), BH, L, d, float(scale),
-                         int(mask), int(window), rp, n, _ptr(O), _ptr(tau),
-                         _ptr(nsup), _ptr(gsum))
+    _load().orc_attn_fwd_alpha(_ptr(Q), _ptr(K), _ptr(V), BH, L, d, float(scale),
+                               int(mask), int(window), float(alpha), rp, n, _ptr(O),
+                               _ptr(tau), _ptr(nsup), _ptr(gsum))
     return O, tau, nsup, gsum
 
 
 def block_mask_head(Qh, Kh, scale: float, mask: int, window: int, br: int,
-                    bc: int, tol: float = 1e-4):
+                    bc: int, tol: float = 1e-4, alpha: float = 1.5):
     """Packed block masks of one head ([L, d] inputs) at tile br x bc.
 
     Returns (exact, must, may, tau); each mask is uint32 [Tr, ceil(Tc/32)]."""
@@ -157,14 +197,14 @@ def block_mask_head(Qh, Kh, scale: float, mask: int, window: int, br: int,
     lo = np.empty((Tr, Wd), dtype=np.uint32)
     hi = np.empty((Tr, Wd), dtype=np.uint32)
     tau = np.empty(L, dtype=np.float64)
-    _load().orc_block_mask_head(_ptr(Qh), _ptr(Kh), L, d, float(scale),
-                                int(mask), int(window), br, bc, float(tol),
-                                _ptr(ex), _ptr(lo), _ptr(hi), _ptr(tau))
+    _load().orc_block_mask_head_alpha(_ptr(Qh), _ptr(Kh), L, d, float(scale),
+                                      int(mask), int(window), float(alpha), br, bc,
+                                      float(tol), _ptr(ex), _ptr(lo), _ptr(hi), _ptr(tau))
     return ex, lo, hi, tau
 
 
 def attn_bwd_head(Qh, Kh, Vh, dOh, scale: float, mask: int = MASK_NONE,
-                  window: int = 0):
+                  window: int = 0, alpha: float = 1.5):
     """Full backward of one head ([L, d] inputs).
 
     Returns (dQ, dK, dV, tau, delta) in fp64."""
@@ -172,20 +212,21 @@ def attn_bwd_head(Qh, Kh, Vh, dOh, scale: float, mask: int = MASK_NONE,
     L, d = Qh.shape
     dQ = np.empty((L, d)); dK = np.empty((L, d)); dV = np.empty((L, d))
     tau = np.empty(L); delta = np.empty(L)
-    _load().orc_attn_bwd_head(_ptr(Qh), _ptr(Kh), _ptr(Vh), _ptr(dOh), L, d,
-                              float(scale), int(mask), int(window), _ptr(dQ),
-                              _ptr(dK), _ptr(dV), _ptr(tau), _ptr(delta))
+    _load().orc_attn_bwd_head_alpha(_ptr(Qh), _ptr(Kh), _ptr(Vh), _ptr(dOh), L, d,
+                                    float(scale), int(mask), int(window), float(alpha),
+                                    _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(tau), _ptr(delta))
     return dQ, dK, dV, tau, delta
 
 
-def attn_bwd_rows(Q, K, V, dO, scale: float, mask: int, window: int, rows):
+def attn_bwd_rows(Q, K, V, dO, scale: float, mask: int, window: int, rows,
+                  alpha: float = 1.5):
     """dQ, delta and tau for the listed flattened query rows of [B,H,L,d]."""
     Q, K, V, dO = _f32(Q), _f32(K), _f32(V), _f32(dO)
     B, H, L, d = Q.shape
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     n = rows.size
     dQ = np.empty((n, d)); delta = np.empty(n); tau = np.empty(n)
-    _load().orc_attn_bwd_rows(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), B * H, L, d,
-                              float(scale), int(mask), int(window), _ptr(rows),
-                              n, _ptr(dQ), _ptr(delta), _ptr(tau))
+    _load().orc_attn_bwd_rows_alpha(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), B * H, L, d,
+                                    float(scale), int(mask), int(window), float(alpha),
+                                    _ptr(rows), n, _ptr(dQ), _ptr(delta), _ptr(tau))
     return dQ, delta, tau

@@ -46,6 +46,21 @@
  *    column block J with A > 0 (AdaSplash-2 sec. 3.3 Phase 3, appendix C.4),
  *    packed 32 column blocks per uint32, bit (J mod 32) of word J / 32.
  *
+ * General alpha in (1, 2] (AdaSplash-2 sec. 2.3, alpha-entmax; its solvers in
+ * sec. 2.4), in the same score units: with e = 1/(alpha - 1),
+ *       p_j = [(alpha - 1)(s_j - tau)]_+^e,   sum_j p_j = 1
+ * (the pages write (alpha - 1) s_j - tau' with tau' = (alpha - 1) tau; for
+ * alpha = 1.5 this is the map above).  tau lies in the bracket
+ * [m - 1/(alpha-1), m - n^(1-alpha)/(alpha-1)] of AdaSplash-2 sec. 2.4
+ * (p_max between 1/n and 1).  alpha = 1.5 keeps the quadratic above;
+ * alpha = 2 (sparsemax) is exact by sorting: for the top-k set the
+ * normaliser sum_{t<=k} (x_t - tau) = 1 is linear, tau_k = (sum_{t<=k} x_t
+ * - 1)/k, and the support is the largest k with x_k > tau_k; any other alpha
+ * is solved by bisection on the bracket down to fp64 resolution.  The backward
+ * keeps its form with g_ij = [(alpha - 1)(s_ij - tau_i)]_+^(e - 1), the
+ * derivative of p_ij in s_ij (g = (s - tau)/2 at alpha = 1.5, the support
+ * indicator at alpha = 2).
+ *
  * All arithmetic is fp64; inputs arrive as fp32 arrays (bf16 and fp32 values
  * are both exactly representable there).  Sums run in index order.  Exact
  * zeros of A are skipped in the products, which changes no result.
@@ -124,12 +139,115 @@ double orc_entmax15(const double* s, int64_t n, double* p, int64_t* k_out) {
     return tau;
 }
 
+/* [u]_+^e for the alpha-entmax map (u = (alpha - 1)(s - tau)). */
+static double pos_pow(double u, double e) {
+    if (!(u > 0.0)) return 0.0;
+    if (e == 1.0) return u;
+    if (e == 2.0) return u * u;
+    return pow(u, e);
+}
+
+/* Exact sparsemax threshold (alpha = 2) of the n active entries of s: sort
+ * descending, tau_k = (sum_{t<=k} x_t - 1)/k, support = largest k with
+ * x_k > tau_k (k = 1 always qualifies). */
+static double sparsemax_tau(const double* s, int64_t n, double* work, int64_t* k_out) {
+    int64_t na = 0;
+    for (int64_t j = 0; j < n; ++j)
+        if (s[j] != -INFINITY) work[na++] = s[j];
+    if (na == 0) {
+        if (k_out) *k_out = 0;
+        return -INFINITY;
+    }
+    qsort(work, (size_t)na, sizeof(double), cmp_desc);
+    double c = 0.0, best = work[0] - 1.0;
+    int64_t kbest = 1;
+    for (int64_t k = 1; k <= na; ++k) {
+        c += work[k - 1];
+        const double t = (c - 1.0) / (double)k;
+        if (work[k - 1] > t) {
+            best = t;
+            kbest = k;
+        }
+    }
+    if (k_out) *k_out = kbest;
+    return best;
+}
+
+/* Bisection for any alpha in (1, 2] on the bracket
+ * [m - 1/(alpha-1), m - n^(1-alpha)/(alpha-1)]: f(t) = sum p_j(t) - 1 is
+ * decreasing, >= 0 at the lower end and <= 0 at the upper end.  Halves until
+ * the midpoint no longer moves (fp64 resolution). */
+double orc_entmax_tau_bisect(const double* s, int64_t n, double alpha) {
+    const double e = 1.0 / (alpha - 1.0);
+    double m = -INFINITY;
+    int64_t na = 0;
+    for (int64_t j = 0; j < n; ++j)
+        if (s[j] != -INFINITY) {
+            m = s[j] > m ? s[j] : m;
+            ++na;
+        }
+    if (na == 0) return -INFINITY;
+    double lo = m - e, hi = m - pow((double)na, 1.0 - alpha) * e;
+    for (int it = 0; it < 2000; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (mid <= lo || mid >= hi) break;
+        double f = -1.0;
+        for (int64_t j = 0; j < n; ++j)
+            if (s[j] != -INFINITY) f += pos_pow((alpha - 1.0) * (s[j] - mid), e);
+        if (f >= 0.0) lo = mid;
+        else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+/* tau of one row for alpha in (1, 2]; *k_out = support size. */
+double orc_entmax_tau_alpha(const double* s, int64_t n, double alpha, double* work,
+                            int64_t* k_out) {
+    if (alpha == 1.5) return orc_entmax15_tau(s, n, work, k_out);
+    double t;
+    if (alpha == 2.0) {
+        t = sparsemax_tau(s, n, work, k_out);
+    } else {
+        t = orc_entmax_tau_bisect(s, n, alpha);
+        if (k_out) {
+            int64_t k = 0;
+            for (int64_t j = 0; j < n; ++j) k += (s[j] != -INFINITY) && (s[j] > t);
+            *k_out = k;
+        }
+    }
+    return t;
+}
+
+/* Weight p and derivative g = dp/ds of one score at threshold tau. */
+static double weight_alpha(double x, double tau, double alpha) {
+    if (alpha == 1.5) {
+        const double g = (x > tau) ? 0.5 * (x - tau) : 0.0;
+        return g * g;
+    }
+    return (x > tau) ? pos_pow((alpha - 1.0) * (x - tau), 1.0 / (alpha - 1.0)) : 0.0;
+}
+static double grad_alpha(double x, double tau, double alpha) {
+    if (alpha == 1.5) return (x > tau) ? 0.5 * (x - tau) : 0.0;
+    if (!(x > tau)) return 0.0;
+    const double e1 = 1.0 / (alpha - 1.0) - 1.0;  /* 0 at alpha = 2: g = 1 on the support */
+    return e1 == 0.0 ? 1.0 : pos_pow((alpha - 1.0) * (x - tau), e1);
+}
+
+/* p of one row for alpha in (1, 2]; returns tau. */
+double orc_entmax_alpha(const double* s, int64_t n, double alpha, double* p, int64_t* k_out) {
+    double* work = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    const double tau = orc_entmax_tau_alpha(s, n, alpha, work, k_out);
+    for (int64_t j = 0; j < n; ++j) p[j] = weight_alpha(s[j], tau, alpha);
+    free(work);
+    return tau;
+}
+
 /*
  * Row-wise entmax of a materialised fp32 score matrix S[rows][ld] (cols used
  * per row).  tau[rows]; P[rows][cols] (row stride cols) may be NULL.
  */
-void orc_tau_rows(const float* S, int64_t rows, int64_t cols, int64_t ld,
-                  double* tau, double* P) {
+void orc_tau_rows_alpha(const float* S, int64_t rows, int64_t cols, int64_t ld,
+                        double alpha, double* tau, double* P) {
 #pragma omp parallel
     {
         double* row = (double*)malloc((size_t)(cols > 0 ? cols : 1) * sizeof(double));
@@ -137,18 +255,20 @@ void orc_tau_rows(const float* S, int64_t rows, int64_t cols, int64_t ld,
 #pragma omp for schedule(dynamic, 16)
         for (int64_t r = 0; r < rows; ++r) {
             for (int64_t c = 0; c < cols; ++c) row[c] = (double)S[r * ld + c];
-            const double t = orc_entmax15_tau(row, cols, work, NULL);
+            const double t = orc_entmax_tau_alpha(row, cols, alpha, work, NULL);
             tau[r] = t;
             if (P) {
-                for (int64_t c = 0; c < cols; ++c) {
-                    const double g = (row[c] > t) ? 0.5 * (row[c] - t) : 0.0;
-                    P[r * cols + c] = g * g;
-                }
+                for (int64_t c = 0; c < cols; ++c) P[r * cols + c] = weight_alpha(row[c], t, alpha);
             }
         }
         free(row);
         free(work);
     }
+}
+
+void orc_tau_rows(const float* S, int64_t rows, int64_t cols, int64_t ld, double* tau,
+                  double* P) {
+    orc_tau_rows_alpha(S, rows, cols, ld, 1.5, tau, P);
 }
 
 /* Active-key predicate of the three mask modes (0-indexed positions). */
@@ -180,13 +300,15 @@ static void head_row_scores(const float* Q, const float* K, int64_t L, int64_t d
  * Attention forward for a list of query rows.  Q, K, V are [BH][L][d].
  * rows[r] indexes the flattened [BH*L] query rows; rows == NULL means all
  * BH*L rows in order (nrows must then equal BH*L).  Outputs per listed row:
- * O[r][d], tau[r], and (optional) support size nsup[r] and the sum of g,
- * gsum[r] = sum_j [(s_j - tau)/2]_+.
+ * O[r][d], tau[r], and (optional) support size nsup[r] and the sum of the
+ * derivatives g over the row, gsum[r] = sum_j g_ij (sum_j [(s_j - tau)/2]_+
+ * at alpha = 1.5).
  */
-void orc_attn_fwd(const float* Q, const float* K, const float* V,
-                  int64_t BH, int64_t L, int64_t d, double scale, int mask,
-                  int64_t window, const int64_t* rows, int64_t nrows,
-                  double* O, double* tau, int64_t* nsup, double* gsum) {
+void orc_attn_fwd_alpha(const float* Q, const float* K, const float* V,
+                        int64_t BH, int64_t L, int64_t d, double scale, int mask,
+                        int64_t window, double alpha, const int64_t* rows,
+                        int64_t nrows, double* O, double* tau, int64_t* nsup,
+                        double* gsum) {
     (void)BH;
 #pragma omp parallel
     {
@@ -201,7 +323,7 @@ void orc_attn_fwd(const float* Q, const float* K, const float* V,
             const float* Vh = V + bh * L * d;
             head_row_scores(Qh, Kh, L, d, scale, mask, window, i, s);
             int64_t k = 0;
-            const double t = orc_entmax15_tau(s, L, work, &k);
+            const double t = orc_entmax_tau_alpha(s, L, alpha, work, &k);
             tau[r] = t;
             if (nsup) nsup[r] = k;
             double* o = O + r * d;
@@ -209,9 +331,8 @@ void orc_attn_fwd(const float* Q, const float* K, const float* V,
             double gs = 0.0;
             for (int64_t j = 0; j < L; ++j) {
                 if (!(s[j] > t)) continue; /* A_ij = 0 exactly */
-                const double g = 0.5 * (s[j] - t);
-                const double a = g * g;
-                gs += g;
+                const double a = weight_alpha(s[j], t, alpha);
+                gs += grad_alpha(s[j], t, alpha);
                 const float* v = Vh + j * d;
                 for (int64_t c = 0; c < d; ++c) o[c] += a * (double)v[c];
             }
@@ -222,6 +343,13 @@ void orc_attn_fwd(const float* Q, const float* K, const float* V,
     }
 }
 
+void orc_attn_fwd(const float* Q, const float* K, const float* V, int64_t BH, int64_t L,
+                  int64_t d, double scale, int mask, int64_t window, const int64_t* rows,
+                  int64_t nrows, double* O, double* tau, int64_t* nsup, double* gsum) {
+    orc_attn_fwd_alpha(Q, K, V, BH, L, d, scale, mask, window, 1.5, rows, nrows, O, tau, nsup,
+                       gsum);
+}
+
 /*
  * Block masks of one head at tile br x bc.  Three masks, each
  * [ceil(L/br)][ceil(ceil(L/bc)/32)] words:
@@ -230,10 +358,10 @@ void orc_attn_fwd(const float* Q, const float* K, const float* V,
  *   m_hi:    tile has an entry with s - tau > -tol     (may be set)
  * tau_out[L] receives the row thresholds when not NULL.
  */
-void orc_block_mask_head(const float* Q, const float* K, int64_t L, int64_t d,
-                         double scale, int mask, int64_t window, int64_t br,
-                         int64_t bc, double tol, uint32_t* m_exact,
-                         uint32_t* m_lo, uint32_t* m_hi, double* tau_out) {
+void orc_block_mask_head_alpha(const float* Q, const float* K, int64_t L, int64_t d,
+                               double scale, int mask, int64_t window, double alpha,
+                               int64_t br, int64_t bc, double tol, uint32_t* m_exact,
+                               uint32_t* m_lo, uint32_t* m_hi, double* tau_out) {
     const int64_t Tr = (L + br - 1) / br, Tc = (L + bc - 1) / bc;
     const int64_t Wd = (Tc + 31) / 32;
     memset(m_exact, 0, (size_t)(Tr * Wd) * sizeof(uint32_t));
@@ -248,7 +376,7 @@ void orc_block_mask_head(const float* Q, const float* K, int64_t L, int64_t d,
         for (int64_t I = 0; I < Tr; ++I) {
             for (int64_t i = I * br; i < L && i < (I + 1) * br; ++i) {
                 head_row_scores(Q, K, L, d, scale, mask, window, i, s);
-                const double t = orc_entmax15_tau(s, L, work, NULL);
+                const double t = orc_entmax_tau_alpha(s, L, alpha, work, NULL);
                 if (tau_out) tau_out[i] = t;
                 for (int64_t j = 0; j < L; ++j) {
                     if (s[j] == -INFINITY) continue;
@@ -265,16 +393,23 @@ void orc_block_mask_head(const float* Q, const float* K, int64_t L, int64_t d,
     }
 }
 
+void orc_block_mask_head(const float* Q, const float* K, int64_t L, int64_t d, double scale,
+                         int mask, int64_t window, int64_t br, int64_t bc, double tol,
+                         uint32_t* m_exact, uint32_t* m_lo, uint32_t* m_hi, double* tau_out) {
+    orc_block_mask_head_alpha(Q, K, L, d, scale, mask, window, 1.5, br, bc, tol, m_exact, m_lo,
+                              m_hi, tau_out);
+}
+
 /*
  * Full backward of one head.  Q, K, V, dO are [L][d]; outputs dQ, dK, dV are
  * [L][d]; tau[L], delta[L] optional.  Row pass (parallel over queries): tau,
  * the support, delta, dQ_i, and the support's (j, A_ij, dS_ij).  Column pass
  * (serial in query order per key): dK_j and dV_j from those entries.
  */
-void orc_attn_bwd_head(const float* Q, const float* K, const float* V,
-                       const float* dO, int64_t L, int64_t d, double scale,
-                       int mask, int64_t window, double* dQ, double* dK,
-                       double* dV, double* tau_out, double* delta_out) {
+void orc_attn_bwd_head_alpha(const float* Q, const float* K, const float* V,
+                             const float* dO, int64_t L, int64_t d, double scale,
+                             int mask, int64_t window, double alpha, double* dQ,
+                             double* dK, double* dV, double* tau_out, double* delta_out) {
     int64_t* sup_off = (int64_t*)calloc((size_t)L + 1, sizeof(int64_t));
     int64_t** sup_j = (int64_t**)calloc((size_t)L, sizeof(int64_t*));
     double** sup_a = (double**)calloc((size_t)L, sizeof(double*));
@@ -287,7 +422,7 @@ void orc_attn_bwd_head(const float* Q, const float* K, const float* V,
         for (int64_t i = 0; i < L; ++i) {
             head_row_scores(Q, K, L, d, scale, mask, window, i, s);
             int64_t k = 0;
-            const double t = orc_entmax15_tau(s, L, work, &k);
+            const double t = orc_entmax_tau_alpha(s, L, alpha, work, &k);
             if (tau_out) tau_out[i] = t;
             int64_t cnt = 0;
             for (int64_t j = 0; j < L; ++j) cnt += (s[j] > t);
@@ -302,13 +437,13 @@ void orc_attn_bwd_head(const float* Q, const float* K, const float* V,
             int64_t c = 0;
             for (int64_t j = 0; j < L; ++j) {
                 if (!(s[j] > t)) continue;
-                const double g = 0.5 * (s[j] - t);
+                const double g = grad_alpha(s[j], t, alpha);
                 const float* v = V + j * d;
                 double dot = 0.0;
                 for (int64_t e = 0; e < d; ++e) dot += (double)go[e] * (double)v[e];
                 jj[c] = j;
                 gg[c] = g;
-                aa[c] = g * g;
+                aa[c] = weight_alpha(s[j], t, alpha);
                 da[c] = dot;
                 num += g * dot;
                 den += g;
@@ -358,15 +493,23 @@ void orc_attn_bwd_head(const float* Q, const float* K, const float* V,
     free(sup_ds);
 }
 
+void orc_attn_bwd_head(const float* Q, const float* K, const float* V, const float* dO,
+                       int64_t L, int64_t d, double scale, int mask, int64_t window,
+                       double* dQ, double* dK, double* dV, double* tau_out,
+                       double* delta_out) {
+    orc_attn_bwd_head_alpha(Q, K, V, dO, L, d, scale, mask, window, 1.5, dQ, dK, dV, tau_out,
+                            delta_out);
+}
+
 /*
  * dQ and delta for a list of query rows of a [BH][L][d] batch (no dK/dV):
  * cheap enough to sample at any size.  dQ[r][d], delta[r], tau[r].
  */
-void orc_attn_bwd_rows(const float* Q, const float* K, const float* V,
-                       const float* dO, int64_t BH, int64_t L, int64_t d,
-                       double scale, int mask, int64_t window,
-                       const int64_t* rows, int64_t nrows, double* dQ,
-                       double* delta_out, double* tau_out) {
+void orc_attn_bwd_rows_alpha(const float* Q, const float* K, const float* V,
+                             const float* dO, int64_t BH, int64_t L, int64_t d,
+                             double scale, int mask, int64_t window, double alpha,
+                             const int64_t* rows, int64_t nrows, double* dQ,
+                             double* delta_out, double* tau_out) {
     (void)BH;
 #pragma omp parallel
     {
@@ -382,12 +525,12 @@ void orc_attn_bwd_rows(const float* Q, const float* K, const float* V,
             const float* Vh = V + bh * L * d;
             const float* go = dO + flat * d;
             head_row_scores(Qh, Kh, L, d, scale, mask, window, i, s);
-            const double t = orc_entmax15_tau(s, L, work, NULL);
+            const double t = orc_entmax_tau_alpha(s, L, alpha, work, NULL);
             if (tau_out) tau_out[r] = t;
             double num = 0.0, den = 0.0;
             for (int64_t j = 0; j < L; ++j) {
                 if (!(s[j] > t)) continue;
-                const double g = 0.5 * (s[j] - t);
+                const double g = grad_alpha(s[j], t, alpha);
                 const float* v = Vh + j * d;
                 double dot = 0.0;
                 for (int64_t e = 0; e < d; ++e) dot += (double)go[e] * (double)v[e];
@@ -401,7 +544,7 @@ void orc_attn_bwd_rows(const float* Q, const float* K, const float* V,
             for (int64_t e = 0; e < d; ++e) dq[e] = 0.0;
             for (int64_t j = 0; j < L; ++j) {
                 if (!(s[j] > t)) continue;
-                const double g = 0.5 * (s[j] - t);
+                const double g = grad_alpha(s[j], t, alpha);
                 const double ds = g * (da[j] - delta);
                 const float* kk = Kh + j * d;
                 for (int64_t e = 0; e < d; ++e) dq[e] += scale * ds * (double)kk[e];
@@ -411,4 +554,12 @@ void orc_attn_bwd_rows(const float* Q, const float* K, const float* V,
         free(work);
         free(da);
     }
+}
+
+void orc_attn_bwd_rows(const float* Q, const float* K, const float* V, const float* dO,
+                       int64_t BH, int64_t L, int64_t d, double scale, int mask,
+                       int64_t window, const int64_t* rows, int64_t nrows, double* dQ,
+                       double* delta_out, double* tau_out) {
+    orc_attn_bwd_rows_alpha(Q, K, V, dO, BH, L, d, scale, mask, window, 1.5, rows, nrows, dQ,
+                            delta_out, tau_out);
 }

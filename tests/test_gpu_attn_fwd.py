@@ -296,3 +296,26 @@ def test_large_v(env, orc, vbig, d):
         vmax = float(np.abs(V).max())
         err = np.abs(O.reshape(-1, d) - O_ref).max()
         assert err <= O_TOL["bf16"] * max(1.0, vmax), f"|v| = {vbig} mode {mode}: O max err {err}"
+
+
+@pytest.mark.parametrize("nc", [16, 4, 1])
+def test_sparsity_sweep_sampled(env, orc, nc):
+    """The block-sparsity sweep's generator (clustered L = 8192 with 16, 4
+    and 1 cluster runs, two heads): sampled rows against the oracle, and the
+    mask of one head."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import gen_config, sweep_configs
+    cfg = [c for c in sweep_configs() if c.clusters == nc][0]
+    inp = gen_config(cfg, H=2)
+    O, tau, bm = run_gpu(api, torch, inp, cfg.scale, cfg.mask, cfg.window)
+    L = cfg.L
+    rng = np.random.default_rng(nc)
+    rows = []
+    for bh in range(2):
+        pick = np.concatenate([[0, L // 2, L - 1], rng.integers(0, L, 40)])
+        rows.extend(bh * L + pick)
+    err = check_rows(orc, inp, cfg.scale, cfg.mask, cfg.window, O, tau, "bf16", rows=np.array(rows),
+                     label=cfg.name)
+    check_mask(orc, inp, cfg.scale, cfg.mask, cfg.window, bm, [1], label=cfg.name)
+    nnz = sum(bin(int(x)).count("1") for x in bm.reshape(-1))
+    print(f"{cfg.name}: max |dO| = {err:.3e}, block sparsity {1 - nnz / (2 * 128 * 128):.4f}")
