@@ -102,9 +102,10 @@ def set_option(option: int, value: int) -> int:
     return r
 
 
-def tau_rows(S, want_p: bool = True, P=None, tau=None):
-    """Row-wise 1.5-entmax of a [rows, cols] fp32 CUDA tensor (row stride may
-    exceed cols).  Returns (tau [rows], P [rows, cols] or None)."""
+def tau_rows(S, want_p: bool = True, P=None, tau=None, alpha: float = 1.5):
+    """Row-wise alpha-entmax (alpha in (1, 2], default 1.5) of a [rows, cols]
+    fp32 CUDA tensor (row stride may exceed cols).  Returns (tau [rows],
+    P [rows, cols] or None)."""
     import torch
     if not S.is_cuda or S.dtype != torch.float32 or S.dim() != 2 or S.stride(1) != 1:
         raise ValueError("S must be a 2-D fp32 CUDA tensor with unit column stride")
@@ -117,7 +118,7 @@ def tau_rows(S, want_p: bool = True, P=None, tau=None):
     if P is not None and P.stride() != (ld, 1) and rows > 1:
         raise ValueError("P must share S's row stride")
     st = lib().entmax_tau_rows(S.data_ptr(), _dev_ptr(P), tau.data_ptr(), rows, cols, ld,
-                               1.5, _stream(S.device))
+                               float(alpha), _stream(S.device))
     _check("entmax_tau_rows", st)
     return tau, P
 

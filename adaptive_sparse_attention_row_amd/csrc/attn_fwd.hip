@@ -306,7 +306,10 @@ __device__ __forceinline__ void sort_desc(float (&x)[N]) {
 }
 
 // Candidate slots per row kept in LDS; further slots live in the workspace.
-constexpr int kLdsCand = 48;
+#ifndef ENTMAX_LDS_CAND
+#define ENTMAX_LDS_CAND 48
+#endif
+constexpr int kLdsCand = ENTMAX_LDS_CAND;
 
 // A row's candidate list: entry i at lds[i * kBR] for i < kLdsCand, else at
 // glob[i * kBR] (both slot-major over the 128 rows of a workgroup, so the

@@ -66,4 +66,48 @@ __device__ __forceinline__ float support_root(float m, float C, float S1, float 
     return m + (S1 - sqrtf(disc)) / C;
 }
 
+// The alpha-entmax map for alpha in (1, 2] in score units ("AdaSplash-2:
+// Faster Differentiable Sparse Attention" sec. 2.3, whose tau' is
+// (alpha - 1) tau here):  p = [u]_+^e with u = (alpha - 1)(s - tau) and
+// e = 1/(alpha - 1).  dp/ds = u^(e-1) = p/u on the support, and
+// d/dtau sum p = -sum u^(e-1).  alpha = 2 (e = 1) is sparsemax, p = u.
+struct AlphaMap {
+    float am1;  // alpha - 1
+    float e;    // 1 / (alpha - 1)
+    int lin;    // alpha == 2
+    __device__ __forceinline__ float pw(float u) const {
+        if (!(u > 0.0f)) return 0.0f;
+        return lin ? u : exp2f(e * log2f(u));
+    }
+    __device__ __forceinline__ float p(float s, float tau) const { return pw(am1 * (s - tau)); }
+    // upper bracket end of a row of n entries with maximum m: p_max >= 1/n
+    __device__ __forceinline__ float hi(float m, float n) const {
+        return m - exp2f(-am1 * log2f(n)) * e;
+    }
+};
+
+// Newton step from below for the alpha-entmax normaliser: f = F - 1 with
+// F = sum p and F1 = sum p/u (so f' = -F1).  f is convex and decreasing in
+// tau for alpha <= 2, so from a point with f >= 0 the step stays at or below
+// the root; steps that leave (lo, hi) fall back to bisection.  Returns the
+// next point and updates the bracket; *done is set when the step is below
+// fp32 resolution (tau is then the returned point).
+__device__ __forceinline__ float newton_or_bisect(float t, float F, float F1, float& lo, float& hi,
+                                                  bool* done) {
+    const float f = F - 1.0f;
+    *done = false;
+    if (f >= 0.0f) {
+        lo = t;
+        const float step = f / F1;
+        const float tn = t + step;
+        if (!(step > 1e-7f * fmaxf(1.0f, fabsf(t)))) {
+            *done = true;
+            return fminf(fmaxf(tn, lo), hi);
+        }
+        return (tn < hi) ? tn : 0.5f * (lo + hi);
+    }
+    hi = t;
+    return 0.5f * (lo + hi);
+}
+
 }  // namespace entmax

@@ -72,13 +72,13 @@ int entmax_set_option(int option, int value) {
 
 int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
                     int64_t ld, float alpha, void* stream) {
-    if (alpha != 1.5f) return ENTMAX_ERR_ALPHA;
+    if (!(alpha > 1.0f && alpha <= 2.0f)) return ENTMAX_ERR_ALPHA;
     if (rows < 0 || cols < 1 || ld < cols || rows > 0x7fffffffLL || cols > 0x7fffffffLL)
         return ENTMAX_ERR_SHAPE;
     if (rows == 0) return ENTMAX_OK;
     if (S == nullptr || tau == nullptr) return ENTMAX_ERR_NULL;
     (void)hipGetLastError();
-    return hip_status(entmax::launch_tau_rows(S, P, tau, rows, cols, ld, (hipStream_t)stream));
+    return hip_status(entmax::launch_tau_rows(S, P, tau, rows, cols, ld, alpha, (hipStream_t)stream));
 }
 
 size_t entmax_attn_threshold_workspace(int B, int H, int L, int d, int dtype, int mask,

@@ -7,8 +7,10 @@
 
 namespace entmax {
 
+struct AlphaMap;
+AlphaMap make_alpha_map(float alpha);
 hipError_t launch_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
-                           int64_t ld, hipStream_t stream);
+                           int64_t ld, float alpha, hipStream_t stream);
 
 // Arguments of one attention call after validation.
 struct AttnArgs {

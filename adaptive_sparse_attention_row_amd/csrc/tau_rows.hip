@@ -21,6 +21,12 @@
 //      element.
 // Wider rows take a 256-thread streaming kernel that reads the row three
 // times (maximum, candidates above m - 2, output).
+//
+// Other alpha in (1, 2] (AdaSplash-2 sec. 2.3; see AlphaMap) take the same
+// structure with p = [(alpha-1)(s - tau)]_+^(1/(alpha-1)): the lower bound is
+// the threshold of the lane maxima (the subset argument holds for every
+// alpha), and tau comes from Newton steps from below on the candidates with
+// a bisection guard (no closed form for general alpha).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -202,6 +208,68 @@ __device__ __forceinline__ float wave_tau(float m, float n, float lo, Each each)
     return 0.5f * (lo + hi);
 }
 
+// General alpha: this thread's F = sum p and F1 = sum p/u at threshold t.
+__device__ __forceinline__ void accumulate_gen(RowSums& s, float x, float t, const AlphaMap& a) {
+    const float u = a.am1 * (x - t);
+    if (u > 0.0f) {
+        const float p = a.pw(u);
+        s.F += p;
+        s.F1 += p / u;
+    }
+}
+
+// General-alpha threshold of a set held by one wave (Newton from below, see
+// newton_or_bisect) in [lo, hi(m, n)].  Every lane returns the same tau;
+// *lo_out receives the final lower bracket end (a point with f >= 0, so a
+// lower bound on tau up to the rounding of the sums).
+template <class Each>
+__device__ __forceinline__ float wave_tau_gen(float m, float n, float lo, const AlphaMap& a, Each each,
+                                              float* lo_out) {
+    float hi = a.hi(m, n);
+    float t = lo;
+    float tau = 0.5f * (lo + hi);
+    for (int it = 0; it < kMaxIter; ++it) {
+        RowSums s = {0.f, 0.f, 0.f, 0.f, 0.f, __builtin_inff()};
+        each(t, s);
+        s.F = wave_sum_dpp(s.F);
+        s.F1 = wave_sum_dpp(s.F1);
+        bool done;
+        const float tn = newton_or_bisect(t, s.F, s.F1, lo, hi, &done);
+        if (done) {
+            tau = tn;
+            break;
+        }
+        if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) {
+            tau = 0.5f * (lo + hi);
+            break;
+        }
+        t = tn;
+        tau = 0.5f * (lo + hi);
+    }
+    if (lo_out) *lo_out = lo;
+    return tau;
+}
+
+// Workgroup form of wave_tau_gen for the streaming kernel.
+template <class Visit>
+__device__ float refine_tau_gen(float m, float total, const AlphaMap& a, Visit visit,
+                                float (*red)[kWaves][6]) {
+    float lo = m - a.e;
+    float hi = a.hi(m, total);
+    float t = lo;
+    for (int it = 0; it < kMaxIter; ++it) {
+        RowSums s = {0.f, 0.f, 0.f, 0.f, 0.f, __builtin_inff()};
+        visit(t, s);
+        s = block_reduce(s, red, it & 1);
+        bool done;
+        const float tn = newton_or_bisect(t, s.F, s.F1, lo, hi, &done);
+        if (done) return tn;
+        if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) break;
+        t = tn;
+    }
+    return 0.5f * (lo + hi);
+}
+
 constexpr int kRowsPerBlock = 1;  // one single-wave workgroup per row
 constexpr int kWaveCand = 2048;                  // LDS candidates per wave
 
@@ -209,11 +277,12 @@ constexpr int kWaveCand = 2048;                  // LDS candidates per wave
 // done), the row register-resident: VPT values per lane (lane l holds columns
 // (64 k + l) * 4 + e for VEC, 64 k + l otherwise).  No barriers.  VEC: float4 accesses
 // (ld % 4 == 0 and 16-byte aligned S / P).
-template <int VPT, bool VEC>
+template <int VPT, bool VEC, bool GEN>
 __global__ __launch_bounds__(kWave, 3) void tau_rows_wave(const float* __restrict__ S,
                                                          float* __restrict__ P,
                                                          float* __restrict__ tau_out,
-                                                         int64_t rows, int cols, int64_t ld) {
+                                                         int64_t rows, int cols, int64_t ld,
+                                                         AlphaMap am) {
     __shared__ float cand_all[kRowsPerBlock][kWaveCand];
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + w;
@@ -268,7 +337,11 @@ __global__ __launch_bounds__(kWave, 3) void tau_rows_wave(const float* __restric
         // largest scores mostly sit in different lanes, so it is close to tau
         // and few scores lie above it.
         const float n1 = wave_sum_dpp(mx > neg_inf() ? 1.0f : 0.0f);
-        const float tlo = wave_tau(m, n1, m - 2.0f, [&](float tt, RowSums& s) { accumulate(s, mx, tt, m); });
+        float tlo;
+        if constexpr (GEN)
+            wave_tau_gen(m, n1, m - am.e, am, [&](float tt, RowSums& s) { accumulate_gen(s, mx, tt, am); }, &tlo);
+        else
+            tlo = wave_tau(m, n1, m - 2.0f, [&](float tt, RowSums& s) { accumulate(s, mx, tt, m); });
         // the scores above it, compacted in register order (elements where no
         // lane has one are skipped)
         int n = 0;
@@ -282,7 +355,17 @@ __global__ __launch_bounds__(kWave, 3) void tau_rows_wave(const float* __restric
                 n += __popcll(b);
             }
         }
-        if (n <= kWaveCand) {
+        if constexpr (GEN) {
+            if (n <= kWaveCand) {
+                tau = wave_tau_gen(m, (float)n, tlo, am, [&](float tt, RowSums& s) {
+                    for (int i = lane; i < n; i += kWave) accumulate_gen(s, cand[i], tt, am);
+                }, nullptr);
+            } else {
+                tau = wave_tau_gen(m, (float)n, tlo, am, [&](float tt, RowSums& s) {
+                    for (int pos = lane; pos < cols; pos += kWave) accumulate_gen(s, src[pos], tt, am);
+                }, nullptr);
+            }
+        } else if (n <= kWaveCand) {
             tau = wave_tau(m, (float)n, tlo, [&](float tt, RowSums& s) {
                 for (int i = lane; i < n; i += kWave) accumulate(s, cand[i], tt, m);
             });
@@ -300,13 +383,17 @@ __global__ __launch_bounds__(kWave, 3) void tau_rows_wave(const float* __restric
     if (P == nullptr) return;
     float* dst = P + row * ld;
     const float h = -0.5f * tau;
+    auto pr = [&](float x) -> float {
+        if constexpr (GEN) return am.p(x, tau);
+        else return prob_h(x, h);
+    };
     if constexpr (VEC) {
 #pragma unroll
         for (int k = 0; k < VPT / 4; ++k) {
             const int pos = (k * kWave + lane) * 4;
             f32x4 q;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) q[e] = prob_h(v[4 * k + e], h);
+            for (int e = 0; e < 4; ++e) q[e] = pr(v[4 * k + e]);
             if (full || pos + 3 < cols) {
                 __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(dst + pos));
             } else {
@@ -319,17 +406,18 @@ __global__ __launch_bounds__(kWave, 3) void tau_rows_wave(const float* __restric
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int pos = k * kWave + lane;
-            if (pos < cols) dst[pos] = prob_h(v[k], h);
+            if (pos < cols) dst[pos] = pr(v[k]);
         }
     }
 }
 
 // Any width: the row is streamed from global memory (L2-resident after the
 // first pass for moderate widths).
+template <bool GEN>
 __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restrict__ S,
                                                            float* __restrict__ P,
                                                            float* __restrict__ tau_out,
-                                                           int64_t cols, int64_t ld) {
+                                                           int64_t cols, int64_t ld, AlphaMap am) {
     __shared__ float cand[kCandCap];
     __shared__ float red[2][kWaves][6];
     __shared__ float mbuf[kWaves];
@@ -347,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restr
     if (m == neg_inf()) {
         tau = neg_inf();
     } else {
-        const float lo0 = m - 2.0f;
+        const float lo0 = GEN ? m - am.e : m - 2.0f;  // lower bracket end
         // Compact candidates in chunk order; placement is deterministic.
         int filled = 0;  // candidates seen so far (may exceed the capacity)
         const int64_t chunks = (cols + kThreads - 1) / kThreads;
@@ -369,7 +457,17 @@ __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restr
             filled += tot;
             __syncthreads();
         }
-        if (filled <= kCandCap) {
+        if constexpr (GEN) {
+            if (filled <= kCandCap) {
+                tau = refine_tau_gen(m, (float)filled, am, [&](float tt, RowSums& s) {
+                    for (int i = t; i < filled; i += kThreads) accumulate_gen(s, cand[i], tt, am);
+                }, red);
+            } else {
+                tau = refine_tau_gen(m, (float)filled, am, [&](float tt, RowSums& s) {
+                    for (int64_t pos = t; pos < cols; pos += kThreads) accumulate_gen(s, src[pos], tt, am);
+                }, red);
+            }
+        } else if (filled <= kCandCap) {
             tau = refine_tau(
                 m, (float)filled,
                 [&](float tt, RowSums& s) {
@@ -388,39 +486,55 @@ __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restr
     if (t == 0) tau_out[row] = tau;
     if (P == nullptr) return;
     float* dst = P + row * ld;
-    for (int64_t pos = t; pos < cols; pos += kThreads) dst[pos] = prob(src[pos], tau);
+    for (int64_t pos = t; pos < cols; pos += kThreads) dst[pos] = GEN ? am.p(src[pos], tau) : prob(src[pos], tau);
 }
 
-template <int VPT, bool VEC>
+template <int VPT, bool VEC, bool GEN>
 hipError_t launch_wave(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
-                       int64_t ld, hipStream_t stream) {
+                       int64_t ld, const AlphaMap& am, hipStream_t stream) {
     const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL((tau_rows_wave<VPT, VEC>), dim3((unsigned)blocks), dim3(kWave), 0, stream, S,
-                       P, tau, rows, (int)cols, ld);
+    hipLaunchKernelGGL((tau_rows_wave<VPT, VEC, GEN>), dim3((unsigned)blocks), dim3(kWave), 0, stream, S,
+                       P, tau, rows, (int)cols, ld, am);
+    return hipGetLastError();
+}
+
+template <bool GEN>
+hipError_t launch_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols, int64_t ld,
+                       const AlphaMap& am, hipStream_t stream) {
+    const bool vec = (ld % 4 == 0) && ((uintptr_t)S % 16 == 0) &&
+                     (P == nullptr || (uintptr_t)P % 16 == 0);
+    if (vec) {
+        if (cols <= 8 * kWave) return launch_wave<8, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
+        if (cols <= 16 * kWave) return launch_wave<16, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
+        if (cols <= 32 * kWave) return launch_wave<32, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
+        if (cols <= 64 * kWave) return launch_wave<64, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
+        if (cols <= 128 * kWave) return launch_wave<128, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
+    } else {
+        if (cols <= 8 * kWave) return launch_wave<8, false, GEN>(S, P, tau, rows, cols, ld, am, stream);
+        if (cols <= 16 * kWave) return launch_wave<16, false, GEN>(S, P, tau, rows, cols, ld, am, stream);
+        if (cols <= 32 * kWave) return launch_wave<32, false, GEN>(S, P, tau, rows, cols, ld, am, stream);
+        if (cols <= 64 * kWave) return launch_wave<64, false, GEN>(S, P, tau, rows, cols, ld, am, stream);
+    }
+    hipLaunchKernelGGL(tau_rows_stream<GEN>, dim3((unsigned)rows), dim3(kThreads), 0, stream, S, P,
+                       tau, cols, ld, am);
     return hipGetLastError();
 }
 
 }  // namespace
 
+AlphaMap make_alpha_map(float alpha) {
+    AlphaMap a;
+    a.am1 = alpha - 1.0f;
+    a.e = 1.0f / a.am1;
+    a.lin = alpha == 2.0f ? 1 : 0;
+    return a;
+}
+
 hipError_t launch_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
-                           int64_t ld, hipStream_t stream) {
-    const bool vec = (ld % 4 == 0) && ((uintptr_t)S % 16 == 0) &&
-                     (P == nullptr || (uintptr_t)P % 16 == 0);
-    if (vec) {
-        if (cols <= 8 * kWave) return launch_wave<8, true>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 16 * kWave) return launch_wave<16, true>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 32 * kWave) return launch_wave<32, true>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 64 * kWave) return launch_wave<64, true>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 128 * kWave) return launch_wave<128, true>(S, P, tau, rows, cols, ld, stream);
-    } else {
-        if (cols <= 8 * kWave) return launch_wave<8, false>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 16 * kWave) return launch_wave<16, false>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 32 * kWave) return launch_wave<32, false>(S, P, tau, rows, cols, ld, stream);
-        if (cols <= 64 * kWave) return launch_wave<64, false>(S, P, tau, rows, cols, ld, stream);
-    }
-    hipLaunchKernelGGL(tau_rows_stream, dim3((unsigned)rows), dim3(kThreads), 0, stream, S, P,
-                       tau, cols, ld);
-    return hipGetLastError();
+                           int64_t ld, float alpha, hipStream_t stream) {
+    const AlphaMap am = make_alpha_map(alpha);
+    if (alpha == 1.5f) return launch_rows<false>(S, P, tau, rows, cols, ld, am, stream);
+    return launch_rows<true>(S, P, tau, rows, cols, ld, am, stream);
 }
 
 }  // namespace entmax
