@@ -58,7 +58,8 @@ def test_tau_rows_validation(api):
     f = L.entmax_tau_rows
     assert f(None, None, FAKE, 4, 8, 8, 1.5, None) == api.ERR_NULL
     assert f(FAKE, None, None, 4, 8, 8, 1.5, None) == api.ERR_NULL
-    assert f(FAKE, None, FAKE, 4, 8, 8, 2.0, None) == api.ERR_ALPHA
+    for bad in (2.5, 1.0, 0.0, float("nan")):
+        assert f(FAKE, None, FAKE, 4, 8, 8, bad, None) == api.ERR_ALPHA
     assert f(FAKE, None, FAKE, -1, 8, 8, 1.5, None) == api.ERR_SHAPE
     assert f(FAKE, None, FAKE, 4, 0, 8, 1.5, None) == api.ERR_SHAPE
     assert f(FAKE, None, FAKE, 4, 9, 8, 1.5, None) == api.ERR_SHAPE
