@@ -139,10 +139,11 @@ def mask_shape(B: int, H: int, L: int, d: int, dtype: int = BF16) -> tuple[int, 
 
 
 def attn_fwd(q, k, v, scale: Optional[float] = None, mask: int = MASK_NONE, window: int = 0,
-             want_block_mask: bool = True, out=None):
-    """1.5-entmax attention forward.  q, k, v: [B, H, L, d] CUDA tensors
-    (bf16 or fp32, contiguous).  Returns (O fp32, tau fp32 [B, H, L],
-    block_mask int32 view of the packed uint32 mask, or None)."""
+             want_block_mask: bool = True, out=None, alpha: float = 1.5):
+    """alpha-entmax attention forward (alpha in (1, 2], default 1.5).  q, k,
+    v: [B, H, L, d] CUDA tensors (bf16 or fp32, contiguous).  Returns (O fp32,
+    tau fp32 [B, H, L], block_mask int32 view of the packed uint32 mask, or
+    None)."""
     import torch
     B, H, L, d = q.shape
     for t in (q, k, v):
@@ -159,14 +160,14 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, mask: int = MASK_NONE, wind
     ws_bytes = lib().entmax_attn_fwd_workspace(B, H, L, d, dt, mask, window)
     ws = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
     st = lib().entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(),
-                               tau.data_ptr(), _dev_ptr(bm), B, H, L, d, float(scale), 1.5, dt,
-                               mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
+                               tau.data_ptr(), _dev_ptr(bm), B, H, L, d, float(scale), float(alpha),
+                               dt, mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
     _check("entmax_attn_fwd", st)
     return O, tau, bm
 
 
 def attn_threshold(q, k, scale: Optional[float] = None, mask: int = MASK_NONE, window: int = 0,
-                   tau=None, block_mask=None, workspace=None):
+                   tau=None, block_mask=None, workspace=None, alpha: float = 1.5):
     """Phases 1-3 only: returns (tau fp32 [B, H, L], packed block mask)."""
     import torch
     B, H, L, d = q.shape
@@ -181,14 +182,14 @@ def attn_threshold(q, k, scale: Optional[float] = None, mask: int = MASK_NONE, w
     if workspace is None:
         workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
     st = lib().entmax_attn_threshold(q.data_ptr(), k.data_ptr(), tau.data_ptr(), block_mask.data_ptr(),
-                                     B, H, L, d, float(scale), 1.5, dt, mask, window,
+                                     B, H, L, d, float(scale), float(alpha), dt, mask, window,
                                      workspace.data_ptr(), workspace.numel(), _stream(q.device))
     _check("entmax_attn_threshold", st)
     return tau, block_mask
 
 
 def attn_output(q, k, v, tau, block_mask, scale: Optional[float] = None, mask: int = MASK_NONE,
-                window: int = 0, out=None):
+                window: int = 0, out=None, alpha: float = 1.5):
     """Phase 4 only: O from a given tau and block mask."""
     import torch
     B, H, L, d = q.shape
@@ -197,14 +198,14 @@ def attn_output(q, k, v, tau, block_mask, scale: Optional[float] = None, mask: i
         scale = 1.0 / math.sqrt(d)
     O = out if out is not None else torch.empty(B, H, L, d, device=q.device, dtype=torch.float32)
     st = lib().entmax_attn_output(q.data_ptr(), k.data_ptr(), v.data_ptr(), tau.data_ptr(),
-                                  block_mask.data_ptr(), O.data_ptr(), B, H, L, d, float(scale), 1.5,
-                                  dt, mask, window, _stream(q.device))
+                                  block_mask.data_ptr(), O.data_ptr(), B, H, L, d, float(scale),
+                                  float(alpha), dt, mask, window, _stream(q.device))
     _check("entmax_attn_output", st)
     return O
 
 
 def attn_bwd(q, k, v, do, tau, block_mask, scale: Optional[float] = None,
-             mask: int = MASK_NONE, window: int = 0):
+             mask: int = MASK_NONE, window: int = 0, alpha: float = 1.5):
     """Backward of attn_fwd.  Returns (dQ, dK, dV), fp32 [B, H, L, d]."""
     import torch
     B, H, L, d = q.shape
@@ -221,7 +222,7 @@ def attn_bwd(q, k, v, do, tau, block_mask, scale: Optional[float] = None,
     ws = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8) if ws_bytes else None
     st = lib().entmax_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
                                tau.data_ptr(), block_mask.data_ptr(), dq.data_ptr(),
-                               dk.data_ptr(), dv.data_ptr(), B, H, L, d, float(scale), 1.5, dt,
-                               mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
+                               dk.data_ptr(), dv.data_ptr(), B, H, L, d, float(scale), float(alpha),
+                               dt, mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
     _check("entmax_attn_bwd", st)
     return dq, dk, dv

@@ -1,4 +1,6 @@
-// attn_bwd.hip -- 1.5-entmax attention backward on gfx950.
+// attn_bwd.hip -- alpha-entmax attention backward on gfx950 (written for
+// alpha = 1.5 below; other alpha in (1, 2] use g = u^(1/(alpha-1) - 1),
+// u = (alpha - 1)(S - tau), the derivative of A in S, in the same formulas).
 //
 // With g = [(S - tau)/2]_+ (so A = g^2), the threshold's implicit derivative
 // gives, on the support only ("AdaSplash-2: Faster Differentiable Sparse
@@ -43,6 +45,8 @@ struct BwdParams {
     float* delta;  // workspace [BH][L]
     int BH, L, mode, W, nQ, nKB, Tc, Tr64, Wd;
     float scale;
+    AlphaMap am;  // the alpha-entmax map
+    int gen;      // alpha != 1.5
 };
 
 // Stage one 64-row tile of X (rows r0 .., zero past L) into LDS, in the
@@ -198,7 +202,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float dd = fmaxf(s[kb][qb][r] * p.scale - tq[qb], 0.0f);
+                    const float sv = s[kb][qb][r] * p.scale;
+                    const float dd = p.gen ? 2.0f * p.am.g(sv, tq[qb]) : fmaxf(sv - tq[qb], 0.0f);
                     num[qb] += dd * da[kb][qb][r];
                     den[qb] += dd;
                 }
@@ -243,7 +248,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float dd = fmaxf(s[kb][qb][r] * p.scale - tq[qb], 0.0f);
+                    const float sv = s[kb][qb][r] * p.scale;
+                    const float dd = p.gen ? 2.0f * p.am.g(sv, tq[qb]) : fmaxf(sv - tq[qb], 0.0f);
                     s[kb][qb][r] = dd * (da[kb][qb][r] - dl[qb]);
                 }
         const bool on[2] = {true, true};
@@ -393,9 +399,16 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
             for (int cb = 0; cb < NBK; ++cb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float dd = fmaxf(s[kb][cb][r] * p.scale - tr[r], 0.0f);
-                    a4[kb][cb][r] = dd * dd;
-                    s[kb][cb][r] = dd * (da[kb][cb][r] - dr[r]);
+                    const float sv = s[kb][cb][r] * p.scale;
+                    if (p.gen) {
+                        // 4A and 2 g, the scaling of the alpha = 1.5 form below
+                        a4[kb][cb][r] = 4.0f * p.am.p(sv, tr[r]);
+                        s[kb][cb][r] = 2.0f * p.am.g(sv, tr[r]) * (da[kb][cb][r] - dr[r]);
+                    } else {
+                        const float dd = fmaxf(sv - tr[r], 0.0f);
+                        a4[kb][cb][r] = dd * dd;
+                        s[kb][cb][r] = dd * (da[kb][cb][r] - dr[r]);
+                    }
                 }
         }
         const bool on[2] = {true, true};
@@ -456,6 +469,8 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream) {
     bp.Tr64 = (a.L + 63) / 64;
     bp.Wd = (bp.Tc + 31) / 32;
     bp.scale = a.scale;
+    bp.am = make_alpha_map(a.alpha);
+    bp.gen = a.alpha != 1.5f ? 1 : 0;
     if (a.dtype == 1) {
         if (a.d == 64) {
             bp.nKB = (a.L + DkvCfg<__bf16, 64>::kKeys - 1) / DkvCfg<__bf16, 64>::kKeys;

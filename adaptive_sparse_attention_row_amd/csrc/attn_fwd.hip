@@ -59,6 +59,8 @@ struct FwdParams {
     int BH, L, mode, W, nQ, Tc, Tr64, Wd;
     float scale;
     int cap;
+    AlphaMap am;  // the alpha-entmax map
+    int gen;      // alpha != 1.5: Newton solves and pow weights
 };
 
 // Candidate slots per row in the workspace lists.
@@ -285,6 +287,37 @@ __device__ __forceinline__ float tau_of_sorted(const float (&x)[N]) {
     return m + best;
 }
 
+// General alpha: a lower bound on the threshold of N values (-inf entries
+// absent): Newton from below from the bracket end max - 1/(alpha-1); the last
+// point with f >= 0, less a margin for the rounding of its sums.
+template <int N>
+__device__ __forceinline__ float tau_lower_gen(const float (&x)[N], const AlphaMap& am) {
+    float m = neg_inf(), n = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        m = fmaxf(m, x[k]);
+        n += x[k] > neg_inf() ? 1.f : 0.f;
+    }
+    float lo = m - am.e, hi = am.hi(m, n), t = lo;
+    for (int it = 0; it < 30; ++it) {
+        float F = 0.f, F1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const float u = am.am1 * (x[k] - t);
+            if (u > 0.f) {
+                const float pp = am.pw(u);
+                F += pp;
+                F1 += pp / u;
+            }
+        }
+        bool fin;
+        const float tn = newton_or_bisect(t, F, F1, lo, hi, &fin);
+        if (fin || hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) break;
+        t = tn;
+    }
+    return lo - 1e-6f * fmaxf(1.0f, fabsf(lo));
+}
+
 // Sort N (a power of two) values descending in registers (bitonic network).
 template <int N>
 __device__ __forceinline__ void sort_desc(float (&x)[N]) {
@@ -417,6 +450,48 @@ __device__ __forceinline__ double solve_candidates(const Src& src, double mx, do
         }
     }
     if (!done) result = 0.5 * (lo + hi);
+    return result;
+}
+
+// General alpha: tau of a candidate list (two lanes per row, sums combined
+// with lane l ^ 32) by Newton steps from below on F = sum p, F1 = sum p/u
+// with a bisection guard (newton_or_bisect).  *lo_out (optional) receives
+// the last point with f >= 0, a lower bound on the list's threshold.
+template <class Src>
+__device__ __forceinline__ float solve_candidates_gen(const Src& src, float lo, float hi, bool active,
+                                                      const AlphaMap& am, float* lo_out = nullptr) {
+    float t = lo, result = lo;
+    bool done = !active;
+    for (int it = 0; it < kMaxIter; ++it) {
+        if (__ballot(!done) == 0) break;
+        float F = 0.f, F1 = 0.f;
+        if (!done) {
+            src.each([&](float x) {
+                const float u = am.am1 * (x - t);
+                if (u > 0.f) {
+                    const float pp = am.pw(u);
+                    F += pp;
+                    F1 += pp / u;
+                }
+            });
+        }
+        F += __shfl_xor(F, 32, kWave);
+        F1 += __shfl_xor(F1, 32, kWave);
+        if (done) continue;
+        bool fin;
+        const float tn = newton_or_bisect(t, F, F1, lo, hi, &fin);
+        if (fin) {
+            result = tn;
+            done = true;
+        } else if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) {
+            result = 0.5f * (lo + hi);
+            done = true;
+        } else {
+            t = tn;
+        }
+    }
+    if (!done) result = 0.5f * (lo + hi);
+    if (lo_out) *lo_out = lo;
     return result;
 }
 
@@ -566,7 +641,7 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
             v[2 * kTop4 + i] = st[1][srow][i] * p.scale;
         }
         sort_desc(v);
-        const float lo = tau_of_sorted(v);
+        const float lo = p.gen ? tau_lower_gen(v, p.am) : tau_of_sorted(v);
         reinterpret_cast<float2*>(p.rowstat)[(size_t)bh * p.L + grow] = make_float2(v[0], lo);
     }
     for (int i = t; i < 2 * p.Tc; i += kNT) {
@@ -736,16 +811,23 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
             // threshold of the kept candidates: a lower bound on the row's tau
             const CandSrc src = {lval + srow, cval + srow, over ? cap : 0, h};
             const float smax = list_max(src);
-            const double ts = solve_candidates(src, smax, (double)smax - 2.0,
-                                               (double)smax - 2.0 / sqrt((double)cap), over);
-            lo_new = __double2float_rd(ts);
+            if (p.gen) {
+                float lb;
+                solve_candidates_gen(src, smax - p.am.e, p.am.hi(smax, (float)cap), over, p.am, &lb);
+                lo_new = lb - 1e-6f * fmaxf(1.0f, fabsf(lb));
+            } else {
+                const double ts = solve_candidates(src, smax, (double)smax - 2.0,
+                                                   (double)smax - 2.0 / sqrt((double)cap), over);
+                lo_new = __double2float_rd(ts);
+            }
         }
         if (h == 0 && open) {
             if (!over) {
                 rstate[srow] = 3;  // list complete, nc entries
             } else {
                 // every score above tau is above lo, so at most nc of them
-                row_hi[srow] = (float)((double)row_m[srow] - 2.0 / sqrt((double)nc));
+                row_hi[srow] = p.gen ? p.am.hi(row_m[srow], (float)nc)
+                                     : (float)((double)row_m[srow] - 2.0 / sqrt((double)nc));
                 const float nl = fmaxf(row_lo[srow], lo_new);
                 if (round == kRounds - 1 || !(nl > row_lo[srow])) rstate[srow] = 2;
                 row_lo[srow] = nl;
@@ -794,10 +876,18 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                         for (int r = 0; r < 16; ++r) {
                             const float s = acc[kb][qb][r] * p.scale;
                             if (s > tq[qb]) {
-                                const float gg = 0.5f * (s - tq[qb]);
                                 sc[qb] += 1.f;
-                                sf[qb] += gg * gg;
-                                sf1[qb] += gg;
+                                if (p.gen) {
+                                    // F = sum p, F1 = sum p/u (Newton)
+                                    const float u = p.am.am1 * (s - tq[qb]);
+                                    const float pp = p.am.pw(u);
+                                    sf[qb] += pp;
+                                    sf1[qb] += pp / u;
+                                } else {
+                                    const float gg = 0.5f * (s - tq[qb]);
+                                    sf[qb] += gg * gg;
+                                    sf1[qb] += gg;
+                                }
                             }
                         }
                 }
@@ -822,13 +912,25 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                 const float F = fb_part[srow][0][1] + fb_part[srow][1][1];
                 const float F1 = fb_part[srow][0][2] + fb_part[srow][1][2];
                 float lo = row_lo[srow], hi = row_hi[srow], tc = fb_t[srow];
-                if (F - 1.0f >= 0.0f) lo = tc; else hi = tc;
-                if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
-                    fb_active[srow] = 0;
-                    row_tau[srow] = 0.5f * (lo + hi);
+                if (p.gen) {
+                    bool fin;
+                    const float tn = newton_or_bisect(tc, F, F1, lo, hi, &fin);
+                    if (fin || hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
+                        fb_active[srow] = 0;
+                        row_tau[srow] = fin ? tn : 0.5f * (lo + hi);
+                    } else {
+                        fb_t[srow] = tn;
+                        atomicOr(&flag_s, 1);
+                    }
                 } else {
-                    fb_t[srow] = halley_or_bisect(tc, F, F1, C, lo, hi);
-                    atomicOr(&flag_s, 1);
+                    if (F - 1.0f >= 0.0f) lo = tc; else hi = tc;
+                    if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
+                        fb_active[srow] = 0;
+                        row_tau[srow] = 0.5f * (lo + hi);
+                    } else {
+                        fb_t[srow] = halley_or_bisect(tc, F, F1, C, lo, hi);
+                        atomicOr(&flag_s, 1);
+                    }
                 }
                 row_lo[srow] = lo;
                 row_hi[srow] = hi;
@@ -869,8 +971,10 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
         RegSrc<kSolveRegs<D>> src;
         src.load(CandSrc{lval + srow, cval + srow, n, h});
         const double mx = row_m[srow];
-        const double tau = solve_candidates(src, mx, row_lo[srow], mx - 2.0 / sqrt((double)(n > 0 ? n : 1)), act);
-        const float tr = (float)tau;
+        const float tr = p.gen ? solve_candidates_gen(src, row_lo[srow], p.am.hi(row_m[srow], (float)(n > 0 ? n : 1)),
+                                                      act, p.am)
+                               : (float)solve_candidates(src, mx, row_lo[srow],
+                                                         mx - 2.0 / sqrt((double)(n > 0 ? n : 1)), act);
         const int nl = nlist_s;
         auto pos_of = [&](int i) -> int {
             return i < kLdsCand ? lpos[i * kBR + srow] : cjt[(size_t)i * kBR + srow];
@@ -920,7 +1024,7 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
 }
 
 // ------------------------------------------------------------ kernel 2
-template <typename T, int D>
+template <typename T, int D, bool GEN>
 __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
     using O = Ops<T, D>;
     constexpr int NBUF = (sizeof(T) == 4 && D == 128) ? 1 : 2;
@@ -977,16 +1081,25 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
 
     sweep<T, D, NBUF, true>(list, nlist_s, Kh, Vh, kbuf, vbuf, qop, R0, g,
                             [&](int, int, f32x16(&acc)[2][2], const T* vt) {
-        // 4A = [s - tau]_+^2 with s = scale * (Q.K)
+        // 4A = [s - tau]_+^2 with s = scale * (Q.K) (general alpha: 4 p)
+        if constexpr (GEN) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float dd = fmaxf(acc[kb][qb][r] * p.scale - tq[qb], 0.0f);
-                    acc[kb][qb][r] = dd * dd;
-                }
+                    for (int r = 0; r < 16; ++r) acc[kb][qb][r] = 4.0f * p.am.p(acc[kb][qb][r] * p.scale, tq[qb]);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float dd = fmaxf(acc[kb][qb][r] * p.scale - tq[qb], 0.0f);
+                        acc[kb][qb][r] = dd * dd;
+                    }
+        }
         const bool on[2] = {true, true};
         O::pv(oa, vt, acc, on);
     });
@@ -1040,7 +1153,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
 // significant bits in fp16, and bf16 V converts exactly within fp16 range.  A
 // workgroup that meets a V entry beyond that range redoes its rows with A
 // split into bf16 hi + lo against bf16 V.
-template <int D>
+template <int D, bool GEN>
 __global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(FwdParams p) {
     using O = Ops<__bf16, D>;
     constexpr int kVRow = O::kVRow;
@@ -1145,13 +1258,20 @@ __global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(Fw
                     if (cls == kPartial) apply_mask<1>(acc, J, R0, g);
                     // A = [(s - tau)/2]_+^2 with s = scale * (Q.K); A <= 1, so no
                     // partial sum of A V exceeds max |V|
+                    if constexpr (GEN) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float dd = 0.5f * fmaxf(acc[kb][0][r] * p.scale - tq, 0.0f);
-                            acc[kb][0][r] = dd * dd;
-                        }
+                            for (int r = 0; r < 16; ++r) acc[kb][0][r] = p.am.p(acc[kb][0][r] * p.scale, tq);
+                    } else {
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const float dd = 0.5f * fmaxf(acc[kb][0][r] * p.scale - tq, 0.0f);
+                                acc[kb][0][r] = dd * dd;
+                            }
+                    }
                     if (f16) {
                         const uint16_t* Vt = vbuf[e & 1];
 #pragma unroll
@@ -1224,10 +1344,17 @@ hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t st
         if (e != hipSuccess) return e;
     }
     if (phase & 4) {
-        if constexpr (sizeof(T) == 2)
-            hipLaunchKernelGGL((fwd_out_bf16_kernel<D>), dim3(grid), dim3(kNT), 0, stream, fp);
-        else
-            hipLaunchKernelGGL((fwd_out_kernel<T, D>), dim3(grid), dim3(kNT), 0, stream, fp);
+        if constexpr (sizeof(T) == 2) {
+            if (fp.gen)
+                hipLaunchKernelGGL((fwd_out_bf16_kernel<D, true>), dim3(grid), dim3(kNT), 0, stream, fp);
+            else
+                hipLaunchKernelGGL((fwd_out_bf16_kernel<D, false>), dim3(grid), dim3(kNT), 0, stream, fp);
+        } else {
+            if (fp.gen)
+                hipLaunchKernelGGL((fwd_out_kernel<T, D, true>), dim3(grid), dim3(kNT), 0, stream, fp);
+            else
+                hipLaunchKernelGGL((fwd_out_kernel<T, D, false>), dim3(grid), dim3(kNT), 0, stream, fp);
+        }
         return hipGetLastError();
     }
     return hipSuccess;
@@ -1287,6 +1414,8 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream) {
     fp.Wd = (fp.Tc + 31) / 32;
     fp.scale = a.scale;
     fp.cap = a.cand_cap;
+    fp.am = make_alpha_map(a.alpha);
+    fp.gen = a.alpha != 1.5f ? 1 : 0;
     const int grid = fp.nQ * fp.BH;
     if (a.dtype == 1) {
         if (a.d == 64) return launch_typed<__bf16, 64>(fp, grid, phase, stream);

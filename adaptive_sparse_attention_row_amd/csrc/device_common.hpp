@@ -80,11 +80,25 @@ struct AlphaMap {
         return lin ? u : exp2f(e * log2f(u));
     }
     __device__ __forceinline__ float p(float s, float tau) const { return pw(am1 * (s - tau)); }
+    // dp/ds = u^(e-1) on the support (1 for sparsemax), 0 off it
+    __device__ __forceinline__ float g(float s, float tau) const {
+        const float u = am1 * (s - tau);
+        if (!(u > 0.0f)) return 0.0f;
+        return lin ? 1.0f : exp2f((e - 1.0f) * log2f(u));
+    }
     // upper bracket end of a row of n entries with maximum m: p_max >= 1/n
     __device__ __forceinline__ float hi(float m, float n) const {
         return m - exp2f(-am1 * log2f(n)) * e;
     }
 };
+
+inline AlphaMap make_alpha_map(float alpha) {
+    AlphaMap a;
+    a.am1 = alpha - 1.0f;
+    a.e = 1.0f / a.am1;
+    a.lin = alpha == 2.0f ? 1 : 0;
+    return a;
+}
 
 // Newton step from below for the alpha-entmax normaliser: f = F - 1 with
 // F = sum p and F1 = sum p/u (so f' = -F1).  f is convex and decreasing in

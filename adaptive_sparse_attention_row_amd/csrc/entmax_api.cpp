@@ -17,7 +17,7 @@ int g_cand_cap = 0;  // 0: the compiled default
 
 // Shared checks of the attention entry points (everything except pointers).
 int check_attn_shape(int B, int H, int L, int d, float alpha, int dtype, int mask, int window) {
-    if (alpha != 1.5f) return ENTMAX_ERR_ALPHA;
+    if (!(alpha > 1.0f && alpha <= 2.0f)) return ENTMAX_ERR_ALPHA;
     if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return ENTMAX_ERR_DTYPE;
     if (mask != ENTMAX_MASK_NONE && mask != ENTMAX_MASK_CAUSAL &&
         mask != ENTMAX_MASK_CAUSAL_WINDOW_SINK)
@@ -39,7 +39,7 @@ const char* entmax_status_str(int status) {
         case ENTMAX_OK: return "ok";
         case ENTMAX_ERR_NULL: return "null pointer argument";
         case ENTMAX_ERR_SHAPE: return "unsupported or inconsistent shape";
-        case ENTMAX_ERR_ALPHA: return "alpha must be 1.5";
+        case ENTMAX_ERR_ALPHA: return "alpha must lie in (1, 2]";
         case ENTMAX_ERR_DTYPE: return "unknown dtype";
         case ENTMAX_ERR_MASK: return "unknown mask mode or negative window";
         case ENTMAX_ERR_WORKSPACE: return "workspace missing or too small";
@@ -109,7 +109,7 @@ int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float
     if (!aligned16(workspace)) return ENTMAX_ERR_ALIGN;
     entmax::AttnArgs a = {};
     a.q = Q; a.k = K; a.v = V; a.o = O; a.tau = tau; a.block_mask = block_mask;
-    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     const int maxcap = entmax::attn_max_candidate_cap(d, dtype);
     a.cand_cap = (g_cand_cap > 0 && g_cand_cap < maxcap) ? g_cand_cap : maxcap;
@@ -135,7 +135,7 @@ int entmax_attn_threshold(const void* Q, const void* K, float* tau, uint32_t* bl
     entmax::AttnArgs a = {};
     a.q = Q; a.k = K; a.tau = tau; a.block_mask = block_mask;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     const int maxcap = entmax::attn_max_candidate_cap(d, dtype);
     a.cand_cap = (g_cand_cap > 0 && g_cand_cap < maxcap) ? g_cand_cap : maxcap;
@@ -156,7 +156,7 @@ int entmax_attn_score_stats(const void* Q, const void* K, int B, int H, int L, i
     if (!aligned16(workspace)) return ENTMAX_ERR_ALIGN;
     entmax::AttnArgs a = {};
     a.q = Q; a.k = K;
-    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     (void)hipGetLastError();
@@ -178,7 +178,7 @@ int entmax_attn_output(const void* Q, const void* K, const void* V, const float*
     entmax::AttnArgs a = {};
     a.q = Q; a.k = K; a.v = V; a.o = O; a.tau = const_cast<float*>(tau);
     a.block_mask = const_cast<uint32_t*>(block_mask);
-    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     (void)hipGetLastError();
     return hip_status(entmax::launch_attn_fwd(a, 4, (hipStream_t)stream));
@@ -211,7 +211,7 @@ int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
     a.q = Q; a.k = K; a.v = V; a.dout = dO; a.tau = const_cast<float*>(tau);
     a.block_mask = const_cast<uint32_t*>(block_mask);
     a.dq = dQ; a.dk = dK; a.dv = dV;
-    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.dtype = dtype;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     (void)hipGetLastError();

@@ -7,8 +7,6 @@
 
 namespace entmax {
 
-struct AlphaMap;
-AlphaMap make_alpha_map(float alpha);
 hipError_t launch_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
                            int64_t ld, float alpha, hipStream_t stream);
 
@@ -26,6 +24,7 @@ struct AttnArgs {
     float* dv;
     int B, H, L, d;
     float scale;
+    float alpha;  // in (1, 2]
     int dtype;  // 0 fp32, 1 bf16
     int mask;   // 0 none, 1 causal, 2 causal window + sink
     int window;

@@ -522,14 +522,6 @@ hipError_t launch_rows(const float* S, float* P, float* tau, int64_t rows, int64
 
 }  // namespace
 
-AlphaMap make_alpha_map(float alpha) {
-    AlphaMap a;
-    a.am1 = alpha - 1.0f;
-    a.e = 1.0f / a.am1;
-    a.lin = alpha == 2.0f ? 1 : 0;
-    return a;
-}
-
 hipError_t launch_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
                            int64_t ld, float alpha, hipStream_t stream) {
     const AlphaMap am = make_alpha_map(alpha);

@@ -23,7 +23,13 @@
  *  - Arguments are validated before any launch; on any error nothing is
  *    launched and no output is touched.  A failed launch returns
  *    ENTMAX_ERR_HIP (the HIP error is consumed).
- *  - alpha must be 1.5f; other values return ENTMAX_ERR_ALPHA.
+ *  - alpha must lie in (1, 2]; other values (and NaN) return
+ *    ENTMAX_ERR_ALPHA.  alpha = 1.5 is the map above and keeps its exact
+ *    closed-form solves; any other alpha uses the alpha-entmax map of
+ *    AdaSplash-2 sec. 2.3 in the same score units,
+ *      A_ij = [(alpha-1)(S_ij - tau_i)]_+^(1/(alpha-1)),
+ *    with tau_i from Newton steps from below (bisection-guarded); alpha = 2
+ *    is sparsemax.
  *  - Outputs are overwritten, never accumulated into.
  *  - The library keeps no per-call state; concurrent calls on different
  *    streams are safe when their outputs and workspaces are disjoint.
@@ -42,7 +48,7 @@ enum {
     ENTMAX_OK = 0,
     ENTMAX_ERR_NULL = 1,      /* a required pointer is NULL */
     ENTMAX_ERR_SHAPE = 2,     /* unsupported or inconsistent size */
-    ENTMAX_ERR_ALPHA = 3,     /* alpha != 1.5 */
+    ENTMAX_ERR_ALPHA = 3,     /* alpha outside (1, 2] */
     ENTMAX_ERR_DTYPE = 4,     /* unknown dtype code */
     ENTMAX_ERR_MASK = 5,      /* unknown mask mode, or window < 0 in mode 2 */
     ENTMAX_ERR_WORKSPACE = 6, /* workspace missing or too small */
@@ -79,7 +85,8 @@ int entmax_version(void);
 int entmax_tile_shape(int d, int dtype, int* block_rows, int* block_cols);
 
 /*
- * Row-wise 1.5-entmax of a materialised fp32 score matrix.
+ * Row-wise alpha-entmax (1.5-entmax for alpha = 1.5) of a materialised
+ * fp32 score matrix.
  *   S    [rows][ld] fp32, row r's scores are S[r*ld + 0 .. cols-1]; -inf
  *        entries are inactive (p = 0, not counted in the row).
  *   P    [rows][ld] fp32 output (same layout as S) or NULL for tau only.
@@ -88,9 +95,11 @@ int entmax_tile_shape(int d, int dtype, int* block_rows, int* block_cols);
  *        entry (its P row is all zero).
  * Requires rows >= 0, 1 <= cols <= ld.  rows == 0 is a no-op (any pointer
  * may then be NULL); otherwise S and tau must be non-NULL.
- * The threshold solve is the hybrid Halley-bisection of "AdaSplash: Adaptive
- * Sparse Flash Attention" (summary, Approach) on the bracket
- * [max - 2, max - 2/sqrt(n)] of AdaSplash-2 sec. 2.4 (scaled to score units),
+ * The threshold solve (alpha = 1.5) is the hybrid Halley-bisection of
+ * "AdaSplash: Adaptive Sparse Flash Attention" (summary, Approach) on the
+ * bracket [max - 2, max - 2/sqrt(n)] of AdaSplash-2 sec. 2.4 (scaled to score
+ * units; [max - 1/(alpha-1), max - n^(1-alpha)/(alpha-1)] for other alpha,
+ * solved by bisection-guarded Newton steps from below),
  * restricted to the scores above max - 2, with an exact finish once the
  * support is known.  NaN inputs give unspecified results.
  */
@@ -113,7 +122,7 @@ size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask
                                  int window);
 
 /*
- * 1.5-entmax attention forward (AdaSplash-2 sec. 3.3, phases: score sweep,
+ * alpha-entmax attention forward (AdaSplash-2 sec. 3.3, phases: score sweep,
  * threshold, block mask, output over non-null blocks only).
  *   Q, K, V    [B][H][L][d] of `dtype`, contiguous, 16-byte aligned.
  *   O          [B][H][L][d] fp32 output.
@@ -174,8 +183,10 @@ size_t entmax_attn_bwd_workspace(int B, int H, int L, int d, int dtype, int mask
                                  int window);
 
 /*
- * 1.5-entmax attention backward, restricted to the support (AdaSplash-2
- * sec. 3.3 "Backward pass" and appendix C.6): with g = [(S - tau)/2]_+,
+ * alpha-entmax attention backward, restricted to the support (AdaSplash-2
+ * sec. 3.3 "Backward pass" and appendix C.6): with g = [(S - tau)/2]_+
+ * at alpha = 1.5 (in general g = dA/dS = [(alpha-1)(S - tau)]_+^(1/(alpha-1)
+ * - 1), the support indicator at alpha = 2),
  *   dA_ij = dO_i . V_j,  delta_i = sum_j g_ij dA_ij / sum_j g_ij,
  *   dS_ij = g_ij (dA_ij - delta_i),
  *   dQ = scale dS K,  dK = scale dS^T Q,  dV = A^T dO.

@@ -79,7 +79,8 @@ def test_attn_fwd_validation(api):
     L = api.lib()
     assert fwd(L, Q=None) == api.ERR_NULL
     assert fwd(L, tau=None) == api.ERR_NULL
-    assert fwd(L, alpha=2.0) == api.ERR_ALPHA
+    for bad in (2.5, 1.0, float("nan")):
+        assert fwd(L, alpha=bad) == api.ERR_ALPHA
     assert fwd(L, dtype=5) == api.ERR_DTYPE
     assert fwd(L, mask=3) == api.ERR_MASK
     assert fwd(L, mask=2, window=-1) == api.ERR_MASK
