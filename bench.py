@@ -15,6 +15,7 @@ on the stream the library launches on:
   * the other forward workloads and the backward;
   * the block-sparsity sweep (clustered L = 8192 with 64 ... 1 cluster runs)
     with a linear fit of forward time against the non-null tile fraction;
+  * the clustered forward and the row kernel at alpha = 1.25 and 2;
 and the fp64 CPU oracle on a bounded sample of the same workload
 (`cpu_baseline`).  Rank 0 prints exactly one JSON line on stdout.
 """
@@ -129,7 +130,7 @@ def structural_tiles(cfg):
     return n * cfg.B * cfg.H
 
 
-def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False):
+def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False, alpha=1.5):
     """Forward (and backward) timing of one attention workload."""
     from adaptive_sparse_attention_row_amd.workloads import gen_config
     inp = gen_config(cfg)
@@ -146,23 +147,23 @@ def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False):
 
     def fwd():
         r = lib.entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(), tau.data_ptr(),
-                                bm.data_ptr(), B, H, L, d, sc, 1.5, dt, cfg.mask, cfg.window, ws.data_ptr(),
+                                bm.data_ptr(), B, H, L, d, sc, alpha, dt, cfg.mask, cfg.window, ws.data_ptr(),
                                 wsb, st)
         assert r == 0, api.status_str(r)
 
     def thr():
         r = lib.entmax_attn_threshold(q.data_ptr(), k.data_ptr(), tau.data_ptr(), bm.data_ptr(), B, H, L, d,
-                                      sc, 1.5, dt, cfg.mask, cfg.window, ws.data_ptr(), wsb, st)
+                                      sc, alpha, dt, cfg.mask, cfg.window, ws.data_ptr(), wsb, st)
         assert r == 0, api.status_str(r)
 
     def stats():
-        r = lib.entmax_attn_score_stats(q.data_ptr(), k.data_ptr(), B, H, L, d, sc, 1.5, dt, cfg.mask,
+        r = lib.entmax_attn_score_stats(q.data_ptr(), k.data_ptr(), B, H, L, d, sc, alpha, dt, cfg.mask,
                                         cfg.window, ws.data_ptr(), wsb, st)
         assert r == 0, api.status_str(r)
 
     def out():
         r = lib.entmax_attn_output(q.data_ptr(), k.data_ptr(), v.data_ptr(), tau.data_ptr(), bm.data_ptr(),
-                                   O.data_ptr(), B, H, L, d, sc, 1.5, dt, cfg.mask, cfg.window, st)
+                                   O.data_ptr(), B, H, L, d, sc, alpha, dt, cfg.mask, cfg.window, st)
         assert r == 0, api.status_str(r)
 
     t_fwd = timer(fwd, steps, warmup)
@@ -196,7 +197,7 @@ def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False):
         def bwd():
             r = lib.entmax_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), tau.data_ptr(),
                                     bm.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d,
-                                    sc, 1.5, dt, cfg.mask, cfg.window, bws.data_ptr(), bwsb, st)
+                                    sc, alpha, dt, cfg.mask, cfg.window, bws.data_ptr(), bwsb, st)
             if r != 0:
                 raise RuntimeError(api.status_str(r))
 
@@ -236,7 +237,22 @@ def bench_sweep(api, torch, timer, steps, warmup):
     return {"points": pts, "fit_ms": {"t0": round(t0, 5), "t1_per_unit_fraction": round(t1, 5)}}
 
 
-def bench_tau_rows(api, torch, timer, steps, warmup):
+def bench_alpha(api, torch, timer, steps, warmup):
+    """The clustered L = 8192 forward and the 8192 x 8192 row kernel at
+    alpha = 1.25 and alpha = 2 (sparsemax): the general-alpha paths (Newton
+    solves, pow weights) next to the alpha = 1.5 numbers."""
+    from adaptive_sparse_attention_row_amd.workloads import C4
+    out = {}
+    for a in (1.25, 2.0):
+        r, _ = bench_attn(api, torch, timer, C4, steps, warmup, alpha=a)
+        out[f"c4_alpha{a}"] = {k: r[k] for k in ("fwd_ms", "score_stats_ms", "solve_ms", "output_ms",
+                                                  "dense_equiv_tflops", "block_sparsity_64")}
+        t = bench_tau_rows(api, torch, timer, steps, warmup, alpha=a)
+        out[f"c2_alpha{a}"] = {"ms": t["ms"], "GB_per_s": t["GB_per_s"]}
+    return out
+
+
+def bench_tau_rows(api, torch, timer, steps, warmup, alpha=1.5):
     from adaptive_sparse_attention_row_amd.workloads import C2, gen_rows
     S0 = gen_rows(C2.rows, C2.cols, C2.seed).cuda()
     sets = [S0] + [S0.roll(i + 1, 0).contiguous() for i in range(2)]
@@ -250,7 +266,7 @@ def bench_tau_rows(api, torch, timer, steps, warmup):
         i = it[0] % 3
         it[0] += 1
         r = lib.entmax_tau_rows(sets[i].data_ptr(), Ps[i].data_ptr(), taus[i].data_ptr(), C2.rows, C2.cols,
-                                C2.cols, 1.5, st)
+                                C2.cols, alpha, st)
         assert r == 0, api.status_str(r)
 
     t = timer(run, max(steps, 30), warmup)
@@ -380,7 +396,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "sweep", "copy"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "sweep", "alpha", "copy"], default=None,
                     help="run one workload only (for profiler passes); prints its record")
     ap.add_argument("--counters-summary", metavar="NAME", default=None,
                     help="write profiles/NAME.counters.{json,md} from rocprofv3 counter CSVs (no GPU)")
@@ -422,6 +438,8 @@ def main():
             rec = bench_attn(api, torch, timer, C4, args.steps, args.warmup)[0]
         elif args.only == "sweep":
             rec = bench_sweep(api, torch, timer, args.steps, args.warmup)
+        elif args.only == "alpha":
+            rec = bench_alpha(api, torch, timer, args.steps, args.warmup)
         else:
             rec = bench_attn(api, torch, timer, C5, args.steps, args.warmup, with_bwd=True)[0]
         print(json.dumps({"only": args.only, "record": rec}), flush=True)
@@ -456,6 +474,8 @@ def main():
         log(f"{C5.name}: {extras[C5.name]}")
         extras["sparsity_sweep"] = bench_sweep(api, torch, timer, args.steps, args.warmup)
         log(f"sparsity sweep fit: {extras['sparsity_sweep']['fit_ms']}")
+        extras["general_alpha"] = bench_alpha(api, torch, timer, args.steps, args.warmup)
+        log(f"general alpha: {extras['general_alpha']}")
 
     cpu = None
     if not args.no_cpu_baseline:
