@@ -67,6 +67,11 @@ def lib() -> ctypes.CDLL:
     L.entmax_attn_output.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P]
     L.entmax_set_option.restype = i32
     L.entmax_set_option.argtypes = [i32, i32]
+    L.entmax_attn_decode_workspace.restype = sz
+    L.entmax_attn_decode_workspace.argtypes = [i32] * 7
+    L.entmax_attn_decode.restype = i32
+    L.entmax_attn_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, f32, f32, i32, i32, i32,
+                                     P, sz, P]
     _lib = L
     return L
 
@@ -226,3 +231,31 @@ def attn_bwd(q, k, v, do, tau, block_mask, scale: Optional[float] = None,
                                dt, mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
     _check("entmax_attn_bwd", st)
     return dq, dk, dv
+
+
+def attn_decode(q, k_cache, v_cache, L: Optional[int] = None, scale: Optional[float] = None,
+                mask: int = MASK_CAUSAL, window: int = 0, alpha: float = 1.5, out=None):
+    """One decode step: q [B, H, d] is the query at position L - 1; k_cache and
+    v_cache are [B, H, cache_len, d] (rows 0 .. L - 1 used; L defaults to
+    cache_len).  Returns (o fp32 [B, H, d], tau fp32 [B, H])."""
+    import torch
+    B, H, Lc, d = k_cache.shape
+    if L is None:
+        L = Lc
+    if q.shape != (B, H, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, H, d] and the caches [B, H, cache_len, d]")
+    for t in (q, k_cache, v_cache):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q and the caches must be contiguous CUDA tensors of one dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty(B, H, d, device=q.device, dtype=torch.float32)
+    tau = torch.empty(B, H, device=q.device, dtype=torch.float32)
+    ws_bytes = lib().entmax_attn_decode_workspace(B, H, L, d, dt, mask, window)
+    ws = torch.empty(max(ws_bytes, 4), device=q.device, dtype=torch.uint8)
+    st = lib().entmax_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+                                  tau.data_ptr(), B, H, L, Lc, d, float(scale), float(alpha), dt, mask,
+                                  window, ws.data_ptr(), ws.numel(), _stream(q.device))
+    _check("entmax_attn_decode", st)
+    return o, tau

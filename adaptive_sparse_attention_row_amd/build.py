@@ -24,6 +24,7 @@ SOURCES = [
     "tau_rows.hip",
     "attn_fwd.hip",
     "attn_bwd.hip",
+    "decode.hip",
 ]
 
 ARCH = "gfx950"

@@ -1,0 +1,272 @@
+// decode.hip -- one decode step of alpha-entmax attention: the newest query
+// of every (batch, head), at position L - 1, against its KV cache.
+//
+// "AdaSplash-2: Faster Differentiable Sparse Attention" names inference as
+// further work; the GPT-2 model card generates with a causal window of W
+// recent keys plus the sink key 0 (Mathematical Formulation item 1).  The
+// step computes exactly the last row of the forward:
+//   s_j = scale q . K_j over the active keys, tau from sum_j p_j = 1,
+//   o = sum_j p_j V_j.
+// Only the support carries weight, so only the support's rows of V are read:
+// the forward's block traversal (AdaSplash-2 sec. 3.3 phase 4) taken down to
+// single keys.  HBM traffic is the K cache of the active keys plus a few
+// dozen V rows, about half of what a dense decode reads.
+//
+// dec_scores  grid (active keys / 256, B*H): each wave dots 64 keys with the
+//             query.  A K row is LPK = d * esize / 16 chunks of 16 bytes; one
+//             load instruction covers 64 / LPK whole rows (each lane a chunk
+//             of one row, so a wave reads 1 KiB contiguous), and after LPK
+//             instructions the LPK lanes of a row group hold LPK partial sums
+//             of LPK keys: a reduce-scatter of LPK - 1 lane exchanges leaves
+//             lane c with the full dot of key c.  Scores go to the workspace.
+// dec_solve   one 256-thread workgroup per (batch, head): the maximum, the
+//             scores above the bracket end m - 1/(alpha-1) compacted with
+//             their positions into LDS, tau by the row solves of
+//             row_solve.hpp, then o from the support's V rows only (the
+//             threads split the head dimension, groups of them split the
+//             support, and the groups are summed through LDS).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "row_solve.hpp"
+
+namespace entmax {
+namespace dec {
+namespace {
+
+using namespace rows;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct DecParams {
+    const void* q;  // [BH][d]
+    const void* k;  // [BH][Lcap][d]
+    const void* v;  // [BH][Lcap][d]
+    float* o;       // [BH][d]
+    float* tau;     // [BH]
+    float* s;       // workspace [BH][nact]: scores of the active keys
+    int BH, L, Lcap, nact, j0;  // active keys: 0 (when j0 > 0), then j0 .. L - 1
+    float scale;
+    AlphaMap am;
+    int gen;  // alpha != 1.5
+};
+
+// Position in the active-key list -> key index.
+__device__ __forceinline__ int key_of(int pos, int j0) {
+    if (j0 == 0) return pos;
+    return pos == 0 ? 0 : j0 + pos - 1;
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack(const u32x4& c, float (&x)[16 / sizeof(T)]) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __builtin_bit_cast(float, c[i] << 16);
+            x[2 * i + 1] = __builtin_bit_cast(float, c[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // (a vector element taken straight into __builtin_bit_cast came out
+            // as element 0 for every i with this compiler: copy it first)
+            const uint32_t wv = c[i];
+            x[i] = __builtin_bit_cast(float, wv);
+        }
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dec_scores(DecParams p) {
+    constexpr int kEpc = 16 / sizeof(T);            // elements per 16-byte chunk
+    constexpr int kLpk = D * (int)sizeof(T) / 16;    // lanes (chunks) per key row
+    constexpr int kKpi = kWave / kLpk;               // key rows per load instruction
+    const int bh = blockIdx.y;
+    const int w = wave_id(), l = lane_id();
+    const int c = l % kLpk, grp = l / kLpk;
+    const int p0 = blockIdx.x * 256 + w * kWave;     // first active position of this wave
+    if (p0 >= p.nact) return;
+
+    // this lane's slice of the query
+    float qv[kEpc];
+    {
+        const u32x4 qc = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.q) + (size_t)bh * D)[c];
+        unpack<T>(qc, qv);
+    }
+    const T* Kh = reinterpret_cast<const T*>(p.k) + (size_t)bh * p.Lcap * D;
+    float part[kLpk];
+#pragma unroll
+    for (int i = 0; i < kLpk; ++i) {
+        int pos = p0 + i * kKpi + grp;
+        pos = pos < p.nact ? pos : p.nact - 1;  // tail lanes repeat the last key; never stored
+        const int key = key_of(pos, p.j0);
+        const u32x4 kc = reinterpret_cast<const u32x4*>(Kh + (size_t)key * D)[c];
+        float kv[kEpc];
+        unpack<T>(kc, kv);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < kEpc; ++e) acc = fmaf(qv[e], kv[e], acc);
+        part[i] = acc;
+    }
+    // reduce-scatter over the kLpk lanes of the row group: after the step with
+    // offset hh, lane c keeps the half of its keys selected by bit hh of c
+#pragma unroll
+    for (int hh = kLpk / 2; hh >= 1; hh >>= 1) {
+        const bool up = (c & hh) != 0;
+#pragma unroll
+        for (int j = 0; j < hh; ++j) {
+            const float mine = up ? part[j + hh] : part[j];
+            const float other = up ? part[j] : part[j + hh];
+            part[j] = mine + __shfl_xor(other, hh, kWave);
+        }
+    }
+    const int pos = p0 + c * kKpi + grp;  // the key whose dot lane c now holds
+    if (pos < p.nact) p.s[(size_t)bh * p.nact + pos] = part[0] * p.scale;
+}
+
+constexpr int kDecCap = 4096;  // candidates kept in LDS per (batch, head)
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dec_solve(DecParams p) {
+    __shared__ float cv[kDecCap];
+    __shared__ int cp[kDecCap];
+    __shared__ float red[2][kWaves][6];
+    __shared__ float mbuf[kWaves];
+    __shared__ int wcnt[kWaves];
+    __shared__ float osum[256];
+
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = wave_id();
+    const int bh = blockIdx.x;
+    const int n = p.nact;
+    const float* srow = p.s + (size_t)bh * n;
+
+    float mx = neg_inf();
+    for (int i = t; i < n; i += 256) mx = fmaxf(mx, srow[i]);
+    const float m = block_max(mx, mbuf);
+
+    // candidates: every score above the lower bracket end (nothing at or
+    // below it carries weight), compacted in position order
+    const float lo0 = p.gen ? m - p.am.e : m - 2.0f;
+    int filled = 0;
+    for (int base = 0; base < n; base += 256) {
+        const int i = base + t;
+        const float x = i < n ? srow[i] : neg_inf();
+        const bool is_c = x > lo0;
+        const uint64_t b = __ballot(is_c);
+        if (lane == 0) wcnt[w] = __popcll(b);
+        __syncthreads();
+        int off = filled, tot = 0;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+            off += (k < w) ? wcnt[k] : 0;
+            tot += wcnt[k];
+        }
+        const int slot = off + lanes_below(b);
+        if (is_c && slot < kDecCap) {
+            cv[slot] = x;
+            cp[slot] = i;
+        }
+        filled += tot;
+        __syncthreads();
+    }
+    const bool fits = filled <= kDecCap;
+
+    float tau;
+    if (p.gen) {
+        tau = fits ? refine_tau_gen(m, (float)filled, p.am, [&](float tt, RowSums& s) {
+            for (int i = t; i < filled; i += 256) accumulate_gen(s, cv[i], tt, p.am);
+        }, red)
+                   : refine_tau_gen(m, (float)filled, p.am, [&](float tt, RowSums& s) {
+            for (int i = t; i < n; i += 256) accumulate_gen(s, srow[i], tt, p.am);
+        }, red);
+    } else {
+        tau = fits ? refine_tau(m, (float)filled, [&](float tt, RowSums& s) {
+            for (int i = t; i < filled; i += 256) accumulate(s, cv[i], tt, m);
+        }, red)
+                   : refine_tau(m, (float)filled, [&](float tt, RowSums& s) {
+            for (int i = t; i < n; i += 256) accumulate(s, srow[i], tt, m);
+        }, red);
+    }
+
+    // o = sum over the support of p_j V_j: thread (g, dim) takes every
+    // kG-th support entry
+    constexpr int kG = 256 / D;
+    const int dim = t % D, g = t / D;
+    const T* Vh = reinterpret_cast<const T*>(p.v) + (size_t)bh * p.Lcap * D;
+    auto weight = [&](float x) -> float {
+        if (p.gen) return p.am.p(x, tau);
+        const float gg = fmaxf(0.5f * (x - tau), 0.0f);
+        return gg * gg;
+    };
+    float acc = 0.f;
+    const int lim = fits ? filled : n;
+    for (int i = g; i < lim; i += kG) {
+        const float x = fits ? cv[i] : srow[i];
+        if (x > tau) {
+            const int key = key_of(fits ? cp[i] : i, p.j0);
+            acc = fmaf(weight(x), (float)Vh[(size_t)key * D + dim], acc);
+        }
+    }
+    osum[t] = acc;
+    __syncthreads();
+    if (t < D) {
+        float o = 0.f;
+#pragma unroll
+        for (int k = 0; k < kG; ++k) o += osum[k * D + t];
+        p.o[(size_t)bh * D + t] = o;
+    }
+    if (t == 0) p.tau[bh] = tau;
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const DecParams& dp, hipStream_t stream) {
+    const dim3 g1((unsigned)((dp.nact + 255) / 256), (unsigned)dp.BH);
+    hipLaunchKernelGGL((dec_scores<T, D>), g1, dim3(256), 0, stream, dp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dec_solve<T, D>), dim3((unsigned)dp.BH), dim3(256), 0, stream, dp);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace dec
+
+// Active keys of the query at position L - 1: all of [0, L) unless the
+// window mode drops the keys more than W behind (the sink key 0 stays).
+static void decode_active(int L, int mask, int window, int* j0, int* nact) {
+    int s = 0;
+    if (mask == 2) {
+        const long long lo = (long long)L - 1 - window;
+        s = lo > 0 ? (int)lo : 0;
+    }
+    *j0 = s;
+    *nact = (L - s) + (s > 0 ? 1 : 0);
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int L, int mask, int window) {
+    int j0, nact;
+    decode_active(L, mask, window, &j0, &nact);
+    return (size_t)B * H * nact * sizeof(float);
+}
+
+hipError_t launch_attn_decode(const AttnArgs& a, int Lcap, hipStream_t stream) {
+    using namespace dec;
+    DecParams dp;
+    dp.q = a.q; dp.k = a.k; dp.v = a.v; dp.o = a.o; dp.tau = a.tau;
+    dp.s = reinterpret_cast<float*>(a.workspace);
+    dp.BH = a.B * a.H; dp.L = a.L; dp.Lcap = Lcap;
+    decode_active(a.L, a.mask, a.window, &dp.j0, &dp.nact);
+    dp.scale = a.scale;
+    dp.am = make_alpha_map(a.alpha);
+    dp.gen = a.alpha != 1.5f ? 1 : 0;
+    if (a.dtype == 1) {
+        if (a.d == 64) return launch_typed<__bf16, 64>(dp, stream);
+        return launch_typed<__bf16, 128>(dp, stream);
+    }
+    if (a.d == 64) return launch_typed<float, 64>(dp, stream);
+    return launch_typed<float, 128>(dp, stream);
+}
+
+}  // namespace entmax

@@ -219,3 +219,54 @@ int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
 }
 
 }  // extern "C"
+
+namespace {
+constexpr int kMaxDecodeLen = 1 << 24;
+
+int check_decode(int B, int H, int L, int Lcap, int d, float alpha, int dtype, int mask,
+                 int window) {
+    if (!(alpha > 1.0f && alpha <= 2.0f)) return ENTMAX_ERR_ALPHA;
+    if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return ENTMAX_ERR_DTYPE;
+    if (mask != ENTMAX_MASK_NONE && mask != ENTMAX_MASK_CAUSAL &&
+        mask != ENTMAX_MASK_CAUSAL_WINDOW_SINK)
+        return ENTMAX_ERR_MASK;
+    if (mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK && window < 0) return ENTMAX_ERR_MASK;
+    if (B < 1 || H < 1 || L < 1 || Lcap < L || L > kMaxDecodeLen || (d != 64 && d != 128))
+        return ENTMAX_ERR_SHAPE;
+    if ((int64_t)B * H > 65535 || (int64_t)B * H * Lcap * d > (int64_t)1 << 40)
+        return ENTMAX_ERR_SHAPE;
+    return ENTMAX_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t entmax_attn_decode_workspace(int B, int H, int L, int d, int dtype, int mask, int window) {
+    if (check_decode(B, H, L, L, d, 1.5f, dtype, mask, window) != ENTMAX_OK) return 0;
+    return entmax::attn_decode_workspace_bytes(B, H, L, mask, window);
+}
+
+int entmax_attn_decode(const void* q, const void* K, const void* V, float* O, float* tau,
+                       int B, int H, int L, int cache_len, int d, float scale, float alpha,
+                       int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (q == nullptr || K == nullptr || V == nullptr || O == nullptr || tau == nullptr)
+        return ENTMAX_ERR_NULL;
+    int st = check_decode(B, H, L, cache_len, d, alpha, dtype, mask, window);
+    if (st != ENTMAX_OK) return st;
+    if (!(scale > 0.0f) || !isfinite(scale)) return ENTMAX_ERR_ARG;
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V)) return ENTMAX_ERR_ALIGN;
+    if (((uintptr_t)O & 3u) || ((uintptr_t)tau & 3u)) return ENTMAX_ERR_ALIGN;
+    const size_t need = entmax::attn_decode_workspace_bytes(B, H, L, mask, window);
+    if (workspace == nullptr || workspace_bytes < need) return ENTMAX_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 3u) return ENTMAX_ERR_ALIGN;
+    entmax::AttnArgs a = {};
+    a.q = q; a.k = K; a.v = V; a.o = O; a.tau = tau;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
+    a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    (void)hipGetLastError();
+    return hip_status(entmax::launch_attn_decode(a, cache_len, (hipStream_t)stream));
+}
+
+}  // extern "C"

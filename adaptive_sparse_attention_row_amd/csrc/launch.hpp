@@ -44,5 +44,9 @@ int attn_max_candidate_cap(int d, int dtype);
 // phase bits: 1 = score statistics, 2 = threshold solve + mask, 4 = output
 hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream);
+// Decode step: a.q is [B][H][d] (the query at position L - 1), a.k / a.v the
+// caches [B][H][Lcap][d] of which rows 0 .. L - 1 are used; a.o [B][H][d].
+size_t attn_decode_workspace_bytes(int B, int H, int L, int mask, int window);
+hipError_t launch_attn_decode(const AttnArgs& a, int Lcap, hipStream_t stream);
 
 }  // namespace entmax

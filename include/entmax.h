@@ -202,6 +202,33 @@ int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step: the newest query of every (batch, head), at position
+ * L - 1, against the first L rows of its KV cache.  Exactly the last query
+ * row of entmax_attn_fwd for the same mask mode (mode 0 and mode 1 both
+ * attend to every cached key; mode 2 to key 0 and the keys at most `window`
+ * positions behind).  Autoregressive generation over a growing cache is the
+ * setting of "GPT-2 with AdaSplash Attention via NeuralOps" (Architecture
+ * Overview; Mathematical Formulation item 1); "AdaSplash-2: Faster
+ * Differentiable Sparse Attention" sec. 5 leaves an inference kernel to
+ * future work.  Only the support's V rows are read (the block traversal of
+ * AdaSplash-2 sec. 3.3 phase 4 at single-key granularity).
+ *   q        [B][H][d] of `dtype`, 16-byte aligned.
+ *   K, V     caches [B][H][cache_len][d] of `dtype`, 16-byte aligned; rows
+ *            0 .. L - 1 are read, L <= cache_len.
+ *   O        [B][H][d] fp32 output;  tau  [B][H] fp32 output (score units).
+ *   d in {64, 128}; 1 <= L <= 2^24; B * H <= 65535; alpha in (1, 2].
+ *   workspace  at least entmax_attn_decode_workspace(B, H, L, d, dtype,
+ *              mask, window) bytes (4 bytes per active key per head).
+ * Returns the codes of entmax_attn_fwd.
+ */
+size_t entmax_attn_decode_workspace(int B, int H, int L, int d, int dtype, int mask,
+                                    int window);
+int entmax_attn_decode(const void* q, const void* K, const void* V, float* O, float* tau,
+                       int B, int H, int L, int cache_len, int d, float scale, float alpha,
+                       int dtype, int mask, int window, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * Process-wide tuning / testing options (not thread-safe; set before use).
  *  ENTMAX_OPT_CANDIDATE_CAP: per-row capacity of the forward's candidate
  *    list, 1 .. 128 (value <= 0 restores 128).  Rows with more candidates

@@ -146,3 +146,31 @@ def test_set_option(api):
         api.set_option(99, 1)
     with pytest.raises(api.EntmaxError):
         api.set_option(api.OPT_CANDIDATE_CAP, 1 << 20)
+
+
+def test_decode_validation(api):
+    L = api.lib()
+
+    def call(q=FAKE, K=FAKE, V=FAKE, O=FAKE, tau=FAKE, B=1, H=2, Lk=100, cap=128, d=64, scale=0.125,
+             alpha=1.5, dtype=1, mask=1, window=0, ws=FAKE, wsb=1 << 20):
+        return L.entmax_attn_decode(q, K, V, O, tau, B, H, Lk, cap, d, scale, alpha, dtype, mask, window,
+                                    ws, wsb, None)
+
+    assert call(q=None) == api.ERR_NULL
+    assert call(tau=None) == api.ERR_NULL
+    assert call(alpha=2.5) == api.ERR_ALPHA
+    assert call(dtype=7) == api.ERR_DTYPE
+    assert call(mask=3) == api.ERR_MASK
+    assert call(mask=2, window=-1) == api.ERR_MASK
+    assert call(Lk=0) == api.ERR_SHAPE
+    assert call(Lk=200, cap=100) == api.ERR_SHAPE   # L beyond the cache
+    assert call(d=96) == api.ERR_SHAPE
+    assert call(scale=0.0) == api.ERR_ARG
+    assert call(q=FAKE + 4) == api.ERR_ALIGN
+    assert call(wsb=10) == api.ERR_WORKSPACE
+    assert call(ws=None) == api.ERR_WORKSPACE
+    # 4 bytes per active key per head; the window keeps key 0 and W + 1 recent keys
+    assert L.entmax_attn_decode_workspace(2, 3, 1000, 64, 1, 1, 0) == 2 * 3 * 1000 * 4
+    assert L.entmax_attn_decode_workspace(2, 3, 1000, 64, 1, 2, 32) == 2 * 3 * 34 * 4
+    assert L.entmax_attn_decode_workspace(2, 3, 20, 64, 1, 2, 32) == 2 * 3 * 20 * 4
+    assert L.entmax_attn_decode_workspace(1, 1, 10, 96, 1, 1, 0) == 0
