@@ -19,12 +19,14 @@
 //             instructions the LPK lanes of a row group hold LPK partial sums
 //             of LPK keys: a reduce-scatter of LPK - 1 lane exchanges leaves
 //             lane c with the full dot of key c.  Scores go to the workspace.
-// dec_solve   one 256-thread workgroup per (batch, head): the maximum, the
-//             scores above the bracket end m - 1/(alpha-1) compacted with
-//             their positions into LDS, tau by the row solves of
-//             row_solve.hpp, then o from the support's V rows only (the
-//             threads split the head dimension, groups of them split the
-//             support, and the groups are summed through LDS).
+// dec_solve   one 256-thread workgroup per (batch, head): each wave scans a
+//             quarter of the score row (its lane maxima and their threshold,
+//             a lower bound on tau; then the scores above the largest of the
+//             four bounds, with their positions, into its own LDS list); tau
+//             by the row solves of row_solve.hpp over the four lists; then o
+//             from the support's V rows only (the threads split the head
+//             dimension, groups of them split the support, and the groups
+//             are summed through LDS).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +41,7 @@ namespace {
 using namespace rows;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct DecParams {
     const void* q;  // [BH][d]
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void dec_scores(DecParams p) {
         int pos = p0 + i * kKpi + grp;
         pos = pos < p.nact ? pos : p.nact - 1;  // tail lanes repeat the last key; never stored
         const int key = key_of(pos, p.j0);
-        const u32x4 kc = reinterpret_cast<const u32x4*>(Kh + (size_t)key * D)[c];
+        const u32x4 kc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kh + (size_t)key * D) + c);
         float kv[kEpc];
         unpack<T>(kc, kv);
         float acc = 0.f;
@@ -126,90 +129,183 @@ __global__ __launch_bounds__(256) void dec_scores(DecParams p) {
     if (pos < p.nact) p.s[(size_t)bh * p.nact + pos] = part[0] * p.scale;
 }
 
-constexpr int kDecCap = 4096;  // candidates kept in LDS per (batch, head)
+constexpr int kDecCap = 4096;            // candidates kept in LDS per (batch, head)
+constexpr int kWaveCap = kDecCap / kWaves; // ... as four per-wave lists
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
     __shared__ float cv[kDecCap];
     __shared__ int cp[kDecCap];
     __shared__ float red[2][kWaves][6];
-    __shared__ float mbuf[kWaves];
+    __shared__ float mbuf[kWaves], wbnd[kWaves];
     __shared__ int wcnt[kWaves];
-    __shared__ float osum[256];
+    __shared__ float osum[4 * 256];
 
     const int t = threadIdx.x, lane = t & (kWave - 1), w = wave_id();
     const int bh = blockIdx.x;
     const int n = p.nact;
     const float* srow = p.s + (size_t)bh * n;
 
-    float mx = neg_inf();
-    for (int i = t; i < n; i += 256) mx = fmaxf(mx, srow[i]);
-    const float m = block_max(mx, mbuf);
-
-    // candidates: every score above the lower bracket end (nothing at or
-    // below it carries weight), compacted in position order
-    const float lo0 = p.gen ? m - p.am.e : m - 2.0f;
-    int filled = 0;
-    for (int base = 0; base < n; base += 256) {
-        const int i = base + t;
-        const float x = i < n ? srow[i] : neg_inf();
-        const bool is_c = x > lo0;
-        const uint64_t b = __ballot(is_c);
-        if (lane == 0) wcnt[w] = __popcll(b);
-        __syncthreads();
-        int off = filled, tot = 0;
+    // Each wave scans a quarter of the score row with 16 loads per lane in
+    // flight per step.  Pass 1: the lane maxima, and the threshold of those 64
+    // values (the row kernel's bound: they are a subset of the row, and a
+    // threshold only rises as scores are added, so it is a lower bound on
+    // tau).  The largest of the four waves' bounds is the row's candidate
+    // threshold.  Pass 2 (the quarter again, now from cache): every score
+    // above it, with its position, into the wave's own LDS list.
+    constexpr int kU = 16;
+    const int q0 = (int)(((int64_t)n * w) / kWaves), q1 = (int)(((int64_t)n * (w + 1)) / kWaves);
+    auto load16 = [&](int base, float (&x)[kU]) {
 #pragma unroll
-        for (int k = 0; k < kWaves; ++k) {
-            off += (k < w) ? wcnt[k] : 0;
-            tot += wcnt[k];
+        for (int u = 0; u < kU; ++u) {
+            const int i = base + u * kWave + lane;
+            x[u] = i < q1 ? srow[i] : neg_inf();
         }
-        const int slot = off + lanes_below(b);
-        if (is_c && slot < kDecCap) {
-            cv[slot] = x;
-            cp[slot] = i;
-        }
-        filled += tot;
-        __syncthreads();
+    };
+    float lm = neg_inf();
+    for (int base = q0; base < q1; base += kU * kWave) {
+        float x[kU];
+        load16(base, x);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) lm = fmaxf(lm, x[u]);
     }
-    const bool fits = filled <= kDecCap;
+    const float wm = wave_max_dpp(lm);
+    float wlo = neg_inf();
+    if (wm > neg_inf()) {
+        const float n1 = wave_sum_dpp(lm > neg_inf() ? 1.0f : 0.0f);
+        if (p.gen)
+            wave_tau_gen(wm, n1, wm - p.am.e, p.am, [&](float tt, RowSums& s) { accumulate_gen(s, lm, tt, p.am); },
+                         &wlo);
+        else
+            wlo = wave_tau(wm, n1, wm - 2.0f, [&](float tt, RowSums& s) { accumulate(s, lm, tt, wm); });
+    }
+    if (lane == 0) {
+        mbuf[w] = wm;
+        wbnd[w] = wlo;
+    }
+    __syncthreads();
+    float m = mbuf[0], bound = wbnd[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+        m = fmaxf(m, mbuf[k]);
+        bound = fmaxf(bound, wbnd[k]);
+    }
+    float* wv = cv + w * kWaveCap;
+    int* wp = cp + w * kWaveCap;
+    int cnt = 0;
+    for (int base = q0; base < q1; base += kU * kWave) {
+        float x[kU];
+        load16(base, x);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const bool is_c = x[u] > bound;
+            const uint64_t b = __ballot(is_c);
+            if (b == 0) continue;
+            const int slot = cnt + lanes_below(b);
+            if (is_c && slot < kWaveCap) {
+                wv[slot] = x[u];
+                wp[slot] = base + u * kWave + lane;
+            }
+            cnt += __popcll(b);
+        }
+    }
+    if (lane == 0) wcnt[w] = cnt;
+    __syncthreads();
+    int filled = 0;
+    bool fits = true;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        filled += wcnt[k];
+        fits = fits && wcnt[k] <= kWaveCap;
+    }
+    // visit the candidates of the four lists (thread t: entries t, t + 256, ...)
+    auto each_cand = [&](auto f) {
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k)
+            for (int i = t; i < wcnt[k]; i += 256) f(cv[k * kWaveCap + i], cp[k * kWaveCap + i]);
+    };
 
     float tau;
     if (p.gen) {
         tau = fits ? refine_tau_gen(m, (float)filled, p.am, [&](float tt, RowSums& s) {
-            for (int i = t; i < filled; i += 256) accumulate_gen(s, cv[i], tt, p.am);
+            each_cand([&](float x, int) { accumulate_gen(s, x, tt, p.am); });
         }, red)
                    : refine_tau_gen(m, (float)filled, p.am, [&](float tt, RowSums& s) {
             for (int i = t; i < n; i += 256) accumulate_gen(s, srow[i], tt, p.am);
         }, red);
     } else {
         tau = fits ? refine_tau(m, (float)filled, [&](float tt, RowSums& s) {
-            for (int i = t; i < filled; i += 256) accumulate(s, cv[i], tt, m);
+            each_cand([&](float x, int) { accumulate(s, x, tt, m); });
         }, red)
                    : refine_tau(m, (float)filled, [&](float tt, RowSums& s) {
             for (int i = t; i < n; i += 256) accumulate(s, srow[i], tt, m);
         }, red);
     }
 
-    // o = sum over the support of p_j V_j: thread (g, dim) takes every
-    // kG-th support entry
-    constexpr int kG = 256 / D;
-    const int dim = t % D, g = t / D;
-    const T* Vh = reinterpret_cast<const T*>(p.v) + (size_t)bh * p.Lcap * D;
+    // o = sum over the support of p_j V_j.  Each wave first compacts the
+    // support of its own list in place (weight, key), in list order, so the
+    // sum below runs in a fixed order.  Then thread t takes 4 consecutive
+    // dimensions of every kG-th support entry (kG = 256 / (D / 4) groups, so
+    // all of a short support's V rows are in flight at once), and the groups
+    // are summed through LDS.
     auto weight = [&](float x) -> float {
         if (p.gen) return p.am.p(x, tau);
         const float gg = fmaxf(0.5f * (x - tau), 0.0f);
         return gg * gg;
     };
-    float acc = 0.f;
-    const int lim = fits ? filled : n;
-    for (int i = g; i < lim; i += kG) {
-        const float x = fits ? cv[i] : srow[i];
-        if (x > tau) {
-            const int key = key_of(fits ? cp[i] : i, p.j0);
-            acc = fmaf(weight(x), (float)Vh[(size_t)key * D + dim], acc);
+    const T* Vh = reinterpret_cast<const T*>(p.v) + (size_t)bh * p.Lcap * D;
+    constexpr int kQ = D / 4;        // threads per V row (4 dimensions each)
+    constexpr int kG = 256 / kQ;     // support entries in flight
+    const int d4 = (t % kQ) * 4, g = t / kQ;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    auto add_row = [&](float wgt, int key) {
+        const T* row = Vh + (size_t)key * D + d4;
+        if constexpr (sizeof(T) == 2) {
+            const u32x2 v2 = *reinterpret_cast<const u32x2*>(row);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t wv2 = v2[e];
+                acc[2 * e] = fmaf(wgt, __builtin_bit_cast(float, wv2 << 16), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(wgt, __builtin_bit_cast(float, wv2 & 0xffff0000u), acc[2 * e + 1]);
+            }
+        } else {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(row);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, v4[e], acc[e]);
+        }
+    };
+    if (fits) {
+        const int mine = wcnt[w] < kWaveCap ? wcnt[w] : kWaveCap;
+        int ns = 0;
+        for (int i0 = 0; i0 < mine; i0 += kWave) {
+            const int i = i0 + lane;
+            const float x = i < mine ? wv[i] : neg_inf();
+            const int pos = i < mine ? wp[i] : 0;
+            const bool on = x > tau;
+            const uint64_t b = __ballot(on);
+            if (on) {
+                const int slot = ns + lanes_below(b);
+                wv[slot] = weight(x);
+                wp[slot] = key_of(pos, p.j0);
+            }
+            ns += __popcll(b);
+        }
+        __syncthreads();  // every wave's reads of its list are done before wcnt changes
+        if (lane == 0) wcnt[w] = ns;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+#pragma unroll 4
+            for (int i = g; i < wcnt[k]; i += kG) add_row(cv[k * kWaveCap + i], cp[k * kWaveCap + i]);
+        }
+    } else {
+        for (int i = g; i < n; i += kG) {
+            const float x = srow[i];
+            if (x > tau) add_row(weight(x), key_of(i, p.j0));
         }
     }
-    osum[t] = acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) osum[g * D + d4 + e] = acc[e];
     __syncthreads();
     if (t < D) {
         float o = 0.f;

@@ -39,106 +39,6 @@ namespace {
 
 using namespace rows;
 
-// DPP sum / min over the 64 lanes of a wave, result in every lane.  Lanes
-// with no source in a step read the identity (0 or +inf).
-__device__ __forceinline__ float wave_sum_dpp(float x) {
-#define ENTMAX_DPP_STEP(op, idv, ctrl, rmask)                                                  \
-    x = op(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                           \
-                  __builtin_bit_cast(int, idv), __builtin_bit_cast(int, x), ctrl, rmask, 0xf, \
-                  false)))
-#define ENTMAX_ADD(a, b) ((a) + (b))
-    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x111, 0xf);
-    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x112, 0xf);
-    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x114, 0xf);
-    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x118, 0xf);
-    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x142, 0xa);
-    ENTMAX_DPP_STEP(ENTMAX_ADD, 0.0f, 0x143, 0xc);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-}
-__device__ __forceinline__ float wave_min_dpp(float x) {
-    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x111, 0xf);
-    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x112, 0xf);
-    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x114, 0xf);
-    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x118, 0xf);
-    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x142, 0xa);
-    ENTMAX_DPP_STEP(fminf, __builtin_inff(), 0x143, 0xc);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-}
-__device__ __forceinline__ float wave_max_dpp(float x) {
-    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x111, 0xf);
-    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x112, 0xf);
-    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x114, 0xf);
-    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x118, 0xf);
-    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x142, 0xa);
-    ENTMAX_DPP_STEP(fmaxf, neg_inf(), 0x143, 0xc);
-#undef ENTMAX_ADD
-#undef ENTMAX_DPP_STEP
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-}
-
-// Threshold of a set held by one wave: `each(t, sums)` adds this lane's part
-// of the sums over {x > t}.  Halley-bisection in the bracket [lo, m - 2/sqrt(n)]
-// (lo a lower bound on tau, no smaller than m - 2; n >= the support size)
-// with the exact finish of refine_tau; all sums are wave reductions.  Every
-// lane returns the same tau.
-template <class Each>
-__device__ __forceinline__ float wave_tau(float m, float n, float lo, Each each) {
-    float hi = m - 2.0f / sqrtf(n);
-    float t = lo;
-    for (int it = 0; it < kMaxIter; ++it) {
-        RowSums s = {0.f, 0.f, 0.f, 0.f, 0.f, __builtin_inff()};
-        each(t, s);
-        s.C = wave_sum_dpp(s.C);
-        s.S1 = wave_sum_dpp(s.S1);
-        s.S2 = wave_sum_dpp(s.S2);
-        s.F = wave_sum_dpp(s.F);
-        s.F1 = wave_sum_dpp(s.F1);
-        s.mn = wave_min_dpp(s.mn);
-        if (s.F - 1.0f >= 0.0f) {
-            const float ts = support_root(m, s.C, s.S1, s.S2);
-            if (ts < s.mn) return fmaxf(ts, t);
-            lo = t;
-        } else {
-            hi = t;
-        }
-        if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) break;
-        t = halley_or_bisect(t, s.F, s.F1, s.C, lo, hi);
-    }
-    return 0.5f * (lo + hi);
-}
-
-// General-alpha threshold of a set held by one wave (Newton from below, see
-// newton_or_bisect) in [lo, hi(m, n)].  Every lane returns the same tau;
-// *lo_out receives the final lower bracket end (a point with f >= 0, so a
-// lower bound on tau up to the rounding of the sums).
-template <class Each>
-__device__ __forceinline__ float wave_tau_gen(float m, float n, float lo, const AlphaMap& a, Each each,
-                                              float* lo_out) {
-    float hi = a.hi(m, n);
-    float t = lo;
-    float tau = 0.5f * (lo + hi);
-    for (int it = 0; it < kMaxIter; ++it) {
-        RowSums s = {0.f, 0.f, 0.f, 0.f, 0.f, __builtin_inff()};
-        each(t, s);
-        s.F = wave_sum_dpp(s.F);
-        s.F1 = wave_sum_dpp(s.F1);
-        bool done;
-        const float tn = newton_or_bisect(t, s.F, s.F1, lo, hi, &done);
-        if (done) {
-            tau = tn;
-            break;
-        }
-        if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) {
-            tau = 0.5f * (lo + hi);
-            break;
-        }
-        t = tn;
-        tau = 0.5f * (lo + hi);
-    }
-    if (lo_out) *lo_out = lo;
-    return tau;
-}
-
 constexpr int kRowsPerBlock = 1;  // one single-wave workgroup per row
 constexpr int kWaveCand = 2048;                  // LDS candidates per wave
 

@@ -16,6 +16,7 @@ on the stream the library launches on:
   * the block-sparsity sweep (clustered L = 8192 with 64 ... 1 cluster runs)
     with a linear fit of forward time against the non-null tile fraction;
   * the clustered forward and the row kernel at alpha = 1.25 and 2;
+  * one decode step over a bf16 KV cache (long causal, and window 32 + sink);
 and the fp64 CPU oracle on a bounded sample of the same workload
 (`cpu_baseline`).  Rank 0 prints exactly one JSON line on stdout.
 """
@@ -237,6 +238,54 @@ def bench_sweep(api, torch, timer, steps, warmup):
     return {"points": pts, "fit_ms": {"t0": round(t0, 5), "t1_per_unit_fraction": round(t1, 5)}}
 
 
+DECODE_WORKLOADS = [
+    # (name, B, H, L, d, mask, window): a long causal cache, and the GPT-2 style
+    # window of 32 recent keys plus the sink
+    ("decode_B16H16L16384d128_causal", 16, 16, 16384, 128, 1, 0),
+    ("decode_B16H12L4096d64_window32_sink", 16, 12, 4096, 64, 2, 32),
+]
+
+
+def bench_decode(api, torch, timer, steps, warmup):
+    """One decode step (the query at position L - 1 over a bf16 KV cache).
+    HBM-bound: the algorithmic bytes are the K rows of the active keys, the V
+    rows of the support only, the query, o and tau.  The support size comes
+    from the step's own score row (workspace) and tau."""
+    from adaptive_sparse_attention_row_amd.workloads import gen_attn
+    out = {}
+    lib = api.lib()
+    for name, B, H, L, d, mask, W in DECODE_WORKLOADS:
+        g = torch.Generator("cpu").manual_seed(60)
+        K = torch.randn(B, H, L, d, generator=g).to(torch.bfloat16).cuda()
+        V = torch.randn(B, H, L, d, generator=g).to(torch.bfloat16).cuda()
+        q = torch.randn(B, H, d, generator=g).to(torch.bfloat16).cuda()
+        o = torch.empty(B, H, d, device="cuda")
+        tau = torch.empty(B, H, device="cuda")
+        wsb = lib.entmax_attn_decode_workspace(B, H, L, d, 1, mask, W)
+        ws = torch.empty(wsb // 4, device="cuda")
+        st = api._stream(q.device)
+        sc = 1.0 / math.sqrt(d)
+
+        def step():
+            r = lib.entmax_attn_decode(q.data_ptr(), K.data_ptr(), V.data_ptr(), o.data_ptr(), tau.data_ptr(),
+                                       B, H, L, L, d, sc, 1.5, 1, mask, W, ws.data_ptr(), wsb, st)
+            assert r == 0, api.status_str(r)
+
+        t = timer(step, max(steps, 20), warmup)
+        nact = wsb // 4 // (B * H)
+        sup = int((ws.view(B * H, nact) > tau.view(B * H, 1)).sum().item())
+        algo = B * H * nact * d * 2 + sup * d * 2 + B * H * d * (2 + 4) + B * H * 4
+        gbs = algo / (t * 1e-3) / 1e9
+        out[name] = {"ms": round(t, 5), "active_keys_per_head": nact, "support_mean": round(sup / (B * H), 1),
+                     "algorithmic_bytes": algo, "GB_per_s": round(gbs, 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
+                     "dense_decode_bytes": B * H * nact * d * 2 * 2}
+        del K, V, q, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_alpha(api, torch, timer, steps, warmup):
     """The clustered L = 8192 forward and the 8192 x 8192 row kernel at
     alpha = 1.25 and alpha = 2 (sparsemax): the general-alpha paths (Newton
@@ -396,7 +445,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "sweep", "alpha", "copy"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "sweep", "alpha", "decode", "copy"], default=None,
                     help="run one workload only (for profiler passes); prints its record")
     ap.add_argument("--counters-summary", metavar="NAME", default=None,
                     help="write profiles/NAME.counters.{json,md} from rocprofv3 counter CSVs (no GPU)")
@@ -440,6 +489,8 @@ def main():
             rec = bench_sweep(api, torch, timer, args.steps, args.warmup)
         elif args.only == "alpha":
             rec = bench_alpha(api, torch, timer, args.steps, args.warmup)
+        elif args.only == "decode":
+            rec = bench_decode(api, torch, timer, args.steps, args.warmup)
         else:
             rec = bench_attn(api, torch, timer, C5, args.steps, args.warmup, with_bwd=True)[0]
         print(json.dumps({"only": args.only, "record": rec}), flush=True)
@@ -476,6 +527,8 @@ def main():
         log(f"sparsity sweep fit: {extras['sparsity_sweep']['fit_ms']}")
         extras["general_alpha"] = bench_alpha(api, torch, timer, args.steps, args.warmup)
         log(f"general alpha: {extras['general_alpha']}")
+        extras["decode"] = bench_decode(api, torch, timer, args.steps, args.warmup)
+        log(f"decode: {extras['decode']}")
 
     cpu = None
     if not args.no_cpu_baseline:
