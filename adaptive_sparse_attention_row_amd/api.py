@@ -18,6 +18,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALPHA, ERR_DTYPE, ERR_MASK, ERR_WORKSPACE, ERR_ALIG
 MASK_NONE, MASK_CAUSAL, MASK_WINDOW_SINK = 0, 1, 2
 F32, BF16 = 0, 1
 OPT_CANDIDATE_CAP = 1
+OPT_ROW_HISTOGRAM = 2
 
 _lib: Optional[ctypes.CDLL] = None
 

@@ -14,6 +14,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int hip_status(hipError_t e) { return e == hipSuccess ? ENTMAX_OK : ENTMAX_ERR_HIP; }
 
 int g_cand_cap = 0;  // 0: the compiled default
+int g_row_hist = 1;  // histogram-initialised bracket for wide rows
 
 // Shared checks of the attention entry points (everything except pointers).
 int check_attn_shape(int B, int H, int L, int d, float alpha, int dtype, int mask, int window) {
@@ -62,6 +63,11 @@ int entmax_tile_shape(int d, int dtype, int* block_rows, int* block_cols) {
 }
 
 int entmax_set_option(int option, int value) {
+    if (option == ENTMAX_OPT_ROW_HISTOGRAM) {
+        const int prev = g_row_hist;
+        g_row_hist = value != 0 ? 1 : 0;
+        return prev;
+    }
     if (option != ENTMAX_OPT_CANDIDATE_CAP) return -ENTMAX_ERR_ARG;
     const int maxcap = entmax::attn_max_candidate_cap(64, ENTMAX_BF16);
     if (value > maxcap) return -ENTMAX_ERR_ARG;
@@ -78,7 +84,8 @@ int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t 
     if (rows == 0) return ENTMAX_OK;
     if (S == nullptr || tau == nullptr) return ENTMAX_ERR_NULL;
     (void)hipGetLastError();
-    return hip_status(entmax::launch_tau_rows(S, P, tau, rows, cols, ld, alpha, (hipStream_t)stream));
+    return hip_status(
+        entmax::launch_tau_rows(S, P, tau, rows, cols, ld, alpha, g_row_hist, (hipStream_t)stream));
 }
 
 size_t entmax_attn_threshold_workspace(int B, int H, int L, int d, int dtype, int mask,

@@ -7,8 +7,9 @@
 
 namespace entmax {
 
+// use_hist: histogram-initialised bracket in the wide-row kernel
 hipError_t launch_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
-                           int64_t ld, float alpha, hipStream_t stream);
+                           int64_t ld, float alpha, int use_hist, hipStream_t stream);
 
 // Arguments of one attention call after validation.
 struct AttnArgs {

@@ -87,9 +87,11 @@ __device__ __forceinline__ void accumulate(RowSums& s, float x, float t, float m
 // Halley-bisection with exact finish.  `visit(t, sums)` adds this thread's
 // contribution at threshold t.  Every thread returns the same tau.
 template <class Visit>
-__device__ float refine_tau(float m, float total, Visit visit, float (*red)[kWaves][6]) {
-    float lo = m - 2.0f;
-    float hi = m - 2.0f / sqrtf(total);
+__device__ float refine_tau(float m, float total, Visit visit, float (*red)[kWaves][6],
+                           float lo_in = -__builtin_inff(), float hi_in = __builtin_inff()) {
+    // the bracket [m - 2, m - 2/sqrt(n)], narrowed to [lo_in, hi_in] when given
+    float lo = fmaxf(m - 2.0f, lo_in);
+    float hi = fminf(m - 2.0f / sqrtf(total), hi_in);
     float t = lo;
     for (int it = 0; it < kMaxIter; ++it) {
         RowSums s = {0.f, 0.f, 0.f, 0.f, 0.f, __builtin_inff()};
@@ -136,9 +138,10 @@ __device__ __forceinline__ void accumulate_gen(RowSums& s, float x, float t, con
 // Workgroup form of wave_tau_gen for the streaming kernel.
 template <class Visit>
 __device__ float refine_tau_gen(float m, float total, const AlphaMap& a, Visit visit,
-                                float (*red)[kWaves][6]) {
-    float lo = m - a.e;
-    float hi = a.hi(m, total);
+                                float (*red)[kWaves][6], float lo_in = -__builtin_inff(),
+                                float hi_in = __builtin_inff()) {
+    float lo = fmaxf(m - a.e, lo_in);
+    float hi = fminf(a.hi(m, total), hi_in);
     float t = lo;
     for (int it = 0; it < kMaxIter; ++it) {
         RowSums s = {0.f, 0.f, 0.f, 0.f, 0.f, __builtin_inff()};
@@ -151,6 +154,46 @@ __device__ float refine_tau_gen(float m, float total, const AlphaMap& a, Visit v
         t = tn;
     }
     return 0.5f * (lo + hi);
+}
+
+// Histogram initialisation ("AdaSplash-2: Faster Differentiable Sparse
+// Attention" sec. 3.1, appendix C.3), in the pages' z-units:
+//   z = (alpha - 1)(s - m) + 1  (z = 1 at the maximum; only z >= 0 can carry
+//   weight), bin k = min(floor(B z), B - 1) (left edges).
+// Replacing every z by its bin's left edge k/B can only lower the normaliser,
+// so the histogram threshold tau_h (the root of sum_k H_k [k/B - tau]_+^e = 1)
+// satisfies tau* - 1/B < tau_h <= tau* (Proposition 3.1): in score units
+// tau lies in [tau_h, tau_h + 1/(B (alpha - 1))].
+constexpr int kHistBins = 64;
+
+__device__ __forceinline__ int hist_bin(float x, float m, float am1) {
+    const float z = __builtin_fmaf(am1, x - m, 1.0f);
+    int k = (int)floorf(z * (float)kHistBins);
+    k = k < kHistBins - 1 ? k : kHistBins - 1;
+    return k > 0 ? k : 0;
+}
+
+// tau_h from the bin counts (one count per lane, lane k = bin k of a 64-lane
+// wave): bisection on the histogram objective over [(B-1)/B - 1, (B-1)/B]
+// (the top bin, which holds the maximum, gives f_h >= 0 at the lower end),
+// every lane taking part.  Returned in score units.
+__device__ __forceinline__ float hist_tau(int count, float m, const AlphaMap& a) {
+    static_assert(kHistBins == kWave, "one bin per lane");
+    const float edge = (float)lane_id() / (float)kHistBins;
+    const float c = (float)count;
+    float lo = (float)(kHistBins - 1) / kHistBins - 1.0f, hi = (float)(kHistBins - 1) / kHistBins;
+    for (int it = 0; it < 40; ++it) {
+        const float mid = 0.5f * (lo + hi);
+        if (!(mid > lo && mid < hi)) break;
+        const float u = edge - mid;
+        float f = (u > 0.0f && c > 0.0f) ? c * (a.lin ? u : exp2f(a.e * log2f(u))) : 0.0f;
+        // wave sum by butterfly (all lanes end with the total)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) f += __shfl_xor(f, o, kWave);
+        if (f >= 1.0f) lo = mid;
+        else hi = mid;
+    }
+    return m + (lo - 1.0f) * a.e;
 }
 
 // DPP sum / min over the 64 lanes of a wave, result in every lane.  Lanes

@@ -20,7 +20,12 @@
 //   5. P from the register copy, so HBM sees one read and one write per
 //      element.
 // Wider rows take a 256-thread streaming kernel that reads the row three
-// times (maximum, candidates above m - 2, output).
+// times (maximum, candidates above m - 2, output).  While it compacts the
+// candidates it also bins them (the histogram initialisation of AdaSplash-2
+// sec. 3.1, 64 left-edge bins): the histogram threshold tau_h brackets tau
+// within one bin width, so the refinement starts from [tau_h, tau_h + h]
+// instead of the whole [m - 2, m - 2/sqrt(n)].  That matters when a dense row
+// overflows the LDS list and every refinement step re-reads the row.
 //
 // Other alpha in (1, 2] (AdaSplash-2 sec. 2.3; see AlphaMap) take the same
 // structure with p = [(alpha-1)(s - tau)]_+^(1/(alpha-1)): the lower bound is
@@ -186,15 +191,19 @@ template <bool GEN>
 __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restrict__ S,
                                                            float* __restrict__ P,
                                                            float* __restrict__ tau_out,
-                                                           int64_t cols, int64_t ld, AlphaMap am) {
+                                                           int64_t cols, int64_t ld, AlphaMap am,
+                                                           int use_hist) {
     __shared__ float cand[kCandCap];
     __shared__ float red[2][kWaves][6];
     __shared__ float mbuf[kWaves];
     __shared__ int wcnt[kWaves];
+    __shared__ int hist[kWaves][kHistBins];
+    __shared__ float tauh_s;
 
     const int t = threadIdx.x, lane = t & (kWave - 1), w = wave_id();
     const int64_t row = blockIdx.x;
     const float* src = S + row * ld;
+    for (int i = t; i < kWaves * kHistBins; i += kThreads) (&hist[0][0])[i] = 0;
 
     float mx = neg_inf();
     for (int64_t pos = t; pos < cols; pos += kThreads) mx = fmaxf(mx, src[pos]);
@@ -223,18 +232,36 @@ __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restr
             }
             const int slot = base + lanes_below(b);
             if (is_c && slot < kCandCap) cand[slot] = x;
+            if (is_c && use_hist) atomicAdd(&hist[w][hist_bin(x, m, am.am1)], 1);
             filled += tot;
             __syncthreads();
+        }
+        // histogram bracket [tau_h, tau_h + 1/(B (alpha - 1))], widened by a
+        // rounding margin (bins come from fp32 z)
+        float blo = neg_inf(), bhi = __builtin_inff();
+        if (use_hist) {
+            if (w == 0) {
+                int cnt = 0;
+#pragma unroll
+                for (int k = 0; k < kWaves; ++k) cnt += hist[k][lane];
+                const float th = hist_tau(cnt, m, am);
+                if (lane == 0) tauh_s = th;
+            }
+            __syncthreads();
+            const float th = tauh_s;
+            const float marg = 1e-6f * fmaxf(1.0f, fabsf(th));
+            blo = th - marg;
+            bhi = th + am.e / (float)kHistBins + marg;
         }
         if constexpr (GEN) {
             if (filled <= kCandCap) {
                 tau = refine_tau_gen(m, (float)filled, am, [&](float tt, RowSums& s) {
                     for (int i = t; i < filled; i += kThreads) accumulate_gen(s, cand[i], tt, am);
-                }, red);
+                }, red, blo, bhi);
             } else {
                 tau = refine_tau_gen(m, (float)filled, am, [&](float tt, RowSums& s) {
                     for (int64_t pos = t; pos < cols; pos += kThreads) accumulate_gen(s, src[pos], tt, am);
-                }, red);
+                }, red, blo, bhi);
             }
         } else if (filled <= kCandCap) {
             tau = refine_tau(
@@ -242,14 +269,14 @@ __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restr
                 [&](float tt, RowSums& s) {
                     for (int i = t; i < filled; i += kThreads) accumulate(s, cand[i], tt, m);
                 },
-                red);
+                red, blo, bhi);
         } else {
             tau = refine_tau(
                 m, (float)filled,
                 [&](float tt, RowSums& s) {
                     for (int64_t pos = t; pos < cols; pos += kThreads) accumulate(s, src[pos], tt, m);
                 },
-                red);
+                red, blo, bhi);
         }
     }
     if (t == 0) tau_out[row] = tau;
@@ -269,7 +296,7 @@ hipError_t launch_wave(const float* S, float* P, float* tau, int64_t rows, int64
 
 template <bool GEN>
 hipError_t launch_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols, int64_t ld,
-                       const AlphaMap& am, hipStream_t stream) {
+                       const AlphaMap& am, int use_hist, hipStream_t stream) {
     const bool vec = (ld % 4 == 0) && ((uintptr_t)S % 16 == 0) &&
                      (P == nullptr || (uintptr_t)P % 16 == 0);
     if (vec) {
@@ -285,17 +312,17 @@ hipError_t launch_rows(const float* S, float* P, float* tau, int64_t rows, int64
         if (cols <= 64 * kWave) return launch_wave<64, false, GEN>(S, P, tau, rows, cols, ld, am, stream);
     }
     hipLaunchKernelGGL(tau_rows_stream<GEN>, dim3((unsigned)rows), dim3(kThreads), 0, stream, S, P,
-                       tau, cols, ld, am);
+                       tau, cols, ld, am, use_hist);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
-                           int64_t ld, float alpha, hipStream_t stream) {
+                           int64_t ld, float alpha, int use_hist, hipStream_t stream) {
     const AlphaMap am = make_alpha_map(alpha);
-    if (alpha == 1.5f) return launch_rows<false>(S, P, tau, rows, cols, ld, am, stream);
-    return launch_rows<true>(S, P, tau, rows, cols, ld, am, stream);
+    if (alpha == 1.5f) return launch_rows<false>(S, P, tau, rows, cols, ld, am, use_hist, stream);
+    return launch_rows<true>(S, P, tau, rows, cols, ld, am, use_hist, stream);
 }
 
 }  // namespace entmax

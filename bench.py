@@ -17,6 +17,7 @@ on the stream the library launches on:
     with a linear fit of forward time against the non-null tile fraction;
   * the clustered forward and the row kernel at alpha = 1.25 and 2;
   * one decode step over a bf16 KV cache (long causal, and window 32 + sink);
+  * dense rows wider than 8192 with and without the histogram bracket;
 and the fp64 CPU oracle on a bounded sample of the same workload
 (`cpu_baseline`).  Rank 0 prints exactly one JSON line on stdout.
 """
@@ -286,6 +287,36 @@ def bench_decode(api, torch, timer, steps, warmup):
     return out
 
 
+def bench_wide_rows(api, torch, timer, steps, warmup):
+    """Rows wider than 8192 that are dense (every score within reach of the
+    maximum, so the candidates overflow the LDS list and each refinement
+    step re-reads the row): the streaming row kernel with and without the
+    histogram-initialised bracket (AdaSplash-2 sec. 3.1)."""
+    rows, cols = 2048, 32768
+    g = torch.Generator("cpu").manual_seed(61)
+    S = (0.02 * torch.randn(rows, cols, generator=g)).cuda()
+    P = torch.empty_like(S)
+    tau = torch.empty(rows, device="cuda")
+    lib = api.lib()
+    st = api._stream(S.device)
+
+    def run():
+        r = lib.entmax_tau_rows(S.data_ptr(), P.data_ptr(), tau.data_ptr(), rows, cols, cols, 1.5, st)
+        assert r == 0, api.status_str(r)
+
+    out = {"workload": f"rows{rows}x{cols}_f32_dense (0.02 N(0, 1))"}
+    for hist in (1, 0):
+        prev = api.set_option(api.OPT_ROW_HISTOGRAM, hist)
+        try:
+            t = timer(run, max(steps // 2, 5), 2)
+        finally:
+            api.set_option(api.OPT_ROW_HISTOGRAM, prev)
+        out["histogram_ms" if hist else "bracket_only_ms"] = round(t, 5)
+    del S, P
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_alpha(api, torch, timer, steps, warmup):
     """The clustered L = 8192 forward and the 8192 x 8192 row kernel at
     alpha = 1.25 and alpha = 2 (sparsemax): the general-alpha paths (Newton
@@ -445,7 +476,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "sweep", "alpha", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "sweep", "alpha", "decode", "wide", "copy"],
+                    default=None,
                     help="run one workload only (for profiler passes); prints its record")
     ap.add_argument("--counters-summary", metavar="NAME", default=None,
                     help="write profiles/NAME.counters.{json,md} from rocprofv3 counter CSVs (no GPU)")
@@ -491,6 +523,8 @@ def main():
             rec = bench_alpha(api, torch, timer, args.steps, args.warmup)
         elif args.only == "decode":
             rec = bench_decode(api, torch, timer, args.steps, args.warmup)
+        elif args.only == "wide":
+            rec = bench_wide_rows(api, torch, timer, args.steps, args.warmup)
         else:
             rec = bench_attn(api, torch, timer, C5, args.steps, args.warmup, with_bwd=True)[0]
         print(json.dumps({"only": args.only, "record": rec}), flush=True)
@@ -529,6 +563,8 @@ def main():
         log(f"general alpha: {extras['general_alpha']}")
         extras["decode"] = bench_decode(api, torch, timer, args.steps, args.warmup)
         log(f"decode: {extras['decode']}")
+        extras["wide_dense_rows"] = bench_wide_rows(api, torch, timer, args.steps, args.warmup)
+        log(f"wide dense rows: {extras['wide_dense_rows']}")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -234,10 +234,16 @@ int entmax_attn_decode(const void* q, const void* K, const void* V, float* O, fl
  *    list, 1 .. 128 (value <= 0 restores 128).  Rows with more candidates
  *    are collected again above a tighter bound, then take the iterative
  *    full-sweep path; tests use a tiny cap to force those paths.
+ *  ENTMAX_OPT_ROW_HISTOGRAM: 1 (default) or 0.  entmax_tau_rows on rows
+ *    wider than 8192 bins the candidates into 64 left-edge bins and starts
+ *    the refinement from the histogram bracket [tau_h, tau_h + 1/(64
+ *    (alpha - 1))] ("AdaSplash-2: Faster Differentiable Sparse Attention"
+ *    sec. 3.1 and Proposition 3.1); 0 starts from [m - 1/(alpha-1),
+ *    m - n^(1-alpha)/(alpha-1)].  Results are the same either way.
  * Returns the previous value, or -ENTMAX_ERR_ARG for an unknown option or an
  * out-of-range value.
  */
-enum { ENTMAX_OPT_CANDIDATE_CAP = 1 };
+enum { ENTMAX_OPT_CANDIDATE_CAP = 1, ENTMAX_OPT_ROW_HISTOGRAM = 2 };
 int entmax_set_option(int option, int value);
 
 #ifdef __cplusplus

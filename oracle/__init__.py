@@ -82,6 +82,8 @@ def _load() -> ctypes.CDLL:
     D = ctypes.c_double
     lib.orc_entmax_tau_bisect.restype = D
     lib.orc_entmax_tau_bisect.argtypes = [P, i64, D]
+    lib.orc_entmax_tau_histogram.restype = D
+    lib.orc_entmax_tau_histogram.argtypes = [P, i64, ctypes.c_float, ctypes.c_int]
     lib.orc_entmax_alpha.restype = D
     lib.orc_entmax_alpha.argtypes = [P, i64, D, P, P]
     lib.orc_tau_rows_alpha.restype = None
@@ -145,6 +147,12 @@ def tau_bisect(s, alpha: float) -> float:
     """tau by plain bisection on the bracket (any alpha in (1, 2])."""
     s = np.ascontiguousarray(np.asarray(s, dtype=np.float64))
     return float(_load().orc_entmax_tau_bisect(_ptr(s), s.size, float(alpha)))
+
+
+def tau_histogram(s, alpha: float = 1.5, bins: int = 64) -> float:
+    """Histogram threshold tau_h of one fp32 row (AdaSplash-2 sec. 3.1)."""
+    s = _f32(s)
+    return float(_load().orc_entmax_tau_histogram(_ptr(s), s.size, float(alpha), int(bins)))
 
 
 def tau_rows(S, want_p: bool = True, alpha: float = 1.5) -> tuple[np.ndarray, Optional[np.ndarray]]:

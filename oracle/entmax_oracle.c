@@ -218,6 +218,75 @@ double orc_entmax_tau_alpha(const double* s, int64_t n, double alpha, double* wo
     return t;
 }
 
+/*
+ * Histogram threshold of AdaSplash-2 sec. 3.1 / appendix C.3 for one row, in
+ * score units.  z_j = (alpha-1)(s_j - m) + 1 is formed in fp32 exactly as
+ * the GPU forms it (fma of the fp32 difference), binned into B left-edge
+ * bins k = min(floor(B z), B - 1) for z >= 0; the histogram objective
+ * sum_k H_k [k/B - tau]_+^e = 1 is then solved in fp64: by the sorting scan
+ * over the bins (from the top) for alpha = 1.5 (a quadratic per prefix) and
+ * alpha = 2 (linear), by bisection otherwise.  Proposition 3.1 of the pages:
+ * tau* - h < tau_h <= tau* with h = 1/(B (alpha-1)) in score units.
+ */
+double orc_entmax_tau_histogram(const float* s, int64_t n, float alpha, int B) {
+    float m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) m = s[j] > m ? s[j] : m;
+    if (m == -INFINITY) return -INFINITY;
+    const float am1 = alpha - 1.0f;
+    double* H = (double*)calloc((size_t)B, sizeof(double));
+    for (int64_t j = 0; j < n; ++j) {
+        if (s[j] == -INFINITY) continue;
+        const float diff = s[j] - m;
+        const float z = fmaf(am1, diff, 1.0f);
+        if (!(z >= 0.0f)) continue;
+        int k = (int)floorf(z * (float)B);
+        if (k > B - 1) k = B - 1;
+        if (k < 0) k = 0;
+        H[k] += 1.0;
+    }
+    const double a1 = (double)am1, e = 1.0 / a1;
+    double tz;
+    if (alpha == 1.5f || alpha == 2.0f) {
+        /* prefix scan over the bins from the top; the support of the binned
+         * problem is the largest prefix whose root lies below its lowest edge */
+        double S0 = 0.0, S1 = 0.0, S2 = 0.0;
+        tz = (double)(B - 1) / B - 1.0;
+        for (int k = B - 1; k >= 0; --k) {
+            if (H[k] == 0.0) continue;
+            const double x = (double)k / B;
+            S0 += H[k];
+            S1 += H[k] * x;
+            S2 += H[k] * x * x;
+            double t;
+            if (alpha == 2.0f) {
+                t = (S1 - 1.0) / S0;
+            } else {
+                /* sum H_k (x_k - t)^2 = 1:  S0 t^2 - 2 S1 t + S2 - 1 = 0 */
+                const double disc = S1 * S1 - S0 * (S2 - 1.0);
+                if (disc < 0.0) continue;
+                t = (S1 - sqrt(disc)) / S0;
+            }
+            if (t < x) tz = t;
+        }
+    } else {
+        double lo = (double)(B - 1) / B - 1.0, hi = (double)(B - 1) / B;
+        for (int it = 0; it < 200; ++it) {
+            const double mid = 0.5 * (lo + hi);
+            if (mid <= lo || mid >= hi) break;
+            double f = -1.0;
+            for (int k = 0; k < B; ++k) {
+                const double u = (double)k / B - mid;
+                if (u > 0.0 && H[k] > 0.0) f += H[k] * pow(u, e);
+            }
+            if (f >= 0.0) lo = mid;
+            else hi = mid;
+        }
+        tz = 0.5 * (lo + hi);
+    }
+    free(H);
+    return (double)m + (tz - 1.0) * e;
+}
+
 /* Weight p and derivative g = dp/ds of one score at threshold tau. */
 static double weight_alpha(double x, double tau, double alpha) {
     if (alpha == 1.5) {

@@ -210,3 +210,29 @@ def test_alpha_out_of_range_rejected(env):
         with pytest.raises(api.EntmaxError) as ei:
             api.tau_rows(S, alpha=bad)
         assert ei.value.status == api.ERR_ALPHA
+
+
+@pytest.mark.parametrize("alpha", [1.5, 1.25, 2.0])
+@pytest.mark.parametrize("hist", [1, 0], ids=["hist", "nohist"])
+def test_wide_rows_histogram_bracket(env, orc, alpha, hist):
+    """Rows wider than 8192 (the streaming kernel), with and without the
+    histogram-initialised bracket: sparse rows, dense rows that overflow the
+    LDS list, near-constant and one-hot rows; same results either way."""
+    api, torch = env
+    a = float(np.float32(alpha))
+    prev = api.set_option(api.OPT_ROW_HISTOGRAM, hist)
+    try:
+        rng = np.random.default_rng(70 + hist)
+        cols = 20000
+        S = rng.normal(size=(8, cols)).astype(np.float32)
+        S[1] *= 0.02                       # dense: every score near the max
+        S[2] = 3.0; S[2, ::7] = 2.9        # near-constant
+        S[3] = -5.0; S[3, 1234] = 5.0      # one-hot
+        S[4] *= 4.0
+        S[5, :10000] = -np.inf             # half masked
+        S[6] = np.linspace(-0.5, 0.5, cols)
+        S[7] *= 0.3
+        tau, P = _run(api, torch, S, alpha=a)
+        _check(S, tau, P, orc, f"wide alpha={alpha} hist={hist}", alpha=a)
+    finally:
+        api.set_option(api.OPT_ROW_HISTOGRAM, prev)

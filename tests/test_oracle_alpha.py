@@ -247,3 +247,44 @@ def test_backward_invariants(orc, alpha):
                                           0.6, 0, 0, rows, alpha=alpha)
     np.testing.assert_array_equal(dQr, dQ[rows])
     np.testing.assert_array_equal(taur, tau[rows])
+
+
+# ------------------------------------------------ histogram initialisation
+# AdaSplash-2 sec. 3.1 / appendix C.3: left-edge bins give a threshold tau_h
+# with tau* - h < tau_h <= tau* (Proposition 3.1), h = 1/(B (alpha - 1)) in
+# score units.
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+@pytest.mark.parametrize("bins", [8, 64])
+def test_histogram_threshold_brackets_tau(orc, alpha, bins):
+    rng = np.random.default_rng(50 + bins)
+    a = float(np.float32(alpha))
+    h = 1.0 / (bins * (a - 1.0))
+    worst = 0.0
+    for _ in range(150):
+        n = int(rng.integers(1, 3000))
+        s = (rng.normal(size=n) * rng.uniform(0.05, 3.0)).astype(np.float32)
+        if rng.random() < 0.2:
+            s[rng.random(n) < 0.5] = -np.inf
+            s[0] = 0.5
+        _, tau, _ = orc.entmax(s.astype(np.float64), a)
+        th = orc.tau_histogram(s, a, bins)
+        assert th <= tau + 1e-9 * max(1.0, abs(tau)), (n, th, tau)
+        assert tau - th <= h + 1e-9, (n, th, tau, h)
+        worst = max(worst, tau - th)
+    print(f"alpha={alpha} B={bins}: worst tau - tau_h = {worst:.4f} (bin width {h:.4f})")
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_histogram_threshold_of_constant_rows(orc, alpha):
+    """A constant row has z = 1 everywhere, and the top bin's left edge is
+    (B-1)/B: every entry moves down by exactly one bin width, so tau_h =
+    tau* - 1/(B (alpha-1)) = c - n^(1-alpha)/(alpha-1) - 1/(B (alpha-1)).
+    (The bound of Proposition 3.1 is attained here, so the bracket the
+    kernels use is closed: [tau_h, tau_h + h].)"""
+    a = float(np.float32(alpha))
+    for B in (8, 64):
+        for n, c in ((1, 0.0), (5, 2.5), (300, -1.0)):
+            th = orc.tau_histogram(np.full(n, c, dtype=np.float32), a, B)
+            expect = c - n ** (1.0 - a) / (a - 1.0) - 1.0 / (B * (a - 1.0))
+            assert abs(th - expect) <= 1e-9 * max(1.0, abs(expect)), (B, n, c, th, expect)
