@@ -244,6 +244,62 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
     __syncthreads();
 }
 
+// The same sweep for a workgroup whose tiles are all full: no mask, every
+// key tile inside L (L a multiple of 64), all 128 query rows below L, and an
+// even number of key tiles.  Pair pp is then tiles 2 pp and 2 pp + 1, so no
+// list is read and no tile class is evaluated, and each wave stages the same
+// half of one tile of every pair from a scalar tile base plus per-lane byte
+// offsets computed once: per pair, what is left besides the products and
+// the statistics is the DMA issue, one wait and the barrier.
+template <typename T, int D, int S, class Fn>
+__device__ __forceinline__ void dense_sweep(int Tc, const T* Kh, T* ring,
+                                            const typename Ops<T, D>::template QOp<2>& qop, Fn fn) {
+    using O = Ops<T, D>;
+    using DMA = TileDMA<T, D>;
+    static_assert(S >= 2, "the dense sweep keeps at least one pair in flight");
+    constexpr int kIpw = DMA::template Lanes<2>::kIpw;  // DMA instructions per thread per pair
+    constexpr int kPerWave = DMA::kTileCh / 2;           // 16-byte slots per wave per pair
+    constexpr int kStage = 2 * DMA::kTileElems;
+    constexpr int kSlotElems = 16 / (int)sizeof(T);
+    constexpr size_t kTileBytes = (size_t)64 * D * sizeof(T);
+    const int w = wave_id(), kh = w >> 1, lane = lane_id();
+    const int npairs = Tc / 2;
+    uint32_t off[kIpw];
+#pragma unroll
+    for (int k = 0; k < kIpw; ++k) {
+        const int qt = (w * kPerWave + k * kWave + lane) % DMA::kTileCh;
+        const int row = qt / DMA::kCPR;
+        off[k] = (uint32_t)((row * D + swz<DMA::kCPR>(row, qt % DMA::kCPR) * kSlotElems) * sizeof(T));
+    }
+    // wave w stages half (w & 1) of tile (w >> 1) of each pair
+    const char* kw = reinterpret_cast<const char*>(Kh) + (size_t)(w >> 1) * kTileBytes;
+    auto issue = [&](int pq, int stage) {
+        const char* tb = kw + (size_t)pq * 2 * kTileBytes;
+        T* base = ring + stage * kStage + w * kPerWave * kSlotElems;
+#pragma unroll
+        for (int k = 0; k < kIpw; ++k)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tb + off[k]),
+                                             (__attribute__((address_space(3))) void*)(base + k * kWave * kSlotElems),
+                                             16, 0, 0);
+    };
+#pragma unroll
+    for (int pp = 0; pp < S - 1; ++pp)
+        if (pp < npairs) issue(pp, pp);
+    int su = 0, si = S - 1;  // stage read this pair, stage the next issue fills
+    for (int pp = 0; pp < npairs; ++pp) {
+        if (npairs - 1 - pp >= S - 2) wait_vmcnt<(S - 2) * kIpw>();
+        else wait_vmcnt<0>();
+        barrier_keep_vm();
+        if (pp + S - 1 < npairs) issue(pp + S - 1, si);
+        f32x16 acc[2][2];
+        O::scores(acc, ring + su * kStage + kh * DMA::kTileElems, qop);
+        fn(2 * pp + kh, 2 * pp + kh, acc);
+        su = su + 1 == S ? 0 : su + 1;
+        si = si + 1 == S ? 0 : si + 1;
+    }
+    __syncthreads();
+}
+
 // Maximum over the 64 lanes of a wave, by DPP row shifts and broadcasts
 // (VALU only), returned to every lane.  Each step is one v_max_f32 with a
 // DPP source; a lane without a source is not written and keeps its value,
@@ -579,7 +635,9 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
     typename O::template QOp<2> qop;
     O::load_q(qop, Qh, R0, p.L);
     for (int i = t; i < 2 * TCMAX; i += kNT) (&umax[0][0])[i] = neg_inf();
-    if (w == 0) {
+    // every tile of this workgroup full: the list-free sweep
+    const bool dense = p.mode == 0 && p.L % kBC == 0 && r0 + kBR <= p.L && p.Tc % 2 == 0;
+    if (w == 0 && !dense) {
         const int n = build_list(list, p.Tc, [&](int J) {
             return (tile_class(J, r0, g) != kSkip ? 1 : 0) | (tile_class(J, r0 + 64, g) != kSkip ? 2 : 0);
         });
@@ -593,7 +651,7 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
 #pragma unroll
         for (int i = 0; i < kTop4; ++i) top[qb][i] = neg_inf();
 
-    ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
+    auto tile_stats = [&](int J, int, f32x16(&acc)[2][2]) {
         float wm = neg_inf();
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -613,7 +671,9 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
         }
         wm = wave_max_dpp(wm);
         if (l == 0) umax[qh][J] = wm;
-    });
+    };
+    if (dense) dense_sweep<T, D, S>(p.Tc, Kh, ring, qop, tile_stats);
+    else ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, tile_stats);
 
     // merge the four lists of each row (two lane halves x two key parities)
 #pragma unroll

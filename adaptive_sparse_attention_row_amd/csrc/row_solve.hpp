@@ -233,6 +233,46 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
+// Exclusive prefix sum of a count over the 64 lanes of a wave (DPP row
+// shifts build the inclusive scan inside each row of 16 lanes, two row
+// broadcasts carry it across rows); *total receives the wave's sum.
+__device__ __forceinline__ int wave_excl_scan(int x, int* total) {
+    int y = x;
+#define ENTMAX_SCAN_STEP(ctrl, rmask) y += __builtin_amdgcn_update_dpp(0, y, ctrl, rmask, 0xf, false)
+    ENTMAX_SCAN_STEP(0x111, 0xf);
+    ENTMAX_SCAN_STEP(0x112, 0xf);
+    ENTMAX_SCAN_STEP(0x114, 0xf);
+    ENTMAX_SCAN_STEP(0x118, 0xf);
+    ENTMAX_SCAN_STEP(0x142, 0xa);
+    ENTMAX_SCAN_STEP(0x143, 0xc);
+#undef ENTMAX_SCAN_STEP
+    *total = __builtin_amdgcn_readlane(y, 63);
+    return y - x;
+}
+
+// A lower bound on the 1.5-entmax threshold of a row from one of its values
+// per lane (a subset, e.g. each lane's maximum; -inf for none): Newton steps
+// from t = m - 2 on the subset's f(t) = sum [(x - t)/2]_+^2 - 1.  f is convex
+// and decreasing and f(m - 2) >= 0 (the maximum alone contributes 1), so
+// every step stays at or below the subset's threshold, which is at most the
+// row's (adding scores only raises a threshold).  The steps stop once f is
+// below 1e-2 (the bound is then within about 1e-2 of the subset's
+// threshold); the result is lowered by a relative 1e-5, more than the
+// rounding of the fp32 sums can move a step (|dF| / F1 <= 64 ulp, since
+// F / F1 <= max g <= 1 and F1 >= 1 below the root).
+__device__ __forceinline__ float wave_newton_lower(float x, float m) {
+    float t = m - 2.0f;
+#pragma unroll 1
+    for (int it = 0; it < 8; ++it) {
+        const float g = fmaxf(0.5f * (x - t), 0.0f);
+        const float f = wave_sum_dpp(g * g) - 1.0f;
+        const float F1 = wave_sum_dpp(g);
+        if (f <= 1e-2f) break;
+        t += f / F1;
+    }
+    return t - 1e-5f * fmaxf(1.0f, fabsf(t));
+}
+
 // Threshold of a set held by one wave: `each(t, sums)` adds this lane's part
 // of the sums over {x > t}.  Halley-bisection in the bracket [lo, m - 2/sqrt(n)]
 // (lo a lower bound on tau, no smaller than m - 2; n >= the support size)

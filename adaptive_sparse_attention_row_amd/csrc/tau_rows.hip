@@ -1,13 +1,15 @@
 // tau_rows.hip -- row-wise 1.5-entmax threshold and probabilities on a
 // materialised fp32 score matrix (the HBM-bound row kernel).
 //
-// Rows up to 8192 wide: one single-wave workgroup per row, the row read from
-// HBM once into registers (128 values per lane at 8192 columns, which leaves
-// room for three waves per SIMD, i.e. 12 rows in flight per CU).  Every
-// reduction is a DPP wave reduction; there are no barriers.  Per row:
+// Rows up to 8192 wide: single-wave workgroups, as many as stay resident,
+// each looping over its rows.  A row is read from HBM once into registers
+// (128 values per lane at 8192 columns, which leaves room for three waves
+// per SIMD, i.e. 12 rows in flight per CU).  Every reduction is a DPP wave
+// reduction; there are no barriers.  Per row:
 //   1. the maximum m;
-//   2. a lower bound on tau: the exact threshold of the 64 lane maxima, a
-//      subset of the row (a threshold only rises as scores are added);
+//   2. a lower bound on tau from the 64 lane maxima, a subset of the row (a
+//      threshold only rises as scores are added): Newton steps from m - 2,
+//      which stay below the subset's threshold;
 //   3. the scores above that bound, compacted into LDS (usually little more
 //      than the support);
 //   4. tau from those candidates by the hybrid Halley-bisection of "AdaSplash:
@@ -18,7 +20,8 @@
 //      to it is a quadratic in tau solved in closed form (the S0/S1/S2 form of
 //      AdaSplash-2 appendix C.3);
 //   5. P from the register copy, so HBM sees one read and one write per
-//      element.
+//      element; the loads of the wave's next row are issued into the
+//      registers as they free up.
 // Wider rows take a 256-thread streaming kernel that reads the row three
 // times (maximum, candidates above m - 2, output).  While it compacts the
 // candidates it also bins them (the histogram initialisation of AdaSplash-2
@@ -35,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "row_solve.hpp"
@@ -44,144 +49,176 @@ namespace {
 
 using namespace rows;
 
-constexpr int kRowsPerBlock = 1;  // one single-wave workgroup per row
-constexpr int kWaveCand = 2048;                  // LDS candidates per wave
+constexpr int kWaveCand = 2048;  // LDS candidates per wave
+constexpr int kMaxDevices = 64;
 
-// One single-wave workgroup per row (its slot frees as soon as that row is
-// done), the row register-resident: VPT values per lane (lane l holds columns
-// (64 k + l) * 4 + e for VEC, 64 k + l otherwise).  No barriers.  VEC: float4 accesses
+// Loads of one row into registers: chunk k of VEC rows is the float4 at
+// column (64 k + lane) * 4, otherwise element 64 k + lane; entries at or past
+// cols read -inf.  FULL: cols == 64 VPT, every chunk lies inside the row (no
+// guards).
+template <int VPT, bool VEC, bool FULL>
+struct RowRegs {
+    float v[VPT];
+
+    __device__ __forceinline__ void load_chunk(const float* src, int k, int cols, int lane) {
+        if constexpr (VEC) {
+            const int pos = (k * kWave + lane) * 4;
+            if constexpr (FULL) {
+                const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + pos));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * k + e] = q[e];
+            } else {
+                // chunks past the end re-read the last chunk that starts
+                // inside the row (ld % 4 == 0, so it lies within the row's
+                // ld span)
+                const int last = ((cols - 1) / 4) * 4;
+                const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + min(pos, last)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * k + e] = (pos + e < cols) ? q[e] : neg_inf();
+            }
+        } else {
+            const int pos = k * kWave + lane;
+            v[k] = (FULL || pos < cols) ? src[pos] : neg_inf();
+        }
+    }
+    static constexpr int kChunks = VEC ? VPT / 4 : VPT;
+};
+
+// Rows up to 64 VPT wide, one wave per workgroup, each wave taking rows
+// blockIdx.x, blockIdx.x + gridDim.x, ... (the grid is what stays resident,
+// so no workgroup waits for a slot).  The row is held in registers (VPT
+// values per lane) and read from HBM once; while the wave computes and
+// stores the probabilities of one row, it issues the loads of its next row
+// into the registers it has just used, so its slot keeps memory requests in
+// flight through the store phase.  No barriers.  VEC: float4 accesses
 // (ld % 4 == 0 and 16-byte aligned S / P).
-template <int VPT, bool VEC, bool GEN>
+template <int VPT, bool VEC, bool FULL, bool GEN>
 __global__ __launch_bounds__(kWave, 3) void tau_rows_wave(const float* __restrict__ S,
                                                          float* __restrict__ P,
                                                          float* __restrict__ tau_out,
                                                          int64_t rows, int cols, int64_t ld,
                                                          AlphaMap am) {
-    __shared__ float cand_all[kRowsPerBlock][kWaveCand];
-    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + w;
+    using Regs = RowRegs<VPT, VEC, FULL>;
+    __shared__ float cand[kWaveCand + kWave];
+    const int lane = threadIdx.x;
+    int64_t row = blockIdx.x;
     if (row >= rows) return;
-    float* cand = cand_all[w];
-    const float* src = S + row * ld;
-    float v[VPT];
+    Regs r;
+    float* v = r.v;
+#pragma unroll
+    for (int k = 0; k < Regs::kChunks; ++k) r.load_chunk(S + row * ld, k, cols, lane);
 
-    // every chunk lies inside the row (wave-uniform): no guards
-    const bool full = cols == VPT * kWave;
-    if constexpr (VEC) {
-        if (full) {
+    for (;;) {
+        const float* src = S + row * ld;
+        float mx = neg_inf();
 #pragma unroll
-            for (int k = 0; k < VPT / 4; ++k) {
-                const f32x4 q =
-                    __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (k * kWave + lane) * 4));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * k + e] = q[e];
-            }
+        for (int k = 0; k < VPT; ++k) mx = fmaxf(mx, v[k]);
+        const float m = wave_max_dpp(mx);
+
+        float tau;
+        if (m == neg_inf()) {
+            tau = neg_inf();  // no active entry: P = 0
         } else {
-            // chunks past the end re-read the last chunk that starts inside the
-            // row (ld % 4 == 0, so it lies within the row's ld span); entries at
-            // or past cols read -inf
-            const int last = ((cols - 1) / 4) * 4;
-#pragma unroll
-            for (int k = 0; k < VPT / 4; ++k) {
-                const int pos = (k * kWave + lane) * 4;
-                const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + min(pos, last)));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * k + e] = (pos + e < cols) ? q[e] : neg_inf();
-            }
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int pos = k * kWave + lane;
-            v[k] = (pos < cols) ? src[pos] : neg_inf();
-        }
-    }
-
-    float mx = neg_inf();
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) mx = fmaxf(mx, v[k]);
-    const float m = wave_max_dpp(mx);
-
-    float tau;
-    if (m == neg_inf()) {
-        tau = neg_inf();  // no active entry: P = 0
-    } else {
-        // Lower bound: the exact threshold of the 64 lane maxima, a subset of
-        // the row (a threshold only rises as scores are added).  The row's
-        // largest scores mostly sit in different lanes, so it is close to tau
-        // and few scores lie above it.
-        const float n1 = wave_sum_dpp(mx > neg_inf() ? 1.0f : 0.0f);
-        float tlo;
-        if constexpr (GEN)
-            wave_tau_gen(m, n1, m - am.e, am, [&](float tt, RowSums& s) { accumulate_gen(s, mx, tt, am); }, &tlo);
-        else
-            tlo = wave_tau(m, n1, m - 2.0f, [&](float tt, RowSums& s) { accumulate(s, mx, tt, m); });
-        // the scores above it, compacted in register order (elements where no
-        // lane has one are skipped)
-        int n = 0;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const bool c = v[k] > tlo;
-            const uint64_t b = __ballot(c);
-            if (b != 0) {
-                const int slot = n + lanes_below(b);
-                if (c && slot < kWaveCand) cand[slot] = v[k];
-                n += __popcll(b);
-            }
-        }
-        if constexpr (GEN) {
-            if (n <= kWaveCand) {
-                tau = wave_tau_gen(m, (float)n, tlo, am, [&](float tt, RowSums& s) {
-                    for (int i = lane; i < n; i += kWave) accumulate_gen(s, cand[i], tt, am);
-                }, nullptr);
+            // Lower bound from the 64 lane maxima, a subset of the row (a
+            // threshold only rises as scores are added).  The row's largest
+            // scores mostly sit in different lanes, so the bound is close to
+            // tau and few scores lie above it.
+            float tlo;
+            if constexpr (GEN) {
+                const float n1 = wave_sum_dpp(mx > neg_inf() ? 1.0f : 0.0f);
+                wave_tau_gen(m, n1, m - am.e, am, [&](float tt, RowSums& s) { accumulate_gen(s, mx, tt, am); },
+                             &tlo);
             } else {
-                tau = wave_tau_gen(m, (float)n, tlo, am, [&](float tt, RowSums& s) {
-                    for (int pos = lane; pos < cols; pos += kWave) accumulate_gen(s, src[pos], tt, am);
-                }, nullptr);
+                tlo = wave_newton_lower(mx, m);
             }
-        } else if (n <= kWaveCand) {
-            tau = wave_tau(m, (float)n, tlo, [&](float tt, RowSums& s) {
-                for (int i = lane; i < n; i += kWave) accumulate(s, cand[i], tt, m);
-            });
-        } else {
-            // more candidates than the LDS buffer (near-constant rows): sweep
-            // the row in memory each iteration (the register copy would be
-            // pinned twice over by the loop)
-            tau = wave_tau(m, (float)n, tlo, [&](float tt, RowSums& s) {
-                for (int pos = lane; pos < cols; pos += kWave) accumulate(s, src[pos], tt, m);
-            });
-        }
-    }
-
-    if (lane == 0) tau_out[row] = tau;
-    if (P == nullptr) return;
-    float* dst = P + row * ld;
-    const float h = -0.5f * tau;
-    auto pr = [&](float x) -> float {
-        if constexpr (GEN) return am.p(x, tau);
-        else return prob_h(x, h);
-    };
-    if constexpr (VEC) {
+            // The scores above it, compacted into LDS in register order.  The
+            // comparisons of 8 registers are taken first, as wave masks, so
+            // the scalar tests that skip registers with no candidate in any
+            // lane do not wait on each comparison in turn; slots past the
+            // list go to the lane's spare word.
+            int n = 0;
 #pragma unroll
-        for (int k = 0; k < VPT / 4; ++k) {
-            const int pos = (k * kWave + lane) * 4;
-            f32x4 q;
+            for (int k0 = 0; k0 < VPT; k0 += 8) {
+                uint64_t b[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) q[e] = pr(v[4 * k + e]);
-            if (full || pos + 3 < cols) {
-                __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(dst + pos));
+                for (int j = 0; j < 8; ++j) b[j] = __ballot(v[k0 + j] > tlo);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (b[j] != 0) {
+                        const int slot = min(n + lanes_below(b[j]), kWaveCand + lane);
+                        if (v[k0 + j] > tlo) cand[slot] = v[k0 + j];
+                        n += __popcll(b[j]);
+                    }
+                }
+            }
+            if constexpr (GEN) {
+                if (n <= kWaveCand) {
+                    tau = wave_tau_gen(m, (float)n, tlo, am, [&](float tt, RowSums& s) {
+                        for (int i = lane; i < n; i += kWave) accumulate_gen(s, cand[i], tt, am);
+                    }, nullptr);
+                } else {
+                    tau = wave_tau_gen(m, (float)n, tlo, am, [&](float tt, RowSums& s) {
+                        for (int pos = lane; pos < cols; pos += kWave) accumulate_gen(s, src[pos], tt, am);
+                    }, nullptr);
+                }
+            } else if (n <= kWaveCand) {
+                tau = wave_tau(m, (float)n, tlo, [&](float tt, RowSums& s) {
+                    for (int i = lane; i < n; i += kWave) accumulate(s, cand[i], tt, m);
+                });
             } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (pos + e < cols) dst[pos + e] = q[e];
+                // more candidates than the LDS list (near-constant rows):
+                // sweep the row in memory each iteration (the register copy
+                // would be pinned twice over by the loop)
+                tau = wave_tau(m, (float)n, tlo, [&](float tt, RowSums& s) {
+                    for (int pos = lane; pos < cols; pos += kWave) accumulate(s, src[pos], tt, m);
+                });
             }
         }
-    } else {
+
+        if (lane == 0) tau_out[row] = tau;
+        // an opaque copy of the lane index for the addresses and bounds
+        // below: keeps the compiler from hoisting them out of the row loop,
+        // which would pin a register or a mask for each chunk
+        int li = lane;
+        asm volatile("" : "+v"(li));
+        const int64_t next = row + gridDim.x;
+        const bool more = next < rows;
+        const float* nsrc = S + (more ? next : row) * ld;
+        if (P == nullptr) {
+            if (!more) break;
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int pos = k * kWave + lane;
-            if (pos < cols) dst[pos] = pr(v[k]);
+            for (int k = 0; k < Regs::kChunks; ++k) r.load_chunk(nsrc, k, cols, li);
+            row = next;
+            continue;
         }
+        float* dst = P + row * ld;
+        const float h = -0.5f * tau;
+        auto pr = [&](float x) -> float {
+            if constexpr (GEN) return am.p(x, tau);
+            else return prob_h(x, h);
+        };
+#pragma unroll
+        for (int k = 0; k < Regs::kChunks; ++k) {
+            if constexpr (VEC) {
+                const int pos = (k * kWave + li) * 4;
+                f32x4 q;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q[e] = pr(v[4 * k + e]);
+                if (FULL || pos + 3 < cols) {
+                    __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(dst + pos));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (pos + e < cols) dst[pos + e] = q[e];
+                }
+            } else {
+                const int pos = k * kWave + li;
+                if (FULL || pos < cols) dst[pos] = pr(v[k]);
+            }
+            if (more) r.load_chunk(nsrc, k, cols, li);
+        }
+        if (!more) break;
+        row = next;
     }
 }
 
@@ -285,13 +322,36 @@ __global__ __launch_bounds__(kThreads) void tau_rows_stream(const float* __restr
     for (int64_t pos = t; pos < cols; pos += kThreads) dst[pos] = GEN ? am.p(src[pos], tau) : prob(src[pos], tau);
 }
 
+template <int VPT, bool VEC, bool FULL, bool GEN>
+hipError_t launch_wave_inst(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
+                       int64_t ld, const AlphaMap& am, hipStream_t stream) {
+    // as many waves as stay resident at once (each loops over its rows)
+    static int per_cu[kMaxDevices] = {};
+    static int cus[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (per_cu[dev] == 0) {
+        int nb = 0, nc = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, tau_rows_wave<VPT, VEC, FULL, GEN>, kWave, 0);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        cus[dev] = nc;
+        per_cu[dev] = nb > 0 ? nb : 1;
+    }
+    const int64_t blocks = std::min<int64_t>(rows, (int64_t)per_cu[dev] * cus[dev]);
+    hipLaunchKernelGGL((tau_rows_wave<VPT, VEC, FULL, GEN>), dim3((unsigned)blocks), dim3(kWave), 0, stream, S,
+                       P, tau, rows, (int)cols, ld, am);
+    return hipGetLastError();
+}
+
 template <int VPT, bool VEC, bool GEN>
 hipError_t launch_wave(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
                        int64_t ld, const AlphaMap& am, hipStream_t stream) {
-    const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL((tau_rows_wave<VPT, VEC, GEN>), dim3((unsigned)blocks), dim3(kWave), 0, stream, S,
-                       P, tau, rows, (int)cols, ld, am);
-    return hipGetLastError();
+    if (cols == VPT * kWave) return launch_wave_inst<VPT, VEC, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
+    return launch_wave_inst<VPT, VEC, false, GEN>(S, P, tau, rows, cols, ld, am, stream);
 }
 
 template <bool GEN>

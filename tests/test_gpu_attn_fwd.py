@@ -81,6 +81,12 @@ SHAPES = [
     (2, 2, 257, 64, "bf16"),
     (1, 2, 1000, 128, "bf16"),
     (1, 1, 640, 64, "f32"),
+    # L a multiple of 128: with no mask every workgroup takes the list-free
+    # dense sweep of the score statistics
+    (1, 2, 256, 64, "bf16"),
+    (2, 1, 512, 64, "bf16"),
+    (1, 1, 384, 128, "bf16"),
+    (1, 1, 256, 128, "f32"),
 ]
 
 
