@@ -56,6 +56,7 @@ STATS_SOURCES = ["adaptive_sparse_attention_row_amd/csrc/attn_fwd.hip",
                  "adaptive_sparse_attention_row_amd/csrc/tile_dma.hpp",
                  "adaptive_sparse_attention_row_amd/csrc/device_common.hpp"]
 TAUROWS_SOURCES = ["adaptive_sparse_attention_row_amd/csrc/tau_rows.hip",
+                   "adaptive_sparse_attention_row_amd/csrc/row_solve.hpp",
                    "adaptive_sparse_attention_row_amd/csrc/device_common.hpp"]
 
 
