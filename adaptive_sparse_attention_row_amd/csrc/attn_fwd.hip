@@ -186,7 +186,7 @@ __device__ __forceinline__ void sweep(const uint16_t* list, int n, const T* Kh, 
 // read after a direct load wait for all loads in flight; reading a stage
 // before issuing the next loads, or hiding the reads from it, measured no
 // faster here, so the plain order stays.)
-template <typename T, int D, int S, class Fn>
+template <typename T, int D, int S, bool PER_QB = false, class Fn>
 __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T* Kh, T* ring,
                                            const typename Ops<T, D>::template QOp<2>& qop, int R0,
                                            const Geom& g, Fn fn) {
@@ -235,10 +235,27 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
         int e = 0, J = 0;
         const int cls = tile_of(pp, e, J);
         if (cls != kSkip) {
-            f32x16 acc[2][2];
-            O::scores(acc, ring + (pp % S) * kStage + kh * DMA::kTileElems, qop);
-            if (cls == kPartial) apply_mask(acc, J, R0, g);
-            fn(J, e, acc);
+            const T* Kt = ring + (pp % S) * kStage + kh * DMA::kTileElems;
+            if constexpr (PER_QB) {
+                // one 32-row block at a time: half the accumulators live, the
+                // tile's operands read twice
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    typename O::template QOp<1> q1;
+                    constexpr int kQs = sizeof(q1.q[0]) / sizeof(q1.q[0][0]);
+#pragma unroll
+                    for (int s = 0; s < kQs; ++s) q1.q[0][s] = qop.q[qb][s];
+                    f32x16 acc[2][1];
+                    O::template scores<1>(acc, Kt, q1);
+                    if (cls == kPartial) apply_mask<1>(acc, J, R0 + 32 * qb, g);
+                    fn(J, e, qb, acc);
+                }
+            } else {
+                f32x16 acc[2][2];
+                O::scores(acc, Kt, qop);
+                if (cls == kPartial) apply_mask(acc, J, R0, g);
+                fn(J, e, acc);
+            }
         }
     }
     __syncthreads();
@@ -475,10 +492,10 @@ __device__ __forceinline__ double solve_candidates(const Src& src, double mx, do
                 mn = fminf(mn, on ? x : __builtin_inff());
             });
         }
-        c += __shfl_xor(c, 32, kWave);
-        S1 += __shfl_xor(S1, 32, kWave);
-        S2 += __shfl_xor(S2, 32, kWave);
-        mn = fminf(mn, __shfl_xor(mn, 32, kWave));
+        c = pair_sum(c);
+        S1 = pair_sum(S1);
+        S2 = pair_sum(S2);
+        mn = pair_min(mn);
         if (done) continue;
         const double C = (double)c, u = t - mx;
         // f(t) = sum ((y - u)/2)^2 - 1 and -f'(t) = sum (y - u)/2 over the set
@@ -603,6 +620,15 @@ struct CollectCfg {
                                 : (sizeof(T) == 2 && D == 128) ? ENTMAX_COLLECT_OCCUPANCY_BF16_128
                                                                : 1;
 };
+
+#ifndef ENTMAX_COLLECT_PER_QB
+#define ENTMAX_COLLECT_PER_QB 0
+#endif
+// The candidate sweeps take one 32-row block at a time (fewer live
+// accumulators, each tile's operands read twice) where that lets the kernel
+// keep more workgroups per CU.
+template <typename T, int D>
+constexpr bool kCollectPerQb = sizeof(T) == 2 && D == 64 && ENTMAX_COLLECT_PER_QB;
 
 constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
 
@@ -802,66 +828,72 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
             const int row = qh * 64 + qb * 32 + m;
             lo_q[qb] = rstate[row] == 1 ? row_lo[row] : __builtin_inff();
         }
-        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int e, f32x16(&acc)[2][2]) {
+        // the candidates of one 32-row block (column c of acc) of list entry e
+        auto collect_qb = [&](int e, int qb, auto& acc, int c) {
+            float bm = neg_inf();
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                float bm = neg_inf();
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[kb][c][r]);
+            if (__ballot(bm * p.scale > lo_q[qb]) == 0) return;
+            const float lo = lo_q[qb];
+            int nb = 0;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[kb][qb][r]);
-                if (__ballot(bm * p.scale > lo_q[qb]) == 0) continue;
-                const float lo = lo_q[qb];
-                int nb = 0;
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    acc[kb][c][r] *= p.scale;
+                    nb += acc[kb][c][r] > lo ? 1 : 0;
+                }
+            const int row = qh * 64 + qb * 32 + m;
+            int base = 0;
+            if (nb) base = atomicAdd(&cnt[row], nb);
+            if (__ballot(base + nb > lds_lim) == 0) {
+                // all in LDS: the lane's candidates take consecutive slots from
+                // base in register order; other elements write the spare word
+                int slot = base;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        acc[kb][qb][r] *= p.scale;
-                        nb += acc[kb][qb][r] > lo ? 1 : 0;
+                        const bool on = acc[kb][c][r] > lo;
+                        const int a = on ? slot * kBR + row : spare;
+                        lval[a] = acc[kb][c][r];
+                        lpos[a] = (uint16_t)e;
+                        slot += on ? 1 : 0;
                     }
-                const int row = qh * 64 + qb * 32 + m;
-                int base = 0;
-                if (nb) base = atomicAdd(&cnt[row], nb);
-                if (__ballot(base + nb > lds_lim) == 0) {
-                    // all in LDS: the lane's candidates take consecutive slots from
-                    // base in register order; other elements write the spare word
-                    int slot = base;
+            } else {
+                // the list spills past LDS: candidates in register order from
+                // base, LDS slots first, then the workspace, the rest dropped
+                // (the row is then collected again with a tighter bound)
+                int slot = base;
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const bool on = acc[kb][qb][r] > lo;
-                            const int a = on ? slot * kBR + row : spare;
-                            lval[a] = acc[kb][qb][r];
-                            lpos[a] = (uint16_t)e;
-                            slot += on ? 1 : 0;
-                        }
-                } else {
-                    uint32_t bits = 0;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            bits |= (acc[kb][qb][r] > lo) ? (1u << (kb * 16 + r)) : 0u;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if ((bits >> (kb * 16 + r)) & 1u) {
-                                const int slot = base + __popc(bits & ((1u << (kb * 16 + r)) - 1u));
-                                const float sv = acc[kb][qb][r];
-                                if (slot < kLdsCand && slot < cap) {
-                                    lval[slot * kBR + row] = sv;
-                                    lpos[slot * kBR + row] = (uint16_t)e;
-                                } else if (slot < cap) {
-                                    cval[(size_t)slot * kBR + row] = sv;
-                                    cjt[(size_t)slot * kBR + row] = (uint16_t)e;
-                                }
+                    for (int r = 0; r < 16; ++r) {
+                        const float sv = acc[kb][c][r];
+                        if (sv > lo) {
+                            if (slot < lds_lim) {
+                                lval[slot * kBR + row] = sv;
+                                lpos[slot * kBR + row] = (uint16_t)e;
+                            } else if (slot < cap) {
+                                cval[(size_t)slot * kBR + row] = sv;
+                                cjt[(size_t)slot * kBR + row] = (uint16_t)e;
                             }
-                }
+                            ++slot;
+                        }
+                    }
             }
-        });
+        };
+        if constexpr (kCollectPerQb<T, D>) {
+            ring_sweep<T, D, S, true>(list, nlist_s, Kh, ring, qop, R0, g,
+                                      [&](int, int e, int qb, f32x16(&acc)[2][1]) { collect_qb(e, qb, acc, 0); });
+        } else {
+            ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int e, f32x16(&acc)[2][2]) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) collect_qb(e, qb, acc, qb);
+            });
+        }
 
         const bool open = rstate[srow] == 1;
         const int nc = cnt[srow];
@@ -926,32 +958,39 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                 tq[qb] = fb_t[row];
             }
             float sc[2] = {0.f, 0.f}, sf[2] = {0.f, 0.f}, sf1[2] = {0.f, 0.f};
-            ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
+            // this lane's sums over the scores above tq of 32-row block qb
+            auto sums_qb = [&](int qb, auto& acc, int c) {
+                if (!aq[qb]) return;
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    if (!aq[qb]) continue;
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float s = acc[kb][qb][r] * p.scale;
-                            if (s > tq[qb]) {
-                                sc[qb] += 1.f;
-                                if (p.gen) {
-                                    // F = sum p, F1 = sum p/u (Newton)
-                                    const float u = p.am.am1 * (s - tq[qb]);
-                                    const float pp = p.am.pw(u);
-                                    sf[qb] += pp;
-                                    sf1[qb] += pp / u;
-                                } else {
-                                    const float gg = 0.5f * (s - tq[qb]);
-                                    sf[qb] += gg * gg;
-                                    sf1[qb] += gg;
-                                }
+                    for (int r = 0; r < 16; ++r) {
+                        const float s = acc[kb][c][r] * p.scale;
+                        if (s > tq[qb]) {
+                            sc[qb] += 1.f;
+                            if (p.gen) {
+                                // F = sum p, F1 = sum p/u (Newton)
+                                const float u = p.am.am1 * (s - tq[qb]);
+                                const float pp = p.am.pw(u);
+                                sf[qb] += pp;
+                                sf1[qb] += pp / u;
+                            } else {
+                                const float gg = 0.5f * (s - tq[qb]);
+                                sf[qb] += gg * gg;
+                                sf1[qb] += gg;
                             }
                         }
-                }
-            });
+                    }
+            };
+            if constexpr (kCollectPerQb<T, D>) {
+                ring_sweep<T, D, S, true>(list, nlist_s, Kh, ring, qop, R0, g,
+                                          [&](int, int, int qb, f32x16(&acc)[2][1]) { sums_qb(qb, acc, 0); });
+            } else {
+                ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) sums_qb(qb, acc, qb);
+                });
+            }
             // combine the two lane halves, then the two key parities
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
@@ -1010,18 +1049,29 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
             aq[qb] = rstate[row] == 2;
             tq[qb] = row_tau[row];
         }
-        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
+        // set the tile's bit if a score of an active row of block qb is above its tau
+        auto mark_qb = [&](int J, int qb, auto& acc, int c) {
             bool any = false;
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                if (!aq[qb]) continue;
+            if (aq[qb]) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) any |= acc[kb][qb][r] * p.scale > tq[qb];
+                    for (int r = 0; r < 16; ++r) any |= acc[kb][c][r] * p.scale > tq[qb];
             }
-            if (__ballot(any) != 0 && l == 0) atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
-        });
+            return any;
+        };
+        if constexpr (kCollectPerQb<T, D>) {
+            ring_sweep<T, D, S, true>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, int qb, f32x16(&acc)[2][1]) {
+                if (__ballot(mark_qb(J, qb, acc, 0)) != 0 && l == 0) atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
+            });
+        } else {
+            ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
+                bool any = false;
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) any |= mark_qb(J, qb, acc, qb);
+                if (__ballot(any) != 0 && l == 0) atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
+            });
+        }
     }
 
     // ---- exact tau of the rows with complete lists
@@ -1052,12 +1102,7 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                 for (int i = h + 2 * kSolveRegs<D>; i < n; i += 2)
                     if (src.tail.at(i) > tr) lm |= 1ull << pos_of(i);
             }
-            uint32_t lo32 = (uint32_t)lm, hi32 = (uint32_t)(lm >> 32);
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                lo32 |= __shfl_xor(lo32, off, kWave);
-                hi32 |= __shfl_xor(hi32, off, kWave);
-            }
+            const uint32_t lo32 = wave_or((uint32_t)lm), hi32 = wave_or((uint32_t)(lm >> 32));
             const uint32_t mine = (l < 32) ? (lo32 >> l) & 1u : (hi32 >> (l - 32)) & 1u;
             if (l < nl && mine) {
                 const int J = list[l] & 0xfff;

@@ -43,6 +43,49 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Lane pairs (l, l ^ 32) without LDS: v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second, so with x in
+// both, the two results hold the x of lanes l & 31 and (l & 31) + 32, in
+// every lane l.  Combining them in that order gives both lanes of a pair the
+// same bits.
+__device__ __forceinline__ void pair_halves(uint32_t x, uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ int pair_sum(int x) {
+    uint32_t a, b;
+    pair_halves((uint32_t)x, a, b);
+    return (int)a + (int)b;
+}
+__device__ __forceinline__ float pair_min(float x) {
+    uint32_t a, b;
+    pair_halves(__builtin_bit_cast(uint32_t, x), a, b);
+    return fminf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ double pair_sum(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    uint32_t a0, b0, a1, b1;
+    pair_halves((uint32_t)u, a0, b0);
+    pair_halves((uint32_t)(u >> 32), a1, b1);
+    return __builtin_bit_cast(double, (uint64_t)a0 | ((uint64_t)a1 << 32)) +
+           __builtin_bit_cast(double, (uint64_t)b0 | ((uint64_t)b1 << 32));
+}
+
+// OR over the 64 lanes of a wave by DPP row shifts and broadcasts, returned
+// to every lane.
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+#define ENTMAX_OR_STEP(ctrl, rmask) x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, rmask, 0xf, false)
+    ENTMAX_OR_STEP(0x111, 0xf);
+    ENTMAX_OR_STEP(0x112, 0xf);
+    ENTMAX_OR_STEP(0x114, 0xf);
+    ENTMAX_OR_STEP(0x118, 0xf);
+    ENTMAX_OR_STEP(0x142, 0xa);
+    ENTMAX_OR_STEP(0x143, 0xc);
+#undef ENTMAX_OR_STEP
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // One Halley step for f(t) = F(t) - 1 with F(t) = sum [(s - t)/2]_+^2:
 // f' = -F1 (F1 = sum [(s - t)/2]_+), f'' = C/2 (C = #{s > t}).
 // Returns the step target, or the bracket midpoint when the step leaves
