@@ -81,6 +81,21 @@ __device__ __forceinline__ void unpack(const u32x4& c, float (&x)[16 / sizeof(T)
     }
 }
 
+// The value of lane l ^ hh (hh a power of two below 32), without LDS where
+// a DPP pattern has it: a rotation by 8 within each row of 16 lanes for 8, the
+// quad permutations for 2 and 1; ds_swizzle's xor mode otherwise.
+__device__ __forceinline__ float xor_lanes(float x, int hh) {
+    const int v = __builtin_bit_cast(int, x);
+#ifndef XD_SHFL
+    if (hh == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false));
+    if (hh == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x4e, 0xf, 0xf, false));
+    if (hh == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, false));
+    if (hh == 4) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(v, 0x1f | (4 << 10)));
+    if (hh == 16) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(v, 0x1f | (16 << 10)));
+#endif
+    return __shfl_xor(x, hh, kWave);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dec_scores(DecParams p) {
     constexpr int kEpc = 16 / sizeof(T);            // elements per 16-byte chunk
@@ -122,7 +137,7 @@ __global__ __launch_bounds__(256) void dec_scores(DecParams p) {
         for (int j = 0; j < hh; ++j) {
             const float mine = up ? part[j + hh] : part[j];
             const float other = up ? part[j] : part[j + hh];
-            part[j] = mine + __shfl_xor(other, hh, kWave);
+            part[j] = mine + xor_lanes(other, hh);
         }
     }
     const int pos = p0 + c * kKpi + grp;  // the key whose dot lane c now holds
