@@ -100,8 +100,10 @@ int entmax_tile_shape(int d, int dtype, int* block_rows, int* block_cols);
  * bracket [max - 2, max - 2/sqrt(n)] of AdaSplash-2 sec. 2.4 (scaled to score
  * units; [max - 1/(alpha-1), max - n^(1-alpha)/(alpha-1)] for other alpha,
  * solved by bisection-guarded Newton steps from below),
- * restricted to the scores above max - 2, with an exact finish once the
- * support is known.  NaN inputs give unspecified results.
+ * restricted to the scores above a lower bound on tau taken from a subset of
+ * the row (at least max - 2, less a relative 1e-5 rounding margin), with an
+ * exact finish once the support is known.  NaN inputs give unspecified
+ * results.
  */
 int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
                     int64_t ld, float alpha, void* stream);
