@@ -128,6 +128,30 @@ def test_overflowing_candidates(env, orc):
         _check(S, tau, P, orc, f"overflow cols={cols}")
 
 
+def test_resident_waves_mixed_rows(env, orc):
+    """More rows than stay resident, so every wave solves several rows in
+    turn: kinds that take different paths (ordinary, one-hot, all masked,
+    all equal, more candidates than LDS holds) interleaved so that each
+    wave meets them one after another."""
+    api, torch = env
+    rows, cols = 4001, 8192
+    rng = np.random.default_rng(11)
+    S = rng.normal(size=(rows, cols)).astype(np.float32)
+    kind = np.arange(rows) % 5
+    S[kind == 0] *= 3.0
+    S[kind == 1] -= 10.0
+    S[kind == 1, 123] = 4.0                       # one-hot (gap > 2)
+    S[kind == 2] = -np.inf                        # no active entry
+    S[kind == 3] = 0.5                            # all equal: p = 1/n
+    S[kind == 4] *= 0.05                          # every score a candidate
+    print("mixed rows generated", flush=True)
+    tau, P = _run(api, torch, S)
+    _check(S, tau, P, orc, "mixed")
+    assert np.all(P[kind == 1, 123] == 1.0)
+    assert np.all(tau[kind == 2] == -np.inf)
+    np.testing.assert_allclose(P[kind == 3], 1.0 / cols, rtol=1e-4)
+
+
 def test_zero_rows(env):
     api, torch = env
     S = torch.empty(0, 10, device="cuda")
