@@ -147,8 +147,11 @@ inline AlphaMap make_alpha_map(float alpha) {
 // F = sum p and F1 = sum p/u (so f' = -F1).  f is convex and decreasing in
 // tau for alpha <= 2, so from a point with f >= 0 the step stays at or below
 // the root; steps that leave (lo, hi) fall back to bisection.  Returns the
-// next point and updates the bracket; *done is set when the step is below
-// fp32 resolution (tau is then the returned point).
+// next point and updates the bracket; *done is set once the step is below
+// 1e-6 relative (tau is then the returned point, one Newton step further, so
+// its error is of the order of the squared step).  A tighter stop would sit
+// at the rounding noise of the fp32 sums, where Newton no longer settles and
+// only the iteration cap ends the loop.
 __device__ __forceinline__ float newton_or_bisect(float t, float F, float F1, float& lo, float& hi,
                                                   bool* done) {
     const float f = F - 1.0f;
@@ -157,7 +160,7 @@ __device__ __forceinline__ float newton_or_bisect(float t, float F, float F1, fl
         lo = t;
         const float step = f / F1;
         const float tn = t + step;
-        if (!(step > 1e-7f * fmaxf(1.0f, fabsf(t)))) {
+        if (!(step > 1e-6f * fmaxf(1.0f, fabsf(t)))) {
             *done = true;
             return fminf(fmaxf(tn, lo), hi);
         }
