@@ -162,10 +162,10 @@ __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
     const float* srow = p.s + (size_t)bh * n;
 
     // Each wave scans a quarter of the score row with 16 loads per lane in
-    // flight per step.  Pass 1: the lane maxima, and the threshold of those 64
-    // values (the row kernel's bound: they are a subset of the row, and a
-    // threshold only rises as scores are added, so it is a lower bound on
-    // tau).  The largest of the four waves' bounds is the row's candidate
+    // flight per step.  Pass 1: the lane maxima, and a lower bound on the
+    // threshold of those 64 values (the row kernel's bound: they are a subset
+    // of the row, and a threshold only rises as scores are added, so it is a
+    // lower bound on tau).  The largest of the four waves' bounds is the row's candidate
     // threshold.  Pass 2 (the quarter again, now from cache): every score
     // above it, with its position, into the wave's own LDS list.
     constexpr int kU = 16;
@@ -187,12 +187,13 @@ __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
     const float wm = wave_max_dpp(lm);
     float wlo = neg_inf();
     if (wm > neg_inf()) {
-        const float n1 = wave_sum_dpp(lm > neg_inf() ? 1.0f : 0.0f);
-        if (p.gen)
+        if (p.gen) {
+            const float n1 = wave_sum_dpp(lm > neg_inf() ? 1.0f : 0.0f);
             wave_tau_gen(wm, n1, wm - p.am.e, p.am, [&](float tt, RowSums& s) { accumulate_gen(s, lm, tt, p.am); },
                          &wlo);
-        else
-            wlo = wave_tau(wm, n1, wm - 2.0f, [&](float tt, RowSums& s) { accumulate(s, lm, tt, wm); });
+        } else {
+            wlo = wave_newton_lower(lm, wm);
+        }
     }
     if (lane == 0) {
         mbuf[w] = wm;
