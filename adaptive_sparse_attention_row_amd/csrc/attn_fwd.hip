@@ -378,9 +378,9 @@ __device__ __forceinline__ float tau_lower_gen(const float (&x)[N], const AlphaM
         for (int k = 0; k < N; ++k) {
             const float u = am.am1 * (x[k] - t);
             if (u > 0.f) {
-                const float pp = am.pw(u);
-                F += pp;
-                F1 += pp / u;
+                const float q = am.pw1(u);  // p / u
+                F = fmaf(q, u, F);
+                F1 += q;
             }
         }
         bool fin;
@@ -542,9 +542,9 @@ __device__ __forceinline__ float solve_candidates_gen(const Src& src, float lo, 
             src.each([&](float x) {
                 const float u = am.am1 * (x - t);
                 if (u > 0.f) {
-                    const float pp = am.pw(u);
-                    F += pp;
-                    F1 += pp / u;
+                    const float q = am.pw1(u);  // p / u
+                    F = fmaf(q, u, F);
+                    F1 += q;
                 }
             });
         }
@@ -971,9 +971,9 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                             if (p.gen) {
                                 // F = sum p, F1 = sum p/u (Newton)
                                 const float u = p.am.am1 * (s - tq[qb]);
-                                const float pp = p.am.pw(u);
-                                sf[qb] += pp;
-                                sf1[qb] += pp / u;
+                                const float q = p.am.pw1(u);  // p / u
+                                sf[qb] = fmaf(q, u, sf[qb]);
+                                sf1[qb] += q;
                             } else {
                                 const float gg = 0.5f * (s - tq[qb]);
                                 sf[qb] += gg * gg;

@@ -123,6 +123,12 @@ struct AlphaMap {
         return lin ? u : exp2f(e * log2f(u));
     }
     __device__ __forceinline__ float p(float s, float tau) const { return pw(am1 * (s - tau)); }
+    // u^(e-1) for u > 0 (1 for sparsemax), 0 otherwise: p = u * pw1(u) and
+    // p/u = pw1(u), so a Newton step needs one power and no division
+    __device__ __forceinline__ float pw1(float u) const {
+        if (!(u > 0.0f)) return 0.0f;
+        return lin ? 1.0f : exp2f((e - 1.0f) * log2f(u));
+    }
     // dp/ds = u^(e-1) on the support (1 for sparsemax), 0 off it
     __device__ __forceinline__ float g(float s, float tau) const {
         const float u = am1 * (s - tau);

@@ -129,9 +129,9 @@ __device__ __forceinline__ float prob_h(float x, float h) {
 __device__ __forceinline__ void accumulate_gen(RowSums& s, float x, float t, const AlphaMap& a) {
     const float u = a.am1 * (x - t);
     if (u > 0.0f) {
-        const float p = a.pw(u);
-        s.F += p;
-        s.F1 += p / u;
+        const float q = a.pw1(u);  // p / u
+        s.F = fmaf(q, u, s.F);
+        s.F1 += q;
     }
 }
 
