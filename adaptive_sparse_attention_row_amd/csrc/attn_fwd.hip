@@ -384,7 +384,7 @@ __device__ __forceinline__ float tau_lower_gen(const float (&x)[N], const AlphaM
             }
         }
         bool fin;
-        const float tn = newton_or_bisect(t, F, F1, lo, hi, &fin);
+        const float tn = newton_or_bisect(t, F, F1, lo, hi, &fin, am);
         if (fin || hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) break;
         t = tn;
     }
@@ -552,7 +552,7 @@ __device__ __forceinline__ float solve_candidates_gen(const Src& src, float lo, 
         F1 += __shfl_xor(F1, 32, kWave);
         if (done) continue;
         bool fin;
-        const float tn = newton_or_bisect(t, F, F1, lo, hi, &fin);
+        const float tn = newton_or_bisect(t, F, F1, lo, hi, &fin, am);
         if (fin) {
             result = tn;
             done = true;
@@ -1013,7 +1013,7 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                 float lo = row_lo[srow], hi = row_hi[srow], tc = fb_t[srow];
                 if (p.gen) {
                     bool fin;
-                    const float tn = newton_or_bisect(tc, F, F1, lo, hi, &fin);
+                    const float tn = newton_or_bisect(tc, F, F1, lo, hi, &fin, p.am);
                     if (fin || hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
                         fb_active[srow] = 0;
                         row_tau[srow] = fin ? tn : 0.5f * (lo + hi);

@@ -149,22 +149,27 @@ inline AlphaMap make_alpha_map(float alpha) {
     return a;
 }
 
-// Newton step from below for the alpha-entmax normaliser: f = F - 1 with
-// F = sum p and F1 = sum p/u (so f' = -F1).  f is convex and decreasing in
-// tau for alpha <= 2, so from a point with f >= 0 the step stays at or below
-// the root; steps that leave (lo, hi) fall back to bisection.  Returns the
-// next point and updates the bracket; *done is set once the step is below
-// 1e-6 relative (tau is then the returned point, one Newton step further, so
-// its error is of the order of the squared step).  A tighter stop would sit
-// at the rounding noise of the fp32 sums, where Newton no longer settles and
-// only the iteration cap ends the loop.
+// Newton step from below for the alpha-entmax normaliser F = sum p = 1, with
+// F1 = sum p/u = -dF/dtau, taken on g = F^(alpha-1) - 1 (the e-norm of the
+// u_i, e = 1/(alpha-1), less 1) rather than on F - 1: g is convex and
+// decreasing in tau like F, so from a point with g >= 0 the step stays at or
+// below the root, and it is close to linear (exactly so while a single score
+// is above tau), where F - 1 grows like a power e of the distance and
+// Newton on it closes only 1 - 1/e of the gap per step far from the root.
+// The step is e (F - F^(2-alpha)) / F1 (the plain Newton step at alpha = 2).
+// Steps that leave (lo, hi) fall back to bisection.  Returns the next point
+// and updates the bracket; *done is set once the step is below 1e-6 relative
+// (tau is then the returned point, one Newton step further, so its error is
+// of the order of the squared step).  A tighter stop would sit at the
+// rounding noise of the fp32 sums, where Newton no longer settles and only
+// the iteration cap ends the loop.
 __device__ __forceinline__ float newton_or_bisect(float t, float F, float F1, float& lo, float& hi,
-                                                  bool* done) {
-    const float f = F - 1.0f;
+                                                  bool* done, const AlphaMap& am) {
     *done = false;
-    if (f >= 0.0f) {
+    if (F - 1.0f >= 0.0f) {
         lo = t;
-        const float step = f / F1;
+        const float Fq = am.lin ? 1.0f : exp2f((1.0f - am.am1) * log2f(F));  // F^(2-alpha)
+        const float step = am.e * (F - Fq) / F1;
         const float tn = t + step;
         if (!(step > 1e-6f * fmaxf(1.0f, fabsf(t)))) {
             *done = true;

@@ -148,7 +148,7 @@ __device__ float refine_tau_gen(float m, float total, const AlphaMap& a, Visit v
         visit(t, s);
         s = block_reduce(s, red, it & 1);
         bool done;
-        const float tn = newton_or_bisect(t, s.F, s.F1, lo, hi, &done);
+        const float tn = newton_or_bisect(t, s.F, s.F1, lo, hi, &done, a);
         if (done) return tn;
         if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(t))) break;
         t = tn;
@@ -320,7 +320,7 @@ __device__ __forceinline__ float wave_tau_gen(float m, float n, float lo, const 
         s.F = wave_sum_dpp(s.F);
         s.F1 = wave_sum_dpp(s.F1);
         bool done;
-        const float tn = newton_or_bisect(t, s.F, s.F1, lo, hi, &done);
+        const float tn = newton_or_bisect(t, s.F, s.F1, lo, hi, &done, a);
         if (done) {
             tau = tn;
             break;
