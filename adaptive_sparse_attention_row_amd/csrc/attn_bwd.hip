@@ -294,6 +294,135 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
     }
 }
 
+// ------------------------------------------------------------ dQ kernel, bf16
+// The same two passes with 32 query rows per wave: the four waves of a
+// workgroup take the 128 rows in quarters and every one of them walks all of
+// the block's listed tiles, so each wave sums over all keys of its rows (no
+// reduction across waves) and holds half the operands and accumulators of
+// the layout above.  That fits two workgroups per CU (one wave's staging
+// then overlaps another's products) where the layout above runs one.
+#ifndef ENTMAX_BWD_DQ32
+#define ENTMAX_BWD_DQ32 1
+#endif
+template <int D>
+__global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
+    using T = __bf16;
+    using O = Ops<T, D>;
+    constexpr int BLK = DqCfg<T, D>::kBlk;
+    __shared__ __attribute__((aligned(16))) T lds[3 * BLK];
+    __shared__ uint16_t list[kMaxTc];
+    __shared__ uint32_t mw[2][kMaxTc / 32];
+    __shared__ int nlist_s;
+
+    const int t = threadIdx.x, w = wave_id();
+    const int l = lane_id(), m = l & 31, h = l >> 5;
+    int bh, r0;
+    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    const int R0 = r0 + 32 * w;  // this wave's rows
+    const int half = w >> 1;     // their 64-row block
+    const Geom g = {p.L, p.mode, p.W};
+    const size_t head_off = (size_t)bh * p.L * D;
+    const T* Qh = reinterpret_cast<const T*>(p.q) + head_off;
+    const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
+    const T* Vh = reinterpret_cast<const T*>(p.v) + head_off;
+    const T* dOh = reinterpret_cast<const T*>(p.dout) + head_off;
+
+    for (int i = t; i < 2 * p.Wd; i += kNT) {
+        const int hh = i / p.Wd, wd = i % p.Wd;
+        const int I = r0 / 64 + hh;
+        mw[hh][wd] = (I < p.Tr64) ? p.mask[((size_t)bh * p.Tr64 + I) * p.Wd + wd] : 0u;
+    }
+    __syncthreads();
+    if (w == 0) {
+        const int n = build_list16(list, p.Tc, [&](int J) {
+            return (int)((mw[0][J >> 5] >> (J & 31)) & 1u) | (int)(((mw[1][J >> 5] >> (J & 31)) & 1u) << 1);
+        });
+        if (l == 0) nlist_s = n;
+    }
+    typename O::template QOp<1> qop, dop;
+    O::load_q(qop, Qh, R0, p.L);
+    O::load_q(dop, dOh, R0, p.L);
+    const int row = R0 + m;
+    const float tq = (row < p.L) ? p.tau[(size_t)bh * p.L + row] : __builtin_inff();
+    __syncthreads();
+    const int n = nlist_s;
+
+    // Stage each listed tile (K and V in the score layout, K in the PV
+    // layout) and call fn(J, cls, Kt, Vt, KPVt) when it is non-null for this
+    // wave's 64-row block and not masked out for its rows.
+    auto walk = [&](auto fn) {
+        for (int e = 0; e < n; ++e) {
+            __syncthreads();
+            const int ent = list[e];
+            const int J = ent & 0xfff;
+            stage_score<T, D>(lds, Kh, J * kBC, p.L);
+            stage_score<T, D>(lds + BLK, Vh, J * kBC, p.L);
+            stage_pv<T, D>(lds + 2 * BLK, Kh, J * kBC, p.L);
+            __syncthreads();
+            if (!((ent >> (12 + half)) & 1)) continue;
+            const int cls = block_class(R0, 32, J * kBC, kBC, g);
+            if (cls == kSkip) continue;
+            fn(J, cls, lds, lds + BLK, lds + 2 * BLK);
+        }
+        __syncthreads();
+    };
+    // 2g (so that the factor cancels in delta), the derivative of A in S
+    auto dd_of = [&](float sv) { return p.gen ? 2.0f * p.am.g(sv, tq) : fmaxf(sv - tq, 0.0f); };
+
+    // ---- pass 1: delta_i = sum g dA / sum g
+    float num = 0.f, den = 0.f;
+    walk([&](int J, int cls, const T* Kt, const T* Vt, const T*) {
+        f32x16 s[2][1], da[2][1];
+        O::template scores<1>(s, Kt, qop);
+        if (cls == kPartial) apply_mask<1>(s, J, R0, g);
+        O::template scores<1>(da, Vt, dop);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float dd = dd_of(s[kb][0][r] * p.scale);
+                num += dd * da[kb][0][r];
+                den += dd;
+            }
+    });
+    num += __shfl_xor(num, 32, kWave);
+    den += __shfl_xor(den, 32, kWave);
+    const float dl = den > 0.f ? num / den : 0.f;
+    if (h == 0 && row < p.L) p.delta[(size_t)bh * p.L + row] = dl;
+
+    // ---- pass 2: dQ^T += K^T (2 dS)^T
+    typename O::template OAcc<1> oa;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oa.o[db][0][i] = 0.f;
+    walk([&](int J, int cls, const T* Kt, const T* Vt, const T* KPVt) {
+        f32x16 s[2][1], da[2][1];
+        O::template scores<1>(s, Kt, qop);
+        if (cls == kPartial) apply_mask<1>(s, J, R0, g);
+        O::template scores<1>(da, Vt, dop);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][0][r] = dd_of(s[kb][0][r] * p.scale) * (da[kb][0][r] - dl);
+        const bool on[2] = {true, true};
+        O::template pv<1>(oa, KPVt, s, on);
+    });
+
+    if (row < p.L) {
+        const float f = 0.5f * p.scale;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = f * oa.o[db][0][4 * r4 + e];
+                *reinterpret_cast<f32x4*>(p.dq + ((size_t)bh * p.L + row) * D + db * 32 + 8 * r4 + 4 * h) = v4;
+            }
+    }
+}
+
 // ------------------------------------------------------------ dK/dV kernel
 template <typename T, int D>
 struct DkvCfg {
@@ -440,7 +569,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
 
 template <typename T, int D>
 hipError_t launch_bwd_typed(const BwdParams& bp, hipStream_t stream) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
+    if constexpr (sizeof(T) == 2 && ENTMAX_BWD_DQ32)
+        hipLaunchKernelGGL((bwd_dq32_kernel<D>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
