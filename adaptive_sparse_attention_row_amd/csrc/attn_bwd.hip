@@ -424,17 +424,27 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ dK/dV kernel
+#ifndef ENTMAX_BWD_DKDV_SPLIT
+#define ENTMAX_BWD_DKDV_SPLIT 1
+#endif
 template <typename T, int D>
 struct DkvCfg {
-    static constexpr int kNBK = (D == 64) ? 2 : 1;  // 32-key blocks per wave
+    // 32-key blocks per wave (one in the split bf16 kernels, which keep two
+    // workgroups per CU)
+    static constexpr int kNBK = (D == 64 && !(sizeof(T) == 2 && ENTMAX_BWD_DKDV_SPLIT)) ? 2 : 1;
     static constexpr int kKW = 32 * kNBK;            // keys per wave
     static constexpr int kKeys = 4 * kKW;            // keys per workgroup
     static constexpr int kBlk = DqCfg<T, D>::kBlk;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
+// PART: 0 both gradients in one sweep; 1 dV only; 2 dK only.  The split
+// pair recomputes S once more but each half holds one accumulator and one
+// set of operands, which fits two workgroups per CU (bf16) where the joint
+// kernel runs one.
+template <typename T, int D, int PART>
+__global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdParams p) {
     using O = Ops<T, D>;
+    constexpr bool kDV = PART != 2, kDK = PART != 1;
     constexpr int NBK = DkvCfg<T, D>::kNBK;
     constexpr int KW = DkvCfg<T, D>::kKW;
     constexpr int BLK = DkvCfg<T, D>::kBlk;
@@ -474,7 +484,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
     typename O::template QOp<NBK> kop, vop;
     O::load_q(kop, Kh, cw, p.L);
-    O::load_q(vop, Vh, cw, p.L);
+    if constexpr (kDK) O::load_q(vop, Vh, cw, p.L);
     typename O::template OAcc<NBK> dka, dva;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -482,8 +492,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
         for (int cb = 0; cb < NBK; ++cb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                dka.o[db][cb][i] = 0.f;
-                dva.o[db][cb][i] = 0.f;
+                if constexpr (kDK) dka.o[db][cb][i] = 0.f;
+                if constexpr (kDV) dva.o[db][cb][i] = 0.f;
             }
     __syncthreads();
     const int n = nlist_s;
@@ -498,13 +508,15 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
         const int i0 = I * 64;
         __syncthreads();
         stage_score<T, D>(Qt, Qh, i0, p.L);
-        stage_score<T, D>(dOt, dOh, i0, p.L);
-        stage_pv<T, D>(QPVt, Qh, i0, p.L);
-        stage_pv<T, D>(dOPVt, dOh, i0, p.L);
+        if constexpr (kDK) {
+            stage_score<T, D>(dOt, dOh, i0, p.L);
+            stage_pv<T, D>(QPVt, Qh, i0, p.L);
+        }
+        if constexpr (kDV) stage_pv<T, D>(dOPVt, dOh, i0, p.L);
         if (t < 64) {
             const int row = i0 + t;
             tau_s[t] = (row < p.L) ? p.tau[(size_t)bh * p.L + row] : __builtin_inff();
-            del_s[t] = (row < p.L) ? p.delta[(size_t)bh * p.L + row] : 0.f;
+            if constexpr (kDK) del_s[t] = (row < p.L) ? p.delta[(size_t)bh * p.L + row] : 0.f;
         }
         __syncthreads();
         if (!((ent >> (12 + w)) & 1)) continue;
@@ -513,36 +525,44 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
         f32x16 s[2][NBK], da[2][NBK];
         O::scores(s, Qt, kop);   // rows: queries (registers), lanes: keys
         if (cls == kPartial) apply_mask_rows_are_queries(s, i0, cw, g);
-        O::scores(da, dOt, vop);
-        f32x16 a4[2][NBK];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            float tr[16], dr[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qi = kb * 32 + key_of_reg(r, h);
-                tr[r] = tau_s[qi];
-                dr[r] = del_s[qi];
-            }
-#pragma unroll
-            for (int cb = 0; cb < NBK; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float sv = s[kb][cb][r] * p.scale;
-                    if (p.gen) {
-                        // 4A and 2 g, the scaling of the alpha = 1.5 form below
-                        a4[kb][cb][r] = 4.0f * p.am.p(sv, tr[r]);
-                        s[kb][cb][r] = 2.0f * p.am.g(sv, tr[r]) * (da[kb][cb][r] - dr[r]);
-                    } else {
-                        const float dd = fmaxf(sv - tr[r], 0.0f);
-                        a4[kb][cb][r] = dd * dd;
-                        s[kb][cb][r] = dd * (da[kb][cb][r] - dr[r]);
-                    }
-                }
-        }
         const bool on[2] = {true, true};
-        O::pv(dva, dOPVt, a4, on);
-        O::pv(dka, QPVt, s, on);
+        if constexpr (kDV) {
+            // 4A (dd^2 with dd = 2g at alpha = 1.5), into dV
+            f32x16 a4[2][NBK];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int cb = 0; cb < NBK; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float sv = s[kb][cb][r] * p.scale;
+                        const float tr = tau_s[kb * 32 + key_of_reg(r, h)];
+                        if (p.gen) {
+                            a4[kb][cb][r] = 4.0f * p.am.p(sv, tr);
+                        } else {
+                            const float dd = fmaxf(sv - tr, 0.0f);
+                            a4[kb][cb][r] = dd * dd;
+                        }
+                    }
+            O::pv(dva, dOPVt, a4, on);
+        }
+        if constexpr (kDK) {
+            O::scores(da, dOt, vop);
+            // 2 dS = dd (dA - delta) in place of S, into dK
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int cb = 0; cb < NBK; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qi = kb * 32 + key_of_reg(r, h);
+                        const float sv = s[kb][cb][r] * p.scale;
+                        const float tr = tau_s[qi];
+                        const float dd = p.gen ? 2.0f * p.am.g(sv, tr) : fmaxf(sv - tr, 0.0f);
+                        s[kb][cb][r] = dd * (da[kb][cb][r] - del_s[qi]);
+                    }
+            O::pv(dka, QPVt, s, on);
+        }
     }
 
     const float fk = 0.5f * p.scale;
@@ -558,11 +578,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdParams p) {
                 f32x4 k4, v4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    k4[e] = fk * dka.o[db][cb][4 * r4 + e];
-                    v4[e] = 0.25f * dva.o[db][cb][4 * r4 + e];
+                    if constexpr (kDK) k4[e] = fk * dka.o[db][cb][4 * r4 + e];
+                    if constexpr (kDV) v4[e] = 0.25f * dva.o[db][cb][4 * r4 + e];
                 }
-                *reinterpret_cast<f32x4*>(p.dk + ((size_t)bh * p.L + key) * D + d) = k4;
-                *reinterpret_cast<f32x4*>(p.dv + ((size_t)bh * p.L + key) * D + d) = v4;
+                if constexpr (kDK) *reinterpret_cast<f32x4*>(p.dk + ((size_t)bh * p.L + key) * D + d) = k4;
+                if constexpr (kDV) *reinterpret_cast<f32x4*>(p.dv + ((size_t)bh * p.L + key) * D + d) = v4;
             }
         }
 }
@@ -575,7 +595,14 @@ hipError_t launch_bwd_typed(const BwdParams& bp, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
+    if constexpr (sizeof(T) == 2 && ENTMAX_BWD_DKDV_SPLIT) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 1>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 2>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
+    } else {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 0>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
+    }
     return hipGetLastError();
 }
 
