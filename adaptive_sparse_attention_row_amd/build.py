@@ -32,8 +32,10 @@ ARCH = "gfx950"
 # own from ordinary float code otherwise).
 # NaN inputs are outside the contract (include/entmax.h), so max/min need no
 # NaN canonicalisation; infinities are still honoured (masked scores are -inf).
+# Loop heads start on 64-byte boundaries: without that, a hot loop's timing
+# moved by up to 6 % with unrelated code changes elsewhere in its kernel.
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fno-honor-nans",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fno-honor-nans", "-falign-loops=64",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -261,16 +261,18 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
     __syncthreads();
 }
 
-// The same sweep for a workgroup whose tiles are all full: no mask, every
-// key tile inside L (L a multiple of 64), all 128 query rows below L, and an
-// even number of key tiles.  Pair pp is then tiles 2 pp and 2 pp + 1, so no
-// list is read and no tile class is evaluated, and each wave stages the same
+// The same sweep for a workgroup whose tiles are the first nt key tiles:
+// no mask (nt = all tiles) or the causal mask (nt = up to the diagonal), with
+// every key tile inside L (L a multiple of 64) and all 128 query rows below
+// L.  Pair pp is then tiles 2 pp and 2 pp + 1, so no list is read, a tile
+// class is evaluated only on the diagonal, and each wave stages the same
 // half of one tile of every pair from a scalar tile base plus per-lane byte
 // offsets computed once: per pair, what is left besides the products and
 // the statistics is the DMA issue, one wait and the barrier.
-template <typename T, int D, int S, class Fn>
-__device__ __forceinline__ void dense_sweep(int Tc, const T* Kh, T* ring,
-                                            const typename Ops<T, D>::template QOp<2>& qop, Fn fn) {
+template <typename T, int D, int S, bool CAUSAL, class Fn>
+__device__ __forceinline__ void dense_sweep(int nt, const T* Kh, T* ring,
+                                            const typename Ops<T, D>::template QOp<2>& qop, int R0,
+                                            const Geom& g, Fn fn) {
     using O = Ops<T, D>;
     using DMA = TileDMA<T, D>;
     static_assert(S >= 2, "the dense sweep keeps at least one pair in flight");
@@ -280,7 +282,7 @@ __device__ __forceinline__ void dense_sweep(int Tc, const T* Kh, T* ring,
     constexpr int kSlotElems = 16 / (int)sizeof(T);
     constexpr size_t kTileBytes = (size_t)64 * D * sizeof(T);
     const int w = wave_id(), kh = w >> 1, lane = lane_id();
-    const int npairs = Tc / 2;
+    const int npairs = (nt + 1) / 2;
     uint32_t off[kIpw];
 #pragma unroll
     for (int k = 0; k < kIpw; ++k) {
@@ -288,10 +290,13 @@ __device__ __forceinline__ void dense_sweep(int Tc, const T* Kh, T* ring,
         const int row = qt / DMA::kCPR;
         off[k] = (uint32_t)((row * D + swz<DMA::kCPR>(row, qt % DMA::kCPR) * kSlotElems) * sizeof(T));
     }
-    // wave w stages half (w & 1) of tile (w >> 1) of each pair
+    // wave w stages half (w & 1) of tile (w >> 1) of each pair; the second
+    // tile of a last, odd pair lies past the range, and its waves re-read the
+    // first (the products skip it)
     const char* kw = reinterpret_cast<const char*>(Kh) + (size_t)(w >> 1) * kTileBytes;
     auto issue = [&](int pq, int stage) {
-        const char* tb = kw + (size_t)pq * 2 * kTileBytes;
+        const char* tb = CAUSAL ? reinterpret_cast<const char*>(Kh) + (size_t)min(2 * pq + (w >> 1), nt - 1) * kTileBytes
+                                : kw + (size_t)pq * 2 * kTileBytes;
         T* base = ring + stage * kStage + w * kPerWave * kSlotElems;
 #pragma unroll
         for (int k = 0; k < kIpw; ++k)
@@ -308,9 +313,21 @@ __device__ __forceinline__ void dense_sweep(int Tc, const T* Kh, T* ring,
         else wait_vmcnt<0>();
         barrier_keep_vm();
         if (pp + S - 1 < npairs) issue(pp + S - 1, si);
-        f32x16 acc[2][2];
-        O::scores(acc, ring + su * kStage + kh * DMA::kTileElems, qop);
-        fn(2 * pp + kh, 2 * pp + kh, acc);
+        const int J = 2 * pp + kh;
+        if constexpr (CAUSAL) {
+            // only the diagonal tiles are partial or empty
+            const int cls = J >= nt ? kSkip : (J * kBC + kBC - 1 <= R0) ? kFull : tile_class(J, R0, g);
+            if (cls != kSkip) {
+                f32x16 acc[2][2];
+                O::scores(acc, ring + su * kStage + kh * DMA::kTileElems, qop);
+                if (cls == kPartial) apply_mask(acc, J, R0, g);
+                fn(J, J, acc);
+            }
+        } else {
+            f32x16 acc[2][2];
+            O::scores(acc, ring + su * kStage + kh * DMA::kTileElems, qop);
+            fn(J, J, acc);
+        }
         su = su + 1 == S ? 0 : su + 1;
         si = si + 1 == S ? 0 : si + 1;
     }
@@ -635,7 +652,11 @@ constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
 // ------------------------------------------------------------ kernel 1a
 // Dense sweep: per row the top tile maxima (-> tau_lo and the maximum) and
 // per (64-row half, tile) the largest raw score.
-template <typename T, int D, int TCMAX>
+// CAUSAL: the instance for the causal mask (its list-free sweep covers the
+// tiles up to the diagonal); the other serves no mask and the window mask
+// (which always takes the list).  Separate instances keep each loop's code
+// as it is alone.
+template <typename T, int D, int TCMAX, bool CAUSAL>
 __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(FwdParams p) {
     using O = Ops<T, D>;
     constexpr int S = StatsCfg<T, D>::kS;
@@ -661,8 +682,10 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
     typename O::template QOp<2> qop;
     O::load_q(qop, Qh, R0, p.L);
     for (int i = t; i < 2 * TCMAX; i += kNT) (&umax[0][0])[i] = neg_inf();
-    // every tile of this workgroup full: the list-free sweep
-    const bool dense = p.mode == 0 && p.L % kBC == 0 && r0 + kBR <= p.L && p.Tc % 2 == 0;
+    // the workgroup's tiles are the first dense_nt (no mask: all; causal: up
+    // to the diagonal), all inside L: the list-free sweep
+    const bool dense = p.L % kBC == 0 && r0 + kBR <= p.L &&
+                       (CAUSAL ? p.mode == 1 : (p.mode == 0 && p.Tc % 2 == 0));
     if (w == 0 && !dense) {
         const int n = build_list(list, p.Tc, [&](int J) {
             return (tile_class(J, r0, g) != kSkip ? 1 : 0) | (tile_class(J, r0 + 64, g) != kSkip ? 2 : 0);
@@ -698,7 +721,7 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
         wm = wave_max_dpp(wm);
         if (l == 0) umax[qh][J] = wm;
     };
-    if (dense) dense_sweep<T, D, S>(p.Tc, Kh, ring, qop, tile_stats);
+    if (dense) dense_sweep<T, D, S, CAUSAL>(CAUSAL ? r0 / kBC + 2 : p.Tc, Kh, ring, qop, R0, g, tile_stats);
     else ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, tile_stats);
 
     // merge the four lists of each row (two lane halves x two key parities)
@@ -1426,15 +1449,23 @@ __global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(Fw
     }
 }
 
+template <typename T, int D, int TCMAX>
+void launch_stats(const FwdParams& fp, int grid, hipStream_t stream) {
+    if (fp.mode == 1)
+        hipLaunchKernelGGL((fwd_stats_kernel<T, D, TCMAX, true>), dim3(grid), dim3(kNT), 0, stream, fp);
+    else
+        hipLaunchKernelGGL((fwd_stats_kernel<T, D, TCMAX, false>), dim3(grid), dim3(kNT), 0, stream, fp);
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t stream) {
     if (phase & 1) {
         if (fp.Tc <= 128)
-            hipLaunchKernelGGL((fwd_stats_kernel<T, D, 128>), dim3(grid), dim3(kNT), 0, stream, fp);
+            launch_stats<T, D, 128>(fp, grid, stream);
         else if (fp.Tc <= 256)
-            hipLaunchKernelGGL((fwd_stats_kernel<T, D, 256>), dim3(grid), dim3(kNT), 0, stream, fp);
+            launch_stats<T, D, 256>(fp, grid, stream);
         else
-            hipLaunchKernelGGL((fwd_stats_kernel<T, D, kMaxTc>), dim3(grid), dim3(kNT), 0, stream, fp);
+            launch_stats<T, D, kMaxTc>(fp, grid, stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
