@@ -86,13 +86,11 @@ __device__ __forceinline__ void unpack(const u32x4& c, float (&x)[16 / sizeof(T)
 // quad permutations for 2 and 1; ds_swizzle's xor mode otherwise.
 __device__ __forceinline__ float xor_lanes(float x, int hh) {
     const int v = __builtin_bit_cast(int, x);
-#ifndef XD_SHFL
     if (hh == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false));
     if (hh == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x4e, 0xf, 0xf, false));
     if (hh == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, false));
     if (hh == 4) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(v, 0x1f | (4 << 10)));
     if (hh == 16) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(v, 0x1f | (16 << 10)));
-#endif
     return __shfl_xor(x, hh, kWave);
 }
 
