@@ -23,7 +23,9 @@
 //             quarter of the score row (its lane maxima and their threshold,
 //             a lower bound on tau; then the scores above the largest of the
 //             four bounds, with their positions, into its own LDS list); tau
-//             by the row solves of row_solve.hpp over the four lists; then o
+//             by the row solves of row_solve.hpp over the four lists (at
+//             alpha = 1.5 each wave solves on all of them with wave
+//             reductions, starting from the bound); then o
 //             from the support's V rows only (the threads split the head
 //             dimension, groups of them split the support, and the groups
 //             are summed through LDS).
@@ -112,34 +114,48 @@ __global__ __launch_bounds__(256) void dec_scores(DecParams p) {
         unpack<T>(qc, qv);
     }
     const T* Kh = reinterpret_cast<const T*>(p.k) + (size_t)bh * p.Lcap * D;
-    float part[kLpk];
+    // Every load of the wave is issued before the first product.  (Written
+    // as two lambdas over the chunk array: the same steps written inline
+    // compiled the reduce-scatter's selects into a select chain over all of
+    // part[], 3.4x the instructions and 5 % slower.)
+    auto load_all = [&](u32x4 (&kc)[kLpk]) {
 #pragma unroll
-    for (int i = 0; i < kLpk; ++i) {
-        int pos = p0 + i * kKpi + grp;
-        pos = pos < p.nact ? pos : p.nact - 1;  // tail lanes repeat the last key; never stored
-        const int key = key_of(pos, p.j0);
-        const u32x4 kc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kh + (size_t)key * D) + c);
-        float kv[kEpc];
-        unpack<T>(kc, kv);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < kEpc; ++e) acc = fmaf(qv[e], kv[e], acc);
-        part[i] = acc;
-    }
-    // reduce-scatter over the kLpk lanes of the row group: after the step with
-    // offset hh, lane c keeps the half of its keys selected by bit hh of c
-#pragma unroll
-    for (int hh = kLpk / 2; hh >= 1; hh >>= 1) {
-        const bool up = (c & hh) != 0;
-#pragma unroll
-        for (int j = 0; j < hh; ++j) {
-            const float mine = up ? part[j + hh] : part[j];
-            const float other = up ? part[j] : part[j + hh];
-            part[j] = mine + xor_lanes(other, hh);
+        for (int i = 0; i < kLpk; ++i) {
+            int pos = p0 + i * kKpi + grp;
+            pos = pos < p.nact ? pos : p.nact - 1;  // tail lanes repeat the last key; never stored
+            const int key = key_of(pos, p.j0);
+            kc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kh + (size_t)key * D) + c);
         }
-    }
-    const int pos = p0 + c * kKpi + grp;  // the key whose dot lane c now holds
-    if (pos < p.nact) p.s[(size_t)bh * p.nact + pos] = part[0] * p.scale;
+    };
+    auto finish = [&](const u32x4 (&kc)[kLpk]) {
+        float part[kLpk];
+#pragma unroll
+        for (int i = 0; i < kLpk; ++i) {
+            float kv[kEpc];
+            unpack<T>(kc[i], kv);
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < kEpc; ++e) acc = fmaf(qv[e], kv[e], acc);
+            part[i] = acc;
+        }
+        // reduce-scatter over the kLpk lanes of the row group: after the step
+        // with offset hh, lane c keeps the half of its keys selected by bit hh of c
+#pragma unroll
+        for (int hh = kLpk / 2; hh >= 1; hh >>= 1) {
+            const bool up = (c & hh) != 0;
+#pragma unroll
+            for (int j = 0; j < hh; ++j) {
+                const float mine = up ? part[j + hh] : part[j];
+                const float other = up ? part[j] : part[j + hh];
+                part[j] = mine + xor_lanes(other, hh);
+            }
+        }
+        const int pos = p0 + c * kKpi + grp;  // the key whose dot lane c now holds
+        if (pos < p.nact) p.s[(size_t)bh * p.nact + pos] = part[0] * p.scale;
+    };
+    u32x4 kc[kLpk];
+    load_all(kc);
+    finish(kc);
 }
 
 constexpr int kDecCap = 4096;            // candidates kept in LDS per (batch, head)
@@ -159,14 +175,16 @@ __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
     const int n = p.nact;
     const float* srow = p.s + (size_t)bh * n;
 
-    // Each wave scans a quarter of the score row with 16 loads per lane in
-    // flight per step.  Pass 1: the lane maxima, and a lower bound on the
-    // threshold of those 64 values (the row kernel's bound: they are a subset
-    // of the row, and a threshold only rises as scores are added, so it is a
-    // lower bound on tau).  The largest of the four waves' bounds is the row's candidate
-    // threshold.  Pass 2 (the quarter again, now from cache): every score
-    // above it, with its position, into the wave's own LDS list.
-    constexpr int kU = 16;
+    // Each wave scans a quarter of the score row.  Pass 1: the lane maxima,
+    // and a lower bound on the threshold of those 64 values (the row kernel's
+    // bound: they are a subset of the row, and a threshold only rises as
+    // scores are added, so it is a lower bound on tau).  The largest of the
+    // four waves' bounds is the row's candidate threshold.  Pass 2: every
+    // score above it, with its position, into the wave's own LDS list.  A
+    // quarter of up to kNB * kU * kWave scores (rows of up to 16384 keys) is
+    // loaded once, all of it in flight together, and pass 2 reads the
+    // registers; longer rows are read in steps of kU loads per lane, twice.
+    constexpr int kU = 16, kNB = 4;
     const int q0 = (int)(((int64_t)n * w) / kWaves), q1 = (int)(((int64_t)n * (w + 1)) / kWaves);
     auto load16 = [&](int base, float (&x)[kU]) {
 #pragma unroll
@@ -175,12 +193,23 @@ __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
             x[u] = i < q1 ? srow[i] : neg_inf();
         }
     };
+    const bool inreg = (q1 - q0) <= kNB * kU * kWave;  // per wave: quarters differ by at most one
+    float xr[kNB][kU];
     float lm = neg_inf();
-    for (int base = q0; base < q1; base += kU * kWave) {
-        float x[kU];
-        load16(base, x);
+    if (inreg) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) lm = fmaxf(lm, x[u]);
+        for (int b = 0; b < kNB; ++b) {
+            load16(q0 + b * kU * kWave, xr[b]);
+#pragma unroll
+            for (int u = 0; u < kU; ++u) lm = fmaxf(lm, xr[b][u]);
+        }
+    } else {
+        for (int base = q0; base < q1; base += kU * kWave) {
+            float x[kU];
+            load16(base, x);
+#pragma unroll
+            for (int u = 0; u < kU; ++u) lm = fmaxf(lm, x[u]);
+        }
     }
     const float wm = wave_max_dpp(lm);
     float wlo = neg_inf();
@@ -207,9 +236,8 @@ __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
     float* wv = cv + w * kWaveCap;
     int* wp = cp + w * kWaveCap;
     int cnt = 0;
-    for (int base = q0; base < q1; base += kU * kWave) {
-        float x[kU];
-        load16(base, x);
+    // append the scores of x above the bound (positions base + u * kWave + lane)
+    auto compact = [&](int base, const float (&x)[kU]) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const bool is_c = x[u] > bound;
@@ -221,6 +249,16 @@ __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
                 wp[slot] = base + u * kWave + lane;
             }
             cnt += __popcll(b);
+        }
+    };
+    if (inreg) {
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) compact(q0 + b * kU * kWave, xr[b]);
+    } else {
+        for (int base = q0; base < q1; base += kU * kWave) {
+            float x[kU];
+            load16(base, x);
+            compact(base, x);
         }
     }
     if (lane == 0) wcnt[w] = cnt;
@@ -247,11 +285,17 @@ __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
                    : refine_tau_gen(m, (float)filled, p.am, [&](float tt, RowSums& s) {
             for (int i = t; i < n; i += 256) accumulate_gen(s, srow[i], tt, p.am);
         }, red);
+    } else if (fits) {
+        // every wave solves on all four lists with wave reductions only (the
+        // same sums in the same order, so the same tau), from the bound:
+        // tau >= m - 2 (the maximum alone has weight 1) and tau >= bound
+        tau = wave_tau(m, (float)filled, fmaxf(bound, m - 2.0f), [&](float tt, RowSums& s) {
+#pragma unroll
+            for (int k = 0; k < kWaves; ++k)
+                for (int i = lane; i < wcnt[k]; i += kWave) accumulate(s, cv[k * kWaveCap + i], tt, m);
+        });
     } else {
-        tau = fits ? refine_tau(m, (float)filled, [&](float tt, RowSums& s) {
-            each_cand([&](float x, int) { accumulate(s, x, tt, m); });
-        }, red)
-                   : refine_tau(m, (float)filled, [&](float tt, RowSums& s) {
+        tau = refine_tau(m, (float)filled, [&](float tt, RowSums& s) {
             for (int i = t; i < n; i += 256) accumulate(s, srow[i], tt, m);
         }, red);
     }
@@ -289,6 +333,7 @@ __global__ __launch_bounds__(256) void dec_solve(DecParams p) {
         }
     };
     if (fits) {
+        __syncthreads();  // every wave's solve has read all four lists
         const int mine = wcnt[w] < kWaveCap ? wcnt[w] : kWaveCap;
         int ns = 0;
         for (int i0 = 0; i0 < mine; i0 += kWave) {

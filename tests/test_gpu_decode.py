@@ -66,6 +66,10 @@ SHAPES = [
     (2, 2, 300, 512, 128, "f32"),
     (1, 2, 4999, 5003, 64, "f32"),
     (1, 2, 20000, 20000, 128, "bf16"),
+    # quarters of 4096 scores (all held in registers) and of 4096 / 4097
+    # (the last wave streams its quarter twice)
+    (1, 1, 16384, 16384, 128, "bf16"),
+    (1, 2, 16385, 16400, 64, "bf16"),
 ]
 
 
