@@ -1,35 +1,34 @@
 // attn_fwd.hip -- 1.5-entmax attention forward on gfx950.
 //
-// Two kernels per call, both one workgroup per 128 query rows of a head:
+// Three kernels per call, each one workgroup per 128 query rows of a head:
 //
-// fwd_tau  (threshold and block mask)
-//   sweep 1  over the tiles the mask mode allows: S^T = K Q^T on MFMA; per
-//            row the maximum and the eight largest tile maxima; per (row
-//            half, tile) the largest score.
-//   bound    tau_lo = the exact threshold of those tile maxima.  Adding
-//            scores to a row only raises its threshold (every term of the
-//            normaliser is non-negative), so tau_lo <= tau, and it also
-//            clears the bracket end max - 2 of "AdaSplash-2: Faster
+// fwd_stats  one sweep over the tiles the mask mode allows: S^T = K Q^T on
+//            MFMA; per row the maximum and the sixteen largest tile maxima
+//            (four per lane half and key parity); per (row half, tile) the
+//            largest score.  tau_lo = the exact threshold of those tile
+//            maxima.  Adding scores to a row only raises its threshold (every
+//            term of the normaliser is non-negative), so tau_lo <= tau, and
+//            it also clears the bracket end max - 2 of "AdaSplash-2: Faster
 //            Differentiable Sparse Attention" sec. 2.4 (score units).
-//   sweep 2  over the tiles whose largest score beats tau_lo: every score
-//            s > tau_lo is appended to its row's candidate list in LDS.
+// fwd_solve  collect: over the tiles whose largest score beats tau_lo, every
+//            score s > tau_lo is appended to its row's candidate list.
 //            Nothing at or below tau_lo can carry weight, so the row's
 //            threshold is the threshold of its candidates alone.
-//   solve    per row, Halley-bisection on the candidates (the hybrid solver
-//            of "AdaSplash: Adaptive Sparse Flash Attention", summary,
-//            Approach) with an exact finish: once tau lies below the support
-//            the normaliser is a quadratic in tau over {s > tau} (S0/S1/S2 of
-//            AdaSplash-2 appendix C.3).  Sums are fp64.
-//   mask     a 64x64 tile is non-null iff one of its candidates exceeds its
-//            row's tau (packed 32 tiles per word, AdaSplash-2 appendix C.4).
-//   fallback rows whose candidates overflow the list are refined by
-//            Halley-bisection sweeps over all their tiles, then a sweep
-//            marks their tiles.
-// fwd_out  (output)
-//   walks only the set mask bits of its two 64-row blocks (find-first-set
-//   over the packed words, AdaSplash-2 sec. 3.3 phase 4), recomputes S,
-//   A = [(S - tau)/2]_+^2 and accumulates O = A V on MFMA (A split into bf16
-//   hi + lo so the product keeps ~16 bits of A).
+//            solve: per row, Newton steps from below on the candidates
+//            (f(t) = sum [(s - t)/2]_+^2 - 1 is convex and decreasing) with a
+//            bisection guard and an exact finish: once tau lies below the
+//            support the normaliser is a quadratic in tau over {s > tau}
+//            (S0/S1/S2 of AdaSplash-2 appendix C.3).  Sums are fp64.
+//            mask: a 64x64 tile is non-null iff one of its candidates exceeds
+//            its row's tau (packed 32 tiles per word, AdaSplash-2 appendix C.4).
+//            fallback: rows whose candidates overflow the list are collected
+//            again with a tighter bound, then refined by Halley-bisection
+//            sweeps over all their tiles, then a sweep marks their tiles.
+// fwd_out    walks only the set mask bits of its two 64-row blocks
+//            (find-first-set over the packed words, AdaSplash-2 sec. 3.3
+//            phase 4), recomputes S, A = [(S - tau)/2]_+^2 and accumulates
+//            O = A V on MFMA (bf16 inputs: A and V in fp16, the pages' own
+//            casts, with a bf16 hi + lo redo where V leaves the fp16 range).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
