@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -159,8 +161,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     const int n = nlist_s;
 
-    // Walk the list; fn(J, Kt, Vt, KPVt) for each tile flagged for this half.
-    auto walk = [&](auto fn) {
+    // Walk the list; fn(J, Kt, Vt, KPVt) for each tile flagged for this half
+    // (K in the PV layout staged only when the pass takes the product with K).
+    auto walk = [&](auto with_pv, auto fn) {
         const int steps = (n + TPS - 1) / TPS;
         for (int st = 0; st < steps; ++st) {
             __syncthreads();
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
                 T* base = lds + u * 3 * BLK;
                 stage_score<T, D>(base, Kh, c0, p.L);
                 stage_score<T, D>(base + BLK, Vh, c0, p.L);
-                stage_pv<T, D>(base + 2 * BLK, Kh, c0, p.L);
+                if constexpr (decltype(with_pv)::value) stage_pv<T, D>(base + 2 * BLK, Kh, c0, p.L);
             }
             __syncthreads();
             const int u = (TPS == 2) ? kh : 0;
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
 
     // ---- pass 1: delta_i = sum g dA / sum g  (2g used on both sides)
     float num[2] = {0.f, 0.f}, den[2] = {0.f, 0.f};
-    walk([&](int J, int cls, const T* Kt, const T* Vt, const T*) {
+    walk(std::false_type{}, [&](int J, int cls, const T* Kt, const T* Vt, const T*) {
         f32x16 s[2][2], da[2][2];
         O::scores(s, Kt, qop);
         if (cls == kPartial) apply_mask(s, J, R0, g);
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oa.o[db][qb][i] = 0.f;
-    walk([&](int J, int cls, const T* Kt, const T* Vt, const T* KPVt) {
+    walk(std::true_type{}, [&](int J, int cls, const T* Kt, const T* Vt, const T* KPVt) {
         f32x16 s[2][2], da[2][2];
         O::scores(s, Kt, qop);
         if (cls == kPartial) apply_mask(s, J, R0, g);
@@ -347,17 +350,18 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
     __syncthreads();
     const int n = nlist_s;
 
-    // Stage each listed tile (K and V in the score layout, K in the PV
-    // layout) and call fn(J, cls, Kt, Vt, KPVt) when it is non-null for this
-    // wave's 64-row block and not masked out for its rows.
-    auto walk = [&](auto fn) {
+    // Stage each listed tile (K and V in the score layout, and K in the PV
+    // layout when the pass takes the product with K) and call fn(J, cls, Kt,
+    // Vt, KPVt) when it is non-null for this wave's 64-row block and not
+    // masked out for its rows.
+    auto walk = [&](auto with_pv, auto fn) {
         for (int e = 0; e < n; ++e) {
             __syncthreads();
             const int ent = list[e];
             const int J = ent & 0xfff;
             stage_score<T, D>(lds, Kh, J * kBC, p.L);
             stage_score<T, D>(lds + BLK, Vh, J * kBC, p.L);
-            stage_pv<T, D>(lds + 2 * BLK, Kh, J * kBC, p.L);
+            if constexpr (decltype(with_pv)::value) stage_pv<T, D>(lds + 2 * BLK, Kh, J * kBC, p.L);
             __syncthreads();
             if (!((ent >> (12 + half)) & 1)) continue;
             const int cls = block_class(R0, 32, J * kBC, kBC, g);
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
 
     // ---- pass 1: delta_i = sum g dA / sum g
     float num = 0.f, den = 0.f;
-    walk([&](int J, int cls, const T* Kt, const T* Vt, const T*) {
+    walk(std::false_type{}, [&](int J, int cls, const T* Kt, const T* Vt, const T*) {
         f32x16 s[2][1], da[2][1];
         O::template scores<1>(s, Kt, qop);
         if (cls == kPartial) apply_mask<1>(s, J, R0, g);
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oa.o[db][0][i] = 0.f;
-    walk([&](int J, int cls, const T* Kt, const T* Vt, const T* KPVt) {
+    walk(std::true_type{}, [&](int J, int cls, const T* Kt, const T* Vt, const T* KPVt) {
         f32x16 s[2][1], da[2][1];
         O::template scores<1>(s, Kt, qop);
         if (cls == kPartial) apply_mask<1>(s, J, R0, g);
