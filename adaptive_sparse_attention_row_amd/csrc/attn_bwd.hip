@@ -51,6 +51,15 @@ struct BwdParams {
     int gen;      // alpha != 1.5
 };
 
+// The kernels are instantiated per alpha class (GEN: alpha != 1.5), and
+// by_alpha<GEN>(f) hands f that class as a type.  A runtime test inside the
+// per-element loops compiled to a branch per element; both paths in one
+// instance cost registers (spills at d = 128).
+template <bool GEN, class F>
+__device__ __forceinline__ void by_alpha(F f) {
+    f(std::integral_constant<bool, GEN>{});
+}
+
 // Stage one 64-row tile of X (rows r0 .., zero past L) into LDS, in the
 // score-operand layout or the PV-operand layout.
 template <typename T, int D>
@@ -69,6 +78,28 @@ __device__ __forceinline__ void stage_score(T* dst, const T* Xh, int r0, int L) 
         if (c < O::kChunks) O::store_k_chunk(dst, c, v[i]);
     }
 }
+
+// The same staging split in two, so that a tile's loads can be in flight
+// while the previous tile is in use: its chunks in registers, then in LDS.
+template <typename T, int D>
+struct ScoreTileRegs {
+    static constexpr int kIt = (Ops<T, D>::kChunks + kNT - 1) / kNT;
+    u32x4 v[kIt];
+    __device__ __forceinline__ void load(const T* Xh, int r0, int L) {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int c = threadIdx.x + i * kNT;
+            if (c < Ops<T, D>::kChunks) v[i] = Ops<T, D>::load_k_chunk(Xh, r0, L, c);
+        }
+    }
+    __device__ __forceinline__ void store(T* dst) const {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int c = threadIdx.x + i * kNT;
+            if (c < Ops<T, D>::kChunks) Ops<T, D>::store_k_chunk(dst, c, v[i]);
+        }
+    }
+};
 
 template <typename T, int D>
 __device__ __forceinline__ void stage_pv(T* dst, const T* Xh, int r0, int L) {
@@ -110,7 +141,7 @@ struct DqCfg {
 };
 
 // ------------------------------------------------------------ dQ kernel
-template <typename T, int D>
+template <typename T, int D, bool GEN>
 __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
     using O = Ops<T, D>;
     constexpr int TPS = DqCfg<T, D>::kTps;
@@ -199,17 +230,19 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
         O::scores(s, Kt, qop);
         if (cls == kPartial) apply_mask(s, J, R0, g);
         O::scores(da, Vt, dop);
+        by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float sv = s[kb][qb][r] * p.scale;
-                    const float dd = p.gen ? 2.0f * p.am.g(sv, tq[qb]) : fmaxf(sv - tq[qb], 0.0f);
-                    num[qb] += dd * da[kb][qb][r];
-                    den[qb] += dd;
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const float sv = s[kb][qb][r] * p.scale;
+                        const float dd = gen_c ? 2.0f * p.am.g(sv, tq[qb]) : fmaxf(sv - tq[qb], 0.0f);
+                        num[qb] += dd * da[kb][qb][r];
+                        den[qb] += dd;
+                    }
+        });
     });
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -245,16 +278,18 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
         O::scores(s, Kt, qop);
         if (cls == kPartial) apply_mask(s, J, R0, g);
         O::scores(da, Vt, dop);
+        by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float sv = s[kb][qb][r] * p.scale;
-                    const float dd = p.gen ? 2.0f * p.am.g(sv, tq[qb]) : fmaxf(sv - tq[qb], 0.0f);
-                    s[kb][qb][r] = dd * (da[kb][qb][r] - dl[qb]);
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const float sv = s[kb][qb][r] * p.scale;
+                        const float dd = gen_c ? 2.0f * p.am.g(sv, tq[qb]) : fmaxf(sv - tq[qb], 0.0f);
+                        s[kb][qb][r] = dd * (da[kb][qb][r] - dl[qb]);
+                    }
+        });
         const bool on[2] = {true, true};
         O::pv(oa, KPVt, s, on);
     });
@@ -307,7 +342,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
 #ifndef ENTMAX_BWD_DQ32
 #define ENTMAX_BWD_DQ32 1
 #endif
-template <int D>
+template <int D, bool GEN>
 __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
     using T = __bf16;
     using O = Ops<T, D>;
@@ -354,15 +389,35 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
     // layout when the pass takes the product with K) and call fn(J, cls, Kt,
     // Vt, KPVt) when it is non-null for this wave's 64-row block and not
     // masked out for its rows.
+    // The score-layout K and V of the next tile are loaded into registers
+    // while the current one is in use, except in the dQ pass at d = 128,
+    // where those registers are not free (the compiler spills).
     auto walk = [&](auto with_pv, auto fn) {
+        constexpr bool kPv = decltype(with_pv)::value;
+        constexpr bool kPf = !kPv || D == 64;
+        ScoreTileRegs<T, D> rk, rv;
+        if (kPf && n > 0) {
+            rk.load(Kh, (list[0] & 0xfff) * kBC, p.L);
+            rv.load(Vh, (list[0] & 0xfff) * kBC, p.L);
+        }
         for (int e = 0; e < n; ++e) {
             __syncthreads();
             const int ent = list[e];
             const int J = ent & 0xfff;
-            stage_score<T, D>(lds, Kh, J * kBC, p.L);
-            stage_score<T, D>(lds + BLK, Vh, J * kBC, p.L);
-            if constexpr (decltype(with_pv)::value) stage_pv<T, D>(lds + 2 * BLK, Kh, J * kBC, p.L);
+            if constexpr (kPf) {
+                rk.store(lds);
+                rv.store(lds + BLK);
+            } else {
+                stage_score<T, D>(lds, Kh, J * kBC, p.L);
+                stage_score<T, D>(lds + BLK, Vh, J * kBC, p.L);
+            }
+            if constexpr (kPv) stage_pv<T, D>(lds + 2 * BLK, Kh, J * kBC, p.L);
             __syncthreads();
+            if (kPf && e + 1 < n) {
+                const int J1 = list[e + 1] & 0xfff;
+                rk.load(Kh, J1 * kBC, p.L);
+                rv.load(Vh, J1 * kBC, p.L);
+            }
             if (!((ent >> (12 + half)) & 1)) continue;
             const int cls = block_class(R0, 32, J * kBC, kBC, g);
             if (cls == kSkip) continue;
@@ -371,7 +426,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
         __syncthreads();
     };
     // 2g (so that the factor cancels in delta), the derivative of A in S
-    auto dd_of = [&](float sv) { return p.gen ? 2.0f * p.am.g(sv, tq) : fmaxf(sv - tq, 0.0f); };
+    auto dd_of = [&](auto gen_c, float sv) { return gen_c ? 2.0f * p.am.g(sv, tq) : fmaxf(sv - tq, 0.0f); };
 
     // ---- pass 1: delta_i = sum g dA / sum g
     float num = 0.f, den = 0.f;
@@ -380,14 +435,16 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
         O::template scores<1>(s, Kt, qop);
         if (cls == kPartial) apply_mask<1>(s, J, R0, g);
         O::template scores<1>(da, Vt, dop);
+        by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float dd = dd_of(s[kb][0][r] * p.scale);
-                num += dd * da[kb][0][r];
-                den += dd;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const float dd = dd_of(gen_c, s[kb][0][r] * p.scale);
+                    num += dd * da[kb][0][r];
+                    den += dd;
+                }
+        });
     });
     num += __shfl_xor(num, 32, kWave);
     den += __shfl_xor(den, 32, kWave);
@@ -405,10 +462,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
         O::template scores<1>(s, Kt, qop);
         if (cls == kPartial) apply_mask<1>(s, J, R0, g);
         O::template scores<1>(da, Vt, dop);
+        by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][0][r] = dd_of(s[kb][0][r] * p.scale) * (da[kb][0][r] - dl);
+                for (int r = 0; r < 16; ++r) s[kb][0][r] = dd_of(gen_c, s[kb][0][r] * p.scale) * (da[kb][0][r] - dl);
+        });
         const bool on[2] = {true, true};
         O::template pv<1>(oa, KPVt, s, on);
     });
@@ -445,7 +504,7 @@ struct DkvCfg {
 // pair recomputes S once more but each half holds one accumulator and one
 // set of operands, which fits two workgroups per CU (bf16) where the joint
 // kernel runs one.
-template <typename T, int D, int PART>
+template <typename T, int D, int PART, bool GEN>
 __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdParams p) {
     using O = Ops<T, D>;
     constexpr bool kDV = PART != 2, kDK = PART != 1;
@@ -511,10 +570,15 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
         const int I = ent & 0xfff;
         const int i0 = I * 64;
         __syncthreads();
+        // one tile at a time (a scheduling barrier after each): the loads of
+        // all of them at once need more registers than the dK sweep has free
         stage_score<T, D>(Qt, Qh, i0, p.L);
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (kDK) {
             stage_score<T, D>(dOt, dOh, i0, p.L);
+            __builtin_amdgcn_sched_barrier(0);
             stage_pv<T, D>(QPVt, Qh, i0, p.L);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (kDV) stage_pv<T, D>(dOPVt, dOh, i0, p.L);
         if (t < 64) {
@@ -533,38 +597,42 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
         if constexpr (kDV) {
             // 4A (dd^2 with dd = 2g at alpha = 1.5), into dV
             f32x16 a4[2][NBK];
+            by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int cb = 0; cb < NBK; ++cb)
+                    for (int cb = 0; cb < NBK; ++cb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float sv = s[kb][cb][r] * p.scale;
-                        const float tr = tau_s[kb * 32 + key_of_reg(r, h)];
-                        if (p.gen) {
-                            a4[kb][cb][r] = 4.0f * p.am.p(sv, tr);
-                        } else {
-                            const float dd = fmaxf(sv - tr, 0.0f);
-                            a4[kb][cb][r] = dd * dd;
+                        for (int r = 0; r < 16; ++r) {
+                            const float sv = s[kb][cb][r] * p.scale;
+                            const float tr = tau_s[kb * 32 + key_of_reg(r, h)];
+                            if constexpr (decltype(gen_c)::value) {
+                                a4[kb][cb][r] = 4.0f * p.am.p(sv, tr);
+                            } else {
+                                const float dd = fmaxf(sv - tr, 0.0f);
+                                a4[kb][cb][r] = dd * dd;
+                            }
                         }
-                    }
+            });
             O::pv(dva, dOPVt, a4, on);
         }
         if constexpr (kDK) {
             O::scores(da, dOt, vop);
             // 2 dS = dd (dA - delta) in place of S, into dK
+            by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int cb = 0; cb < NBK; ++cb)
+                    for (int cb = 0; cb < NBK; ++cb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int qi = kb * 32 + key_of_reg(r, h);
-                        const float sv = s[kb][cb][r] * p.scale;
-                        const float tr = tau_s[qi];
-                        const float dd = p.gen ? 2.0f * p.am.g(sv, tr) : fmaxf(sv - tr, 0.0f);
-                        s[kb][cb][r] = dd * (da[kb][cb][r] - del_s[qi]);
-                    }
+                        for (int r = 0; r < 16; ++r) {
+                            const int qi = kb * 32 + key_of_reg(r, h);
+                            const float sv = s[kb][cb][r] * p.scale;
+                            const float tr = tau_s[qi];
+                            const float dd = gen_c ? 2.0f * p.am.g(sv, tr) : fmaxf(sv - tr, 0.0f);
+                            s[kb][cb][r] = dd * (da[kb][cb][r] - del_s[qi]);
+                        }
+            });
             O::pv(dka, QPVt, s, on);
         }
     }
@@ -591,23 +659,28 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
         }
 }
 
-template <typename T, int D>
-hipError_t launch_bwd_typed(const BwdParams& bp, hipStream_t stream) {
+template <typename T, int D, bool GEN>
+hipError_t launch_bwd_class(const BwdParams& bp, hipStream_t stream) {
     if constexpr (sizeof(T) == 2 && ENTMAX_BWD_DQ32)
-        hipLaunchKernelGGL((bwd_dq32_kernel<D>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
+        hipLaunchKernelGGL((bwd_dq32_kernel<D, GEN>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, GEN>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (sizeof(T) == 2 && ENTMAX_BWD_DKDV_SPLIT) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 1>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 1, GEN>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 2>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 2, GEN>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
     } else {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 0>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 0, GEN>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
     }
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_typed(const BwdParams& bp, hipStream_t stream) {
+    return bp.gen ? launch_bwd_class<T, D, true>(bp, stream) : launch_bwd_class<T, D, false>(bp, stream);
 }
 
 }  // namespace
