@@ -118,6 +118,26 @@ __device__ __forceinline__ void stage_pv(T* dst, const T* Xh, int r0, int L) {
     }
 }
 
+template <typename T, int D>
+struct PvTileRegs {
+    static constexpr int kIt = (Ops<T, D>::kVUnits + kNT - 1) / kNT;
+    typename Ops<T, D>::VRegs v[kIt];
+    __device__ __forceinline__ void load(const T* Xh, int r0, int L) {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int u = threadIdx.x + i * kNT;
+            if (u < Ops<T, D>::kVUnits) v[i] = Ops<T, D>::load_v_unit(Xh, r0, L, u);
+        }
+    }
+    __device__ __forceinline__ void store(T* dst) const {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int u = threadIdx.x + i * kNT;
+            if (u < Ops<T, D>::kVUnits) Ops<T, D>::store_v_unit(dst, u, v[i]);
+        }
+    }
+};
+
 template <class FlagsOf>
 __device__ __forceinline__ int build_list16(uint16_t* list, int n_items, FlagsOf flags_of) {
     const int l = lane_id();
@@ -565,28 +585,43 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
     T* QPVt = lds + 2 * BLK;
     T* dOPVt = lds + 3 * BLK;
 
+    // The dV sweep (PART 1) loads the next query tile's Q and dO into
+    // registers while the current one is in use; the other sweeps have no
+    // registers to spare for it and stage synchronously.
+    constexpr bool kPf = PART == 1;
+    ScoreTileRegs<T, D> rq;
+    PvTileRegs<T, D> rdo;
+    if (kPf && n > 0) {
+        rq.load(Qh, (list[0] & 0xfff) * 64, p.L);
+        rdo.load(dOh, (list[0] & 0xfff) * 64, p.L);
+    }
     for (int e = 0; e < n; ++e) {
         const int ent = list[e];
         const int I = ent & 0xfff;
         const int i0 = I * 64;
         __syncthreads();
-        // one tile at a time (a scheduling barrier after each): the loads of
-        // all of them at once need more registers than the dK sweep has free
-        stage_score<T, D>(Qt, Qh, i0, p.L);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kDK) {
-            stage_score<T, D>(dOt, dOh, i0, p.L);
-            __builtin_amdgcn_sched_barrier(0);
-            stage_pv<T, D>(QPVt, Qh, i0, p.L);
-            __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kPf) {
+            rq.store(Qt);
+            rdo.store(dOPVt);
+        } else {
+            stage_score<T, D>(Qt, Qh, i0, p.L);
+            if constexpr (kDK) {
+                stage_score<T, D>(dOt, dOh, i0, p.L);
+                stage_pv<T, D>(QPVt, Qh, i0, p.L);
+            }
+            if constexpr (kDV) stage_pv<T, D>(dOPVt, dOh, i0, p.L);
         }
-        if constexpr (kDV) stage_pv<T, D>(dOPVt, dOh, i0, p.L);
         if (t < 64) {
             const int row = i0 + t;
             tau_s[t] = (row < p.L) ? p.tau[(size_t)bh * p.L + row] : __builtin_inff();
             if constexpr (kDK) del_s[t] = (row < p.L) ? p.delta[(size_t)bh * p.L + row] : 0.f;
         }
         __syncthreads();
+        if (kPf && e + 1 < n) {
+            const int i1 = (list[e + 1] & 0xfff) * 64;
+            rq.load(Qh, i1, p.L);
+            rdo.load(dOh, i1, p.L);
+        }
         if (!((ent >> (12 + w)) & 1)) continue;
         const int cls = block_class(i0, 64, cw, KW, g);
         if (cls == kSkip) continue;
