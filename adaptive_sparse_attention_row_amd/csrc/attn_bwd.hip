@@ -11,14 +11,19 @@
 // Both kernels walk the forward's block mask, so null 64x64 tiles cost
 // nothing (AdaSplash-2 uses M for dQ and its transpose for dK, dV).
 //
-// bwd_dq    one workgroup per 128 query rows (the forward's layout: lanes
-//           are queries).  Pass 1 over the row's non-null tiles: S^T = K Q^T
-//           and dA^T = V dO^T on MFMA, accumulating sum g dA and sum g per
-//           row -> delta (also written for the other kernel).  Pass 2:
-//           dS, then dQ^T += K^T dS^T on MFMA.
-// bwd_dkdv  one workgroup per 128 (d = 128) or 256 (d = 64) keys; lanes are
+// bwd_dq32  (bf16) one workgroup per 128 query rows, each wave 32 of them
+//           and every listed tile of the block (lanes are queries).  Pass 1
+//           over the rows' non-null tiles: S^T = K Q^T and dA^T = V dO^T on
+//           MFMA, accumulating sum g dA and sum g per row -> delta (also
+//           written for the dK sweep).  Pass 2: dS, then dQ^T += K^T dS^T.
+// bwd_dq    (fp32) the same two passes with 64 rows per wave and the key
+//           tiles split between wave pairs.
+// bwd_dkdv  one workgroup per 128 keys (fp32 at d = 64: 256), lanes are
 //           keys.  For every query tile of the mask column: S = Q K^T and
-//           dA = dO V^T on MFMA, then dV^T += dO^T A and dK^T += Q^T dS.
+//           dA = dO V^T on MFMA, then dV^T += dO^T A and dK^T += Q^T dS;
+//           for bf16 as two sweeps, dV (PART 1) then dK (PART 2), each
+//           holding one accumulator and operand set.
+// Every kernel has one instance per alpha class (GEN: alpha != 1.5).
 // Weights fed to MFMA (A, dS) are split into bf16 hi + lo; accumulation is
 // fp32; all gradients are written in fp32.
 #include <hip/hip_runtime.h>
