@@ -154,3 +154,28 @@ def test_sparse_rows(env, orc):
     inp = gen(1, 2, 513, 64, "bf16", seed=31, q_std=4.0)
     dq, dk, dv = gpu_fwd_bwd(api, torch, inp, 0.125, 0, 0)
     check_heads(orc, inp, 0.125, 0, 0, dq, dk, dv, [0, 1], "sparse")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_empty_mask_columns(env, orc, d):
+    """Every query attends only among keys 0..7, so the mask has one non-null
+    tile column: the dK/dV workgroups of the other keys find no query tile
+    (their lists are empty) and must write zeros, and the dQ walk sees one
+    tile per row block."""
+    api, torch = env
+    import torch as T
+    L = 512
+    inp = gen(1, 2, L, d, "bf16", seed=11 + d)
+    g = T.Generator().manual_seed(5 + d)
+    u = T.randn(d, generator=g)
+    u = u / u.norm()
+    for key in ("q", "k"):
+        x = inp[key].float() * 0.05
+        x[:, :, :, :] += 8.0 * u if key == "q" else 0.0
+        if key == "k":
+            x[:, :, :8, :] += 8.0 * u + 0.3 * T.randn(1, 2, 8, d, generator=g)
+        inp[key] = x.to(T.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = gpu_fwd_bwd(api, torch, inp, scale, 0, 0)
+    assert np.all(dk[:, :, 64:] == 0) and np.all(dv[:, :, 64:] == 0)
+    check_heads(orc, inp, scale, 0, 0, dq, dk, dv, [0, 1], f"empty columns d={d}")
