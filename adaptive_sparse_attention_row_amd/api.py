@@ -17,8 +17,11 @@ LIB_PATH = os.path.join(PKG, "libentmax.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_ALPHA, ERR_DTYPE, ERR_MASK, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_ARG = range(10)
 MASK_NONE, MASK_CAUSAL, MASK_WINDOW_SINK = 0, 1, 2
 F32, BF16 = 0, 1
-OPT_CANDIDATE_CAP = 1
-OPT_ROW_HISTOGRAM = 2
+
+
+class Options(ctypes.Structure):
+    """entmax_options of include/entmax.h (per-call; all zero = defaults)."""
+    _fields_ = [("candidate_cap", ctypes.c_int), ("row_plain_bracket", ctypes.c_int)]
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -66,8 +69,15 @@ def lib() -> ctypes.CDLL:
     L.entmax_attn_score_stats.argtypes = [P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P, sz, P]
     L.entmax_attn_output.restype = i32
     L.entmax_attn_output.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P]
-    L.entmax_set_option.restype = i32
-    L.entmax_set_option.argtypes = [i32, i32]
+    OP = ctypes.POINTER(Options)
+    L.entmax_tau_rows_ex.restype = i32
+    L.entmax_tau_rows_ex.argtypes = [P, P, P, i64, i64, i64, f32, OP, P]
+    L.entmax_attn_fwd_ex.restype = i32
+    L.entmax_attn_fwd_ex.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, i32,
+                                     i32, i32, P, sz, OP, P]
+    L.entmax_attn_threshold_ex.restype = i32
+    L.entmax_attn_threshold_ex.argtypes = [P, P, P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P, sz,
+                                           OP, P]
     L.entmax_attn_decode_workspace.restype = sz
     L.entmax_attn_decode_workspace.argtypes = [i32] * 7
     L.entmax_attn_decode.restype = i32
@@ -101,17 +111,17 @@ def tile_shape(d: int, dtype: int = BF16) -> tuple[int, int]:
     return br.value, bc.value
 
 
-def set_option(option: int, value: int) -> int:
-    r = lib().entmax_set_option(option, value)
-    if r < 0:
-        raise EntmaxError("entmax_set_option", -r)
-    return r
+def _opts(candidate_cap: int = 0, row_plain_bracket: bool = False):
+    """A per-call options struct, or None when every field is at its default."""
+    if candidate_cap == 0 and not row_plain_bracket:
+        return None
+    return ctypes.byref(Options(int(candidate_cap), 1 if row_plain_bracket else 0))
 
 
-def tau_rows(S, want_p: bool = True, P=None, tau=None, alpha: float = 1.5):
+def tau_rows(S, want_p: bool = True, P=None, tau=None, alpha: float = 1.5, row_plain_bracket: bool = False):
     """Row-wise alpha-entmax (alpha in (1, 2], default 1.5) of a [rows, cols]
     fp32 CUDA tensor (row stride may exceed cols).  Returns (tau [rows],
-    P [rows, cols] or None)."""
+    P [rows, cols] or None).  row_plain_bracket: see entmax_options."""
     import torch
     if not S.is_cuda or S.dtype != torch.float32 or S.dim() != 2 or S.stride(1) != 1:
         raise ValueError("S must be a 2-D fp32 CUDA tensor with unit column stride")
@@ -123,8 +133,8 @@ def tau_rows(S, want_p: bool = True, P=None, tau=None, alpha: float = 1.5):
         tau = torch.empty(rows, device=S.device, dtype=torch.float32)
     if P is not None and P.stride() != (ld, 1) and rows > 1:
         raise ValueError("P must share S's row stride")
-    st = lib().entmax_tau_rows(S.data_ptr(), _dev_ptr(P), tau.data_ptr(), rows, cols, ld,
-                               float(alpha), _stream(S.device))
+    st = lib().entmax_tau_rows_ex(S.data_ptr(), _dev_ptr(P), tau.data_ptr(), rows, cols, ld,
+                                  float(alpha), _opts(0, row_plain_bracket), _stream(S.device))
     _check("entmax_tau_rows", st)
     return tau, P
 
@@ -145,11 +155,11 @@ def mask_shape(B: int, H: int, L: int, d: int, dtype: int = BF16) -> tuple[int, 
 
 
 def attn_fwd(q, k, v, scale: Optional[float] = None, mask: int = MASK_NONE, window: int = 0,
-             want_block_mask: bool = True, out=None, alpha: float = 1.5):
+             want_block_mask: bool = True, out=None, alpha: float = 1.5, candidate_cap: int = 0):
     """alpha-entmax attention forward (alpha in (1, 2], default 1.5).  q, k,
     v: [B, H, L, d] CUDA tensors (bf16 or fp32, contiguous).  Returns (O fp32,
     tau fp32 [B, H, L], block_mask int32 view of the packed uint32 mask, or
-    None)."""
+    None).  candidate_cap: see entmax_options (0: the default)."""
     import torch
     B, H, L, d = q.shape
     for t in (q, k, v):
@@ -165,15 +175,16 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, mask: int = MASK_NONE, wind
         bm = torch.empty(mask_shape(B, H, L, d, dt), device=q.device, dtype=torch.int32)
     ws_bytes = lib().entmax_attn_fwd_workspace(B, H, L, d, dt, mask, window)
     ws = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
-    st = lib().entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(),
-                               tau.data_ptr(), _dev_ptr(bm), B, H, L, d, float(scale), float(alpha),
-                               dt, mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
+    st = lib().entmax_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(),
+                                  tau.data_ptr(), _dev_ptr(bm), B, H, L, d, float(scale), float(alpha),
+                                  dt, mask, window, _dev_ptr(ws), ws_bytes, _opts(candidate_cap),
+                                  _stream(q.device))
     _check("entmax_attn_fwd", st)
     return O, tau, bm
 
 
 def attn_threshold(q, k, scale: Optional[float] = None, mask: int = MASK_NONE, window: int = 0,
-                   tau=None, block_mask=None, workspace=None, alpha: float = 1.5):
+                   tau=None, block_mask=None, workspace=None, alpha: float = 1.5, candidate_cap: int = 0):
     """Phases 1-3 only: returns (tau fp32 [B, H, L], packed block mask)."""
     import torch
     B, H, L, d = q.shape
@@ -187,9 +198,10 @@ def attn_threshold(q, k, scale: Optional[float] = None, mask: int = MASK_NONE, w
     ws_bytes = lib().entmax_attn_threshold_workspace(B, H, L, d, dt, mask, window)
     if workspace is None:
         workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
-    st = lib().entmax_attn_threshold(q.data_ptr(), k.data_ptr(), tau.data_ptr(), block_mask.data_ptr(),
-                                     B, H, L, d, float(scale), float(alpha), dt, mask, window,
-                                     workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    st = lib().entmax_attn_threshold_ex(q.data_ptr(), k.data_ptr(), tau.data_ptr(), block_mask.data_ptr(),
+                                        B, H, L, d, float(scale), float(alpha), dt, mask, window,
+                                        workspace.data_ptr(), workspace.numel(), _opts(candidate_cap),
+                                        _stream(q.device))
     _check("entmax_attn_threshold", st)
     return tau, block_mask
 

@@ -53,8 +53,9 @@ struct FwdParams {
     uint32_t* mask;   // [BH][Tr64][Wd]
     float* rowstat;   // workspace [BH][L][2]: row max, tau_lo (score units)
     float* umax;      // workspace [BH][Tr64][Tc]: largest raw score per (64-row block, tile)
-    float* cval;      // workspace [BH * nQ][kCandCap][128]: candidate scores, slot-major per row block
-    uint16_t* cjt;    // workspace, same shape: position of each candidate's tile in the tile list
+    u32x2* clist;     // workspace [BH * nQ][kCandCap][128]: candidates (score bits, key index), slot-major per row block
+    int* ostate;      // workspace [BH * nQ]: 1 where the solve kernel wrote O itself (null: the output kernel writes all)
+    int gather;       // the solve kernel writes O from the candidate lists where it can
     int BH, L, mode, W, nQ, Tc, Tr64, Wd;
     float scale;
     int cap;
@@ -62,7 +63,7 @@ struct FwdParams {
     int gen;      // alpha != 1.5: Newton solves and pow weights
 };
 
-// Candidate slots per row in the workspace lists.
+// Candidate slots per row (all four sub-lists, LDS and workspace).
 constexpr int kCandCap = 128;
 
 // ------------------------------------------------------------ tile lists
@@ -185,7 +186,7 @@ __device__ __forceinline__ void sweep(const uint16_t* list, int n, const T* Kh, 
 // read after a direct load wait for all loads in flight; reading a stage
 // before issuing the next loads, or hiding the reads from it, measured no
 // faster here, so the plain order stays.)
-template <typename T, int D, int S, bool PER_QB = false, class Fn>
+template <typename T, int D, int S, class Fn>
 __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T* Kh, T* ring,
                                            const typename Ops<T, D>::template QOp<2>& qop, int R0,
                                            const Geom& g, Fn fn) {
@@ -235,26 +236,10 @@ __device__ __forceinline__ void ring_sweep(const uint16_t* list, int n, const T*
         const int cls = tile_of(pp, e, J);
         if (cls != kSkip) {
             const T* Kt = ring + (pp % S) * kStage + kh * DMA::kTileElems;
-            if constexpr (PER_QB) {
-                // one 32-row block at a time: half the accumulators live, the
-                // tile's operands read twice
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    typename O::template QOp<1> q1;
-                    constexpr int kQs = sizeof(q1.q[0]) / sizeof(q1.q[0][0]);
-#pragma unroll
-                    for (int s = 0; s < kQs; ++s) q1.q[0][s] = qop.q[qb][s];
-                    f32x16 acc[2][1];
-                    O::template scores<1>(acc, Kt, q1);
-                    if (cls == kPartial) apply_mask<1>(acc, J, R0 + 32 * qb, g);
-                    fn(J, e, qb, acc);
-                }
-            } else {
-                f32x16 acc[2][2];
-                O::scores(acc, Kt, qop);
-                if (cls == kPartial) apply_mask(acc, J, R0, g);
-                fn(J, e, acc);
-            }
+            f32x16 acc[2][2];
+            O::scores(acc, Kt, qop);
+            if (cls == kPartial) apply_mask(acc, J, R0, g);
+            fn(J, e, acc);
         }
     }
     __syncthreads();
@@ -427,56 +412,81 @@ __device__ __forceinline__ void sort_desc(float (&x)[N]) {
             }
 }
 
-// Candidate slots per row kept in LDS; further slots live in the workspace.
-#ifndef ENTMAX_LDS_CAND
-#define ENTMAX_LDS_CAND 48
-#endif
-constexpr int kLdsCand = ENTMAX_LDS_CAND;
+// ------------------------------------------------------------ candidate lists
+// A row's candidates live in four sub-lists, one for each (key-parity wave
+// kh, lane half h) that sweeps the row: entry c of sub-list q = 2 kh + h
+// sits in slot 4c + q of the workspace, slot-major over the 128 rows of the
+// workgroup, as (score bits, key index within the head).  Each sub-list is
+// written by one lane only, in the order that lane meets its scores (tile-list
+// order, then register order): no atomics, and the lists -- and every sum
+// taken over them in list order -- are the same on every call.
+constexpr int kCapQ = kCandCap / 4;     // entries per sub-list
 
-// A row's candidate list: entry i at lds[i * kBR] for i < kLdsCand, else at
-// glob[i * kBR] (both slot-major over the 128 rows of a workgroup, so the
-// lanes of a wave touch consecutive words).  Two lanes share a row: the lane
-// with parity h takes entries start, start + 2, ... (start = h at first).
+// The entries read by lane half h of the pair of lanes that solves a row:
+// sub-list h (wave kh = 0), then sub-list 2 + h (wave kh = 1).
 struct CandSrc {
-    const float* lds;
-    const float* glob;
-    int n, start;
-    __device__ __forceinline__ float at(int i) const {
-        return i < kLdsCand ? lds[i * kBR] : glob[(size_t)i * kBR];
+    const u32x2* glob;  // clist + row
+    int n0, n1;         // entries of the two sub-lists
+    int h;
+    __device__ __forceinline__ int n() const { return n0 + n1; }
+    __device__ __forceinline__ int slot(int i) const { return i < n0 ? 4 * i + h : 4 * (i - n0) + 2 + h; }
+    __device__ __forceinline__ u32x2 entry(int i) const { return glob[(size_t)slot(i) * kBR]; }
+    __device__ __forceinline__ float at(int i) const { return __builtin_bit_cast(float, entry(i)[0]); }
+    // f(x) for entries i0, i0 + 1, ... in order
+    template <class F>
+    __device__ __forceinline__ void each_from(int i0, F f) const {
+#pragma unroll 2
+        for (int c = i0; c < n0; ++c) f(__builtin_bit_cast(float, glob[(size_t)(4 * c + h) * kBR][0]));
+#pragma unroll 2
+        for (int c = i0 > n0 ? i0 - n0 : 0; c < n1; ++c)
+            f(__builtin_bit_cast(float, glob[(size_t)(4 * c + 2 + h) * kBR][0]));
     }
     template <class F>
-    __device__ __forceinline__ void each(F f) const {
-        const int nl = n < kLdsCand ? n : kLdsCand;
-#pragma unroll 4
-        for (int i = start; i < nl; i += 2) f(lds[i * kBR]);
-#pragma unroll 4
-        for (int i = start > kLdsCand ? start : kLdsCand + (start & 1); i < n; i += 2) f(glob[(size_t)i * kBR]);
-    }
+    __device__ __forceinline__ void each(F f) const { each_from(0, f); }
 };
 
-// The same list with the lane's first KR entries held in registers; missing
-// entries read -inf, which no threshold test passes.
+// The same entries with the first KR held in registers; missing entries
+// read -inf, which no threshold test passes.
 template <int KR>
 struct RegSrc {
     float v[KR];
-    CandSrc tail;  // the lane's entries from start + 2 * KR on
-    static_assert(2 * KR <= kLdsCand, "register entries come from LDS");
-    __device__ __forceinline__ void load(const CandSrc& src) {
+    uint32_t key[KR];
+    CandSrc src;
+    __device__ __forceinline__ void load(const CandSrc& s) {
+        src = s;
+        const int n = s.n();
 #pragma unroll
         for (int k = 0; k < KR; ++k) {
-            const int i = src.start + 2 * k;
-            v[k] = (i < src.n) ? src.lds[i * kBR] : neg_inf();
+            const u32x2 e = (k < n) ? s.entry(k) : u32x2{__builtin_bit_cast(uint32_t, neg_inf()), 0u};
+            v[k] = __builtin_bit_cast(float, e[0]);
+            key[k] = e[1];
         }
-        tail = src;
-        tail.start = src.start + 2 * KR;
     }
     template <class F>
     __device__ __forceinline__ void each(F f) const {
 #pragma unroll
         for (int k = 0; k < KR; ++k) f(v[k]);
-        tail.each(f);
+        src.each_from(KR, f);
     }
 };
+
+// The raw dot-product threshold equivalent to a score threshold: x > raw
+// exactly when fl(x * scale) > lo (fl(x * scale) is non-decreasing in x),
+// so the sweeps compare raw products and scale only what they keep.
+__device__ __forceinline__ float next_up(float x) {
+    if (x == __builtin_inff() || x != x) return x;
+    if (x == 0.0f) return __builtin_bit_cast(float, 1u);
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    return __builtin_bit_cast(float, x > 0.0f ? b + 1u : b - 1u);
+}
+__device__ __forceinline__ float next_down(float x) { return -next_up(-x); }
+__device__ __forceinline__ float raw_threshold(float lo, float scale) {
+    if (!(lo > neg_inf()) || !(lo < __builtin_inff())) return lo;
+    float r = lo / scale;
+    for (int i = 0; i < 4 && r * scale > lo; ++i) r = next_down(r);
+    for (int i = 0; i < 4 && next_up(r) * scale <= lo; ++i) r = next_up(r);
+    return r;
+}
 
 // Threshold of a row from its candidates: every entry is above `lo`, and
 // none of the row's other scores is.  Two lanes share a row (sums are
@@ -584,67 +594,22 @@ __device__ __forceinline__ float solve_candidates_gen(const Src& src, float lo, 
     return result;
 }
 
-// Largest entry of a candidate list (two lanes per row).
-template <class Src>
-__device__ __forceinline__ float list_max(const Src& src) {
-    float mx = neg_inf();
-    src.each([&](float x) { mx = fmaxf(mx, x); });
-    return fmaxf(mx, __shfl_xor(mx, 32, kWave));
-}
-
-constexpr int kRounds = 3;  // candidate collections before the sweep fallback
-
-#ifndef ENTMAX_STATS_STAGES_BF16_64
-#define ENTMAX_STATS_STAGES_BF16_64 3
-#endif
-#ifndef ENTMAX_STATS_STAGES_BF16_128
-#define ENTMAX_STATS_STAGES_BF16_128 2
-#endif
-#ifndef ENTMAX_STATS_OCCUPANCY
-#define ENTMAX_STATS_OCCUPANCY 3
-#endif
-// Ring stages (pairs of tiles in flight + 1) of the score-statistics sweep,
-// and the number of key tiles per row its on-chip tables are sized for
-// (TCMAX * 64 >= L): small tables leave room for three workgroups per CU.
+// Workgroups per CU of the score-statistics sweep (three fit in the register
+// file at <= 168 VGPRs).
+constexpr int kStatsOcc = 3;
+// Ring stages (pairs of tiles in flight + 1) of the score-statistics sweep.
 template <typename T, int D>
 struct StatsCfg {
-    static constexpr int kS = (sizeof(T) == 2 && D == 64) ? ENTMAX_STATS_STAGES_BF16_64
-                              : (sizeof(T) == 2) ? ENTMAX_STATS_STAGES_BF16_128
-                              : ((D == 128) ? 2 : 3);
+    static constexpr int kS = (sizeof(T) == 2 && D == 64) ? 3 : (sizeof(T) == 2) ? 2 : ((D == 128) ? 2 : 3);
 };
-#ifndef ENTMAX_COLLECT_STAGES
-#define ENTMAX_COLLECT_STAGES 2
-#endif
-#ifndef ENTMAX_COLLECT_OCCUPANCY
-#define ENTMAX_COLLECT_OCCUPANCY 2
-#endif
-// Ring stages and workgroups per CU of the candidate sweep.
-#ifndef ENTMAX_COLLECT_STAGES_BF16_128
-#define ENTMAX_COLLECT_STAGES_BF16_128 1
-#endif
-#ifndef ENTMAX_COLLECT_OCCUPANCY_BF16_128
-#define ENTMAX_COLLECT_OCCUPANCY_BF16_128 2
-#endif
-// (bf16, d = 128: a one-stage ring leaves room in LDS for two workgroups per
-// CU, whose sweeps then hide each other's loads.)
+// Ring stages and workgroups per CU of the candidate sweeps (bf16, d = 128: a
+// one-stage ring leaves room in LDS for two workgroups per CU, whose sweeps
+// then hide each other's loads).
 template <typename T, int D>
 struct CollectCfg {
-    static constexpr int kS = (sizeof(T) == 4 && D == 128) ? 1
-                              : (sizeof(T) == 2 && D == 128) ? ENTMAX_COLLECT_STAGES_BF16_128
-                                                             : ENTMAX_COLLECT_STAGES;
-    static constexpr int kOcc = (sizeof(T) == 2 && D == 64)    ? ENTMAX_COLLECT_OCCUPANCY
-                                : (sizeof(T) == 2 && D == 128) ? ENTMAX_COLLECT_OCCUPANCY_BF16_128
-                                                               : 1;
+    static constexpr int kS = (D == 128) ? 1 : 2;
+    static constexpr int kOcc = (sizeof(T) == 2) ? 2 : 1;
 };
-
-#ifndef ENTMAX_COLLECT_PER_QB
-#define ENTMAX_COLLECT_PER_QB 0
-#endif
-// The candidate sweeps take one 32-row block at a time (fewer live
-// accumulators, each tile's operands read twice) where that lets the kernel
-// keep more workgroups per CU.
-template <typename T, int D>
-constexpr bool kCollectPerQb = sizeof(T) == 2 && D == 64 && ENTMAX_COLLECT_PER_QB;
 
 constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
 
@@ -656,7 +621,7 @@ constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
 // (which always takes the list).  Separate instances keep each loop's code
 // as it is alone.
 template <typename T, int D, int TCMAX, bool CAUSAL>
-__global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(FwdParams p) {
+__global__ __launch_bounds__(kNT, kStatsOcc) void fwd_stats_kernel(FwdParams p) {
     using O = Ops<T, D>;
     constexpr int S = StatsCfg<T, D>::kS;
     __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
@@ -759,26 +724,115 @@ __global__ __launch_bounds__(kNT, ENTMAX_STATS_OCCUPANCY) void fwd_stats_kernel(
     }
 }
 
+// O of a block's rows from their candidate lists: O_i = sum over the entries
+// above tau_i of p(s) V_key (exactly the output over the non-null blocks,
+// since every score of a row outside its list is at or below tau), fp32
+// products and sums in list order.  D / 32 lanes per row, each with 32
+// elements of d; the lanes of a row load each entry's V row piece by
+// 16-byte loads, kB entries in flight.
+template <typename T, int D>
+__device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, const u32x2* clist,
+                                            const int (&cntq)[4][kBR], const float* row_tau) {
+    constexpr int kLpr = D / 32;              // lanes per row
+    constexpr int kRpp = kNT / kLpr;          // rows per pass
+    constexpr int kVec = 16 / (int)sizeof(T); // elements per 16-byte load
+    constexpr int kLd = 32 / kVec;            // loads per entry per lane
+    constexpr int kB = sizeof(T) == 2 ? 4 : 2;
+    const T* Vh = reinterpret_cast<const T*>(p.v) + (size_t)bh * p.L * D;
+    const int t = threadIdx.x, part = t % kLpr;
+    for (int rp = 0; rp < kBR; rp += kRpp) {
+        const int row = rp + t / kLpr;
+        if (r0 + row >= p.L) continue;
+        const float tau = row_tau[row];
+        const int n0 = cntq[0][row], n1 = n0 + cntq[1][row], n2 = n1 + cntq[2][row], n = n2 + cntq[3][row];
+        float acc[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+        for (int i0 = 0; i0 < n; i0 += kB) {
+            float a[kB];
+            uint32_t key[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const int i = min(i0 + u, n - 1);
+                const int qq = (i >= n0) + (i >= n1) + (i >= n2);
+                const int c = i - (qq == 0 ? 0 : qq == 1 ? n0 : qq == 2 ? n1 : n2);
+                const u32x2 e = clist[(size_t)(4 * c + qq) * kBR + row];
+                const float sv = __builtin_bit_cast(float, e[0]);
+                float w;
+                if (p.gen) {
+                    w = p.am.p(sv, tau);
+                } else {
+                    const float dd = 0.5f * fmaxf(sv - tau, 0.0f);
+                    w = dd * dd;
+                }
+                a[u] = (i0 + u < n) ? w : 0.0f;
+                key[u] = e[1];
+            }
+            u32x4 v[kB][kLd];
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+#pragma unroll
+                for (int j = 0; j < kLd; ++j)
+                    v[u][j] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key[u] * D + part * 32 + j * kVec);
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+#pragma unroll
+                for (int j = 0; j < kLd; ++j)
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        // (the element is copied out first: a bit_cast of an
+                        // indexed vector element read element 0 here)
+                        const uint32_t bits = v[u][j][sizeof(T) == 2 ? e >> 1 : e];
+                        const float x = sizeof(T) == 2 ? __builtin_bit_cast(float, (bits >> ((e & 1) * 16)) << 16)
+                                                       : __builtin_bit_cast(float, bits);
+                        acc[j * kVec + e] = fmaf(a[u], x, acc[j * kVec + e]);
+                    }
+        }
+        float* orow = p.o + ((size_t)bh * p.L + r0 + row) * D + part * 32;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            f32x4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = acc[4 * j + e];
+            *reinterpret_cast<f32x4*>(orow + 4 * j) = o4;
+        }
+    }
+}
+
 // ------------------------------------------------------------ kernel 1b
-// Candidate sweep over the tiles whose best score beats tau_lo: every score
-// above its row's tau_lo goes to the row's list (global memory, so the
-// workgroup's LDS stays small).  Rows whose list overflows get a tighter
-// bound (the threshold of the candidates they kept, a lower bound on tau
-// since tau only grows with the set) and are collected again; rows still
-// overflowing after kRounds are solved by Halley-bisection sweeps.  Then the
-// exact tau of every complete list (two lanes per row, the first
-// 2 * kSolveRegs<D> candidates in registers), its non-null tiles (those holding
-// a candidate above tau), and tau and the mask words of both 64-row blocks.
-#ifndef ENTMAX_SOLVE_REGS
-#define ENTMAX_SOLVE_REGS 16
-#endif
-#ifndef ENTMAX_SOLVE_REGS_128
-#define ENTMAX_SOLVE_REGS_128 8
-#endif
-// (d = 128 keeps fewer candidates in registers: its query operand takes twice
-// the registers, and the kernel runs two workgroups per CU.)
+// Threshold of the 128 rows of a block from their score statistics.
+//
+// collect   sweep the tiles whose largest score beats the smallest bound of
+//           the row half; every score above its row's bound goes to the
+//           row's sub-list of the sweeping lane (a register takes the store
+//           path only when some lane of the wave holds such a score in it).
+//           Nothing at or below a lower bound on tau carries weight, so a row
+//           whose four sub-lists all fit holds its whole support in them.
+// solve     exact tau of every complete row (two lanes per row, fp64 sums in
+//           list order); the tiles of its support are set in the block mask.
+// overflow  rows whose sub-lists overflow (wide supports) take the histogram
+//           initialisation of "AdaSplash-2: Faster Differentiable Sparse
+//           Attention" (sec. 3.1, sec. 3.3 phase 2): one sweep bins every
+//           score above the row's bound into 32 left-edge bins spanning
+//           [bound, max]; the exact threshold tau_h of the binned scores
+//           satisfies tau - w < tau_h <= tau (Proposition 3.1, w the bin
+//           width).  A row whose scores above tau_h fit the lists is collected
+//           again above tau_h and solved exactly; any other row is refined by
+//           Halley-bisection sweeps on [tau_h, tau_h + w] (phase 3), and a
+//           last sweep sets its tiles in the mask.
 template <int D>
-constexpr int kSolveRegs = D == 128 ? ENTMAX_SOLVE_REGS_128 : ENTMAX_SOLVE_REGS;
+constexpr int kSolveRegs = D == 128 ? 8 : 16;  // candidates per lane held in registers
+constexpr int kHistBins = 32;
+
+// The solve kernel writes O itself from the candidate lists when
+// kGatherRatio * (list entries) < kGatherTileCost * (non-null tiles of its two
+// 64-row blocks): a tile of the output pass (score recompute and product over
+// 64 x 64 pairs) measured about 40 times the cost of one list entry's V row.
+constexpr int kGatherRatio = 1;
+constexpr int kGatherTileCost = 32;
+
+// Row states of the solve kernel.
+enum { kRowNone = 0, kRowCollect = 1, kRowSweep = 2, kRowDone = 3, kRowOver = 4 };
 
 template <typename T, int D, int TCMAX>
 __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kernel(FwdParams p) {
@@ -786,18 +840,17 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
     constexpr int S = CollectCfg<T, D>::kS;
     constexpr int WD = TCMAX / 32;
     __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
-    // candidate slots [slot][row], then one spare word per thread
-    __shared__ float lval[kLdsCand * kBR + kNT];
-    __shared__ uint16_t lpos[kLdsCand * kBR + kNT];
+    __shared__ int hist[kHistBins * kBR];  // overflow path: counts [bin][row]
     __shared__ uint16_t list[TCMAX];
     __shared__ float um_s[2][TCMAX];
-    __shared__ int cnt[kBR], rstate[kBR];
+    __shared__ int cntq[4][kBR], rstate[kBR];
     __shared__ float row_m[kBR], row_lo[kBR], row_hi[kBR], row_tau[kBR];
     __shared__ uint32_t maskw[2][WD];
     __shared__ int nlist_s, flag_s;
 
     const int t = threadIdx.x, w = wave_id(), qh = w & 1, kh = w >> 1;
     const int l = lane_id(), m = l & 31, h = l >> 5;
+    const int q = 2 * kh + h;  // this lane's sub-list of the rows it sweeps
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
     const size_t blk = (size_t)bh * p.nQ + r0 / kBR;
@@ -807,20 +860,21 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
     const T* Qh = reinterpret_cast<const T*>(p.q) + head_off;
     const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
     const int cap = p.cap < kCandCap ? p.cap : kCandCap;
-    float* cval = p.cval + blk * kCandCap * kBR;
-    uint16_t* cjt = p.cjt + blk * kCandCap * kBR;
+    const int capq = cap >= 4 ? cap / 4 : 1;  // entries per sub-list
+    u32x2* clist = p.clist + blk * kCandCap * kBR;
     const float2* rowstat = reinterpret_cast<const float2*>(p.rowstat) + (size_t)bh * p.L;
 
     typename O::template QOp<2> qop;
     O::load_q(qop, Qh, R0, p.L);
-    // row statistics and the tile maxima of both row blocks, loaded together
+    // row statistics and the tile maxima of both row blocks
     if (t < kBR) {
         const bool valid = (r0 + t) < p.L;
         const float2 rs = valid ? rowstat[r0 + t] : make_float2(neg_inf(), __builtin_inff());
         row_m[t] = rs.x;
         row_lo[t] = rs.y;
-        cnt[t] = 0;
-        rstate[t] = valid ? 1 : 0;  // 1: to collect, 3: list complete, 2: sweep fallback, 0: no row
+        rstate[t] = valid ? kRowCollect : kRowNone;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) cntq[qq][t] = 0;
     }
     for (int i = t; i < 2 * p.Tc; i += kNT) {
         const int hh = i / p.Tc, J = i - hh * p.Tc;
@@ -830,7 +884,7 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
     for (int i = t; i < 2 * WD; i += kNT) (&maskw[0][0])[i] = 0u;
     __syncthreads();
 
-    // tiles whose best score beats the smallest tau_lo of the row half
+    // tiles whose best score beats the smallest bound of the row half
     if (w == 0) {
         const float th0 = wave_min(row_lo[l]), th1 = wave_min(row_lo[64 + l]);
         const int n = build_list(list, p.Tc, [&](int J) {
@@ -840,133 +894,196 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
     }
     __syncthreads();
 
-    const int srow = qh * 64 + kh * 32 + m;  // the row this lane handles (with lane l ^ 32)
-    const int lds_lim = cap < kLdsCand ? cap : kLdsCand;
-    const int spare = kLdsCand * kBR + t;
-    for (int round = 0; round < kRounds; ++round) {
-        float lo_q[2];
+    const int srow = qh * 64 + kh * 32 + m;  // the row this lane solves (with lane l ^ 32)
+
+    // ---- collect the scores above each collecting row's bound
+    auto collect = [&]() {
+        float lr[2];
+        int cc[2] = {0, 0};
+        bool coll[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = qh * 64 + qb * 32 + m;
-            lo_q[qb] = rstate[row] == 1 ? row_lo[row] : __builtin_inff();
+            coll[qb] = rstate[row] == kRowCollect;
+            lr[qb] = coll[qb] ? raw_threshold(row_lo[row], p.scale) : __builtin_inff();
         }
-        // the candidates of one 32-row block (column c of acc) of list entry e
-        auto collect_qb = [&](int e, int qb, auto& acc, int c) {
-            float bm = neg_inf();
+        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[kb][c][r]);
-            if (__ballot(bm * p.scale > lo_q[qb]) == 0) return;
-            const float lo = lo_q[qb];
-            int nb = 0;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    acc[kb][c][r] *= p.scale;
-                    nb += acc[kb][c][r] > lo ? 1 : 0;
-                }
-            const int row = qh * 64 + qb * 32 + m;
-            int base = 0;
-            if (nb) base = atomicAdd(&cnt[row], nb);
-            if (__ballot(base + nb > lds_lim) == 0) {
-                // all in LDS: the lane's candidates take consecutive slots from
-                // base in register order; other elements write the spare word
-                int slot = base;
+            for (int qb = 0; qb < 2; ++qb) {
+                const int row = qh * 64 + qb * 32 + m;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const bool on = acc[kb][c][r] > lo;
-                        const int a = on ? slot * kBR + row : spare;
-                        lval[a] = acc[kb][c][r];
-                        lpos[a] = (uint16_t)e;
-                        slot += on ? 1 : 0;
-                    }
-            } else {
-                // the list spills past LDS: candidates in register order from
-                // base, LDS slots first, then the workspace, the rest dropped
-                // (the row is then collected again with a tighter bound)
-                int slot = base;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float sv = acc[kb][c][r];
-                        if (sv > lo) {
-                            if (slot < lds_lim) {
-                                lval[slot * kBR + row] = sv;
-                                lpos[slot * kBR + row] = (uint16_t)e;
-                            } else if (slot < cap) {
-                                cval[(size_t)slot * kBR + row] = sv;
-                                cjt[(size_t)slot * kBR + row] = (uint16_t)e;
-                            }
-                            ++slot;
+                        const float x = acc[kb][qb][r];
+                        if (x > lr[qb]) {
+                            // past the capacity the last slot is overwritten: the
+                            // count shows the overflow and the list is not used
+                            const int c = min(cc[qb], capq - 1);
+                            u32x2 e;
+                            e[0] = __builtin_bit_cast(uint32_t, x * p.scale);
+                            e[1] = (uint32_t)(J * kBC + kb * 32 + key_of_reg(r, h));
+                            clist[(size_t)(4 * c + q) * kBR + row] = e;
+                            cc[qb] += 1;
                         }
                     }
             }
-        };
-        if constexpr (kCollectPerQb<T, D>) {
-            ring_sweep<T, D, S, true>(list, nlist_s, Kh, ring, qop, R0, g,
-                                      [&](int, int e, int qb, f32x16(&acc)[2][1]) { collect_qb(e, qb, acc, 0); });
-        } else {
-            ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int e, f32x16(&acc)[2][2]) {
+        });
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) collect_qb(e, qb, acc, qb);
-            });
-        }
+        for (int qb = 0; qb < 2; ++qb)
+            if (coll[qb]) cntq[q][qh * 64 + qb * 32 + m] = cc[qb];
+        __syncthreads();
+    };
 
-        const bool open = rstate[srow] == 1;
-        const int nc = cnt[srow];
-        const bool over = open && nc > cap;
-        float lo_new = neg_inf();
-        if (__ballot(over) != 0) {
-            // threshold of the kept candidates: a lower bound on the row's tau
-            const CandSrc src = {lval + srow, cval + srow, over ? cap : 0, h};
-            const float smax = list_max(src);
-            if (p.gen) {
-                float lb;
-                solve_candidates_gen(src, smax - p.am.e, p.am.hi(smax, (float)cap), over, p.am, &lb);
-                lo_new = lb - 1e-6f * fmaxf(1.0f, fabsf(lb));
-            } else {
-                const double ts = solve_candidates(src, smax, (double)smax - 2.0,
-                                                   (double)smax - 2.0 / sqrt((double)cap), over);
-                lo_new = __double2float_rd(ts);
+    // ---- exact tau of the collecting rows whose sub-lists all fit
+    auto solve = [&]() {
+        const bool open = rstate[srow] == kRowCollect;
+        const int a0 = cntq[h][srow], a1 = cntq[2 + h][srow];
+        const int b0 = cntq[h ^ 1][srow], b1 = cntq[2 + (h ^ 1)][srow];
+        const bool act = open && max(max(a0, a1), max(b0, b1)) <= capq;
+        const int n = act ? a0 + a1 + b0 + b1 : 1;
+        RegSrc<kSolveRegs<D>> src;
+        src.load(CandSrc{clist + srow, act ? a0 : 0, act ? a1 : 0, h});
+        const double mx = row_m[srow];
+        const float tr = p.gen ? solve_candidates_gen(src, row_lo[srow], p.am.hi(row_m[srow], (float)n), act, p.am)
+                               : (float)solve_candidates(src, mx, row_lo[srow], mx - 2.0 / sqrt((double)n), act);
+        if (act) {
+            // the tiles of the support (a lane meets its entries in tile order)
+            int lastJ = -1;
+            const int na = a0 + a1;
+            auto mark = [&](float x, uint32_t key) {
+                if (x > tr) {
+                    const int J = (int)(key >> 6);
+                    if (J != lastJ) atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
+                    lastJ = J;
+                }
+            };
+#pragma unroll
+            for (int k = 0; k < kSolveRegs<D>; ++k) mark(src.v[k], src.key[k]);
+            for (int i = kSolveRegs<D>; i < na; ++i) {
+                const u32x2 e = src.src.entry(i);
+                mark(__builtin_bit_cast(float, e[0]), e[1]);
             }
-        }
-        if (h == 0 && open) {
-            if (!over) {
-                rstate[srow] = 3;  // list complete, nc entries
-            } else {
-                // every score above tau is above lo, so at most nc of them
-                row_hi[srow] = p.gen ? p.am.hi(row_m[srow], (float)nc)
-                                     : (float)((double)row_m[srow] - 2.0 / sqrt((double)nc));
-                const float nl = fmaxf(row_lo[srow], lo_new);
-                if (round == kRounds - 1 || !(nl > row_lo[srow])) rstate[srow] = 2;
-                row_lo[srow] = nl;
-                cnt[srow] = 0;
+            if (h == 0) {
+                row_tau[srow] = tr;
+                rstate[srow] = kRowDone;
             }
+        } else if (open && h == 0) {
+            rstate[srow] = kRowOver;
         }
+        __syncthreads();
+    };
+
+    // any row of the block in state st?
+    auto any_row = [&](int st) -> bool {
         if (t == 0) flag_s = 0;
         __syncthreads();
-        if (h == 0 && rstate[srow] == 1) atomicOr(&flag_s, 1);
+        if (t < kBR && rstate[t] == st) atomicOr(&flag_s, 1);
         __syncthreads();
-        if (!flag_s) break;
+        return flag_s != 0;
+    };
+
+    collect();
+    solve();
+
+    if (any_row(kRowOver)) {
+        // ---- histogram of the scores above the bound of each overflowing row
+        for (int i = t; i < kHistBins * kBR; i += kNT) hist[i] = 0;
+        float lr[2], hlo[2], hinv[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = qh * 64 + qb * 32 + m;
+            const bool over = rstate[row] == kRowOver;
+            hlo[qb] = row_lo[row];
+            hinv[qb] = over ? (float)kHistBins / (row_m[row] - row_lo[row]) : 0.0f;
+            lr[qb] = over ? raw_threshold(row_lo[row], p.scale) : __builtin_inff();
+        }
+        __syncthreads();
+        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int row = qh * 64 + qb * 32 + m;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float x = acc[kb][qb][r];
+                        const bool on = x > lr[qb];
+                        if (__builtin_amdgcn_ballot_w64(on) != 0) {
+                            if (on) {
+                                const int k = min((int)((x * p.scale - hlo[qb]) * hinv[qb]), kHistBins - 1);
+                                atomicAdd(&hist[k * kBR + row], 1);
+                            }
+                        }
+                    }
+            }
+        });
+        // tau_h from the bin counts (one thread per row), the bracket
+        // [tau_h, tau_h + w], and whether the scores above tau_h fit the lists
+        if (t < kBR && rstate[t] == kRowOver) {
+            const double lo = row_lo[t], mx = row_m[t];
+            const double wd = (mx - lo) / kHistBins;
+            double th;
+            if (!p.gen) {
+                // the sorting solve on the bins, from the top (each bin's
+                // scores stand at its left edge)
+                double S0 = 0.0, S1 = 0.0, S2 = 0.0, best = -2.0;
+                for (int k = kHistBins - 1; k >= 0; --k) {
+                    const double H = (double)hist[k * kBR + t];
+                    if (H == 0.0) continue;
+                    const double y = lo + k * wd - mx;
+                    S0 += H;
+                    S1 += H * y;
+                    S2 += H * y * y;
+                    const double disc = S1 * S1 - S0 * (S2 - 4.0);
+                    if (disc < 0.0) continue;
+                    const double tk = (S1 - sqrt(disc)) / S0;
+                    if (tk <= y) best = tk;
+                }
+                th = mx + best;
+            } else {
+                // bisection on the binned normaliser
+                double a = lo - wd, b = mx;
+                for (int it = 0; it < 60; ++it) {
+                    const double mid = 0.5 * (a + b);
+                    double F = 0.0;
+                    for (int k = 0; k < kHistBins; ++k) {
+                        const int H = hist[k * kBR + t];
+                        const double u = (double)p.am.am1 * (lo + k * wd - mid);
+                        if (H > 0 && u > 0.0) F += H * (p.am.lin ? u : pow(u, (double)p.am.e));
+                    }
+                    if (F >= 1.0) a = mid; else b = mid;
+                }
+                th = a;
+            }
+            // margins for the fp32 binning arithmetic
+            const double mg = 1e-6 * fmax(1.0, fabs(th));
+            const float tlo = (float)fmax(th - mg, lo);
+            const float thi = (float)fmin(th + wd + mg, mx);
+            int above = 0;
+            const int k0 = max((int)floor((tlo - lo) / wd) - 1, 0);
+            for (int k = k0; k < kHistBins; ++k) above += hist[k * kBR + t];
+            row_lo[t] = fmaxf(row_lo[t], tlo);
+            row_hi[t] = thi;
+            rstate[t] = (above <= 3 * capq) ? kRowCollect : kRowSweep;
+        }
+        __syncthreads();
+        if (any_row(kRowCollect)) {
+            collect();
+            solve();
+            // rows still overflowing keep the histogram bracket
+            if (t < kBR && rstate[t] == kRowOver) rstate[t] = kRowSweep;
+            __syncthreads();
+        }
     }
 
-    if (t == 0) flag_s = 0;
-    __syncthreads();
-    if (h == 0 && rstate[srow] == 2) atomicOr(&flag_s, 1);
-    __syncthreads();
-
-    // ---- fallback: Halley-bisection sweeps for rows whose list overflowed
-    if (flag_s) {
+    // ---- Halley-bisection sweeps for rows whose lists overflowed
+    if (any_row(kRowSweep)) {
         __shared__ float fb_t[kBR];
         __shared__ int fb_active[kBR];
         __shared__ float fb_part[kBR][2][3];
         if (h == 0) {
-            fb_active[srow] = rstate[srow] == 2 ? 1 : 0;
+            fb_active[srow] = rstate[srow] == kRowSweep ? 1 : 0;
             fb_t[srow] = row_lo[srow];
         }
         __syncthreads();
@@ -980,39 +1097,32 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                 tq[qb] = fb_t[row];
             }
             float sc[2] = {0.f, 0.f}, sf[2] = {0.f, 0.f}, sf1[2] = {0.f, 0.f};
-            // this lane's sums over the scores above tq of 32-row block qb
-            auto sums_qb = [&](int qb, auto& acc, int c) {
-                if (!aq[qb]) return;
+            ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int qb = 0; qb < 2; ++qb) {
+                    if (!aq[qb]) continue;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float s = acc[kb][c][r] * p.scale;
-                        if (s > tq[qb]) {
-                            sc[qb] += 1.f;
-                            if (p.gen) {
-                                // F = sum p, F1 = sum p/u (Newton)
-                                const float u = p.am.am1 * (s - tq[qb]);
-                                const float q = p.am.pw1(u);  // p / u
-                                sf[qb] = fmaf(q, u, sf[qb]);
-                                sf1[qb] += q;
-                            } else {
-                                const float gg = 0.5f * (s - tq[qb]);
-                                sf[qb] += gg * gg;
-                                sf1[qb] += gg;
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float s = acc[kb][qb][r] * p.scale;
+                            if (s > tq[qb]) {
+                                sc[qb] += 1.f;
+                                if (p.gen) {
+                                    // F = sum p, F1 = sum p/u (Newton)
+                                    const float u = p.am.am1 * (s - tq[qb]);
+                                    const float pu = p.am.pw1(u);  // p / u
+                                    sf[qb] = fmaf(pu, u, sf[qb]);
+                                    sf1[qb] += pu;
+                                } else {
+                                    const float gg = 0.5f * (s - tq[qb]);
+                                    sf[qb] += gg * gg;
+                                    sf1[qb] += gg;
+                                }
                             }
                         }
-                    }
-            };
-            if constexpr (kCollectPerQb<T, D>) {
-                ring_sweep<T, D, S, true>(list, nlist_s, Kh, ring, qop, R0, g,
-                                          [&](int, int, int qb, f32x16(&acc)[2][1]) { sums_qb(qb, acc, 0); });
-            } else {
-                ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) sums_qb(qb, acc, qb);
-                });
-            }
+                }
+            });
             // combine the two lane halves, then the two key parities
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
@@ -1062,84 +1172,47 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
         // rows still active after the cap take their bracket midpoint
         if (h == 0 && fb_active[srow]) row_tau[srow] = 0.5f * (row_lo[srow] + row_hi[srow]);
         __syncthreads();
-        // mark the tiles of the fallback rows
+        // mark the tiles of the swept rows
         float tq[2];
         bool aq[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = qh * 64 + qb * 32 + m;
-            aq[qb] = rstate[row] == 2;
+            aq[qb] = rstate[row] == kRowSweep;
             tq[qb] = row_tau[row];
         }
-        // set the tile's bit if a score of an active row of block qb is above its tau
-        auto mark_qb = [&](int J, int qb, auto& acc, int c) {
+        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
             bool any = false;
-            if (aq[qb]) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                if (!aq[qb]) continue;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) any |= acc[kb][c][r] * p.scale > tq[qb];
+                    for (int r = 0; r < 16; ++r) any |= acc[kb][qb][r] * p.scale > tq[qb];
             }
-            return any;
-        };
-        if constexpr (kCollectPerQb<T, D>) {
-            ring_sweep<T, D, S, true>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, int qb, f32x16(&acc)[2][1]) {
-                if (__ballot(mark_qb(J, qb, acc, 0)) != 0 && l == 0) atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
-            });
-        } else {
-            ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
-                bool any = false;
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) any |= mark_qb(J, qb, acc, qb);
-                if (__ballot(any) != 0 && l == 0) atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
-            });
-        }
-    }
-
-    // ---- exact tau of the rows with complete lists
-    {
-        const bool act = rstate[srow] == 3;
-        const int n = act ? cnt[srow] : 0;
-        RegSrc<kSolveRegs<D>> src;
-        src.load(CandSrc{lval + srow, cval + srow, n, h});
-        const double mx = row_m[srow];
-        const float tr = p.gen ? solve_candidates_gen(src, row_lo[srow], p.am.hi(row_m[srow], (float)(n > 0 ? n : 1)),
-                                                      act, p.am)
-                               : (float)solve_candidates(src, mx, row_lo[srow],
-                                                         mx - 2.0 / sqrt((double)(n > 0 ? n : 1)), act);
-        const int nl = nlist_s;
-        auto pos_of = [&](int i) -> int {
-            return i < kLdsCand ? lpos[i * kBR + srow] : cjt[(size_t)i * kBR + srow];
-        };
-        if (nl <= 64) {
-            // list positions holding a support entry, OR-ed over the wave, then
-            // one lane per position sets the tile's bit
-            uint64_t lm = 0;
-            if (act) {
-#pragma unroll
-                for (int k = 0; k < kSolveRegs<D>; ++k) {
-                    const uint64_t b = 1ull << (pos_of(h + 2 * k) & 63);
-                    lm |= (src.v[k] > tr) ? b : 0ull;
-                }
-                for (int i = h + 2 * kSolveRegs<D>; i < n; i += 2)
-                    if (src.tail.at(i) > tr) lm |= 1ull << pos_of(i);
-            }
-            const uint32_t lo32 = wave_or((uint32_t)lm), hi32 = wave_or((uint32_t)(lm >> 32));
-            const uint32_t mine = (l < 32) ? (lo32 >> l) & 1u : (hi32 >> (l - 32)) & 1u;
-            if (l < nl && mine) {
-                const int J = list[l] & 0xfff;
-                atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
-            }
-        } else if (act) {
-            for (int i = h; i < n; i += 2)
-                if (src.tail.at(i) > tr) {
-                    const int J = list[pos_of(i)] & 0xfff;
-                    atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
-                }
-        }
-        if (act && h == 0) row_tau[srow] = tr;
+            if (__ballot(any) != 0 && l == 0) atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
+        });
     }
     __syncthreads();
+
+    // ---- O straight from the candidate lists when every row has one and the
+    // lists are short next to the tiles the output pass would sweep
+    if (p.gather) {
+        bool gathered = !any_row(kRowSweep);
+        if (gathered) {
+            if (t == 0) flag_s = 0;
+            __syncthreads();
+            int work = 0;
+            if (t < kBR) work += kGatherRatio * (cntq[0][t] + cntq[1][t] + cntq[2][t] + cntq[3][t]);
+            if (t < 2 * WD) work -= kGatherTileCost * __popc((&maskw[0][0])[t]);
+            if (work != 0) atomicAdd(&flag_s, work);
+            __syncthreads();
+            gathered = flag_s < 0;
+        }
+        if (gathered) gather_rows<T, D>(p, bh, r0, clist, cntq, row_tau);
+        if (t == 0) p.ostate[blk] = gathered ? 1 : 0;
+    }
 
     // ---- outputs: tau and the packed mask of both 64-row blocks
     if (t < kBR && r0 + t < p.L) p.tau[(size_t)bh * p.L + r0 + t] = row_tau[t];
@@ -1170,6 +1243,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    if (p.ostate != nullptr && p.ostate[(size_t)bh * p.nQ + r0 / kBR]) return;  // O already written
     const int R0 = r0 + 64 * qh;
     const Geom g = {p.L, p.mode, p.W};
     const size_t head_off = (size_t)bh * p.L * D;
@@ -1296,6 +1370,7 @@ __global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(Fw
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    if (p.ostate != nullptr && p.ostate[(size_t)bh * p.nQ + r0 / kBR]) return;  // O already written
     const int R0 = r0 + 32 * w;  // this wave's rows
     const int hh = w >> 1;       // their 64-row block
     const Geom g = {p.L, p.mode, p.W};
@@ -1515,7 +1590,7 @@ size_t attn_threshold_workspace_bytes(int B, int H, int L) {
     using namespace attn;
     const size_t rows = cand_rows(B, H, L);
     return round256(rowstat_bytes(B, H, L)) + round256(umax_bytes(B, H, L)) +
-           round256(rows * kCandCap * sizeof(float)) + round256(rows * kCandCap * sizeof(uint16_t));
+           round256(rows * kCandCap * sizeof(u32x2)) + round256(rows / kBR * sizeof(int));
 }
 
 size_t attn_fwd_workspace_bytes(int B, int H, int L, int, int) {
@@ -1536,9 +1611,13 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream) {
     fp.umax = reinterpret_cast<float*>(ws + off);
     off += round256(umax_bytes(a.B, a.H, a.L));
     const size_t rows = cand_rows(a.B, a.H, a.L);
-    fp.cval = reinterpret_cast<float*>(ws + off);
-    off += round256(rows * kCandCap * sizeof(float));
-    fp.cjt = reinterpret_cast<uint16_t*>(ws + off);
+    fp.clist = reinterpret_cast<u32x2*>(ws + off);
+    off += round256(rows * kCandCap * sizeof(u32x2));
+    // the whole forward: the solve kernel writes O from the candidate lists of
+    // the blocks it can, and the output kernel skips those blocks
+    const bool whole = (phase & 6) == 6;
+    fp.ostate = whole ? reinterpret_cast<int*>(ws + off) : nullptr;
+    fp.gather = whole ? 1 : 0;
     fp.mask = a.block_mask ? a.block_mask
                            : reinterpret_cast<uint32_t*>(ws + attn_threshold_workspace_bytes(a.B, a.H, a.L));
     fp.BH = a.B * a.H; fp.L = a.L; fp.mode = a.mask;

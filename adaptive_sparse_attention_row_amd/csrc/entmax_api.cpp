@@ -13,8 +13,18 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ENTMAX_OK : ENTMAX_ERR_HIP; }
 
-int g_cand_cap = 0;  // 0: the compiled default
-int g_row_hist = 1;  // histogram-initialised bracket for wide rows
+// Options of one call (NULL: defaults); ENTMAX_ERR_ARG for values out of range.
+int read_options(const entmax_options* o, int* cand_cap, int* row_hist) {
+    *cand_cap = 0;
+    *row_hist = 1;
+    if (o == nullptr) return ENTMAX_OK;
+    if (o->candidate_cap < 0 || o->candidate_cap > entmax::attn_max_candidate_cap(64, ENTMAX_BF16))
+        return ENTMAX_ERR_ARG;
+    if (o->row_plain_bracket != 0 && o->row_plain_bracket != 1) return ENTMAX_ERR_ARG;
+    *cand_cap = o->candidate_cap;
+    *row_hist = o->row_plain_bracket ? 0 : 1;
+    return ENTMAX_OK;
+}
 
 // Shared checks of the attention entry points (everything except pointers).
 int check_attn_shape(int B, int H, int L, int d, float alpha, int dtype, int mask, int window) {
@@ -62,30 +72,24 @@ int entmax_tile_shape(int d, int dtype, int* block_rows, int* block_cols) {
     return ENTMAX_OK;
 }
 
-int entmax_set_option(int option, int value) {
-    if (option == ENTMAX_OPT_ROW_HISTOGRAM) {
-        const int prev = g_row_hist;
-        g_row_hist = value != 0 ? 1 : 0;
-        return prev;
-    }
-    if (option != ENTMAX_OPT_CANDIDATE_CAP) return -ENTMAX_ERR_ARG;
-    const int maxcap = entmax::attn_max_candidate_cap(64, ENTMAX_BF16);
-    if (value > maxcap) return -ENTMAX_ERR_ARG;
-    const int prev = g_cand_cap;
-    g_cand_cap = value > 0 ? value : 0;
-    return prev;
-}
-
-int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
-                    int64_t ld, float alpha, void* stream) {
+int entmax_tau_rows_ex(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
+                       int64_t ld, float alpha, const entmax_options* options, void* stream) {
     if (!(alpha > 1.0f && alpha <= 2.0f)) return ENTMAX_ERR_ALPHA;
     if (rows < 0 || cols < 1 || ld < cols || rows > 0x7fffffffLL || cols > 0x7fffffffLL)
         return ENTMAX_ERR_SHAPE;
+    int cap, row_hist;
+    const int st = read_options(options, &cap, &row_hist);
+    if (st != ENTMAX_OK) return st;
     if (rows == 0) return ENTMAX_OK;
     if (S == nullptr || tau == nullptr) return ENTMAX_ERR_NULL;
     (void)hipGetLastError();
     return hip_status(
-        entmax::launch_tau_rows(S, P, tau, rows, cols, ld, alpha, g_row_hist, (hipStream_t)stream));
+        entmax::launch_tau_rows(S, P, tau, rows, cols, ld, alpha, row_hist, (hipStream_t)stream));
+}
+
+int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
+                    int64_t ld, float alpha, void* stream) {
+    return entmax_tau_rows_ex(S, P, tau, rows, cols, ld, alpha, nullptr, stream);
 }
 
 size_t entmax_attn_threshold_workspace(int B, int H, int L, int d, int dtype, int mask,
@@ -99,10 +103,10 @@ size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask
     return entmax::attn_fwd_workspace_bytes(B, H, L, d, dtype);
 }
 
-int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float* tau,
-                    uint32_t* block_mask, int B, int H, int L, int d, float scale, float alpha,
-                    int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+int entmax_attn_fwd_ex(const void* Q, const void* K, const void* V, float* O, float* tau,
+                       uint32_t* block_mask, int B, int H, int L, int d, float scale, float alpha,
+                       int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
+                       const entmax_options* options, void* stream) {
     if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr || tau == nullptr)
         return ENTMAX_ERR_NULL;
     int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
@@ -114,21 +118,32 @@ int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float
                                    : entmax::attn_fwd_workspace_bytes(B, H, L, d, dtype);
     if (workspace == nullptr || workspace_bytes < need) return ENTMAX_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ENTMAX_ERR_ALIGN;
+    int cap, row_hist;
+    st = read_options(options, &cap, &row_hist);
+    if (st != ENTMAX_OK) return st;
     entmax::AttnArgs a = {};
     a.q = Q; a.k = K; a.v = V; a.o = O; a.tau = tau; a.block_mask = block_mask;
     a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     const int maxcap = entmax::attn_max_candidate_cap(d, dtype);
-    a.cand_cap = (g_cand_cap > 0 && g_cand_cap < maxcap) ? g_cand_cap : maxcap;
+    a.cand_cap = (cap > 0 && cap < maxcap) ? cap : maxcap;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     (void)hipGetLastError();
     return hip_status(entmax::launch_attn_fwd(a, 7, (hipStream_t)stream));
 }
 
-int entmax_attn_threshold(const void* Q, const void* K, float* tau, uint32_t* block_mask,
-                          int B, int H, int L, int d, float scale, float alpha, int dtype,
-                          int mask, int window, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float* tau,
+                    uint32_t* block_mask, int B, int H, int L, int d, float scale, float alpha,
+                    int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    return entmax_attn_fwd_ex(Q, K, V, O, tau, block_mask, B, H, L, d, scale, alpha, dtype, mask,
+                              window, workspace, workspace_bytes, nullptr, stream);
+}
+
+int entmax_attn_threshold_ex(const void* Q, const void* K, float* tau, uint32_t* block_mask,
+                             int B, int H, int L, int d, float scale, float alpha, int dtype,
+                             int mask, int window, void* workspace, size_t workspace_bytes,
+                             const entmax_options* options, void* stream) {
     if (Q == nullptr || K == nullptr || tau == nullptr || block_mask == nullptr)
         return ENTMAX_ERR_NULL;
     int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
@@ -139,15 +154,26 @@ int entmax_attn_threshold(const void* Q, const void* K, float* tau, uint32_t* bl
     if (workspace == nullptr || workspace_bytes < entmax::attn_threshold_workspace_bytes(B, H, L))
         return ENTMAX_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ENTMAX_ERR_ALIGN;
+    int cap, row_hist;
+    st = read_options(options, &cap, &row_hist);
+    if (st != ENTMAX_OK) return st;
     entmax::AttnArgs a = {};
     a.q = Q; a.k = K; a.tau = tau; a.block_mask = block_mask;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     const int maxcap = entmax::attn_max_candidate_cap(d, dtype);
-    a.cand_cap = (g_cand_cap > 0 && g_cand_cap < maxcap) ? g_cand_cap : maxcap;
+    a.cand_cap = (cap > 0 && cap < maxcap) ? cap : maxcap;
     (void)hipGetLastError();
     return hip_status(entmax::launch_attn_fwd(a, 3, (hipStream_t)stream));
+}
+
+int entmax_attn_threshold(const void* Q, const void* K, float* tau, uint32_t* block_mask,
+                          int B, int H, int L, int d, float scale, float alpha, int dtype,
+                          int mask, int window, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return entmax_attn_threshold_ex(Q, K, tau, block_mask, B, H, L, d, scale, alpha, dtype, mask,
+                                    window, workspace, workspace_bytes, nullptr, stream);
 }
 
 int entmax_attn_score_stats(const void* Q, const void* K, int B, int H, int L, int d, float scale,

@@ -301,17 +301,15 @@ def bench_wide_rows(api, torch, timer, steps, warmup):
     lib = api.lib()
     st = api._stream(S.device)
 
-    def run():
-        r = lib.entmax_tau_rows(S.data_ptr(), P.data_ptr(), tau.data_ptr(), rows, cols, cols, 1.5, st)
-        assert r == 0, api.status_str(r)
-
     out = {"workload": f"rows{rows}x{cols}_f32_dense (0.02 N(0, 1))"}
     for hist in (1, 0):
-        prev = api.set_option(api.OPT_ROW_HISTOGRAM, hist)
-        try:
-            t = timer(run, max(steps // 2, 5), 2)
-        finally:
-            api.set_option(api.OPT_ROW_HISTOGRAM, prev)
+        opts = api._opts(0, row_plain_bracket=not hist)
+
+        def run():
+            r = lib.entmax_tau_rows_ex(S.data_ptr(), P.data_ptr(), tau.data_ptr(), rows, cols, cols, 1.5, opts, st)
+            assert r == 0, api.status_str(r)
+
+        t = timer(run, max(steps // 2, 5), 2)
         out["histogram_ms" if hist else "bracket_only_ms"] = round(t, 5)
     del S, P
     torch.cuda.empty_cache()

@@ -31,8 +31,10 @@
  *    with tau_i from Newton steps from below (bisection-guarded); alpha = 2
  *    is sparsemax.
  *  - Outputs are overwritten, never accumulated into.
- *  - The library keeps no per-call state; concurrent calls on different
- *    streams are safe when their outputs and workspaces are disjoint.
+ *  - The library keeps no mutable host state: every choice a call makes comes
+ *    from its own arguments (the _ex variants take an options struct).
+ *    Concurrent calls on different streams are safe when their outputs and
+ *    workspaces are disjoint.
  */
 #ifndef ENTMAX_H
 #define ENTMAX_H
@@ -111,9 +113,9 @@ int entmax_tau_rows(const float* S, float* P, float* tau, int64_t rows, int64_t 
 /*
  * Workspace bytes entmax_attn_fwd needs: per-row statistics of the score
  * sweep (8 bytes per query row), the largest score of every (64-row block,
- * 64-key tile) (4 bytes each), and per query row (L rounded up to 128) a
- * list of up to 128 candidate scores with their key tiles
- * (768 bytes per row), plus room for the block mask (used only when
+ * 64-key tile) (4 bytes each), per query row (L rounded up to 128) a list of
+ * up to 128 candidate scores with their key indices (1024 bytes per row),
+ * 4 bytes per 128-row block, plus room for the block mask (used only when
  * block_mask == NULL).  entmax_attn_threshold needs the same minus the
  * mask part: entmax_attn_threshold_workspace.  Both return 0 for invalid
  * arguments; the calls report those.
@@ -231,22 +233,35 @@ int entmax_attn_decode(const void* q, const void* K, const void* V, float* O, fl
                        size_t workspace_bytes, void* stream);
 
 /*
- * Process-wide tuning / testing options (not thread-safe; set before use).
- *  ENTMAX_OPT_CANDIDATE_CAP: per-row capacity of the forward's candidate
- *    list, 1 .. 128 (value <= 0 restores 128).  Rows with more candidates
- *    are collected again above a tighter bound, then take the iterative
- *    full-sweep path; tests use a tiny cap to force those paths.
- *  ENTMAX_OPT_ROW_HISTOGRAM: 1 (default) or 0.  entmax_tau_rows on rows
- *    wider than 8192 bins the candidates into 64 left-edge bins and starts
- *    the refinement from the histogram bracket [tau_h, tau_h + 1/(64
- *    (alpha - 1))] ("AdaSplash-2: Faster Differentiable Sparse Attention"
- *    sec. 3.1 and Proposition 3.1); 0 starts from [m - 1/(alpha-1),
- *    m - n^(1-alpha)/(alpha-1)].  Results are the same either way.
- * Returns the previous value, or -ENTMAX_ERR_ARG for an unknown option or an
- * out-of-range value.
+ * Per-call options of the _ex entry points below.  A zero-initialised struct
+ * (or a NULL pointer) selects the defaults, which are what the plain entry
+ * points use.
+ *  candidate_cap: per-row capacity of the forward's candidate list, 1 .. 128
+ *    (0: 128).  Rows with more candidates above their lower bound take the
+ *    histogram-initialised sweeps (AdaSplash-2 sec. 3.1 and sec. 3.3 phases
+ *    2-3); tests use a tiny cap to force that path.  Results agree either way
+ *    within the tolerances.  Values outside 0 .. 128 give ENTMAX_ERR_ARG.
+ *  row_plain_bracket: entmax_tau_rows on rows wider than 8192 starts its
+ *    refinement from the histogram bracket [tau_h, tau_h + 1/(64 (alpha-1))]
+ *    of AdaSplash-2 sec. 3.1 and Proposition 3.1 (0, the default), or from the
+ *    plain bracket [m - 1/(alpha-1), m - n^(1-alpha)/(alpha-1)] (1).  Other
+ *    values give ENTMAX_ERR_ARG.
  */
-enum { ENTMAX_OPT_CANDIDATE_CAP = 1, ENTMAX_OPT_ROW_HISTOGRAM = 2 };
-int entmax_set_option(int option, int value);
+typedef struct entmax_options {
+    int candidate_cap;
+    int row_plain_bracket;
+} entmax_options;
+
+int entmax_tau_rows_ex(const float* S, float* P, float* tau, int64_t rows, int64_t cols,
+                       int64_t ld, float alpha, const entmax_options* options, void* stream);
+int entmax_attn_fwd_ex(const void* Q, const void* K, const void* V, float* O, float* tau,
+                       uint32_t* block_mask, int B, int H, int L, int d, float scale, float alpha,
+                       int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
+                       const entmax_options* options, void* stream);
+int entmax_attn_threshold_ex(const void* Q, const void* K, float* tau, uint32_t* block_mask,
+                             int B, int H, int L, int d, float scale, float alpha, int dtype,
+                             int mask, int window, void* workspace, size_t workspace_bytes,
+                             const entmax_options* options, void* stream);
 
 #ifdef __cplusplus
 }

@@ -220,31 +220,29 @@ double orc_entmax_tau_alpha(const double* s, int64_t n, double alpha, double* wo
 
 /*
  * Histogram threshold of AdaSplash-2 sec. 3.1 / appendix C.3 for one row, in
- * score units.  z_j = (alpha-1)(s_j - m) + 1 is formed in fp32 exactly as
- * the GPU forms it (fma of the fp32 difference), binned into B left-edge
- * bins k = min(floor(B z), B - 1) for z >= 0; the histogram objective
- * sum_k H_k [k/B - tau]_+^e = 1 is then solved in fp64: by the sorting scan
- * over the bins (from the top) for alpha = 1.5 (a quadratic per prefix) and
- * alpha = 2 (linear), by bisection otherwise.  Proposition 3.1 of the pages:
- * tau* - h < tau_h <= tau* with h = 1/(B (alpha-1)) in score units.
+ * score units.  z_j = (alpha-1)(s_j - m) + 1 (the pages' (alpha-1)s - (m'-1)
+ * with m' = (alpha-1) max s) is formed in fp64 from the fp32 inputs, binned
+ * into B left-edge bins k = min(floor(B z), B - 1) for z >= 0; the histogram
+ * objective sum_k H_k [k/B - tau]_+^e = 1 is then solved in fp64: by the
+ * sorting scan over the bins (from the top) for alpha = 1.5 (a quadratic per
+ * prefix) and alpha = 2 (linear), by bisection otherwise.  Proposition 3.1 of
+ * the pages: tau* - h < tau_h <= tau* with h = 1/(B (alpha-1)) in score units.
  */
 double orc_entmax_tau_histogram(const float* s, int64_t n, float alpha, int B) {
-    float m = -INFINITY;
-    for (int64_t j = 0; j < n; ++j) m = s[j] > m ? s[j] : m;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) m = (double)s[j] > m ? (double)s[j] : m;
     if (m == -INFINITY) return -INFINITY;
-    const float am1 = alpha - 1.0f;
+    const double a1 = (double)alpha - 1.0, e = 1.0 / a1;
     double* H = (double*)calloc((size_t)B, sizeof(double));
     for (int64_t j = 0; j < n; ++j) {
         if (s[j] == -INFINITY) continue;
-        const float diff = s[j] - m;
-        const float z = fmaf(am1, diff, 1.0f);
-        if (!(z >= 0.0f)) continue;
-        int k = (int)floorf(z * (float)B);
+        const double z = a1 * ((double)s[j] - m) + 1.0;
+        if (!(z >= 0.0)) continue;
+        int k = (int)floor(z * (double)B);
         if (k > B - 1) k = B - 1;
         if (k < 0) k = 0;
         H[k] += 1.0;
     }
-    const double a1 = (double)am1, e = 1.0 / a1;
     double tz;
     if (alpha == 1.5f || alpha == 2.0f) {
         /* prefix scan over the bins from the top; the support of the binned
@@ -284,7 +282,7 @@ double orc_entmax_tau_histogram(const float* s, int64_t n, float alpha, int B) {
         tz = 0.5 * (lo + hi);
     }
     free(H);
-    return (double)m + (tz - 1.0) * e;
+    return m + (tz - 1.0) * e;
 }
 
 /* Weight p and derivative g = dp/ds of one score at threshold tau. */

@@ -138,14 +138,20 @@ def test_attn_bwd_validation(api):
     assert call(6, FAKE + 4) == api.ERR_ALIGN
 
 
-def test_set_option(api):
-    prev = api.set_option(api.OPT_CANDIDATE_CAP, 5)
-    assert api.set_option(api.OPT_CANDIDATE_CAP, 0) == 5
-    assert api.set_option(api.OPT_CANDIDATE_CAP, prev) == 0
-    with pytest.raises(api.EntmaxError):
-        api.set_option(99, 1)
-    with pytest.raises(api.EntmaxError):
-        api.set_option(api.OPT_CANDIDATE_CAP, 1 << 20)
+def test_options_validation(api):
+    """Per-call options: out-of-range values are rejected before any launch."""
+    import ctypes as C
+    L = api.lib()
+    bad = [api.Options(-1, 0), api.Options(129, 0), api.Options(0, 2)]
+    for o in bad:
+        assert L.entmax_tau_rows_ex(FAKE, None, FAKE, 4, 8, 8, 1.5, C.byref(o), None) == api.ERR_ARG
+        assert L.entmax_attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 64, 0.125, 1.5, 1, 0, 0,
+                                    FAKE, 1 << 24, C.byref(o), None) == api.ERR_ARG
+        assert L.entmax_attn_threshold_ex(FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 64, 0.125, 1.5, 1, 0, 0,
+                                          FAKE, 1 << 24, C.byref(o), None) == api.ERR_ARG
+    # NULL options and an all-zero struct are the defaults: rows == 0 is a no-op either way
+    assert L.entmax_tau_rows_ex(None, None, None, 0, 8, 8, 1.5, None, None) == api.OK
+    assert L.entmax_tau_rows_ex(None, None, None, 0, 8, 8, 1.5, C.byref(api.Options(0, 0)), None) == api.OK
 
 
 def test_decode_validation(api):

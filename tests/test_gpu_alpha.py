@@ -38,9 +38,10 @@ def gen(B, H, L, d, dtype, seed, clusters=0, with_grad=False):
     return gen_attn(B, H, L, d, dtype, seed, clusters=clusters, with_grad=with_grad)
 
 
-def check_fwd(api, torch, orc, inp, scale, mode, W, alpha, dtype, rows=None, mask_heads=None, label=""):
+def check_fwd(api, torch, orc, inp, scale, mode, W, alpha, dtype, rows=None, mask_heads=None, label="",
+              candidate_cap=0):
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
-    O, tau, bm = api.attn_fwd(q, k, v, scale=scale, mask=mode, window=W, alpha=alpha)
+    O, tau, bm = api.attn_fwd(q, k, v, scale=scale, mask=mode, window=W, alpha=alpha, candidate_cap=candidate_cap)
     torch.cuda.synchronize()
     O, tau, bm = O.cpu().numpy(), tau.cpu().numpy(), bm.cpu().numpy().view(np.uint32)
     Q, K, V = (inp[n].float().numpy() for n in ("q", "k", "v"))
@@ -100,20 +101,16 @@ def test_alpha_clustered_long_rows_sampled(env, orc, alpha):
 
 
 @pytest.mark.parametrize("alpha", [1.25, 2.0])
-@pytest.mark.parametrize("cap", [1, 3])
+@pytest.mark.parametrize("cap", [1, 8])
 def test_alpha_forced_fallback(env, orc, alpha, cap):
     """Tiny candidate capacity: the overflow rounds and the full-sweep
     Newton-bisection path at general alpha."""
     api, torch = env
     a = f32(alpha)
-    prev = api.set_option(api.OPT_CANDIDATE_CAP, cap)
-    try:
-        for (B, H, L, d, dtype, mode, W) in ((1, 2, 300, 64, "bf16", 1, 0), (1, 1, 130, 128, "f32", 2, 7)):
-            inp = gen(B, H, L, d, dtype, seed=cap * 10 + L)
-            check_fwd(api, torch, orc, inp, 1.0 / math.sqrt(d), mode, W, a, dtype,
-                      label=f"fallback alpha={alpha} cap={cap}")
-    finally:
-        api.set_option(api.OPT_CANDIDATE_CAP, prev)
+    for (B, H, L, d, dtype, mode, W) in ((1, 2, 300, 64, "bf16", 1, 0), (1, 1, 130, 128, "f32", 2, 7)):
+        inp = gen(B, H, L, d, dtype, seed=cap * 10 + L)
+        check_fwd(api, torch, orc, inp, 1.0 / math.sqrt(d), mode, W, a, dtype,
+                  label=f"fallback alpha={alpha} cap={cap}", candidate_cap=cap)
 
 
 def test_alpha_out_of_range_rejected(env):

@@ -26,9 +26,10 @@ def env():
     return api, torch
 
 
-def run_gpu(api, torch, inp, scale, mode, W, want_mask=True):
+def run_gpu(api, torch, inp, scale, mode, W, want_mask=True, candidate_cap=0):
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
-    O, tau, bm = api.attn_fwd(q, k, v, scale=scale, mask=mode, window=W, want_block_mask=want_mask)
+    O, tau, bm = api.attn_fwd(q, k, v, scale=scale, mask=mode, window=W, want_block_mask=want_mask,
+                              candidate_cap=candidate_cap)
     torch.cuda.synchronize()
     return O.cpu().numpy(), tau.cpu().numpy(), (bm.cpu().numpy().view(np.uint32) if bm is not None else None)
 
@@ -158,20 +159,22 @@ def test_c4_full_size_sampled(env, orc):
 
 
 def test_c5_forward_sampled(env, orc):
-    """B1 H16 L16384 d128 causal: sampled rows of every head."""
+    """B1 H16 L16384 d128 causal: every row of one head, sampled rows of
+    every other head."""
     api, torch = env
     from adaptive_sparse_attention_row_amd.workloads import C5, gen_config
     inp = gen_config(C5)
     O, tau, bm = run_gpu(api, torch, inp, C5.scale, C5.mask, C5.window)
     L = C5.L
     rng = np.random.default_rng(1)
-    rows = []
+    full_head = 11
+    rows = [full_head * L + np.arange(L)]
     for bh in range(C5.B * C5.H):
-        pick = np.concatenate([[0, 1, 63, 64, 127, 128, L - 1], rng.integers(0, L, 24)])
-        rows.extend(bh * L + pick)
-    rows = np.array(rows)
+        if bh != full_head:
+            rows.append(bh * L + np.concatenate([[0, 1, 63, 64, 127, 128, L - 1], rng.integers(0, L, 24)]))
+    rows = np.concatenate(rows)
     err = check_rows(orc, inp, C5.scale, C5.mask, C5.window, O, tau, "bf16", rows=rows, label="c5")
-    print(f"c5 sampled max |dO| = {err:.3e}")
+    print(f"c5 (head {full_head} whole, others sampled) max |dO| = {err:.3e}")
 
 
 def test_degenerate_rows(env, orc):
@@ -183,7 +186,7 @@ def test_degenerate_rows(env, orc):
     inp = gen(B, H, L, d, "bf16", seed=9)
     inp["q"][0, 0] = 0            # head 0: all scores 0 -> uniform weights
     # head 1: each query aligned with its own key far above the rest
-    k1 = T.randn(L, d)
+    k1 = T.randn(L, d, generator=T.Generator().manual_seed(90))
     inp["k"][0, 1] = k1.to(T.bfloat16)
     inp["q"][0, 1] = (8.0 * k1).to(T.bfloat16)
     for mode, W in ((0, 0), (1, 0), (2, 3)):
@@ -192,21 +195,17 @@ def test_degenerate_rows(env, orc):
         check_mask(orc, inp, 1.0 / 8, mode, W, bm, [0, 1], label=f"degenerate mode {mode}")
 
 
-@pytest.mark.parametrize("cap", [1, 3])
+@pytest.mark.parametrize("cap", [1, 8])
 def test_forced_fallback(env, orc, cap):
     """A tiny candidate capacity sends every row with more candidates than
-    `cap` through the iterative full-sweep path."""
+    `cap` through the overflow path."""
     api, torch = env
-    prev = api.set_option(api.OPT_CANDIDATE_CAP, cap)
-    try:
-        for (B, H, L, d, dtype, mode, W) in ((1, 2, 300, 64, "bf16", 1, 0), (1, 1, 200, 128, "bf16", 0, 0),
-                                            (1, 1, 130, 64, "f32", 2, 7)):
-            inp = gen(B, H, L, d, dtype, seed=cap * 100 + L)
-            O, tau, bm = run_gpu(api, torch, inp, 1.0 / math.sqrt(d), mode, W)
-            check_rows(orc, inp, 1.0 / math.sqrt(d), mode, W, O, tau, dtype, label=f"fallback cap={cap}")
-            check_mask(orc, inp, 1.0 / math.sqrt(d), mode, W, bm, range(B * H), label=f"fallback cap={cap}")
-    finally:
-        api.set_option(api.OPT_CANDIDATE_CAP, prev)
+    for (B, H, L, d, dtype, mode, W) in ((1, 2, 300, 64, "bf16", 1, 0), (1, 1, 200, 128, "bf16", 0, 0),
+                                        (1, 1, 130, 64, "f32", 2, 7)):
+        inp = gen(B, H, L, d, dtype, seed=cap * 100 + L)
+        O, tau, bm = run_gpu(api, torch, inp, 1.0 / math.sqrt(d), mode, W, candidate_cap=cap)
+        check_rows(orc, inp, 1.0 / math.sqrt(d), mode, W, O, tau, dtype, label=f"fallback cap={cap}")
+        check_mask(orc, inp, 1.0 / math.sqrt(d), mode, W, bm, range(B * H), label=f"fallback cap={cap}")
 
 
 def test_no_mask_output_and_window_extremes(env, orc):
@@ -285,8 +284,14 @@ def test_score_stats_bounds(env, orc, cfgname):
 @pytest.mark.parametrize("d", [64, 128])
 def test_large_v(env, orc, vbig, d):
     """bf16 V entries beyond fp16 range (|v| > 65504) send their workgroup
-    through the bf16 hi + lo product; entries inside it stay on fp16.  Both
-    must match the oracle to the bf16 bound relative to max |V|."""
+    through the bf16 hi + lo product; entries inside it stay on fp16.
+
+    Bound per row: a row whose support (widened by the 1e-4 tie band below
+    tau) holds none of the planted large V rows is held to the plain 2e-3
+    absolute bound, also when its workgroup took the hi + lo redo; a row
+    that attends to one is held to 2e-3 times the largest |V_j| on its own
+    (widened) support, since the error of any rounding of A scales with the
+    V rows it multiplies."""
     api, torch = env
     import torch as T
     inp = gen(1, 2, 300, d, "bf16", seed=77 + d)
@@ -294,14 +299,32 @@ def test_large_v(env, orc, vbig, d):
     v[0, 0, 5] = vbig          # one key row of head 0
     v[0, 1, 130, : d // 2] = -vbig   # part of a key row of head 1
     inp["v"] = v.to(T.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    Q, K, V = np32(inp["q"]), np32(inp["k"]), np32(inp["v"])
+    B, H, L, _ = Q.shape
+    vrow = np.abs(V.astype(np.float64)).max(axis=-1).reshape(B * H, L)   # max |V_j| per key row
     for mode, W in ((0, 0), (1, 0)):
-        O, tau, _ = run_gpu(api, torch, inp, 1.0 / math.sqrt(d), mode, W, want_mask=False)
+        O, tau, _ = run_gpu(api, torch, inp, scale, mode, W, want_mask=False)
         assert np.all(np.isfinite(O)), f"non-finite O for |v| = {vbig}"
-        Q, K, V = np32(inp["q"]), np32(inp["k"]), np32(inp["v"])
-        O_ref, tau_ref, _, _ = orc.attn_fwd(Q, K, V, 1.0 / math.sqrt(d), mode, W)
-        vmax = float(np.abs(V).max())
-        err = np.abs(O.reshape(-1, d) - O_ref).max()
-        assert err <= O_TOL["bf16"] * max(1.0, vmax), f"|v| = {vbig} mode {mode}: O max err {err}"
+        O_ref, tau_ref, _, _ = orc.attn_fwd(Q, K, V, scale, mode, W)
+        err = np.abs(O.reshape(-1, d) - O_ref).max(axis=1).reshape(B * H, L)
+        tref = tau_ref.reshape(B * H, L)
+        n_big = 0
+        for bh in range(B * H):
+            b, h = divmod(bh, H)
+            S = scale * (Q[b, h].astype(np.float64) @ K[b, h].astype(np.float64).T)
+            if mode == 1:
+                S = np.where(np.tril(np.ones((L, L), dtype=bool)), S, -np.inf)
+            near = S > (tref[bh] - BAND)[:, None]          # support plus the tie band
+            vsup = np.where(near, vrow[bh][None, :], 0.0).max(axis=1)
+            big = vsup >= 0.5 * vbig      # a planted row is on the support
+            n_big += int(big.sum())
+            bound = np.where(big, O_TOL["bf16"] * vsup, O_TOL["bf16"])
+            bad = np.nonzero(err[bh] > bound)[0]
+            assert bad.size == 0, (f"|v| = {vbig} mode {mode} head {bh}: rows {bad[:8]} err "
+                                   f"{err[bh][bad[:8]]} bound {bound[bad[:8]]}")
+        print(f"|v| = {vbig:.1e} d={d} mode {mode}: {n_big} rows with a large V entry on their support; "
+              f"max err on the others {np.where(err > 0, err, 0).max():.3e}")
 
 
 @pytest.mark.parametrize("nc", [16, 4, 1])
@@ -325,3 +348,50 @@ def test_sparsity_sweep_sampled(env, orc, nc):
     check_mask(orc, inp, cfg.scale, cfg.mask, cfg.window, bm, [1], label=cfg.name)
     nnz = sum(bin(int(x)).count("1") for x in bm.reshape(-1))
     print(f"{cfg.name}: max |dO| = {err:.3e}, block sparsity {1 - nnz / (2 * 128 * 128):.4f}")
+
+
+def _fwd_raw(api, torch, q, k, v, scale, mode, W, fill, alpha=1.5):
+    """entmax_attn_fwd through the C ABI with a workspace pre-filled with
+    `fill` (the contract says its contents on entry are ignored)."""
+    B, H, L, d = q.shape
+    dt = api._dtype_code(q)
+    lib = api.lib()
+    O = torch.full((B, H, L, d), float("nan"), device="cuda")
+    tau = torch.full((B, H, L), float("nan"), device="cuda")
+    bm = torch.full(api.mask_shape(B, H, L, d, dt), -1, device="cuda", dtype=torch.int32)
+    wsb = lib.entmax_attn_fwd_workspace(B, H, L, d, dt, mode, W)
+    ws = torch.full((wsb,), fill, device="cuda", dtype=torch.uint8)
+    st = lib.entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(), tau.data_ptr(),
+                             bm.data_ptr(), B, H, L, d, float(scale), float(alpha), dt, mode, W,
+                             ws.data_ptr(), wsb, api._stream(q.device))
+    assert st == 0, api.status_str(st)
+    torch.cuda.synchronize()
+    return O.cpu().numpy(), tau.cpu().numpy(), bm.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["c3a_h4", "c5_h2_L4096", "dense_rows", "alpha1.25", "win32"])
+def test_forward_deterministic(env, case):
+    """Two calls on the same inputs, each with a workspace holding different
+    garbage, give bit-identical tau, O and block mask.  The candidate lists
+    are filled in an order that depends on timing; every sum over them must
+    not."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C3A, C5, gen_config
+    alpha, mode, W = 1.5, 1, 0
+    if case == "c3a_h4":
+        inp, scale = gen_config(C3A, B=1, H=4), C3A.scale
+    elif case == "c5_h2_L4096":
+        inp, scale = gen_config(C5, H=2, L=4096), C5.scale
+    elif case == "dense_rows":
+        # near-uniform scores: lists overflow on almost every row
+        inp, scale, mode = gen(1, 2, 1500, 64, "bf16", seed=5, q_std=0.05), 0.125, 0
+    elif case == "alpha1.25":
+        inp, scale, alpha = gen_config(C3A, B=1, H=2), C3A.scale, 1.25
+    else:
+        inp, scale, mode, W = gen_config(C3A, B=1, H=2), C3A.scale, 2, 32
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    a = _fwd_raw(api, torch, q, k, v, scale, mode, W, 0x00, alpha)
+    b = _fwd_raw(api, torch, q, k, v, scale, mode, W, 0xA5, alpha)
+    for name, x, y in zip(("O", "tau", "mask"), a, b):
+        assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                              y.view(np.uint32) if y.dtype == np.float32 else y), f"{case}: {name} differs between calls"

@@ -46,7 +46,7 @@ def _check(S_np, tau_gpu, P_gpu, orc, label="", alpha=1.5):
     assert np.all(P_gpu[~finite_rows] == 0), label
 
 
-def _run(api, torch, S_np, want_p=True, ld=None, alpha=1.5):
+def _run(api, torch, S_np, want_p=True, ld=None, alpha=1.5, row_plain_bracket=False):
     rows, cols = S_np.shape
     if ld is None or ld == cols:
         S = torch.from_numpy(S_np).cuda()
@@ -54,7 +54,7 @@ def _run(api, torch, S_np, want_p=True, ld=None, alpha=1.5):
         big = torch.zeros(rows, ld, dtype=torch.float32)
         big[:, :cols] = torch.from_numpy(S_np)
         S = big.cuda()[:, :cols]
-    tau, P = api.tau_rows(S, want_p=want_p, alpha=alpha)
+    tau, P = api.tau_rows(S, want_p=want_p, alpha=alpha, row_plain_bracket=row_plain_bracket)
     torch.cuda.synchronize()
     return tau.cpu().numpy(), (P.cpu().numpy() if P is not None else None)
 
@@ -244,19 +244,15 @@ def test_wide_rows_histogram_bracket(env, orc, alpha, hist):
     LDS list, near-constant and one-hot rows; same results either way."""
     api, torch = env
     a = float(np.float32(alpha))
-    prev = api.set_option(api.OPT_ROW_HISTOGRAM, hist)
-    try:
-        rng = np.random.default_rng(70 + hist)
-        cols = 20000
-        S = rng.normal(size=(8, cols)).astype(np.float32)
-        S[1] *= 0.02                       # dense: every score near the max
-        S[2] = 3.0; S[2, ::7] = 2.9        # near-constant
-        S[3] = -5.0; S[3, 1234] = 5.0      # one-hot
-        S[4] *= 4.0
-        S[5, :10000] = -np.inf             # half masked
-        S[6] = np.linspace(-0.5, 0.5, cols)
-        S[7] *= 0.3
-        tau, P = _run(api, torch, S, alpha=a)
-        _check(S, tau, P, orc, f"wide alpha={alpha} hist={hist}", alpha=a)
-    finally:
-        api.set_option(api.OPT_ROW_HISTOGRAM, prev)
+    rng = np.random.default_rng(70 + hist)
+    cols = 20000
+    S = rng.normal(size=(8, cols)).astype(np.float32)
+    S[1] *= 0.02                       # dense: every score near the max
+    S[2] = 3.0; S[2, ::7] = 2.9        # near-constant
+    S[3] = -5.0; S[3, 1234] = 5.0      # one-hot
+    S[4] *= 4.0
+    S[5, :10000] = -np.inf             # half masked
+    S[6] = np.linspace(-0.5, 0.5, cols)
+    S[7] *= 0.3
+    tau, P = _run(api, torch, S, alpha=a, row_plain_bracket=not hist)
+    _check(S, tau, P, orc, f"wide alpha={alpha} hist={hist}", alpha=a)
