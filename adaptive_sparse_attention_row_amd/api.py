@@ -14,7 +14,8 @@ from typing import Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libentmax.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALPHA, ERR_DTYPE, ERR_MASK, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_ARG = range(10)
+(OK, ERR_NULL, ERR_SHAPE, ERR_ALPHA, ERR_DTYPE, ERR_MASK, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_ARG,
+ ERR_SCRATCH) = range(11)
 MASK_NONE, MASK_CAUSAL, MASK_WINDOW_SINK = 0, 1, 2
 F32, BF16 = 0, 1
 
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
     L.entmax_attn_decode.restype = i32
     L.entmax_attn_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, f32, f32, i32, i32, i32,
                                      P, sz, P]
+    L.entmax_attn_decode_noalloc.restype = i32
+    L.entmax_attn_decode_noalloc.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, f32, f32, i32, i32,
+                                             i32, P]
     _lib = L
     return L
 
@@ -271,4 +275,31 @@ def attn_decode(q, k_cache, v_cache, L: Optional[int] = None, scale: Optional[fl
                                   tau.data_ptr(), B, H, L, Lc, d, float(scale), float(alpha), dt, mask,
                                   window, ws.data_ptr(), ws.numel(), _stream(q.device))
     _check("entmax_attn_decode", st)
+    return o, tau
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, L: Optional[int] = None, scale: Optional[float] = None,
+                        mask: int = MASK_CAUSAL, window: int = 0, alpha: float = 1.5, out=None, tau=None):
+    """attn_decode through the allocation-free entry point: no workspace; the
+    library's static per-device scratch holds the scores (calls that overlap
+    on one device race).  `out` and `tau` may be passed in so that the call
+    itself allocates nothing."""
+    import torch
+    B, H, Lc, d = k_cache.shape
+    if L is None:
+        L = Lc
+    if q.shape != (B, H, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, H, d] and the caches [B, H, cache_len, d]")
+    for t in (q, k_cache, v_cache):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q and the caches must be contiguous CUDA tensors of one dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty(B, H, d, device=q.device, dtype=torch.float32)
+    tau = tau if tau is not None else torch.empty(B, H, device=q.device, dtype=torch.float32)
+    st = lib().entmax_attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+                                          tau.data_ptr(), B, H, L, Lc, d, float(scale), float(alpha), dt, mask,
+                                          window, _stream(q.device))
+    _check("entmax_attn_decode_noalloc", st)
     return o, tau

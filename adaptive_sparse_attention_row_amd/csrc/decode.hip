@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "row_solve.hpp"
@@ -422,6 +424,37 @@ hipError_t launch_attn_decode(const AttnArgs& a, int Lcap, hipStream_t stream) {
     }
     if (a.d == 64) return launch_typed<float, 64>(dp, stream);
     return launch_typed<float, 128>(dp, stream);
+}
+
+// ------------------------------------------------ allocation-free decode
+// The per-key scores of entmax_attn_decode_noalloc live in this file-scope
+// array instead of a caller workspace: every device the library runs on
+// holds its own copy, at its own address, until the process ends.  In host
+// code `scratch` names a host-side stand-in, so its device address is looked
+// up once per device (hipGetSymbolAddress with that device current) and only
+// that address is ever handed to a kernel.
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace entmax

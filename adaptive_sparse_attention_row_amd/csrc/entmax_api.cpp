@@ -57,6 +57,7 @@ const char* entmax_status_str(int status) {
         case ENTMAX_ERR_ALIGN: return "pointer not 16-byte aligned";
         case ENTMAX_ERR_HIP: return "HIP launch failed";
         case ENTMAX_ERR_ARG: return "invalid argument";
+        case ENTMAX_ERR_SCRATCH: return "input exceeds the static scratch of the allocation-free entry point";
         default: return "unknown status";
     }
 }
@@ -299,6 +300,33 @@ int entmax_attn_decode(const void* q, const void* K, const void* V, float* O, fl
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     (void)hipGetLastError();
+    return hip_status(entmax::launch_attn_decode(a, cache_len, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int entmax_attn_decode_noalloc(const void* q, const void* K, const void* V, float* O, float* tau,
+                               int B, int H, int L, int cache_len, int d, float scale, float alpha,
+                               int dtype, int mask, int window, void* stream) {
+    if (q == nullptr || K == nullptr || V == nullptr || O == nullptr || tau == nullptr)
+        return ENTMAX_ERR_NULL;
+    int st = check_decode(B, H, L, cache_len, d, alpha, dtype, mask, window);
+    if (st != ENTMAX_OK) return st;
+    if (!(scale > 0.0f) || !isfinite(scale)) return ENTMAX_ERR_ARG;
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V)) return ENTMAX_ERR_ALIGN;
+    if (((uintptr_t)O & 3u) || ((uintptr_t)tau & 3u)) return ENTMAX_ERR_ALIGN;
+    if (entmax::attn_decode_workspace_bytes(B, H, L, mask, window) > entmax::kDecodeScratchBytes)
+        return ENTMAX_ERR_SCRATCH;
+    void* scratch = nullptr;
+    (void)hipGetLastError();
+    if (entmax::decode_scratch_address(&scratch) != hipSuccess) return ENTMAX_ERR_HIP;
+    entmax::AttnArgs a = {};
+    a.q = q; a.k = K; a.v = V; a.o = O; a.tau = tau;
+    a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
+    a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
+    a.workspace = scratch; a.workspace_bytes = entmax::kDecodeScratchBytes;
     return hip_status(entmax::launch_attn_decode(a, cache_len, (hipStream_t)stream));
 }
 

@@ -49,5 +49,9 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream);
 // caches [B][H][Lcap][d] of which rows 0 .. L - 1 are used; a.o [B][H][d].
 size_t attn_decode_workspace_bytes(int B, int H, int L, int mask, int window);
 hipError_t launch_attn_decode(const AttnArgs& a, int Lcap, hipStream_t stream);
+// Bytes of the static per-device scratch of the allocation-free decode, and
+// its device address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch_address(void** out);
 
 }  // namespace entmax

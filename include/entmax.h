@@ -34,7 +34,8 @@
  *  - The library keeps no mutable host state: every choice a call makes comes
  *    from its own arguments (the _ex variants take an options struct).
  *    Concurrent calls on different streams are safe when their outputs and
- *    workspaces are disjoint.
+ *    workspaces are disjoint.  The one exception is entmax_attn_decode_noalloc,
+ *    whose calls on one device share a static scratch (see there).
  */
 #ifndef ENTMAX_H
 #define ENTMAX_H
@@ -56,7 +57,9 @@ enum {
     ENTMAX_ERR_WORKSPACE = 6, /* workspace missing or too small */
     ENTMAX_ERR_ALIGN = 7,     /* a pointer is not 16-byte aligned */
     ENTMAX_ERR_HIP = 8,       /* a HIP launch failed */
-    ENTMAX_ERR_ARG = 9        /* other invalid argument (scale, option) */
+    ENTMAX_ERR_ARG = 9,       /* other invalid argument (scale, option) */
+    ENTMAX_ERR_SCRATCH = 10   /* input larger than the static scratch of the
+                                 allocation-free entry point */
 };
 
 /* Mask modes (0-indexed positions i = query, j = key).
@@ -231,6 +234,26 @@ int entmax_attn_decode(const void* q, const void* K, const void* V, float* O, fl
                        int B, int H, int L, int cache_len, int d, float scale, float alpha,
                        int dtype, int mask, int window, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * entmax_attn_decode without a workspace, for callers that cannot allocate
+ * device memory around the call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and error
+ * codes as entmax_attn_decode, minus the workspace pair; it calls no
+ * allocating routine.  The per-key scores go to a static scratch array of
+ * ENTMAX_DECODE_SCRATCH_BYTES bytes that each device holds until the process
+ * ends: B * H * (active keys per head) * 4 bytes must fit in it (8,388,608
+ * active keys over all heads; e.g. B * H = 256 heads of 32768 cached keys),
+ * else ENTMAX_ERR_SCRATCH before any launch.  Every call on one device
+ * shares that device's scratch: calls that overlap on one device (different
+ * streams, different threads) race and must be serialised by the caller.
+ * Nothing in the scratch needs clearing between calls (each call writes the
+ * scores before reading them).
+ */
+#define ENTMAX_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int entmax_attn_decode_noalloc(const void* q, const void* K, const void* V, float* O, float* tau,
+                               int B, int H, int L, int cache_len, int d, float scale, float alpha,
+                               int dtype, int mask, int window, void* stream);
 
 /*
  * Per-call options of the _ex entry points below.  A zero-initialised struct

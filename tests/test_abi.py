@@ -38,7 +38,7 @@ def test_header_symbols_exported(api):
 
 
 def test_status_strings(api):
-    for s in range(10):
+    for s in range(11):
         assert api.status_str(s) and api.status_str(s) != "unknown status"
     assert api.status_str(99) == "unknown status"
 
@@ -180,3 +180,27 @@ def test_decode_validation(api):
     assert L.entmax_attn_decode_workspace(2, 3, 1000, 64, 1, 2, 32) == 2 * 3 * 34 * 4
     assert L.entmax_attn_decode_workspace(2, 3, 20, 64, 1, 2, 32) == 2 * 3 * 20 * 4
     assert L.entmax_attn_decode_workspace(1, 1, 10, 96, 1, 1, 0) == 0
+
+
+def test_decode_noalloc_validation(api):
+    """The allocation-free decode checks its arguments like the decode, and
+    rejects inputs whose scores do not fit its static scratch, all before
+    touching the device."""
+    L = api.lib()
+
+    def call(q=FAKE, K=FAKE, V=FAKE, O=FAKE, tau=FAKE, B=1, H=2, Lk=100, cap=128, d=64, scale=0.125,
+             alpha=1.5, dtype=1, mask=1, window=0):
+        return L.entmax_attn_decode_noalloc(q, K, V, O, tau, B, H, Lk, cap, d, scale, alpha, dtype, mask,
+                                            window, None)
+
+    assert call(q=None) == api.ERR_NULL
+    assert call(alpha=0.9) == api.ERR_ALPHA
+    assert call(Lk=200, cap=100) == api.ERR_SHAPE
+    assert call(scale=float("inf")) == api.ERR_ARG
+    assert call(K=FAKE + 8) == api.ERR_ALIGN
+    limit = 32 << 20                        # ENTMAX_DECODE_SCRATCH_BYTES
+    keys = limit // 4                       # active keys over all heads that fit
+    assert call(B=1, H=1, Lk=keys + 1, cap=keys + 1) == api.ERR_SCRATCH
+    assert call(B=2, H=4, Lk=keys // 8 + 1, cap=keys // 8 + 1) == api.ERR_SCRATCH
+    # a window keeps the active keys per head small whatever the cache length
+    assert L.entmax_attn_decode_workspace(64, 64, 1 << 20, 64, 1, 2, 32) <= limit
