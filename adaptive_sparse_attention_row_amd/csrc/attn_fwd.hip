@@ -911,20 +911,29 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const int row = qh * 64 + qb * 32 + m;
+                // skip the 32 x 64 block when no lane holds a candidate in it
+                float mx = neg_inf();
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][qb][r]);
+                if (__builtin_amdgcn_ballot_w64(mx > lr[qb]) == 0) continue;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float x = acc[kb][qb][r];
                         if (x > lr[qb]) {
-                            // past the capacity the last slot is overwritten: the
-                            // count shows the overflow and the list is not used
-                            const int c = min(cc[qb], capq - 1);
-                            u32x2 e;
-                            e[0] = __builtin_bit_cast(uint32_t, x * p.scale);
-                            e[1] = (uint32_t)(J * kBC + kb * 32 + key_of_reg(r, h));
-                            clist[(size_t)(4 * c + q) * kBR + row] = e;
-                            cc[qb] += 1;
+                            // past the capacity only the count goes on: it shows
+                            // the overflow, and the list is not used
+                            const int c = cc[qb];
+                            if (c < capq) {
+                                u32x2 e;
+                                e[0] = __builtin_bit_cast(uint32_t, x * p.scale);
+                                e[1] = (uint32_t)(J * kBC + kb * 32 + key_of_reg(r, h));
+                                clist[(size_t)(4 * c + q) * kBR + row] = e;
+                            }
+                            cc[qb] = c + 1;
                         }
                     }
             }
@@ -1003,17 +1012,20 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const int row = qh * 64 + qb * 32 + m;
+                float mx = neg_inf();
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][qb][r]);
+                if (__builtin_amdgcn_ballot_w64(mx > lr[qb]) == 0) continue;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float x = acc[kb][qb][r];
-                        const bool on = x > lr[qb];
-                        if (__builtin_amdgcn_ballot_w64(on) != 0) {
-                            if (on) {
-                                const int k = min((int)((x * p.scale - hlo[qb]) * hinv[qb]), kHistBins - 1);
-                                atomicAdd(&hist[k * kBR + row], 1);
-                            }
+                        if (x > lr[qb]) {
+                            const int k = min((int)((x * p.scale - hlo[qb]) * hinv[qb]), kHistBins - 1);
+                            atomicAdd(&hist[k * kBR + row], 1);
                         }
                     }
             }
@@ -1081,42 +1093,49 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
     if (any_row(kRowSweep)) {
         __shared__ float fb_t[kBR];
         __shared__ int fb_active[kBR];
-        __shared__ float fb_part[kBR][2][3];
+        __shared__ float fb_part[kBR][2][4];
         if (h == 0) {
             fb_active[srow] = rstate[srow] == kRowSweep ? 1 : 0;
             fb_t[srow] = row_lo[srow];
         }
         __syncthreads();
         for (int it = 0; it < kFbMaxIter; ++it) {
-            float tq[2];
-            bool aq[2];
+            float tq[2], lr[2];
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const int row = qh * 64 + qb * 32 + m;
-                aq[qb] = fb_active[row] != 0;
                 tq[qb] = fb_t[row];
+                lr[qb] = fb_active[row] != 0 ? raw_threshold(tq[qb], p.scale) : __builtin_inff();
             }
             float sc[2] = {0.f, 0.f}, sf[2] = {0.f, 0.f}, sf1[2] = {0.f, 0.f};
+            float smn[2] = {__builtin_inff(), __builtin_inff()};
             ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
-                    if (!aq[qb]) continue;
+                    float mx = neg_inf();
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][qb][r]);
+                    if (__builtin_amdgcn_ballot_w64(mx > lr[qb]) == 0) continue;
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const float s = acc[kb][qb][r] * p.scale;
-                            if (s > tq[qb]) {
+                            const float x = acc[kb][qb][r];
+                            if (x > lr[qb]) {
+                                const float sv = x * p.scale;
                                 sc[qb] += 1.f;
+                                smn[qb] = fminf(smn[qb], sv);
                                 if (p.gen) {
                                     // F = sum p, F1 = sum p/u (Newton)
-                                    const float u = p.am.am1 * (s - tq[qb]);
+                                    const float u = p.am.am1 * (sv - tq[qb]);
                                     const float pu = p.am.pw1(u);  // p / u
                                     sf[qb] = fmaf(pu, u, sf[qb]);
                                     sf1[qb] += pu;
                                 } else {
-                                    const float gg = 0.5f * (s - tq[qb]);
-                                    sf[qb] += gg * gg;
+                                    const float gg = 0.5f * (sv - tq[qb]);
+                                    sf[qb] = fmaf(gg, gg, sf[qb]);
                                     sf1[qb] += gg;
                                 }
                             }
@@ -1129,11 +1148,13 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                 sc[qb] += __shfl_xor(sc[qb], 32, kWave);
                 sf[qb] += __shfl_xor(sf[qb], 32, kWave);
                 sf1[qb] += __shfl_xor(sf1[qb], 32, kWave);
+                smn[qb] = fminf(smn[qb], __shfl_xor(smn[qb], 32, kWave));
                 if (h == 0) {
                     const int row = qh * 64 + qb * 32 + m;
                     fb_part[row][kh][0] = sc[qb];
                     fb_part[row][kh][1] = sf[qb];
                     fb_part[row][kh][2] = sf1[qb];
+                    fb_part[row][kh][3] = smn[qb];
                 }
             }
             if (t == 0) flag_s = 0;
@@ -1142,6 +1163,7 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                 const float C = fb_part[srow][0][0] + fb_part[srow][1][0];
                 const float F = fb_part[srow][0][1] + fb_part[srow][1][1];
                 const float F1 = fb_part[srow][0][2] + fb_part[srow][1][2];
+                const float mn = fminf(fb_part[srow][0][3], fb_part[srow][1][3]);
                 float lo = row_lo[srow], hi = row_hi[srow], tc = fb_t[srow];
                 if (p.gen) {
                     bool fin;
@@ -1154,12 +1176,29 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
                         atomicOr(&flag_s, 1);
                     }
                 } else {
-                    if (F - 1.0f >= 0.0f) lo = tc; else hi = tc;
-                    if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
+                    const bool below = F - 1.0f >= 0.0f;
+                    if (below) lo = tc; else hi = tc;
+                    // exact finish: the normaliser over the scores above tc is
+                    // the quadratic (C/4) u^2 - F1 u + F - 1 in u = tau - tc;
+                    // when its smaller root stays below all of those scores,
+                    // they are the support and tc + u is tau
+                    const float disc = fmaxf(F1 * F1 - C * (F - 1.0f), 0.0f);
+                    const float te = tc + (F1 - sqrtf(disc)) / (0.5f * C);
+                    const float tn = halley_or_bisect(tc, F, F1, C, lo, hi);
+                    if (below && C > 0.0f && te < mn) {
+                        fb_active[srow] = 0;
+                        row_tau[srow] = fmaxf(te, tc);
+                    } else if (below && fabsf(tn - tc) <= 1e-6f * fmaxf(1.0f, fabsf(tc))) {
+                        // Halley steps from below approach tau from one side, so
+                        // the bracket need not close: a step under 1e-6
+                        // relative (the fp32 sums round near 1e-7) ends it
+                        fb_active[srow] = 0;
+                        row_tau[srow] = tn;
+                    } else if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
                         fb_active[srow] = 0;
                         row_tau[srow] = 0.5f * (lo + hi);
                     } else {
-                        fb_t[srow] = halley_or_bisect(tc, F, F1, C, lo, hi);
+                        fb_t[srow] = tn;
                         atomicOr(&flag_s, 1);
                     }
                 }
@@ -1172,24 +1211,24 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
         // rows still active after the cap take their bracket midpoint
         if (h == 0 && fb_active[srow]) row_tau[srow] = 0.5f * (row_lo[srow] + row_hi[srow]);
         __syncthreads();
-        // mark the tiles of the swept rows
-        float tq[2];
-        bool aq[2];
+        // mark the tiles of the swept rows: a tile is set when some score of
+        // such a row exceeds its tau (compared as raw products)
+        float lr[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = qh * 64 + qb * 32 + m;
-            aq[qb] = rstate[row] == kRowSweep;
-            tq[qb] = row_tau[row];
+            lr[qb] = rstate[row] == kRowSweep ? raw_threshold(row_tau[row], p.scale) : __builtin_inff();
         }
         ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
             bool any = false;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                if (!aq[qb]) continue;
+                float mx = neg_inf();
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) any |= acc[kb][qb][r] * p.scale > tq[qb];
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][qb][r]);
+                any |= mx > lr[qb];
             }
             if (__ballot(any) != 0 && l == 0) atomicOr(&maskw[qh][J >> 5], 1u << (J & 31));
         });

@@ -34,6 +34,7 @@ class AttnConfig:
     seed: int
     clusters: int = 0   # > 0: clustered Q/K (contiguous runs per centroid)
     with_grad: bool = False
+    q_std: float = 1.0  # standard deviation of Q in plain mode
 
     @property
     def scale(self) -> float:
@@ -111,7 +112,7 @@ def gen_config(cfg: AttnConfig, L: Optional[int] = None, H: Optional[int] = None
                B: Optional[int] = None) -> dict:
     """Inputs of a named attention config, optionally at a smaller B/H/L."""
     return gen_attn(B or cfg.B, H or cfg.H, L or cfg.L, cfg.d, cfg.dtype, cfg.seed,
-                    clusters=cfg.clusters, with_grad=cfg.with_grad)
+                    clusters=cfg.clusters, with_grad=cfg.with_grad, q_std=cfg.q_std)
 
 
 def sweep_configs() -> list[AttnConfig]:
@@ -121,3 +122,17 @@ def sweep_configs() -> list[AttnConfig]:
         out.append(AttnConfig(f"sweep_nc{nc}", 1, 12, 8192, 64, "bf16", MASK_NONE, 0,
                               seed=40 + i, clusters=nc))
     return out
+
+
+QVAR_STDS = (0.1, 0.25, 0.5, 1.0, 2.0, 4.0, 8.0, 16.0, 32.0)
+
+
+def qvar_configs() -> list[AttnConfig]:
+    """Query-variance sweep ("AdaSplash-2: Faster Differentiable Sparse
+    Attention", sec. 4.2: Gaussian Q/K/V, d = 64, bf16, block sparsity set by
+    the variance of the queries): B1 H12 L8192 d64, K and V ~ N(0, 1),
+    Q ~ N(0, s^2) for each s of QVAR_STDS, scale 1/8, no mask.  Small s gives
+    near-uniform rows with supports of hundreds of keys, large s near one-hot
+    rows."""
+    return [AttnConfig(f"qvar_std{sd:g}", 1, 12, 8192, 64, "bf16", MASK_NONE, 0, seed=50 + i, q_std=sd)
+            for i, sd in enumerate(QVAR_STDS)]

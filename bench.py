@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix / vector, published
 METRIC = "1.5-entmax attn fwd ms + effective TFLOP/s at L=8192; tau-row kernel GB/s"
 
 
@@ -74,11 +75,14 @@ def counter_traffic(name, sources):
 
 
 class Timer:
-    """HIP-event timing of a callable over K launches on torch's current stream
-    (the stream the library is handed)."""
+    """HIP-event timing of a callable on torch's current stream (the stream the
+    library is handed): an event before the first call and after every call,
+    so each call's duration is the gap between consecutive events.  Returns
+    the median in ms; `last` keeps the median, minimum and mean of the call."""
 
     def __init__(self, torch):
         self.torch = torch
+        self.last = None
 
     def __call__(self, fn, steps, warmup):
         torch = self.torch
@@ -86,14 +90,17 @@ class Timer:
             fn()
         torch.cuda.synchronize()
         st = torch.cuda.current_stream()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(st)
+        for i in range(steps):
             fn()
-        e1.record(st)
+            ev[i + 1].record(st)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps  # ms per call
+        d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        med = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
+        self.last = {"median_ms": round(med, 5), "min_ms": round(d[0], 5),
+                     "mean_ms": round(sum(d) / len(d), 5), "calls": steps}
+        return med
 
 
 def pairs_of(cfg):
@@ -133,8 +140,59 @@ def structural_tiles(cfg):
     return n * cfg.B * cfg.H
 
 
-def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False, alpha=1.5):
-    """Forward (and backward) timing of one attention workload."""
+def issued_mfma_flop(cfg, ws, bm, scale):
+    """Matrix-core FLOPs the forward issues, counted from what its kernels
+    sweep (every 64-row x 64-key product is issued whole, masked or not):
+      * the score sweep: every (64-row block, key tile) the mask allows, one
+        product of 2*64*64*d;
+      * the candidate sweep: per 64-row half of a 128-row block, the tiles
+        whose largest score beats the smallest lower bound of the half's rows
+        (the workspace's row statistics and tile maxima after the call);
+      * the output pass: two products (scores again, then A.V) per non-null
+        (64-row block, tile) of the blocks whose O the solve kernel did not
+        write from its candidate lists (the workspace's per-block flags).
+    Sweeps of rows whose lists overflow are not counted.  ws is the workspace
+    as a numpy uint8 array after a full forward, laid out as the forward
+    kernels lay it out: row statistics [BH][L] (max, lower bound), the
+    tile maxima [BH][Tr64][Tc] at the next 256-byte boundary, the candidate
+    lists (1 KiB per row of L rounded up to 128), then one int per 128-row
+    block."""
+    import numpy as np
+    BH, L, d = cfg.B * cfg.H, cfg.L, cfg.d
+    T = -(-L // 64)
+    nQ = -(-L // 128)
+    r256 = lambda x: (x + 255) & ~255
+    o_um = r256(BH * L * 8)
+    o_cl = o_um + r256(BH * T * T * 4)
+    o_os = o_cl + r256(BH * nQ * 128 * 128 * 8)
+    rowstat = ws[: BH * L * 8].view(np.float32).reshape(BH, L, 2)
+    umax = ws[o_um: o_um + BH * T * T * 4].view(np.float32).reshape(BH, T, T) * np.float32(scale)
+    ostate = ws[o_os: o_os + BH * nQ * 4].view(np.int32).reshape(BH, nQ)
+    unit = 2 * 64 * 64 * d
+    stats = structural_tiles(cfg)
+    # the (64-row block, tile) pairs the mask allows
+    act = np.zeros((T, T), dtype=bool)
+    for I in range(T):
+        for J in range(T):
+            i0, i1, c0, c1 = 64 * I, min(64 * I + 63, L - 1), 64 * J, min(64 * J + 63, L - 1)
+            act[I, J] = cfg.mask == 0 or (c0 <= i1 and (cfg.mask == 1 or J == 0 or i0 - c1 <= cfg.window))
+    lo = rowstat[:, :, 1]
+    pad = np.full((BH, T * 64 - L), np.inf, dtype=np.float32)
+    half_min = np.concatenate([lo, pad], axis=1).reshape(BH, T, 64).min(axis=2)   # [BH][Tr64]
+    collect = int(((umax > half_min[:, :, None]) & act[None]).sum())
+    bits = np.unpackbits(bm.view(np.uint8).reshape(BH, T, -1), axis=2, bitorder="little")[:, :, :T]
+    tile_blocks = np.repeat(ostate == 0, 2, axis=1)[:, :T]
+    output = int((bits.astype(bool) & tile_blocks[:, :, None]).sum())
+    return {"score_sweep": stats * unit, "candidate_sweep": collect * unit, "output": output * 2 * unit,
+            "total": (stats + collect + 2 * output) * unit,
+            "blocks_from_lists": int((ostate != 0).sum()), "blocks": BH * nQ}
+
+
+def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False, alpha=1.5, bwd_steps=10):
+    """Forward (and backward) timing of one attention workload: the whole
+    forward, its threshold half, the score sweep alone, and the output pass
+    alone (entmax_attn_output over every block), each the median of `steps`
+    calls; plus the MFMA work the forward issued."""
     from adaptive_sparse_attention_row_amd.workloads import gen_config
     inp = gen_config(cfg)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
@@ -169,26 +227,41 @@ def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False, alpha=1.5)
                                    O.data_ptr(), B, H, L, d, sc, alpha, dt, cfg.mask, cfg.window, st)
         assert r == 0, api.status_str(r)
 
-    t_fwd = timer(fwd, steps, warmup)
-    t_thr = timer(thr, steps, warmup)
     t_stats = timer(stats, steps, warmup)
+    stats_t = timer.last
+    t_thr = timer(thr, steps, warmup)
     t_out = timer(out, steps, warmup)
+    t_fwd = timer(fwd, steps, warmup)   # last: the workspace then holds this call's state
+    fwd_t = timer.last
     torch.cuda.synchronize()
-    nnz = popcount_mask(bm.cpu().numpy())
+    bmn = bm.cpu().numpy()
+    nnz = popcount_mask(bmn)
     struct = structural_tiles(cfg)
     pairs = pairs_of(cfg)
+    issued = issued_mfma_flop(cfg, ws.cpu().numpy(), bmn, cfg.scale)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     res = {
         "fwd_ms": round(t_fwd, 5),
+        "fwd_min_ms": fwd_t["min_ms"],
         "threshold_ms": round(t_thr, 5),
         "score_stats_ms": round(t_stats, 5),
+        "score_stats_min_ms": stats_t["min_ms"],
         "solve_ms": round(t_thr - t_stats, 5),
-        "output_ms": round(t_out, 5),
+        "output_pass_alone_ms": round(t_out, 5),
+        "after_threshold_ms": round(t_fwd - t_thr, 5),
         "dense_equiv_tflops": round(4 * d * pairs / (t_fwd * 1e-3) / 1e12, 3),
         "score_stats_mfma_tflops": round(2 * d * pairs / (t_stats * 1e-3) / 1e12, 3),
+        "issued_mfma_tflop": round(issued["total"] / 1e12, 4),
+        "issued_mfma_tflops": round(issued["total"] / (t_fwd * 1e-3) / 1e12, 2),
+        "mfma_util_on_issued_work": round(issued["total"] / (t_fwd * 1e-3) / 1e12 / peak, 4),
+        "issued_split_tflop": {k2: round(v2 / 1e12, 4) for k2, v2 in issued.items()
+                               if k2 in ("score_sweep", "candidate_sweep", "output")},
+        "blocks_with_O_from_lists": f"{issued['blocks_from_lists']} of {issued['blocks']}",
         "nonnull_tiles_64": nnz,
         "structural_tiles_64": struct,
         "block_sparsity_64": round(1.0 - nnz / struct, 5),
         "pairs": pairs,
+        "calls_per_timing": steps,
     }
     if with_bwd:
         do = inp["do"].cuda()
@@ -201,43 +274,62 @@ def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False, alpha=1.5)
             r = lib.entmax_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), tau.data_ptr(),
                                     bm.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d,
                                     sc, alpha, dt, cfg.mask, cfg.window, bws.data_ptr(), bwsb, st)
-            if r != 0:
-                raise RuntimeError(api.status_str(r))
+            assert r == 0, api.status_str(r)
 
-        try:
-            t_bwd = timer(bwd, max(1, steps // 2), 1)
-            res["bwd_ms"] = round(t_bwd, 5)
-            res["bwd_dense_equiv_tflops"] = round(10 * d * pairs / (t_bwd * 1e-3) / 1e12, 3)
-        except RuntimeError as e:
-            res["bwd"] = f"not available: {e}"
+        t_bwd = timer(bwd, bwd_steps, 2)
+        res["bwd_ms"] = round(t_bwd, 5)
+        res["bwd_min_ms"] = timer.last["min_ms"]
+        res["bwd_calls"] = bwd_steps
+        res["bwd_dense_equiv_tflops"] = round(10 * d * pairs / (t_bwd * 1e-3) / 1e12, 3)
+        res["bwd_12dp_tflops"] = round(12 * d * pairs / (t_bwd * 1e-3) / 1e12, 3)
+        res["bwd_frac_of_peak_12dp"] = round(12 * d * pairs / (t_bwd * 1e-3) / 1e12 / peak, 4)
     del q, k, v, O
     torch.cuda.empty_cache()
     return res, (t_fwd, t_stats, t_out)
 
 
-def bench_sweep(api, torch, timer, steps, warmup):
-    """Block-sparsity sweep: the clustered L = 8192 generator with 64 ... 1
-    cluster runs per head.  Fits t = t0 + t1 * (non-null tile fraction): t0 is
-    the part every configuration pays (the dense score sweep), t1 the part
-    that scales with the non-null tiles ("AdaSplash-2: Faster Differentiable
-    Sparse Attention", sec. 4.2: runtime falling with block sparsity)."""
-    from adaptive_sparse_attention_row_amd.workloads import sweep_configs
-    pts = []
-    for cfg in sweep_configs():
-        r, _ = bench_attn(api, torch, timer, cfg, steps, warmup)
-        frac = r["nonnull_tiles_64"] / r["structural_tiles_64"]
-        pts.append({"workload": cfg.name, "clusters": cfg.clusters, "nonnull_fraction": round(frac, 5),
-                    "fwd_ms": r["fwd_ms"], "score_stats_ms": r["score_stats_ms"], "solve_ms": r["solve_ms"],
-                    "output_ms": r["output_ms"], "dense_equiv_tflops": r["dense_equiv_tflops"]})
-        log(f"sweep {cfg.name}: non-null {frac:.4f} fwd {r['fwd_ms']:.4f} ms")
-    n = len(pts)
-    xs = [p["nonnull_fraction"] for p in pts]
-    ys = [p["fwd_ms"] for p in pts]
+def linear_fit(xs, ys):
+    """Least squares y = t0 + t1 x, with the coefficient of determination."""
+    n = len(xs)
     mx, my = sum(xs) / n, sum(ys) / n
     sxx = sum((x - mx) ** 2 for x in xs)
     t1 = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx if sxx > 0 else 0.0
     t0 = my - t1 * mx
-    return {"points": pts, "fit_ms": {"t0": round(t0, 5), "t1_per_unit_fraction": round(t1, 5)}}
+    ss_res = sum((y - t0 - t1 * x) ** 2 for x, y in zip(xs, ys))
+    ss_tot = sum((y - my) ** 2 for y in ys)
+    return {"t0": round(t0, 5), "t1_per_unit_fraction": round(t1, 5),
+            "r2": round(1.0 - ss_res / ss_tot, 4) if ss_tot > 0 else None}
+
+
+def sweep_points(api, torch, timer, cfgs, steps, warmup, key):
+    pts = []
+    for cfg in cfgs:
+        r, _ = bench_attn(api, torch, timer, cfg, steps, warmup)
+        frac = r["nonnull_tiles_64"] / r["structural_tiles_64"]
+        pts.append({"workload": cfg.name, key: getattr(cfg, key), "nonnull_fraction": round(frac, 5),
+                    "fwd_ms": r["fwd_ms"], "score_stats_ms": r["score_stats_ms"], "solve_ms": r["solve_ms"],
+                    "after_threshold_ms": r["after_threshold_ms"], "dense_equiv_tflops": r["dense_equiv_tflops"],
+                    "mfma_util_on_issued_work": r["mfma_util_on_issued_work"],
+                    "blocks_with_O_from_lists": r["blocks_with_O_from_lists"]})
+        log(f"sweep {cfg.name}: non-null {frac:.4f} fwd {r['fwd_ms']:.4f} ms")
+    xs = [p["nonnull_fraction"] for p in pts]
+    fits = {ph: linear_fit(xs, [p[ph] for p in pts])
+            for ph in ("fwd_ms", "score_stats_ms", "solve_ms", "after_threshold_ms")}
+    return {"points": pts, "fit_ms": fits}
+
+
+def bench_sweep(api, torch, timer, steps, warmup):
+    """Block-sparsity sweeps at L = 8192, d = 64, bf16 ("AdaSplash-2: Faster
+    Differentiable Sparse Attention", sec. 4.2: runtime falling with block
+    sparsity): the clustered generator with 64 ... 1 cluster runs per head,
+    and Gaussian Q/K/V with the query standard deviation as the knob (the
+    pages' own method; at this length it spans 0 to about 55 % block
+    sparsity).  Each fits t = t0 + t1 * (non-null tile fraction) per phase
+    (whole forward, score sweep, candidate solve, after the threshold) with
+    R^2."""
+    from adaptive_sparse_attention_row_amd.workloads import qvar_configs, sweep_configs
+    return {"clustered": sweep_points(api, torch, timer, sweep_configs(), steps, warmup, "clusters"),
+            "query_variance": sweep_points(api, torch, timer, qvar_configs(), steps, warmup, "q_std")}
 
 
 DECODE_WORKLOADS = [
@@ -324,7 +416,7 @@ def bench_alpha(api, torch, timer, steps, warmup):
     out = {}
     for a in (1.25, 2.0):
         r, _ = bench_attn(api, torch, timer, C4, steps, warmup, alpha=a)
-        out[f"c4_alpha{a}"] = {k: r[k] for k in ("fwd_ms", "score_stats_ms", "solve_ms", "output_ms",
+        out[f"c4_alpha{a}"] = {k: r[k] for k in ("fwd_ms", "score_stats_ms", "solve_ms", "after_threshold_ms",
                                                   "dense_equiv_tflops", "block_sparsity_64")}
         t = bench_tau_rows(api, torch, timer, steps, warmup, alpha=a)
         out[f"c2_alpha{a}"] = {"ms": t["ms"], "GB_per_s": t["GB_per_s"]}
@@ -468,6 +560,52 @@ def cpu_baseline(cfg, target_s=15.0):
     }
 
 
+def oracle_timings():
+    """Wall time of the fp64 oracle on bounded samples of the other workloads,
+    on the host cores (the same threads as the CPU baseline): C2 rows, C5
+    forward rows, and one whole head of the C5 backward."""
+    import numpy as np
+    import oracle
+    from adaptive_sparse_attention_row_amd.workloads import C2, C5, gen_config, gen_rows
+    oracle.build(force=False)
+    out = {"cores": oracle.num_threads()}
+    S = gen_rows(1024, C2.cols, C2.seed).numpy()
+    t0 = time.perf_counter()
+    oracle.tau_rows(S)
+    dt = time.perf_counter() - t0
+    out["c2_rows"] = {"sample": f"1024 of {C2.rows} rows of {C2.name}", "s": round(dt, 3),
+                      "rows_per_s": round(1024 / dt, 1), "GB_per_s": round(1024 * C2.cols * 8 / dt / 1e9, 3)}
+    inp = gen_config(C5, H=1)
+    Q, K, V, dO = (inp[n].float().numpy() for n in ("q", "k", "v", "do"))
+    rows = np.linspace(0, C5.L - 1, 2048).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(Q, K, V, C5.scale, C5.mask, C5.window, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = int((rows + 1).sum())
+    out["c5_fwd_rows"] = {"sample": f"2048 evenly spaced query rows of one head of {C5.name}", "s": round(dt, 3),
+                          "dense_equiv_tflops": round(4 * C5.d * pairs / dt / 1e12, 6)}
+    t0 = time.perf_counter()
+    oracle.attn_bwd_head(Q[0, 0], K[0, 0], V[0, 0], dO[0, 0], C5.scale, C5.mask, C5.window)
+    dt = time.perf_counter() - t0
+    pairs = C5.L * (C5.L + 1) // 2
+    out["c5_bwd_head"] = {"sample": f"the full backward of one head of {C5.name}", "s": round(dt, 3),
+                          "dense_equiv_tflops": round(10 * C5.d * pairs / dt / 1e12, 6)}
+    return out
+
+
+def gpu_clock():
+    """The GPU's current and peak shader clock as rocm-smi reports them (None
+    where the tool or the field is missing)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        rec = json.loads(r.stdout)
+        card = next(iter(rec.values()))
+        return {k: v for k, v in card.items() if "sclk" in k.lower() or "fclk" in k.lower() or "mclk" in k.lower()}
+    except Exception as e:  # the clock is reported, not required
+        return {"error": str(e)[:120]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -475,7 +613,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "sweep", "alpha", "decode", "wide", "copy"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "sweep", "alpha", "decode", "wide", "copy"],
                     default=None,
                     help="run one workload only (for profiler passes); prints its record")
     ap.add_argument("--counters-summary", metavar="NAME", default=None,
@@ -499,7 +637,7 @@ def main():
 
     import torch
     from adaptive_sparse_attention_row_amd import api
-    from adaptive_sparse_attention_row_amd.workloads import C3A, C3B, C4, C5
+    from adaptive_sparse_attention_row_amd.workloads import C1, C3A, C3B, C4, C5
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -509,6 +647,8 @@ def main():
     if args.only is not None:
         if args.only == "copy":
             rec = bench_copy(torch, timer, args.steps, args.warmup)
+        elif args.only == "c1":
+            rec = bench_attn(api, torch, timer, C1, args.steps, args.warmup)[0]
         elif args.only == "c2":
             rec = bench_tau_rows(api, torch, timer, args.steps, args.warmup)
         elif args.only == "c3":
@@ -525,11 +665,12 @@ def main():
         elif args.only == "wide":
             rec = bench_wide_rows(api, torch, timer, args.steps, args.warmup)
         else:
-            rec = bench_attn(api, torch, timer, C5, args.steps, args.warmup, with_bwd=True)[0]
+            rec = bench_attn(api, torch, timer, C5, args.steps, args.warmup, with_bwd=True, bwd_steps=args.steps)[0]
         print(json.dumps({"only": args.only, "record": rec}), flush=True)
         return
 
     t_wall0 = time.perf_counter()
+    clock_before = gpu_clock()
     head, (t_fwd, t_stats, t_out) = bench_attn(api, torch, timer, C4, args.steps, args.warmup)
     log(f"c4 fwd {head['fwd_ms']:.4f} ms  stats {t_stats:.4f} ms  solve {head['solve_ms']:.4f} ms  output {t_out:.4f} ms  "
         f"{head['dense_equiv_tflops']} TFLOP/s dense-eq, block sparsity {head['block_sparsity_64']}")
@@ -549,15 +690,17 @@ def main():
 
     extras = {}
     if not args.no_extras:
+        extras[C1.name], _ = bench_attn(api, torch, timer, C1, args.steps, args.warmup)
+        log(f"{C1.name}: fwd {extras[C1.name]['fwd_ms']} ms")
         extras["c2_tau_rows"] = bench_tau_rows(api, torch, timer, args.steps, args.warmup)
         log(f"c2 tau_rows {extras['c2_tau_rows']['ms']} ms {extras['c2_tau_rows']['GB_per_s']} GB/s")
         for cfg in (C3A, C3B):
             extras[cfg.name], _ = bench_attn(api, torch, timer, cfg, args.steps, args.warmup)
             log(f"{cfg.name}: {extras[cfg.name]}")
-        extras[C5.name], _ = bench_attn(api, torch, timer, C5, max(2, args.steps // 4), 2, with_bwd=True)
+        extras[C5.name], _ = bench_attn(api, torch, timer, C5, 10, 2, with_bwd=True, bwd_steps=10)
         log(f"{C5.name}: {extras[C5.name]}")
         extras["sparsity_sweep"] = bench_sweep(api, torch, timer, args.steps, args.warmup)
-        log(f"sparsity sweep fit: {extras['sparsity_sweep']['fit_ms']}")
+        log(f"sparsity sweep fits: {[(k, v['fit_ms']['fwd_ms']) for k, v in extras['sparsity_sweep'].items()]}")
         extras["general_alpha"] = bench_alpha(api, torch, timer, args.steps, args.warmup)
         log(f"general alpha: {extras['general_alpha']}")
         extras["decode"] = bench_decode(api, torch, timer, args.steps, args.warmup)
@@ -565,10 +708,14 @@ def main():
         extras["wide_dense_rows"] = bench_wide_rows(api, torch, timer, args.steps, args.warmup)
         log(f"wide dense rows: {extras['wide_dense_rows']}")
 
+    clock_after = gpu_clock()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(C4)
         log(f"cpu baseline: {cpu}")
+        if not args.no_extras:
+            extras["oracle_other_workloads"] = oracle_timings()
+            log(f"oracle timings: {extras['oracle_other_workloads']}")
 
     value = head["dense_equiv_tflops"]
     line = {
@@ -590,6 +737,9 @@ def main():
         "c4_fwd": head,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "timing": "HIP events around every call on the library's stream; ms values are medians "
+                  "(the *_min_ms fields the minima) of `steps` calls after `warmup` calls (C5: 10 of each)",
+        "gpu_clock": {"before": clock_before, "after": clock_after},
         "paths": extras,
         "bench_wall_s": round(time.perf_counter() - t_wall0, 1),
     }

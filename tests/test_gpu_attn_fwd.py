@@ -395,3 +395,28 @@ def test_forward_deterministic(env, case):
     for name, x, y in zip(("O", "tau", "mask"), a, b):
         assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
                               y.view(np.uint32) if y.dtype == np.float32 else y), f"{case}: {name} differs between calls"
+
+
+@pytest.mark.parametrize("sd", [0.1, 1.0, 16.0])
+def test_query_variance_sweep_sampled(env, orc, sd):
+    """Three points of the query-variance sweep (Gaussian Q/K/V at L = 8192,
+    d = 64, Q ~ N(0, sd^2), two heads): sd = 0.1 gives near-uniform rows whose
+    supports of about a thousand keys overflow every candidate list (the
+    histogram-initialised sweeps), sd = 16 near one-hot rows.  Sampled rows
+    against the oracle, and the mask of one head."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import gen_config, qvar_configs
+    cfg = [c for c in qvar_configs() if c.q_std == sd][0]
+    inp = gen_config(cfg, H=2)
+    O, tau, bm = run_gpu(api, torch, inp, cfg.scale, cfg.mask, cfg.window)
+    L = cfg.L
+    rng = np.random.default_rng(int(sd * 10))
+    rows = []
+    for bh in range(2):
+        pick = np.concatenate([[0, L // 2, L - 1], rng.integers(0, L, 40)])
+        rows.extend(bh * L + pick)
+    err = check_rows(orc, inp, cfg.scale, cfg.mask, cfg.window, O, tau, "bf16", rows=np.array(rows),
+                     label=cfg.name)
+    check_mask(orc, inp, cfg.scale, cfg.mask, cfg.window, bm, [0], label=cfg.name)
+    nnz = sum(bin(int(x)).count("1") for x in bm.reshape(-1))
+    print(f"{cfg.name}: max |dO| = {err:.3e}, block sparsity {1 - nnz / (2 * 128 * 128):.4f}")
