@@ -613,6 +613,17 @@ struct CollectCfg {
 
 constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
 
+// Per-row and per-tile state of a 128-row block, kept in LDS across the
+// phases of the forward (score statistics, threshold solve, output).
+template <int TCMAX>
+struct BlockLds {
+    uint16_t list[TCMAX];         // the tile list of the current sweep
+    float um_s[2][TCMAX];         // largest score per (64-row half, key tile)
+    float row_m[kBR], row_lo[kBR], row_tau[kBR];
+    uint32_t maskw[2][TCMAX / 32];
+    int nlist_s, flag_s, vover_s;
+};
+
 // ------------------------------------------------------------ kernel 1a
 // Dense sweep: per row the top tile maxima (-> tau_lo and the maximum) and
 // per (64-row half, tile) the largest raw score.
@@ -620,14 +631,16 @@ constexpr int kTop4 = 4;  // tile maxima kept per lane half per row
 // tiles up to the diagonal); the other serves no mask and the window mask
 // (which always takes the list).  Separate instances keep each loop's code
 // as it is alone.
+// keep: also leave each row's maximum and bound, and the tile maxima (raw),
+// in the block's LDS state for the solve that follows in the same workgroup.
 template <typename T, int D, int TCMAX, bool CAUSAL>
-__global__ __launch_bounds__(kNT, kStatsOcc) void fwd_stats_kernel(FwdParams p) {
-    using O = Ops<T, D>;
+__device__ __forceinline__ void stats_phase(const FwdParams& p, int bh, int r0,
+                                            const typename Ops<T, D>::template QOp<2>& qop, T* ring,
+                                            BlockLds<TCMAX>& bl, bool keep) {
     constexpr int S = StatsCfg<T, D>::kS;
-    __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
-    __shared__ uint16_t list[TCMAX];
-    __shared__ float umax[2][TCMAX];
-    __shared__ int nlist_s;
+    uint16_t* const list = bl.list;
+    float(&umax)[2][TCMAX] = bl.um_s;
+    int& nlist_s = bl.nlist_s;
     // the per-row lists are merged through the ring once the sweep is over
     typedef float StRow[kBR][2 * kTop4];
     static_assert(sizeof(float) * 2 * kBR * 2 * kTop4 <= sizeof(T) * S * 2 * 64 * D, "merge space");
@@ -635,16 +648,10 @@ __global__ __launch_bounds__(kNT, kStatsOcc) void fwd_stats_kernel(FwdParams p) 
 
     const int t = threadIdx.x, w = wave_id(), qh = w & 1, kh = w >> 1;
     const int l = lane_id(), m = l & 31, h = l >> 5;
-    int bh, r0;
-    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
     const int R0 = r0 + 64 * qh;
     const Geom g = {p.L, p.mode, p.W};
-    const size_t head_off = (size_t)bh * p.L * D;
-    const T* Qh = reinterpret_cast<const T*>(p.q) + head_off;
-    const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
+    const T* Kh = reinterpret_cast<const T*>(p.k) + (size_t)bh * p.L * D;
 
-    typename O::template QOp<2> qop;
-    O::load_q(qop, Qh, R0, p.L);
     for (int i = t; i < 2 * TCMAX; i += kNT) (&umax[0][0])[i] = neg_inf();
     // the workgroup's tiles are the first dense_nt (no mask: all; causal: up
     // to the diagonal), all inside L: the list-free sweep
@@ -716,12 +723,31 @@ __global__ __launch_bounds__(kNT, kStatsOcc) void fwd_stats_kernel(FwdParams p) 
         sort_desc(v);
         const float lo = p.gen ? tau_lower_gen(v, p.am) : tau_of_sorted(v);
         reinterpret_cast<float2*>(p.rowstat)[(size_t)bh * p.L + grow] = make_float2(v[0], lo);
+        if (keep) {
+            bl.row_m[srow] = v[0];
+            bl.row_lo[srow] = lo;
+        }
+    } else if (h == 0 && keep) {
+        bl.row_m[srow] = neg_inf();
+        bl.row_lo[srow] = __builtin_inff();
     }
     for (int i = t; i < 2 * p.Tc; i += kNT) {
         const int hh = i / p.Tc, J = i % p.Tc;
         const int I = r0 / 64 + hh;
         if (I < p.Tr64) p.umax[((size_t)bh * p.Tr64 + I) * p.Tc + J] = umax[hh][J];
     }
+}
+
+template <typename T, int D, int TCMAX, bool CAUSAL>
+__global__ __launch_bounds__(kNT, kStatsOcc) void fwd_stats_kernel(FwdParams p) {
+    using O = Ops<T, D>;
+    __shared__ __attribute__((aligned(16))) T ring[StatsCfg<T, D>::kS * 2 * 64 * D];
+    __shared__ BlockLds<TCMAX> bl;
+    int bh, r0;
+    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    typename O::template QOp<2> qop;
+    O::load_q(qop, reinterpret_cast<const T*>(p.q) + (size_t)bh * p.L * D, r0 + 64 * (wave_id() & 1), p.L);
+    stats_phase<T, D, TCMAX, CAUSAL>(p, bh, r0, qop, ring, bl, false);
 }
 
 // O of a block's rows from their candidate lists: O_i = sum over the entries
@@ -732,7 +758,7 @@ __global__ __launch_bounds__(kNT, kStatsOcc) void fwd_stats_kernel(FwdParams p) 
 // 16-byte loads, kB entries in flight.
 template <typename T, int D>
 __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, const u32x2* clist,
-                                            const int (&cntq)[4][kBR], const float* row_tau) {
+                                            const uint16_t (&cntq)[4][kBR], const float* row_tau) {
     constexpr int kLpr = D / 32;              // lanes per row
     constexpr int kRpp = kNT / kLpr;          // rows per pass
     constexpr int kVec = 16 / (int)sizeof(T); // elements per 16-byte load
@@ -834,44 +860,63 @@ constexpr int kGatherTileCost = 32;
 // Row states of the solve kernel.
 enum { kRowNone = 0, kRowCollect = 1, kRowSweep = 2, kRowDone = 3, kRowOver = 4 };
 
-template <typename T, int D, int TCMAX>
-__global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kernel(FwdParams p) {
-    using O = Ops<T, D>;
-    constexpr int S = CollectCfg<T, D>::kS;
+// LDS of the solve phase alone: per-row state, and the scratch of the
+// overflow path (the histogram, then the sweep sums).
+struct SolveScratch {
+    float row_hi[kBR];
+    int rstate[kBR];
+    uint16_t cntq[4][kBR];  // entries met per candidate sub-list
+    union {
+        int hist[kHistBins * kBR];  // counts [bin][row]
+        struct {
+            float t[kBR];
+            int active[kBR];
+            float part[kBR][2][4];
+        } fb;
+    };
+};
+
+// from_stats: the block's row statistics and raw tile maxima are already in
+// bl (the score sweep ran in this workgroup); otherwise they are read from
+// the workspace.  Returns whether it wrote O from the candidate lists.
+template <typename T, int D, int TCMAX, int S>
+__device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
+                                            const typename Ops<T, D>::template QOp<2>& qop, T* ring,
+                                            SolveScratch& ss, BlockLds<TCMAX>& bl, bool from_stats) {
     constexpr int WD = TCMAX / 32;
-    __shared__ __attribute__((aligned(16))) T ring[S * 2 * 64 * D];
-    __shared__ int hist[kHistBins * kBR];  // overflow path: counts [bin][row]
-    __shared__ uint16_t list[TCMAX];
-    __shared__ float um_s[2][TCMAX];
-    __shared__ int cntq[4][kBR], rstate[kBR];
-    __shared__ float row_m[kBR], row_lo[kBR], row_hi[kBR], row_tau[kBR];
-    __shared__ uint32_t maskw[2][WD];
-    __shared__ int nlist_s, flag_s;
+    int* const hist = ss.hist;
+    uint16_t* const list = bl.list;
+    float(&um_s)[2][TCMAX] = bl.um_s;
+    uint16_t(&cntq)[4][kBR] = ss.cntq;
+    int* const rstate = ss.rstate;
+    float* const row_m = bl.row_m;
+    float* const row_lo = bl.row_lo;
+    float* const row_hi = ss.row_hi;
+    float* const row_tau = bl.row_tau;
+    uint32_t(&maskw)[2][WD] = bl.maskw;
+    int& nlist_s = bl.nlist_s;
+    int& flag_s = bl.flag_s;
 
     const int t = threadIdx.x, w = wave_id(), qh = w & 1, kh = w >> 1;
     const int l = lane_id(), m = l & 31, h = l >> 5;
     const int q = 2 * kh + h;  // this lane's sub-list of the rows it sweeps
-    int bh, r0;
-    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
     const size_t blk = (size_t)bh * p.nQ + r0 / kBR;
     const int R0 = r0 + 64 * qh;
     const Geom g = {p.L, p.mode, p.W};
-    const size_t head_off = (size_t)bh * p.L * D;
-    const T* Qh = reinterpret_cast<const T*>(p.q) + head_off;
-    const T* Kh = reinterpret_cast<const T*>(p.k) + head_off;
+    const T* Kh = reinterpret_cast<const T*>(p.k) + (size_t)bh * p.L * D;
     const int cap = p.cap < kCandCap ? p.cap : kCandCap;
     const int capq = cap >= 4 ? cap / 4 : 1;  // entries per sub-list
     u32x2* clist = p.clist + blk * kCandCap * kBR;
     const float2* rowstat = reinterpret_cast<const float2*>(p.rowstat) + (size_t)bh * p.L;
 
-    typename O::template QOp<2> qop;
-    O::load_q(qop, Qh, R0, p.L);
     // row statistics and the tile maxima of both row blocks
     if (t < kBR) {
         const bool valid = (r0 + t) < p.L;
-        const float2 rs = valid ? rowstat[r0 + t] : make_float2(neg_inf(), __builtin_inff());
-        row_m[t] = rs.x;
-        row_lo[t] = rs.y;
+        if (!from_stats) {
+            const float2 rs = valid ? rowstat[r0 + t] : make_float2(neg_inf(), __builtin_inff());
+            row_m[t] = rs.x;
+            row_lo[t] = rs.y;
+        }
         rstate[t] = valid ? kRowCollect : kRowNone;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) cntq[qq][t] = 0;
@@ -879,7 +924,8 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
     for (int i = t; i < 2 * p.Tc; i += kNT) {
         const int hh = i / p.Tc, J = i - hh * p.Tc;
         const int I = r0 / 64 + hh;
-        um_s[hh][J] = (I < p.Tr64) ? p.umax[((size_t)bh * p.Tr64 + I) * p.Tc + J] * p.scale : neg_inf();
+        if (from_stats) um_s[hh][J] *= p.scale;
+        else um_s[hh][J] = (I < p.Tr64) ? p.umax[((size_t)bh * p.Tr64 + I) * p.Tc + J] * p.scale : neg_inf();
     }
     for (int i = t; i < 2 * WD; i += kNT) (&maskw[0][0])[i] = 0u;
     __syncthreads();
@@ -1091,9 +1137,9 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
 
     // ---- Halley-bisection sweeps for rows whose lists overflowed
     if (any_row(kRowSweep)) {
-        __shared__ float fb_t[kBR];
-        __shared__ int fb_active[kBR];
-        __shared__ float fb_part[kBR][2][4];
+        float* const fb_t = ss.fb.t;
+        int* const fb_active = ss.fb.active;
+        float(&fb_part)[kBR][2][4] = ss.fb.part;
         if (h == 0) {
             fb_active[srow] = rstate[srow] == kRowSweep ? 1 : 0;
             fb_t[srow] = row_lo[srow];
@@ -1237,8 +1283,9 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
 
     // ---- O straight from the candidate lists when every row has one and the
     // lists are short next to the tiles the output pass would sweep
+    bool gathered = false;
     if (p.gather) {
-        bool gathered = !any_row(kRowSweep);
+        gathered = !any_row(kRowSweep);
         if (gathered) {
             if (t == 0) flag_s = 0;
             __syncthreads();
@@ -1250,7 +1297,7 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
             gathered = flag_s < 0;
         }
         if (gathered) gather_rows<T, D>(p, bh, r0, clist, cntq, row_tau);
-        if (t == 0) p.ostate[blk] = gathered ? 1 : 0;
+        if (t == 0 && p.ostate != nullptr) p.ostate[blk] = gathered ? 1 : 0;
     }
 
     // ---- outputs: tau and the packed mask of both 64-row blocks
@@ -1260,6 +1307,20 @@ __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kerne
         const int I = r0 / 64 + hh;
         if (I < p.Tr64) p.mask[((size_t)bh * p.Tr64 + I) * p.Wd + wd] = maskw[hh][wd];
     }
+    return gathered;
+}
+
+template <typename T, int D, int TCMAX>
+__global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kernel(FwdParams p) {
+    using O = Ops<T, D>;
+    __shared__ __attribute__((aligned(16))) T ring[CollectCfg<T, D>::kS * 2 * 64 * D];
+    __shared__ SolveScratch ss;
+    __shared__ BlockLds<TCMAX> bl;
+    int bh, r0;
+    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    typename O::template QOp<2> qop;
+    O::load_q(qop, reinterpret_cast<const T*>(p.q) + (size_t)bh * p.L * D, r0 + 64 * (wave_id() & 1), p.L);
+    solve_phase<T, D, TCMAX, CollectCfg<T, D>::kS>(p, bh, r0, qop, ring, ss, bl, false);
 }
 
 // ------------------------------------------------------------ kernel 2
@@ -1393,23 +1454,27 @@ __global__ __launch_bounds__(kNT, 1) void fwd_out_kernel(FwdParams p) {
 // significant bits in fp16, and bf16 V converts exactly within fp16 range.  A
 // workgroup that meets a V entry beyond that range redoes its rows with A
 // split into bf16 hi + lo against bf16 V.
+template <int D>
+struct OutLds {
+    __bf16 kbuf[2][Ops<__bf16, D>::kKTile];
+    uint16_t vbuf[2][D * Ops<__bf16, D>::kVRow];  // fp16 or bf16 bits
+};
+
+// The block's rows from the tiles whose bits are set in mw0 / mw1 (its two
+// 64-row blocks' mask words).
 template <int D, bool GEN>
-__global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(FwdParams p) {
+__device__ __forceinline__ void out_phase_bf16(const FwdParams& p, int bh, int r0, OutLds<D>& ol,
+                                               const uint32_t* mw0, const uint32_t* mw1, uint16_t* list,
+                                               int& nlist_s, int& vover_s, const float* tau_lds) {
     using O = Ops<__bf16, D>;
     constexpr int kVRow = O::kVRow;
     constexpr int kKPer = O::kChunks / kNT;  // K chunks per thread per tile
     static_assert(O::kChunks % kNT == 0 && O::kVUnits <= kNT, "staging split");
-    __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][O::kKTile];
-    __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][D * kVRow];  // fp16 or bf16 bits
-    __shared__ uint16_t list[kMaxTc];
-    __shared__ uint32_t mw[2][kMaxTc / 32];
-    __shared__ int nlist_s, vover_s;
+    auto& kbuf = ol.kbuf;
+    auto& vbuf = ol.vbuf;
 
     const int t = threadIdx.x, w = wave_id();
     const int l = lane_id(), m = l & 31, h = l >> 5;
-    int bh, r0;
-    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
-    if (p.ostate != nullptr && p.ostate[(size_t)bh * p.nQ + r0 / kBR]) return;  // O already written
     const int R0 = r0 + 32 * w;  // this wave's rows
     const int hh = w >> 1;       // their 64-row block
     const Geom g = {p.L, p.mode, p.W};
@@ -1418,22 +1483,18 @@ __global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(Fw
     const __bf16* Kh = reinterpret_cast<const __bf16*>(p.k) + head_off;
     const __bf16* Vh = reinterpret_cast<const __bf16*>(p.v) + head_off;
 
-    for (int i = t; i < 2 * p.Wd; i += kNT) {
-        const int b = i / p.Wd, wd = i % p.Wd;
-        const int I = r0 / 64 + b;
-        mw[b][wd] = (I < p.Tr64) ? p.mask[((size_t)bh * p.Tr64 + I) * p.Wd + wd] : 0u;
-    }
     if (t == 0) vover_s = 0;
     __syncthreads();
     if (w == 0) {
         const int n = build_list(list, p.Tc, [&](int J) {
-            return (int)((mw[0][J >> 5] >> (J & 31)) & 1u) | (int)(((mw[1][J >> 5] >> (J & 31)) & 1u) << 1);
+            return (int)((mw0[J >> 5] >> (J & 31)) & 1u) | (int)(((mw1[J >> 5] >> (J & 31)) & 1u) << 1);
         });
         if (l == 0) nlist_s = n;
     }
     typename O::template QOp<1> qop;
     O::load_q(qop, Qh, R0, p.L);
-    const float tq = (R0 + m < p.L) ? p.tau[(size_t)bh * p.L + R0 + m] : __builtin_inff();
+    const float tq = (R0 + m >= p.L) ? __builtin_inff()
+                     : tau_lds != nullptr ? tau_lds[R0 + m - r0] : p.tau[(size_t)bh * p.L + R0 + m];
     __syncthreads();
     const int n = nlist_s;
 
@@ -1562,6 +1623,71 @@ __global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(Fw
     }
 }
 
+template <int D, bool GEN>
+__global__ __launch_bounds__(kNT, (D == 64 ? 3 : 2)) void fwd_out_bf16_kernel(FwdParams p) {
+    __shared__ __attribute__((aligned(16))) OutLds<D> ol;
+    __shared__ uint16_t list[kMaxTc];
+    __shared__ uint32_t mw[2][kMaxTc / 32];
+    __shared__ int nlist_s, vover_s;
+    const int t = threadIdx.x;
+    int bh, r0;
+    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    if (p.ostate != nullptr && p.ostate[(size_t)bh * p.nQ + r0 / kBR]) return;  // O already written
+    for (int i = t; i < 2 * p.Wd; i += kNT) {
+        const int b = i / p.Wd, wd = i % p.Wd;
+        const int I = r0 / 64 + b;
+        mw[b][wd] = (I < p.Tr64) ? p.mask[((size_t)bh * p.Tr64 + I) * p.Wd + wd] : 0u;
+    }
+    out_phase_bf16<D, GEN>(p, bh, r0, ol, mw[0], mw[1], list, nlist_s, vover_s, nullptr);
+}
+
+// ------------------------------------------------------------ fused, bf16
+// The whole forward of a 128-row block in one workgroup: the score
+// statistics, the threshold solve, then O (from the candidate lists, or over
+// the non-null tiles).  The row statistics, tile maxima, tile lists and mask
+// stay in LDS between the phases, the phases' buffers overlap, and Q is read
+// once for the first two.  With no O requested (p.o null) it stops after the
+// solve.
+template <int D, int TCMAX>
+struct FusedCfg {
+    // three workgroups per CU fit (<= 168 VGPRs, <= 53 KB LDS) at d = 64 with
+    // tables for up to 128 key tiles
+    static constexpr int kOcc = (D == 64 && TCMAX <= 128) ? 3 : 2;
+};
+
+template <int D, int TCMAX, bool CAUSAL>
+__global__ __launch_bounds__(kNT, (FusedCfg<D, TCMAX>::kOcc)) void fwd_fused_kernel(FwdParams p) {
+    using T = __bf16;
+    using O = Ops<T, D>;
+    __shared__ BlockLds<TCMAX> bl;
+    union Work {
+        T sring[StatsCfg<T, D>::kS * 2 * 64 * D];
+        struct {
+            T ring[2 * 64 * D];  // one stage
+            SolveScratch ss;
+        } solve;
+        OutLds<D> out;
+    };
+    __shared__ __attribute__((aligned(16))) Work wk;
+    int bh, r0;
+    decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    {
+        typename O::template QOp<2> qop;
+        O::load_q(qop, reinterpret_cast<const T*>(p.q) + (size_t)bh * p.L * D, r0 + 64 * (wave_id() & 1), p.L);
+        stats_phase<T, D, TCMAX, CAUSAL>(p, bh, r0, qop, wk.sring, bl, true);
+        __syncthreads();
+        if (solve_phase<T, D, TCMAX, 1>(p, bh, r0, qop, wk.solve.ring, wk.solve.ss, bl, true)) return;
+    }
+    if (p.o == nullptr) return;
+    __syncthreads();
+    if (p.gen)
+        out_phase_bf16<D, true>(p, bh, r0, wk.out, bl.maskw[0], bl.maskw[1], bl.list, bl.nlist_s, bl.vover_s,
+                                bl.row_tau);
+    else
+        out_phase_bf16<D, false>(p, bh, r0, wk.out, bl.maskw[0], bl.maskw[1], bl.list, bl.nlist_s, bl.vover_s,
+                                 bl.row_tau);
+}
+
 template <typename T, int D, int TCMAX>
 void launch_stats(const FwdParams& fp, int grid, hipStream_t stream) {
     if (fp.mode == 1)
@@ -1570,8 +1696,24 @@ void launch_stats(const FwdParams& fp, int grid, hipStream_t stream) {
         hipLaunchKernelGGL((fwd_stats_kernel<T, D, TCMAX, false>), dim3(grid), dim3(kNT), 0, stream, fp);
 }
 
+template <int D, int TCMAX>
+void launch_fused(const FwdParams& fp, int grid, hipStream_t stream) {
+    if (fp.mode == 1)
+        hipLaunchKernelGGL((fwd_fused_kernel<D, TCMAX, true>), dim3(grid), dim3(kNT), 0, stream, fp);
+    else
+        hipLaunchKernelGGL((fwd_fused_kernel<D, TCMAX, false>), dim3(grid), dim3(kNT), 0, stream, fp);
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const FwdParams& fp, int grid, int phase, hipStream_t stream) {
+    // bf16 threshold (with or without O) up to L = 16384: one fused kernel
+    if constexpr (sizeof(T) == 2) {
+        if ((phase == 3 || phase == 7) && fp.Tc <= 256) {
+            if (fp.Tc <= 128) launch_fused<D, 128>(fp, grid, stream);
+            else launch_fused<D, 256>(fp, grid, stream);
+            return hipGetLastError();
+        }
+    }
     if (phase & 1) {
         if (fp.Tc <= 128)
             launch_stats<T, D, 128>(fp, grid, stream);
