@@ -23,9 +23,13 @@
 //           dA = dO V^T on MFMA, then dV^T += dO^T A and dK^T += Q^T dS;
 //           for bf16 as two sweeps, dV (PART 1) then dK (PART 2), each
 //           holding one accumulator and operand set.
+// bwd_range (bf16) the largest magnitudes of Q, K, V and dO, from which
+//           every workgroup derives the power-of-two scales of its fp16
+//           weight products.
 // Every kernel has one instance per alpha class (GEN: alpha != 1.5).
-// Weights fed to MFMA (A, dS) are split into bf16 hi + lo; accumulation is
-// fp32; all gradients are written in fp32.
+// For bf16 the products with the weights (A, dS) run on fp16 MFMA with both
+// operands scaled by powers of two; for fp32 on the fp32 path of the shared
+// tile operations.  Accumulation is fp32; all gradients are written in fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,6 +54,7 @@ struct BwdParams {
     float* dk;
     float* dv;
     float* delta;  // workspace [BH][L]
+    const uint32_t* range;  // workspace [kRangeBlocks][4]: max |Q|, |K|, |V|, |dO| bits per block (bf16)
     int BH, L, mode, W, nQ, nKB, Tc, Tr64, Wd;
     float scale;
     AlphaMap am;  // the alpha-entmax map
@@ -141,7 +146,117 @@ struct PvTileRegs {
             if (u < Ops<T, D>::kVUnits) Ops<T, D>::store_v_unit(dst, u, v[i]);
         }
     }
+    // The tile in fp16 times sc (bf16 only).
+    __device__ __forceinline__ void store16(uint16_t* dst, float sc) const {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int u = threadIdx.x + i * kNT;
+            if (u < Ops<T, D>::kVUnits) Ops<T, D>::store_v_unit_f16(dst, u, v[i], sc);
+        }
+    }
 };
+
+// The PV-layout tile of X for the weight products: fp16 times sc for bf16
+// inputs (sc a power of two), the input type itself for fp32.
+template <typename T, int D>
+__device__ __forceinline__ void stage_pvw(T* dst, const T* Xh, int r0, int L, float sc) {
+    if constexpr (sizeof(T) == 2) {
+        PvTileRegs<T, D> r;
+        r.load(Xh, r0, L);
+        r.store16(reinterpret_cast<uint16_t*>(dst), sc);
+    } else {
+        stage_pv<T, D>(dst, Xh, r0, L);
+    }
+}
+
+// ------------------------------------------------------------ fp16 products
+// For bf16 inputs the products with the weights (4A into dV, 2 dS into dK and
+// dQ) run as one fp16 MFMA per block, not a bf16 hi + lo pair.  Both operands
+// are scaled by powers of two, so that no product leaves fp16's range and the
+// results are scaled back exactly: Q, K and dO by 2^(15 - E) where 2^E bounds
+// the tensor's largest magnitude (bf16 -> fp16 is then exact down to 29
+// binades below that maximum), 4A <= 4 by 2^12, and 2 dS by the same rule
+// applied to its bound |2 dS| = |dd (dA - delta)| <= 4 |dA|max
+// <= 4 d max|dO| max|V| (dd <= 2 on the support, delta an average of dA).
+// A range pass over the inputs records the maxima; every workgroup reads
+// them and derives the same scales.
+constexpr int kRangeBlocks = 256;
+
+__global__ __launch_bounds__(kNT) void bwd_range_kernel(const __bf16* q, const __bf16* k, const __bf16* v,
+                                                        const __bf16* dout, size_t n, uint32_t* out) {
+    __shared__ uint32_t red[4];
+    if (threadIdx.x < 4) red[threadIdx.x] = 0u;
+    __syncthreads();
+    const __bf16* src[4] = {q, k, v, dout};
+    const size_t n8 = n / 8;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        uint32_t mx = 0u;  // largest |x| as bf16 bits (monotone for finite values)
+        const u32x4* p = reinterpret_cast<const u32x4*>(src[a]);
+        for (size_t i = (size_t)blockIdx.x * kNT + threadIdx.x; i < n8; i += (size_t)kRangeBlocks * kNT) {
+            const u32x4 x = p[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mx = max(mx, max(x[j] & 0x7fffu, (x[j] >> 16) & 0x7fffu));
+        }
+        if (blockIdx.x == 0 && threadIdx.x < n - n8 * 8) {
+            const uint32_t b = __builtin_bit_cast(uint16_t, src[a][n8 * 8 + threadIdx.x]);
+            mx = max(mx, b & 0x7fffu);
+        }
+        atomicMax(&red[a], mx);
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) out[blockIdx.x * 4 + threadIdx.x] = red[threadIdx.x];
+}
+
+struct F16Scales {
+    float q, k, o, a, s;  // operand scales: Q, K, dO tiles; 4A and 2 dS weights
+};
+
+// The exponent E with |x| < 2^E for the bf16 bit pattern b (E = 0 for 0).
+__device__ __forceinline__ int bound_exp(uint32_t b) {
+    return b ? (int)((b >> 7) & 0xffu) - 126 : 0;
+}
+
+__device__ __forceinline__ float pow2(int e) {
+    e = e < -60 ? -60 : (e > 60 ? 60 : e);
+    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+// The scales of the fp16 products (all 1 for fp32 inputs); `red` is 4 words
+// of LDS.  The same in every workgroup.  Ends with a barrier.
+template <typename T, int D>
+__device__ __forceinline__ F16Scales f16_scales(const BwdParams& p, uint32_t* red) {
+    F16Scales f = {1.f, 1.f, 1.f, 1.f, 1.f};
+    if constexpr (sizeof(T) == 2) {
+        if (threadIdx.x < 4) red[threadIdx.x] = 0u;
+        __syncthreads();
+        if (threadIdx.x < kRangeBlocks) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) atomicMax(&red[a], p.range[threadIdx.x * 4 + a]);
+        }
+        __syncthreads();
+        constexpr int kLogD = D == 128 ? 7 : 6;
+        const int eq = bound_exp(red[0]), ek = bound_exp(red[1]), ev = bound_exp(red[2]), eo = bound_exp(red[3]);
+        f.q = pow2(15 - eq);
+        f.k = pow2(15 - ek);
+        f.o = pow2(15 - eo);
+        f.a = 4096.0f;
+        f.s = pow2(15 - (eo + ev + 2 + kLogD));
+        __syncthreads();
+    }
+    return f;
+}
+
+// The weight product for the tile type: fp16 with weight scale ws for bf16
+// (the tile staged by stage_pvw), the fp32 product for fp32.
+template <typename T, int D, int NB>
+__device__ __forceinline__ void pv_w(typename Ops<T, D>::template OAcc<NB>& oa, const T* Vt,
+                                     const f32x16 (&a)[2][NB], const bool (&on)[2], float ws) {
+    if constexpr (sizeof(T) == 2)
+        Ops<T, D>::template pv_f16<NB>(oa, reinterpret_cast<const uint16_t*>(Vt), a, on, ws);
+    else
+        Ops<T, D>::template pv<NB>(oa, Vt, a, on);
+}
 
 template <class FlagsOf>
 __device__ __forceinline__ int build_list16(uint16_t* list, int n_items, FlagsOf flags_of) {
@@ -364,9 +479,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdParams p) {
 // reduction across waves) and holds half the operands and accumulators of
 // the layout above.  That fits two workgroups per CU (one wave's staging
 // then overlaps another's products) where the layout above runs one.
-#ifndef ENTMAX_BWD_DQ32
-#define ENTMAX_BWD_DQ32 1
-#endif
 template <int D, bool GEN>
 __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
     using T = __bf16;
@@ -375,12 +487,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) T lds[3 * BLK];
     __shared__ uint16_t list[kMaxTc];
     __shared__ uint32_t mw[2][kMaxTc / 32];
+    __shared__ uint32_t red[4];
     __shared__ int nlist_s;
 
     const int t = threadIdx.x, w = wave_id();
     const int l = lane_id(), m = l & 31, h = l >> 5;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
+    const F16Scales fs = f16_scales<T, D>(p, red);
     const int R0 = r0 + 32 * w;  // this wave's rows
     const int half = w >> 1;     // their 64-row block
     const Geom g = {p.L, p.mode, p.W};
@@ -436,7 +550,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
                 stage_score<T, D>(lds, Kh, J * kBC, p.L);
                 stage_score<T, D>(lds + BLK, Vh, J * kBC, p.L);
             }
-            if constexpr (kPv) stage_pv<T, D>(lds + 2 * BLK, Kh, J * kBC, p.L);
+            if constexpr (kPv) stage_pvw<T, D>(lds + 2 * BLK, Kh, J * kBC, p.L, fs.k);
             __syncthreads();
             if (kPf && e + 1 < n) {
                 const int J1 = list[e + 1] & 0xfff;
@@ -494,11 +608,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
                 for (int r = 0; r < 16; ++r) s[kb][0][r] = dd_of(gen_c, s[kb][0][r] * p.scale) * (da[kb][0][r] - dl);
         });
         const bool on[2] = {true, true};
-        O::template pv<1>(oa, KPVt, s, on);
+        pv_w<T, D, 1>(oa, KPVt, s, on, fs.s);
     });
 
     if (row < p.L) {
-        const float f = 0.5f * p.scale;
+        const float f = 0.5f * p.scale / fs.s / fs.k;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -512,14 +626,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ dK/dV kernel
-#ifndef ENTMAX_BWD_DKDV_SPLIT
-#define ENTMAX_BWD_DKDV_SPLIT 1
-#endif
 template <typename T, int D>
 struct DkvCfg {
     // 32-key blocks per wave (one in the split bf16 kernels, which keep two
     // workgroups per CU)
-    static constexpr int kNBK = (D == 64 && !(sizeof(T) == 2 && ENTMAX_BWD_DKDV_SPLIT)) ? 2 : 1;
+    static constexpr int kNBK = (D == 64 && sizeof(T) == 4) ? 2 : 1;
     static constexpr int kKW = 32 * kNBK;            // keys per wave
     static constexpr int kKeys = 4 * kKW;            // keys per workgroup
     static constexpr int kBlk = DqCfg<T, D>::kBlk;
@@ -539,10 +650,12 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
     __shared__ __attribute__((aligned(16))) T lds[4 * BLK];
     __shared__ uint16_t list[kMaxTc];
     __shared__ float tau_s[64], del_s[64];
+    __shared__ uint32_t red[4];
     __shared__ int nlist_s;
 
     const int t = threadIdx.x, w = wave_id();
     const int l = lane_id(), m = l & 31, h = l >> 5;
+    const F16Scales fs = f16_scales<T, D>(p, red);
     const int bh = blockIdx.x % p.BH;
     const int c0 = (blockIdx.x / p.BH) * DkvCfg<T, D>::kKeys;
     const int cw = c0 + w * KW;  // this wave's first key
@@ -607,14 +720,15 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
         __syncthreads();
         if constexpr (kPf) {
             rq.store(Qt);
-            rdo.store(dOPVt);
+            if constexpr (sizeof(T) == 2) rdo.store16(reinterpret_cast<uint16_t*>(dOPVt), fs.o);
+            else rdo.store(dOPVt);
         } else {
             stage_score<T, D>(Qt, Qh, i0, p.L);
             if constexpr (kDK) {
                 stage_score<T, D>(dOt, dOh, i0, p.L);
-                stage_pv<T, D>(QPVt, Qh, i0, p.L);
+                stage_pvw<T, D>(QPVt, Qh, i0, p.L, fs.q);
             }
-            if constexpr (kDV) stage_pv<T, D>(dOPVt, dOh, i0, p.L);
+            if constexpr (kDV) stage_pvw<T, D>(dOPVt, dOh, i0, p.L, fs.o);
         }
         if (t < 64) {
             const int row = i0 + t;
@@ -654,7 +768,7 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
                             }
                         }
             });
-            O::pv(dva, dOPVt, a4, on);
+            pv_w<T, D, NBK>(dva, dOPVt, a4, on, fs.a);
         }
         if constexpr (kDK) {
             O::scores(da, dOt, vop);
@@ -673,11 +787,11 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
                             s[kb][cb][r] = dd * (da[kb][cb][r] - del_s[qi]);
                         }
             });
-            O::pv(dka, QPVt, s, on);
+            pv_w<T, D, NBK>(dka, QPVt, s, on, fs.s);
         }
     }
 
-    const float fk = 0.5f * p.scale;
+    const float fk = 0.5f * p.scale / fs.s / fs.q, fv = 0.25f / fs.a / fs.o;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -691,7 +805,7 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (kDK) k4[e] = fk * dka.o[db][cb][4 * r4 + e];
-                    if constexpr (kDV) v4[e] = 0.25f * dva.o[db][cb][4 * r4 + e];
+                    if constexpr (kDV) v4[e] = fv * dva.o[db][cb][4 * r4 + e];
                 }
                 if constexpr (kDK) *reinterpret_cast<f32x4*>(p.dk + ((size_t)bh * p.L + key) * D + d) = k4;
                 if constexpr (kDV) *reinterpret_cast<f32x4*>(p.dv + ((size_t)bh * p.L + key) * D + d) = v4;
@@ -701,13 +815,22 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
 
 template <typename T, int D, bool GEN>
 hipError_t launch_bwd_class(const BwdParams& bp, hipStream_t stream) {
-    if constexpr (sizeof(T) == 2 && ENTMAX_BWD_DQ32)
+    if constexpr (sizeof(T) == 2) {
+        const size_t n = (size_t)bp.BH * bp.L * D;
+        hipLaunchKernelGGL(bwd_range_kernel, dim3(kRangeBlocks), dim3(kNT), 0, stream,
+                           reinterpret_cast<const __bf16*>(bp.q), reinterpret_cast<const __bf16*>(bp.k),
+                           reinterpret_cast<const __bf16*>(bp.v), reinterpret_cast<const __bf16*>(bp.dout), n,
+                           const_cast<uint32_t*>(bp.range));
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+    }
+    if constexpr (sizeof(T) == 2)
         hipLaunchKernelGGL((bwd_dq32_kernel<D, GEN>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
     else
         hipLaunchKernelGGL((bwd_dq_kernel<T, D, GEN>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (sizeof(T) == 2 && ENTMAX_BWD_DKDV_SPLIT) {
+    if constexpr (sizeof(T) == 2) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, 1, GEN>), dim3(bp.nKB * bp.BH), dim3(kNT), 0, stream, bp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -727,7 +850,8 @@ hipError_t launch_bwd_typed(const BwdParams& bp, hipStream_t stream) {
 }  // namespace attn
 
 size_t attn_bwd_workspace_bytes(int B, int H, int L, int, int) {
-    return ((size_t)B * H * L * sizeof(float) + 255) & ~(size_t)255;
+    // delta per row, then the range pass's per-block maxima
+    return (((size_t)B * H * L * sizeof(float) + 255) & ~(size_t)255) + attn::kRangeBlocks * 4 * sizeof(uint32_t);
 }
 
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream) {
@@ -738,6 +862,8 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream) {
     bp.tau = a.tau; bp.mask = a.block_mask;
     bp.dq = a.dq; bp.dk = a.dk; bp.dv = a.dv;
     bp.delta = reinterpret_cast<float*>(a.workspace);
+    bp.range = reinterpret_cast<const uint32_t*>(reinterpret_cast<char*>(a.workspace) +
+                                                 (((size_t)a.B * a.H * a.L * sizeof(float) + 255) & ~(size_t)255));
     bp.BH = a.B * a.H; bp.L = a.L; bp.mode = a.mask;
     bp.W = a.window < a.L ? a.window : a.L;  // a window of L or more is plain causal
     bp.nQ = (a.L + kBR - 1) / kBR;

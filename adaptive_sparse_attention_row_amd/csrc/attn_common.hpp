@@ -183,10 +183,64 @@ struct Ops<__bf16, D> {
         }
     }
 
+    // The same transposed tile in fp16, each value times sc (a power of two
+    // chosen so that the tile's largest magnitude stays below 2^15: then the
+    // conversion is exact down to 2^-14, 29 binades below that maximum).
+    __device__ __forceinline__ static void store_v_unit_f16(uint16_t* Vt, int u, const VRegs& x, float sc) {
+        const int kg = u % (kBC / 4), dg = u / (kBC / 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t bits = (x.r[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                w[i] = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_bit_cast(float, bits << 16) * sc));
+            }
+            u32x2 pk;
+            pk[0] = w[0] | (w[1] << 16);
+            pk[1] = w[2] | (w[3] << 16);
+            *reinterpret_cast<u32x2*>(Vt + (dg * 8 + e) * kVRow + 4 * kg) = pk;
+        }
+    }
+
     template <int NB = 2>
     struct OAcc {
         f32x16 o[D / 32][NB];
     };
+
+    // The product below with the tile in fp16 (store_v_unit_f16) and the
+    // weights times ws rounded to fp16: one MFMA per block instead of a
+    // hi + lo pair.  ws must keep every |weight| * ws below 65504; rounding
+    // to 11 bits errs by at most 2^-12 relative.
+    template <int NB>
+    __device__ __forceinline__ static void pv_f16(OAcc<NB>& oa, const uint16_t* Vt, const f32x16 (&a4)[2][NB],
+                                                  const bool (&on)[2], float ws) {
+        const int l = lane_id(), m = l & 31, h = l >> 5;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (!on[kb]) continue;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f16x8 b[NB];
+#pragma unroll
+                for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) b[qb][p] = (_Float16)(a4[kb][qb][8 * t + p] * ws);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const uint16_t* row = Vt + (db * 32 + m) * kVRow + kb * 32 + 16 * t + 4 * h;
+                    const u32x2 lo4 = *reinterpret_cast<const u32x2*>(row);
+                    const u32x2 hi4 = *reinterpret_cast<const u32x2*>(row + 8);
+                    u32x4 vv;
+                    vv[0] = lo4[0]; vv[1] = lo4[1]; vv[2] = hi4[0]; vv[3] = hi4[1];
+                    const f16x8 va = __builtin_bit_cast(f16x8, vv);
+#pragma unroll
+                    for (int qb = 0; qb < NB; ++qb)
+                        oa.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, b[qb], oa.o[db][qb], 0, 0, 0);
+                }
+            }
+        }
+    }
 
     // O^T[d][c] += Vt^T[d][tile rows of block kb] . W[rows][c] for the NB
     // operand blocks c: W arrives in score-block layout (tile rows in

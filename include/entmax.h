@@ -184,7 +184,9 @@ int entmax_attn_output(const void* Q, const void* K, const void* V, const float*
                        void* stream);
 
 /*
- * Workspace bytes entmax_attn_bwd needs (per-row statistics).
+ * Workspace bytes entmax_attn_bwd needs: delta per query row (4 B each,
+ * rounded up to 256 B) and 4 KiB for the largest magnitudes of Q, K, V and
+ * dO, from which the bf16 path scales its fp16 weight products.
  */
 size_t entmax_attn_bwd_workspace(int B, int H, int L, int d, int dtype, int mask,
                                  int window);
@@ -201,6 +203,9 @@ size_t entmax_attn_bwd_workspace(int B, int H, int L, int d, int dtype, int mask
  *   written by entmax_attn_fwd for the same Q, K, V, scale, mask, window.
  *   dQ, dK, dV   [B][H][L][d] fp32 outputs (overwritten).
  *   workspace    at least entmax_attn_bwd_workspace(...) bytes.
+ * For bf16 inputs the products with A and dS take fp16 operands scaled by
+ * powers of two, so any finite input range is handled; Q, K, V, dO must be
+ * finite.
  */
 int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
                     const float* tau, const uint32_t* block_mask, float* dQ, float* dK,

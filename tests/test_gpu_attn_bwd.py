@@ -177,3 +177,21 @@ def test_empty_mask_columns(env, orc, d):
     dq, dk, dv = gpu_fwd_bwd(api, torch, inp, scale, 0, 0)
     assert np.all(dk[:, :, 64:] == 0) and np.all(dv[:, :, 64:] == 0)
     check_heads(orc, inp, scale, 0, 0, dq, dk, dv, [0, 1], f"empty columns d={d}")
+
+
+@pytest.mark.parametrize("case", ["big_dO", "big_V", "tiny_q_big_k", "tiny_dO"])
+def test_operand_ranges(env, orc, case):
+    """Inputs whose magnitudes leave fp16's range (or sit deep in its
+    subnormals) unless the weight products scale their operands: the bf16
+    gradients must still match the oracle to the same relative bound."""
+    api, torch = env
+    import torch as T
+    inp = gen(1, 2, 200, 64, "bf16", seed=41)
+    f = {"big_dO": {"do": 3e5}, "big_V": {"v": 2e4, "do": 40.0},
+         "tiny_q_big_k": {"q": 2e-5, "k": 5e4}, "tiny_dO": {"do": 1e-9}}[case]
+    for key, c in f.items():
+        inp[key] = (inp[key].float() * c).to(T.bfloat16)
+    dq, dk, dv = gpu_fwd_bwd(api, torch, inp, 0.125, 1, 0)
+    for g in (dq, dk, dv):
+        assert np.all(np.isfinite(g))
+    check_heads(orc, inp, 0.125, 1, 0, dq, dk, dv, [0, 1], case)
