@@ -1,34 +1,49 @@
 // attn_fwd.hip -- 1.5-entmax attention forward on gfx950.
 //
-// Three kernels per call, each one workgroup per 128 query rows of a head:
+// One workgroup per 128 query rows of a head runs three phases:
 //
-// fwd_stats  one sweep over the tiles the mask mode allows: S^T = K Q^T on
-//            MFMA; per row the maximum and the sixteen largest tile maxima
-//            (four per lane half and key parity); per (row half, tile) the
-//            largest score.  tau_lo = the exact threshold of those tile
-//            maxima.  Adding scores to a row only raises its threshold (every
-//            term of the normaliser is non-negative), so tau_lo <= tau, and
-//            it also clears the bracket end max - 2 of "AdaSplash-2: Faster
-//            Differentiable Sparse Attention" sec. 2.4 (score units).
-// fwd_solve  collect: over the tiles whose largest score beats tau_lo, every
-//            score s > tau_lo is appended to its row's candidate list.
-//            Nothing at or below tau_lo can carry weight, so the row's
-//            threshold is the threshold of its candidates alone.
-//            solve: per row, Newton steps from below on the candidates
-//            (f(t) = sum [(s - t)/2]_+^2 - 1 is convex and decreasing) with a
-//            bisection guard and an exact finish: once tau lies below the
-//            support the normaliser is a quadratic in tau over {s > tau}
-//            (S0/S1/S2 of AdaSplash-2 appendix C.3).  Sums are fp64.
-//            mask: a 64x64 tile is non-null iff one of its candidates exceeds
-//            its row's tau (packed 32 tiles per word, AdaSplash-2 appendix C.4).
-//            fallback: rows whose candidates overflow the list are collected
-//            again with a tighter bound, then refined by Halley-bisection
-//            sweeps over all their tiles, then a sweep marks their tiles.
-// fwd_out    walks only the set mask bits of its two 64-row blocks
-//            (find-first-set over the packed words, AdaSplash-2 sec. 3.3
-//            phase 4), recomputes S, A = [(S - tau)/2]_+^2 and accumulates
-//            O = A V on MFMA (bf16 inputs: A and V in fp16, the pages' own
-//            casts, with a bf16 hi + lo redo where V leaves the fp16 range).
+// stats   one sweep over the tiles the mask mode allows: S^T = K Q^T on
+//         MFMA; per row the maximum and the sixteen largest tile maxima
+//         (four per lane half and key parity); per (row half, tile) the
+//         largest score.  tau_lo = the exact threshold of those tile
+//         maxima.  Adding scores to a row only raises its threshold (every
+//         term of the normaliser is non-negative), so tau_lo <= tau, and
+//         it also clears the bracket end max - 2 of "AdaSplash-2: Faster
+//         Differentiable Sparse Attention" sec. 2.4 (score units).
+// solve   collect: over the tiles whose largest score beats tau_lo, every
+//         score s > tau_lo is appended to its row's candidate sub-list of
+//         the sweeping lane (no atomics: the lists and every sum over them
+//         are the same on every call).  Nothing at or below tau_lo can carry
+//         weight, so the row's threshold is the threshold of its candidates.
+//         solve: per row, Newton steps from below on the candidates
+//         (f(t) = sum [(s - t)/2]_+^2 - 1 is convex and decreasing) with a
+//         bisection guard and an exact finish: once tau lies below the
+//         support the normaliser is a quadratic in tau over {s > tau}
+//         (S0/S1/S2 of AdaSplash-2 appendix C.3).  Sums are fp64.
+//         mask: a 64x64 tile is non-null iff one of its candidates exceeds
+//         its row's tau (packed 32 tiles per word, AdaSplash-2 appendix C.4).
+//         overflow: rows whose lists overflow take the histogram
+//         initialisation of AdaSplash-2 sec. 3.1 (left-edge bins, exact
+//         solve on the bin counts), are collected again above tau_h when
+//         that fits, else refined by Halley-bisection sweeps on the
+//         histogram bracket.
+// out     O: from the candidate lists (the support's V rows) when they are
+//         short next to the non-null tiles; otherwise by walking only the set
+//         mask bits (find-first-set over the packed words, AdaSplash-2
+//         sec. 3.3 phase 4), recomputing S and A = [(S - tau)/2]_+^2 and
+//         accumulating O = A V on MFMA.  For bf16 inputs the product takes A
+//         and V in fp16 (A <= 1 keeps 11 significant bits, and bf16 V
+//         converts exactly while |V| <= 65504; a bf16 A alone measured
+//         6.6e-3 error against the 2e-3 bound), with a bf16 hi + lo redo of
+//         a block whose V leaves the fp16 range.
+//
+// For bf16 inputs with L <= 16384 the three phases run in one fused kernel
+// (fwd_fused_kernel) whose row statistics, tile maxima, tile lists and mask
+// stay in LDS between the phases.  fp32 inputs, longer sequences and the
+// phase entry points (entmax_attn_score_stats, entmax_attn_output) launch
+// each phase as its own kernel (fwd_stats_kernel, fwd_solve_kernel,
+// fwd_out_kernel / fwd_out_bf16_kernel), passing state through the
+// workspace.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
