@@ -450,9 +450,9 @@ struct CandSrc {
     // f(x) for entries i0, i0 + 1, ... in order
     template <class F>
     __device__ __forceinline__ void each_from(int i0, F f) const {
-#pragma unroll 2
+#pragma unroll 4
         for (int c = i0; c < n0; ++c) f(__builtin_bit_cast(float, glob[(size_t)(4 * c + h) * kBR][0]));
-#pragma unroll 2
+#pragma unroll 4
         for (int c = i0 > n0 ? i0 - n0 : 0; c < n1; ++c)
             f(__builtin_bit_cast(float, glob[(size_t)(4 * c + 2 + h) * kBR][0]));
     }
@@ -510,7 +510,9 @@ __device__ __forceinline__ float raw_threshold(float lo, float scale) {
 // f >= 0 stays at or below the root (bisection takes over if rounding lands
 // above it).  Exact finish: when the closed-form root of {x > t} lies below
 // the set's smallest member, that set is the support and the root is tau.
-// Sums in fp64.  Returns tau; lanes with active == false only take part in
+// Sums in fp64.  A step from a point above the root (rounding) is a Newton
+// step too: the tangent of a convex decreasing function meets zero at or
+// below the root.  Returns tau; lanes with active == false only take part in
 // the exchanges.
 template <class Src>
 __device__ __forceinline__ double solve_candidates(const Src& src, double mx, double lo, double hi,
@@ -556,7 +558,9 @@ __device__ __forceinline__ double solve_candidates(const Src& src, double mx, do
             t = tn;
         } else {
             hi = t;
-            t = 0.5 * (lo + hi);
+            double tn = (F1 > 0.0) ? t + f / F1 : 0.5 * (lo + hi);
+            if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
+            t = tn;
         }
         if (hi - lo <= 1e-12 * fmax(1.0, fabs(t))) {
             result = 0.5 * (lo + hi);
@@ -881,6 +885,8 @@ struct SolveScratch {
     float row_hi[kBR];
     int rstate[kBR];
     uint16_t cntq[4][kBR];  // entries met per candidate sub-list
+    int state_s;            // bit s set: some row of the block is in state s after the last solve
+    int gwork_s;            // list entries of the block (the gather decision)
     union {
         int hist[kHistBins * kBR];  // counts [bin][row]
         struct {
@@ -1007,6 +1013,10 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
 
     // ---- exact tau of the collecting rows whose sub-lists all fit
     auto solve = [&]() {
+        if (t == 0) {
+            ss.state_s = 0;
+            ss.gwork_s = 0;
+        }
         const bool open = rstate[srow] == kRowCollect;
         const int a0 = cntq[h][srow], a1 = cntq[2 + h][srow];
         const int b0 = cntq[h ^ 1][srow], b1 = cntq[2 + (h ^ 1)][srow];
@@ -1041,6 +1051,11 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
         } else if (open && h == 0) {
             rstate[srow] = kRowOver;
         }
+        if (h == 0) {
+            atomicOr(&ss.state_s, 1 << rstate[srow]);
+            const int ne = a0 + a1 + b0 + b1;
+            if (ne != 0) atomicAdd(&ss.gwork_s, kGatherRatio * ne);
+        }
         __syncthreads();
     };
 
@@ -1056,7 +1071,9 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
     collect();
     solve();
 
-    if (any_row(kRowOver)) {
+    // (no row overflowed: no row can be in the sweep state below)
+    const bool overflowed = (ss.state_s >> kRowOver) & 1;
+    if (overflowed) {
         // ---- histogram of the scores above the bound of each overflowing row
         for (int i = t; i < kHistBins * kBR; i += kNT) hist[i] = 0;
         float lr[2], hlo[2], hinv[2];
@@ -1151,7 +1168,8 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
     }
 
     // ---- Halley-bisection sweeps for rows whose lists overflowed
-    if (any_row(kRowSweep)) {
+    const bool swept = overflowed && any_row(kRowSweep);
+    if (swept) {
         float* const fb_t = ss.fb.t;
         int* const fb_active = ss.fb.active;
         float(&fb_part)[kBR][2][4] = ss.fb.part;
@@ -1300,16 +1318,15 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
     // lists are short next to the tiles the output pass would sweep
     bool gathered = false;
     if (p.gather) {
-        gathered = !any_row(kRowSweep);
+        gathered = !swept;
         if (gathered) {
-            if (t == 0) flag_s = 0;
+            // the solve summed the list entries; less the tiles' cost
+            if (t < 2 * WD) {
+                const int pc = __popc((&maskw[0][0])[t]);
+                if (pc != 0) atomicAdd(&ss.gwork_s, -kGatherTileCost * pc);
+            }
             __syncthreads();
-            int work = 0;
-            if (t < kBR) work += kGatherRatio * (cntq[0][t] + cntq[1][t] + cntq[2][t] + cntq[3][t]);
-            if (t < 2 * WD) work -= kGatherTileCost * __popc((&maskw[0][0])[t]);
-            if (work != 0) atomicAdd(&flag_s, work);
-            __syncthreads();
-            gathered = flag_s < 0;
+            gathered = ss.gwork_s < 0;
         }
         if (gathered) gather_rows<T, D>(p, bh, r0, clist, cntq, row_tau);
         if (t == 0 && p.ostate != nullptr) p.ostate[blk] = gathered ? 1 : 0;

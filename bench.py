@@ -6,10 +6,14 @@
 A timed step is one full forward (threshold + block mask + sparse output) of
 the long-context workload: B=1, H=12, L=8192, d=64, bf16, 64 clustered
 centroids, no mask.  The metric is its effective (dense-equivalent)
-throughput, 4*d*pairs / time.  The same run also times, each with HIP events
-on the stream the library launches on:
-  * the threshold kernel alone (the dominant kernel: one dense MFMA score
-    sweep, 2*d*pairs FLOP) -> the `roofline` object;
+throughput, 4*d*pairs / time.  For bf16 inputs the forward is one kernel
+launch (the fused score sweep, threshold solve and output), so its time is
+that kernel's -> the `roofline` object, against the algorithmic matrix work
+(one dense score sweep, 2*d*pairs, plus score recompute and A.V on the
+non-null 64x64 tiles, 4*d*pairs*non-null fraction).  The same run also
+times, each with HIP events on the stream the library launches on:
+  * the score sweep alone (entmax_attn_score_stats, 2*d*pairs FLOP) ->
+    `roofline_score_sweep`;
   * the row-wise tau kernel on the 8192 x 8192 fp32 score matrix (HBM-bound;
     3 rotating buffer sets so the 256 MB Infinity Cache cannot serve it);
   * the other forward workloads and the backward;
@@ -52,7 +56,7 @@ def source_digest(files):
     return h.hexdigest()[:16]
 
 
-STATS_SOURCES = ["adaptive_sparse_attention_row_amd/csrc/attn_fwd.hip",
+FWD_SOURCES = ["adaptive_sparse_attention_row_amd/csrc/attn_fwd.hip",
                  "adaptive_sparse_attention_row_amd/csrc/attn_common.hpp",
                  "adaptive_sparse_attention_row_amd/csrc/tile_dma.hpp",
                  "adaptive_sparse_attention_row_amd/csrc/device_common.hpp"]
@@ -76,9 +80,13 @@ def counter_traffic(name, sources):
 
 class Timer:
     """HIP-event timing of a callable on torch's current stream (the stream the
-    library is handed): an event before the first call and after every call,
-    so each call's duration is the gap between consecutive events.  Returns
-    the median in ms; `last` keeps the median, minimum and mean of the call."""
+    library is handed).  First an event before the first call and after every
+    call, so each call's duration is the gap between consecutive events (the
+    median and minimum come from these).  Then the same number of calls
+    back to back between two events only: their mean is the launch duration
+    a kernel trace reports (an event between every two calls adds a gap of a
+    few microseconds).  Returns the median in ms; `last` keeps the median,
+    minimum, per-call-event mean and batched mean."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -98,8 +106,15 @@ class Timer:
         torch.cuda.synchronize()
         d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
         med = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for i in range(steps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
         self.last = {"median_ms": round(med, 5), "min_ms": round(d[0], 5),
-                     "mean_ms": round(sum(d) / len(d), 5), "calls": steps}
+                     "event_mean_ms": round(sum(d) / len(d), 5),
+                     "mean_ms": round(e0.elapsed_time(e1) / steps, 5), "calls": steps}
         return med
 
 
@@ -243,9 +258,11 @@ def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False, alpha=1.5,
     res = {
         "fwd_ms": round(t_fwd, 5),
         "fwd_min_ms": fwd_t["min_ms"],
+        "fwd_mean_ms": fwd_t["mean_ms"],
         "threshold_ms": round(t_thr, 5),
         "score_stats_ms": round(t_stats, 5),
         "score_stats_min_ms": stats_t["min_ms"],
+        "score_stats_mean_ms": stats_t["mean_ms"],
         "solve_ms": round(t_thr - t_stats, 5),
         "output_pass_alone_ms": round(t_out, 5),
         "after_threshold_ms": round(t_fwd - t_thr, 5),
@@ -441,13 +458,16 @@ def bench_tau_rows(api, torch, timer, steps, warmup, alpha=1.5):
         assert r == 0, api.status_str(r)
 
     t = timer(run, max(steps, 30), warmup)
+    tl = timer.last
     algo_bytes = 4 * C2.rows * C2.cols * 2 + 4 * C2.rows
-    gbs = algo_bytes / (t * 1e-3) / 1e9
+    gbs = algo_bytes / (tl["mean_ms"] * 1e-3) / 1e9
     del sets, Ps, taus, S0
     torch.cuda.empty_cache()
     return {
         "workload": C2.name,
         "ms": round(t, 5),
+        "min_ms": tl["min_ms"],
+        "mean_launch_ms": tl["mean_ms"],
         "algorithmic_bytes": algo_bytes,
         "GB_per_s": round(gbs, 1),
         "roofline": {
@@ -497,7 +517,7 @@ def counters_summary(args):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a kernel by what the
     same counters read for the copy of known size, and record the HBM bytes
     per launch with the digest of the kernel's sources."""
-    sources = {"stats": STATS_SOURCES, "taurows": TAUROWS_SOURCES}[args.sources]
+    sources = {"fwd": FWD_SOURCES, "taurows": TAUROWS_SOURCES}[args.sources]
     kf, nkf = read_counter_csv(args.fetch_csv, args.kernel, "FETCH_SIZE")
     kw, nkw = read_counter_csv(args.write_csv, args.kernel, "WRITE_SIZE")
     cf, _ = read_counter_csv(args.copy_fetch_csv, args.copy_kernel, "FETCH_SIZE")
@@ -529,6 +549,105 @@ def counters_summary(args):
         f.write(f"Scale (true/counted): fetch {ff:.4f}, write {fw:.4f}.  HBM bytes per launch: "
                 f"{int(fetch_b)} read + {int(write_b)} written = {int(fetch_b + write_b)}.\n")
     print(json.dumps(rec))
+
+
+def _short_kernel_name(n):
+    import re
+    import subprocess
+    if n.startswith("_Z"):
+        # kernel templates over __bf16 (which c++filt does not demangle):
+        # <len><name>I<args>E with args DF16b, f, Li<n>E, Lb<0|1>E
+        m = re.search(r"_GLOBAL__N_1(\d+)", n)
+        if m:
+            k = m.end()
+            name = n[k:k + int(m.group(1))]
+            rest, args = n[k + int(m.group(1)):], []
+            if rest.startswith("I"):
+                rest = rest[1:]
+                while rest and not rest.startswith("E"):
+                    a = re.match(r"DF16b|f|Li(\d+)E|Lb([01])E", rest)
+                    if not a:
+                        break
+                    t = a.group(0)
+                    args.append("bf16" if t == "DF16b" else "float" if t == "f" else a.group(1) if a.group(1)
+                                else ("true" if a.group(2) == "1" else "false"))
+                    rest = rest[a.end():]
+            n = f"{name}<{', '.join(args)}>" if args else name
+        else:
+            try:
+                n = subprocess.run(["c++filt"], input=n, capture_output=True, text=True,
+                                   timeout=10).stdout.strip() or n
+            except (OSError, subprocess.SubprocessError):
+                pass
+    n = re.sub(r"entmax::attn::\(anonymous namespace\)::|entmax::\(anonymous namespace\)::|entmax::", "", n)
+    n = re.sub(r"\(FwdParams\)|\(BwdParams\)|\(\w*Params\)", "", n)
+    return n.replace("__bf16", "bf16").strip()
+
+
+def trace_summary(args):
+    """profiles/NAME.kernel_trace.md from rocprofv3's kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(args.stats_csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = os.path.join(ROOT, "profiles", f"{args.trace_summary}.kernel_trace.md")
+    with open(out, "w") as f:
+        f.write(f"# Kernel trace: {args.title}\n\n")
+        f.write("Command (on the GPU host, from the repository root, TMPDIR=/tmp):\n\n```\n")
+        f.write(args.commands.replace(";;", "\n") + "\n```\n\n")
+        f.write("From the run's `kernel_stats.csv` (durations in microseconds):\n\n")
+        f.write("| kernel | calls | mean | min | max | share |\n|---|---|---|---|---|---|\n")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            f.write(f"| `{_short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                    f"{100.0 * float(r['TotalDurationNs']) / total:.1f} % |\n")
+    print(out)
+
+
+MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE"]
+
+
+def mfma_summary(args):
+    """profiles/NAME.mfma.md: per-dispatch means of the matrix-core and issue
+    counters of the named kernels from rocprofv3's counter_collection.csv.
+    MOPS counters count matrix operations in units of 512 FLOP."""
+    import csv
+    recs = {}
+    for r in csv.DictReader(open(args.pmc_csv)):
+        recs.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = \
+            float(r["Counter_Value"])
+    out = os.path.join(ROOT, "profiles", f"{args.mfma_summary}.mfma.md")
+    with open(out, "w") as f:
+        f.write(f"# Matrix-core and issue counters: {args.title}\n\n")
+        f.write("Command (on the GPU host, from the repository root, TMPDIR=/tmp):\n\n```\n")
+        f.write(args.commands.replace(";;", "\n") + "\n```\n\n")
+        f.write("Per-dispatch means over the run's dispatches of each kernel.  MFMA FLOP = "
+                "(MOPS_BF16 + MOPS_F16) x 512 (for the score sweep this equals 2*d*pairs exactly).  "
+                "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs): the busy "
+                "counter read as a sum over the SIMDs and GRBM_GUI_ACTIVE as a sum over the XCDs.\n\n")
+        f.write("| kernel | dispatches | MFMA GFLOP | MFMA instrs | VALU / MFMA | LDS / MFMA | SALU / MFMA | "
+                "MFMA busy |\n|---|---|---|---|---|---|---|---|\n")
+        for sub in [k for k in args.kernels.split(";") if k]:
+            names = [n for n in recs if sub in n]
+            for n in names:
+                c = recs[n]
+                mean = lambda k: (sum(c[k].values()) / len(c[k])) if k in c and c[k] else float("nan")
+                nd = max(len(v) for v in c.values())
+                fl = (mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") + mean("SQ_INSTS_VALU_MFMA_MOPS_F16")) * 512
+                mf = mean("SQ_INSTS_MFMA")
+                f.write(f"| `{_short_kernel_name(n)}` | {nd} | {fl / 1e9:.2f} | {mf:.4g} | "
+                        f"{mean('SQ_INSTS_VALU') / mf:.2f} | {mean('SQ_INSTS_LDS') / mf:.2f} | "
+                        f"{mean('SQ_INSTS_SALU') / mf:.2f} | "
+                        f"{mean('SQ_VALU_MFMA_BUSY_CYCLES') / (1024 * mean('GRBM_GUI_ACTIVE') / 8):.3f} |\n")
+        f.write("\nRaw per-dispatch means:\n\n| kernel | " + " | ".join(MFMA_COUNTERS) + " |\n|---|" +
+                "---|" * len(MFMA_COUNTERS) + "\n")
+        for sub in [k for k in args.kernels.split(";") if k]:
+            for n in [n for n in recs if sub in n]:
+                c = recs[n]
+                vals = [(sum(c[k].values()) / len(c[k])) if k in c and c[k] else float("nan") for k in MFMA_COUNTERS]
+                f.write(f"| `{_short_kernel_name(n)}` | " + " | ".join(f"{v:.4g}" for v in vals) + " |\n")
+    print(out)
 
 
 def cpu_baseline(cfg, target_s=15.0):
@@ -619,16 +738,30 @@ def main():
     ap.add_argument("--counters-summary", metavar="NAME", default=None,
                     help="write profiles/NAME.counters.{json,md} from rocprofv3 counter CSVs (no GPU)")
     ap.add_argument("--kernel", default=None, help="kernel name substring (with --counters-summary)")
-    ap.add_argument("--sources", choices=["stats", "taurows"], default="stats")
+    ap.add_argument("--sources", choices=["fwd", "taurows"], default="fwd")
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")
     ap.add_argument("--copy-fetch-csv")
     ap.add_argument("--copy-write-csv")
     ap.add_argument("--copy-kernel", default="copyBuffer")
     ap.add_argument("--commands", default="", help="the profiling commands, ';;'-separated")
+    ap.add_argument("--trace-summary", metavar="NAME", default=None,
+                    help="write profiles/NAME.kernel_trace.md from a rocprofv3 kernel_stats.csv (no GPU)")
+    ap.add_argument("--stats-csv")
+    ap.add_argument("--mfma-summary", metavar="NAME", default=None,
+                    help="write profiles/NAME.mfma.md from a rocprofv3 counter_collection.csv (no GPU)")
+    ap.add_argument("--pmc-csv")
+    ap.add_argument("--kernels", default="", help="';'-separated kernel name substrings (with --mfma-summary)")
+    ap.add_argument("--title", default="")
     args = ap.parse_args()
     if args.counters_summary is not None:
         counters_summary(args)
+        return
+    if args.trace_summary is not None:
+        trace_summary(args)
+        return
+    if args.mfma_summary is not None:
+        mfma_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -676,16 +809,36 @@ def main():
         f"{head['dense_equiv_tflops']} TFLOP/s dense-eq, block sparsity {head['block_sparsity_64']}")
 
     d, pairs = C4.d, head["pairs"]
-    achieved = 2 * d * pairs / (t_stats * 1e-3) / 1e12
+    # the forward is one launch of the fused kernel; its algorithmic work is
+    # the dense score sweep plus recompute and A.V over the non-null tiles
+    nonnull_frac = head["nonnull_tiles_64"] / head["structural_tiles_64"]
+    alg = int(2 * d * pairs + 4 * d * pairs * nonnull_frac)
+    t_fwd_mean = head["fwd_mean_ms"]
+    achieved = alg / (t_fwd_mean * 1e-3) / 1e12
     roofline = {
-        "kernel": "fwd_stats_kernel (entmax_attn_score_stats: the dense MFMA score sweep)",
+        "kernel": "fwd_fused_kernel<64, 128, false> (entmax_attn_fwd: score sweep, threshold solve and "
+                  "sparse output in one launch)",
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": counter_traffic("fwd_stats_c4", STATS_SOURCES),
+        "traffic": counter_traffic("fwd_fused_c4", FWD_SOURCES),
+        "algorithmic_flop_per_launch": alg,
+        "flop_accounting": "2*d*pairs (dense score sweep) + 4*d*pairs*non-null 64x64 tile fraction "
+                           "(score recompute and A.V on the non-null tiles), over the mean launch time",
+        "mean_launch_ms": t_fwd_mean,
+    }
+    achieved_s = 2 * d * pairs / (head["score_stats_mean_ms"] * 1e-3) / 1e12
+    roofline_sweep = {
+        "kernel": "fwd_stats_kernel<bf16, 64, 128, false> (entmax_attn_score_stats: the dense score sweep alone)",
+        "bound": "mfma",
+        "achieved": round(achieved_s, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved_s / PEAK_BF16_TFLOPS, 4),
         "algorithmic_flop_per_launch": 2 * d * pairs,
+        "mean_launch_ms": head["score_stats_mean_ms"],
     }
 
     extras = {}
@@ -736,6 +889,7 @@ def main():
         "block_sparsity_64": head["block_sparsity_64"],
         "c4_fwd": head,
         "roofline": roofline,
+        "roofline_score_sweep": roofline_sweep,
         "cpu_baseline": cpu,
         "timing": "HIP events around every call on the library's stream; ms values are medians "
                   "(the *_min_ms fields the minima) of `steps` calls after `warmup` calls (C5: 10 of each)",
