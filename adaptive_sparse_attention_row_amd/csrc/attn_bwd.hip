@@ -77,10 +77,19 @@ __device__ __forceinline__ void stage_score(T* dst, const T* Xh, int r0, int L) 
     using O = Ops<T, D>;
     constexpr int kIt = (O::kChunks + kNT - 1) / kNT;
     u32x4 v[kIt];
+    // (a tile wholly below L loads without the per-row bounds)
+    if (r0 + kBC <= L) {
 #pragma unroll
-    for (int i = 0; i < kIt; ++i) {
-        const int c = threadIdx.x + i * kNT;
-        if (c < O::kChunks) v[i] = O::load_k_chunk(Xh, r0, L, c);
+        for (int i = 0; i < kIt; ++i) {
+            const int c = threadIdx.x + i * kNT;
+            if (c < O::kChunks) v[i] = O::template load_k_chunk<true>(Xh, r0, L, c);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int c = threadIdx.x + i * kNT;
+            if (c < O::kChunks) v[i] = O::load_k_chunk(Xh, r0, L, c);
+        }
     }
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
@@ -96,10 +105,18 @@ struct ScoreTileRegs {
     static constexpr int kIt = (Ops<T, D>::kChunks + kNT - 1) / kNT;
     u32x4 v[kIt];
     __device__ __forceinline__ void load(const T* Xh, int r0, int L) {
+        if (r0 + kBC <= L) {
 #pragma unroll
-        for (int i = 0; i < kIt; ++i) {
-            const int c = threadIdx.x + i * kNT;
-            if (c < Ops<T, D>::kChunks) v[i] = Ops<T, D>::load_k_chunk(Xh, r0, L, c);
+            for (int i = 0; i < kIt; ++i) {
+                const int c = threadIdx.x + i * kNT;
+                if (c < Ops<T, D>::kChunks) v[i] = Ops<T, D>::template load_k_chunk<true>(Xh, r0, L, c);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kIt; ++i) {
+                const int c = threadIdx.x + i * kNT;
+                if (c < Ops<T, D>::kChunks) v[i] = Ops<T, D>::load_k_chunk(Xh, r0, L, c);
+            }
         }
     }
     __device__ __forceinline__ void store(T* dst) const {
@@ -116,10 +133,18 @@ __device__ __forceinline__ void stage_pv(T* dst, const T* Xh, int r0, int L) {
     using O = Ops<T, D>;
     constexpr int kIt = (O::kVUnits + kNT - 1) / kNT;
     typename O::VRegs v[kIt];
+    if (r0 + kBC <= L) {
 #pragma unroll
-    for (int i = 0; i < kIt; ++i) {
-        const int u = threadIdx.x + i * kNT;
-        if (u < O::kVUnits) v[i] = O::load_v_unit(Xh, r0, L, u);
+        for (int i = 0; i < kIt; ++i) {
+            const int u = threadIdx.x + i * kNT;
+            if (u < O::kVUnits) v[i] = O::template load_v_unit<true>(Xh, r0, L, u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int u = threadIdx.x + i * kNT;
+            if (u < O::kVUnits) v[i] = O::load_v_unit(Xh, r0, L, u);
+        }
     }
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
@@ -133,10 +158,18 @@ struct PvTileRegs {
     static constexpr int kIt = (Ops<T, D>::kVUnits + kNT - 1) / kNT;
     typename Ops<T, D>::VRegs v[kIt];
     __device__ __forceinline__ void load(const T* Xh, int r0, int L) {
+        if (r0 + kBC <= L) {
 #pragma unroll
-        for (int i = 0; i < kIt; ++i) {
-            const int u = threadIdx.x + i * kNT;
-            if (u < Ops<T, D>::kVUnits) v[i] = Ops<T, D>::load_v_unit(Xh, r0, L, u);
+            for (int i = 0; i < kIt; ++i) {
+                const int u = threadIdx.x + i * kNT;
+                if (u < Ops<T, D>::kVUnits) v[i] = Ops<T, D>::template load_v_unit<true>(Xh, r0, L, u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kIt; ++i) {
+                const int u = threadIdx.x + i * kNT;
+                if (u < Ops<T, D>::kVUnits) v[i] = Ops<T, D>::load_v_unit(Xh, r0, L, u);
+            }
         }
     }
     __device__ __forceinline__ void store(T* dst) const {

@@ -119,6 +119,35 @@ struct Ops<__bf16, D> {
     template <int NB>
     __device__ __forceinline__ static void scores(f32x16 (&acc)[2][NB], const __bf16* Kt, const QOp<NB>& op) {
         const int l = lane_id(), m = l & 31, h = l >> 5;
+        if constexpr (NB == 1) {
+            // one product per operand read: the next k-slice's operands are
+            // read before this slice's products are issued, so that the LDS
+            // latency overlaps the matrix core (the scheduler otherwise
+            // waits on each read right before its product)
+            auto rd = [&](int s, int kb) {
+                const int row = kb * 32 + m;
+                return __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(Kt + row * kKRow + swz<kCPR>(row, 2 * s + h) * 8));
+            };
+            bf16x8 k[2][2];
+            k[0][0] = rd(0, 0);
+            k[0][1] = rd(0, 1);
+            const f32x16 zero = {};
+#pragma unroll
+            for (int s = 0; s < kNS; ++s) {
+                if (s + 1 < kNS) {
+                    k[(s + 1) & 1][0] = rd(s + 1, 0);
+                    k[(s + 1) & 1][1] = rd(s + 1, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    acc[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[s & 1][kb], op.q[0][s],
+                                                                         s == 0 ? zero : acc[kb][0], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -139,9 +168,12 @@ struct Ops<__bf16, D> {
         }
     }
 
-    // Global -> registers: chunk c of the tile starting at key c0 (zero past L).
+    // Global -> registers: chunk c of the tile starting at key c0 (zero past
+    // L; FULL: the caller knows the whole tile lies below L).
+    template <bool FULL = false>
     __device__ __forceinline__ static u32x4 load_k_chunk(const __bf16* Kh, int c0, int L, int c) {
         const int key = c / (D / 8), ch = c % (D / 8);
+        if (FULL) return *reinterpret_cast<const u32x4*>(Kh + (size_t)(c0 + key) * D + ch * 8);
         u32x4 v = {0u, 0u, 0u, 0u};
         if (c0 + key < L) v = *reinterpret_cast<const u32x4*>(Kh + (size_t)(c0 + key) * D + ch * 8);
         return v;
@@ -156,15 +188,20 @@ struct Ops<__bf16, D> {
     struct VRegs {
         u32x4 r[4];
     };
+    template <bool FULL = false>
     __device__ __forceinline__ static VRegs load_v_unit(const __bf16* Vh, int c0, int L, int u) {
         const int kg = u % (kBC / 4), dg = u / (kBC / 4);
         VRegs x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = c0 + 4 * kg + i;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (key < L) v = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dg * 8);
-            x.r[i] = v;
+            if (FULL) {
+                x.r[i] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dg * 8);
+            } else {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (key < L) v = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dg * 8);
+                x.r[i] = v;
+            }
         }
         return x;
     }
@@ -216,6 +253,35 @@ struct Ops<__bf16, D> {
     __device__ __forceinline__ static void pv_f16(OAcc<NB>& oa, const uint16_t* Vt, const f32x16 (&a4)[2][NB],
                                                   const bool (&on)[2], float ws) {
         const int l = lane_id(), m = l & 31, h = l >> 5;
+        if constexpr (NB == 1) {
+            // products in (kb, t, db) order, each operand read one product
+            // ahead (as in scores)
+            constexpr int kDB = D / 32, kIt = 2 * 2 * kDB;
+            auto rd = [&](int it) {
+                const int kb = it / (2 * kDB), t = (it / kDB) & 1, db = it % kDB;
+                const uint16_t* row = Vt + (db * 32 + m) * kVRow + kb * 32 + 16 * t + 4 * h;
+                const u32x2 lo4 = *reinterpret_cast<const u32x2*>(row);
+                const u32x2 hi4 = *reinterpret_cast<const u32x2*>(row + 8);
+                u32x4 vv;
+                vv[0] = lo4[0]; vv[1] = lo4[1]; vv[2] = hi4[0]; vv[3] = hi4[1];
+                return __builtin_bit_cast(f16x8, vv);
+            };
+            f16x8 va[2], b;
+            va[0] = rd(0);
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int kb = it / (2 * kDB), t = (it / kDB) & 1, db = it % kDB;
+                if (db == 0) {
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) b[p] = (_Float16)(a4[kb][0][8 * t + p] * ws);
+                }
+                if (it + 1 < kIt) va[(it + 1) & 1] = rd(it + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (on[kb]) oa.o[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[it & 1], b, oa.o[db][0], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (!on[kb]) continue;
@@ -334,8 +400,10 @@ struct Ops<float, D> {
         }
     }
 
+    template <bool FULL = false>
     __device__ __forceinline__ static u32x4 load_k_chunk(const float* Kh, int c0, int L, int c) {
         const int key = c / (D / 4), ch = c % (D / 4);
+        if (FULL) return *reinterpret_cast<const u32x4*>(Kh + (size_t)(c0 + key) * D + ch * 4);
         u32x4 v = {0u, 0u, 0u, 0u};
         if (c0 + key < L) v = *reinterpret_cast<const u32x4*>(Kh + (size_t)(c0 + key) * D + ch * 4);
         return v;
@@ -350,9 +418,10 @@ struct Ops<float, D> {
     struct VRegs {
         u32x4 r;
     };
+    template <bool FULL = false>
     __device__ __forceinline__ static VRegs load_v_unit(const float* Vh, int c0, int L, int u) {
         VRegs x;
-        x.r = load_k_chunk(Vh, c0, L, u);
+        x.r = load_k_chunk<FULL>(Vh, c0, L, u);
         return x;
     }
     __device__ __forceinline__ static void store_v_unit(float* Vt, int u, const VRegs& x) {
