@@ -38,6 +38,7 @@
 #include "attn_common.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "tile_dma.hpp"
 
 namespace entmax {
 namespace attn {
@@ -199,6 +200,31 @@ __device__ __forceinline__ void stage_pvw(T* dst, const T* Xh, int r0, int L, fl
         r.store16(reinterpret_cast<uint16_t*>(dst), sc);
     } else {
         stage_pv<T, D>(dst, Xh, r0, L);
+    }
+}
+
+// Direct global -> LDS staging of one 64-row tile in the score layout (the
+// swizzled natural layout of store_k_chunk): each wave issues a quarter of
+// the tile's 16-byte chunks; rows past L read row L - 1, whose scores the
+// callers mask.  r0 (< L) must be wave-uniform.  Addresses are recomputed per
+// call rather than kept in registers.
+template <typename T, int D>
+__device__ __forceinline__ void dma_tile(T* dst, const T* Xh, int r0, int L) {
+    using DMA = TileDMA<T, D>;
+    constexpr int kCPR = DMA::kCPR, kPerWave = DMA::kTileCh / 4, kIpw = kPerWave / kWave;
+    constexpr int kSlot = 16 / (int)sizeof(T);
+    static_assert(kPerWave % kWave == 0, "chunks per wave");
+    const int w = wave_id(), lane = lane_id();
+    const T* tb = Xh + (size_t)r0 * D;
+#pragma unroll
+    for (int k = 0; k < kIpw; ++k) {
+        const int q = w * kPerWave + k * kWave + lane;
+        int row = q / kCPR;
+        const int col = swz<kCPR>(row, q % kCPR) * kSlot;
+        row = r0 + row < L ? row : L - 1 - r0;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tb + row * D + col),
+                                         (__attribute__((address_space(3))) void*)(dst + (w * kPerWave + k * kWave) * kSlot),
+                                         16, 0, 0);
     }
 }
 
@@ -557,56 +583,57 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
     __syncthreads();
     const int n = nlist_s;
 
-    // Stage each listed tile (K and V in the score layout, and K in the PV
-    // layout when the pass takes the product with K) and call fn(J, cls, Kt,
-    // Vt, KPVt) when it is non-null for this wave's 64-row block and not
-    // masked out for its rows.
-    // The score-layout K and V of the next tile are loaded into registers
-    // while the current one is in use, except in the dQ pass at d = 128,
-    // where those registers are not free (the compiler spills).
-    auto walk = [&](auto with_pv, auto fn) {
+    // Walk the listed tiles.  K and V in the score layout go to LDS by
+    // direct global -> LDS loads, issued for the next tile as soon as every
+    // wave has taken its score products from the current one; the K tile in
+    // the PV layout (fp16, scaled), which the dQ pass needs, is loaded into
+    // registers while the score products run and converted into LDS after
+    // them (registers for a whole step ahead are not free at d = 128).  fa(J, cls, s, da) takes the products from the score tiles,
+    // fc(J, cls, s, da) the rest; both run only for tiles that are non-null
+    // for this wave's 64-row block and not masked out for its rows (every
+    // wave takes part in the barriers).  DMA rows past L repeat row L - 1:
+    // their scores are masked, so their weights are zero.
+    T* const kbuf = lds;
+    T* const vbuf = lds + BLK;
+    T* const kpv = lds + 2 * BLK;
+    auto walk = [&](auto with_pv, auto fa, auto fc) {
         constexpr bool kPv = decltype(with_pv)::value;
-        constexpr bool kPf = !kPv || D == 64;
-        ScoreTileRegs<T, D> rk, rv;
-        if (kPf && n > 0) {
-            rk.load(Kh, (list[0] & 0xfff) * kBC, p.L);
-            rv.load(Vh, (list[0] & 0xfff) * kBC, p.L);
-        }
+        PvTileRegs<T, D> rkp;
+        auto issue = [&](int e) {
+            const int r0 = (__builtin_amdgcn_readfirstlane(list[e]) & 0xfff) * kBC;
+            dma_tile<T, D>(kbuf, Kh, r0, p.L);
+            dma_tile<T, D>(vbuf, Vh, r0, p.L);
+        };
+        if (n > 0) issue(0);
         for (int e = 0; e < n; ++e) {
-            __syncthreads();
             const int ent = list[e];
             const int J = ent & 0xfff;
-            if constexpr (kPf) {
-                rk.store(lds);
-                rv.store(lds + BLK);
-            } else {
-                stage_score<T, D>(lds, Kh, J * kBC, p.L);
-                stage_score<T, D>(lds + BLK, Vh, J * kBC, p.L);
-            }
-            if constexpr (kPv) stage_pvw<T, D>(lds + 2 * BLK, Kh, J * kBC, p.L, fs.k);
+            wait_vmcnt<0>();
             __syncthreads();
-            if (kPf && e + 1 < n) {
-                const int J1 = list[e + 1] & 0xfff;
-                rk.load(Kh, J1 * kBC, p.L);
-                rv.load(Vh, J1 * kBC, p.L);
-            }
-            if (!((ent >> (12 + half)) & 1)) continue;
-            const int cls = block_class(R0, 32, J * kBC, kBC, g);
-            if (cls == kSkip) continue;
-            fn(J, cls, lds, lds + BLK, lds + 2 * BLK);
+            if constexpr (kPv) rkp.load(Kh, J * kBC, p.L);
+            const int cls = ((ent >> (12 + half)) & 1) ? block_class(R0, 32, J * kBC, kBC, g) : kSkip;
+            f32x16 sc[2][1], da[2][1];
+            if (cls != kSkip) fa(J, cls, sc, da);
+            if constexpr (kPv) rkp.store16(reinterpret_cast<uint16_t*>(kpv), fs.k);
+            __syncthreads();
+            if (e + 1 < n) issue(e + 1);
+            if (cls != kSkip) fc(J, cls, sc, da);
         }
         __syncthreads();
     };
     // 2g (so that the factor cancels in delta), the derivative of A in S
     auto dd_of = [&](auto gen_c, float sv) { return gen_c ? 2.0f * p.am.g(sv, tq) : fmaxf(sv - tq, 0.0f); };
 
+    // the products from the score-layout tiles (both passes)
+    auto score_products = [&](int J, int cls, f32x16(&s)[2][1], f32x16(&da)[2][1]) {
+        O::template scores<1>(s, kbuf, qop);
+        if (cls == kPartial) apply_mask<1>(s, J, R0, g);
+        O::template scores<1>(da, vbuf, dop);
+    };
+
     // ---- pass 1: delta_i = sum g dA / sum g
     float num = 0.f, den = 0.f;
-    walk(std::false_type{}, [&](int J, int cls, const T* Kt, const T* Vt, const T*) {
-        f32x16 s[2][1], da[2][1];
-        O::template scores<1>(s, Kt, qop);
-        if (cls == kPartial) apply_mask<1>(s, J, R0, g);
-        O::template scores<1>(da, Vt, dop);
+    walk(std::false_type{}, score_products, [&](int, int, f32x16(&s)[2][1], f32x16(&da)[2][1]) {
         by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -629,11 +656,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oa.o[db][0][i] = 0.f;
-    walk(std::true_type{}, [&](int J, int cls, const T* Kt, const T* Vt, const T* KPVt) {
-        f32x16 s[2][1], da[2][1];
-        O::template scores<1>(s, Kt, qop);
-        if (cls == kPartial) apply_mask<1>(s, J, R0, g);
-        O::template scores<1>(da, Vt, dop);
+    walk(std::true_type{}, score_products, [&](int, int, f32x16(&s)[2][1], f32x16(&da)[2][1]) {
         by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -641,7 +664,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
                 for (int r = 0; r < 16; ++r) s[kb][0][r] = dd_of(gen_c, s[kb][0][r] * p.scale) * (da[kb][0][r] - dl);
         });
         const bool on[2] = {true, true};
-        pv_w<T, D, 1>(oa, KPVt, s, on, fs.s);
+        pv_w<T, D, 1>(oa, kpv, s, on, fs.s);
     });
 
     if (row < p.L) {
@@ -736,26 +759,39 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
     T* QPVt = lds + 2 * BLK;
     T* dOPVt = lds + 3 * BLK;
 
-    // The dV sweep (PART 1) loads the next query tile's Q and dO into
-    // registers while the current one is in use; the other sweeps have no
-    // registers to spare for it and stage synchronously.
-    constexpr bool kPf = PART == 1;
-    ScoreTileRegs<T, D> rq;
-    PvTileRegs<T, D> rdo;
-    if (kPf && n > 0) {
-        rq.load(Qh, (list[0] & 0xfff) * 64, p.L);
-        rdo.load(dOh, (list[0] & 0xfff) * 64, p.L);
-    }
+    // The bf16 sweeps (PART 1, 2) stage the score-layout tiles (Q, and dO for
+    // dK) by direct global -> LDS loads, issued for the next query tile as
+    // soon as every wave has taken its score products from the current one;
+    // the sweep's PV-layout tile (dO for dV, Q for dK; fp16, scaled) goes
+    // through registers: in the dV sweep it is loaded a whole step ahead
+    // (there are registers for it), in the dK sweep while the score products
+    // run, and converted into LDS after them.  DMA rows past L repeat row L - 1: their tau is
+    // +inf, so their weights are zero.  The fp32 joint sweep (PART 0) stages
+    // synchronously.
+    constexpr bool kDma = PART != 0;
+    PvTileRegs<T, D> rpv;
+    T* const pvt = PART == 1 ? dOPVt : QPVt;
+    auto issue = [&](int e) {
+        const int r0 = (__builtin_amdgcn_readfirstlane(list[e]) & 0xfff) * 64;
+        dma_tile<T, D>(Qt, Qh, r0, p.L);
+        if constexpr (kDK) dma_tile<T, D>(dOt, dOh, r0, p.L);
+        if constexpr (PART == 1) rpv.load(dOh, r0, p.L);
+    };
+    if (kDma && n > 0) issue(0);
     for (int e = 0; e < n; ++e) {
         const int ent = list[e];
         const int I = ent & 0xfff;
         const int i0 = I * 64;
-        __syncthreads();
-        if constexpr (kPf) {
-            rq.store(Qt);
-            if constexpr (sizeof(T) == 2) rdo.store16(reinterpret_cast<uint16_t*>(dOPVt), fs.o);
-            else rdo.store(dOPVt);
+        if constexpr (kDma) {
+            wait_vmcnt<0>();
+            __syncthreads();
+            if constexpr (PART == 1) {
+                if constexpr (sizeof(T) == 2) rpv.store16(reinterpret_cast<uint16_t*>(pvt), fs.o);
+            } else {
+                rpv.load(Qh, i0, p.L);
+            }
         } else {
+            __syncthreads();
             stage_score<T, D>(Qt, Qh, i0, p.L);
             if constexpr (kDK) {
                 stage_score<T, D>(dOt, dOh, i0, p.L);
@@ -768,18 +804,20 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
             tau_s[t] = (row < p.L) ? p.tau[(size_t)bh * p.L + row] : __builtin_inff();
             if constexpr (kDK) del_s[t] = (row < p.L) ? p.delta[(size_t)bh * p.L + row] : 0.f;
         }
-        __syncthreads();
-        if (kPf && e + 1 < n) {
-            const int i1 = (list[e + 1] & 0xfff) * 64;
-            rq.load(Qh, i1, p.L);
-            rdo.load(dOh, i1, p.L);
-        }
-        if (!((ent >> (12 + w)) & 1)) continue;
-        const int cls = block_class(i0, 64, cw, KW, g);
-        if (cls == kSkip) continue;
+        if constexpr (!kDma) __syncthreads();
+        const int cls = ((ent >> (12 + w)) & 1) ? block_class(i0, 64, cw, KW, g) : kSkip;
         f32x16 s[2][NBK], da[2][NBK];
-        O::scores(s, Qt, kop);   // rows: queries (registers), lanes: keys
-        if (cls == kPartial) apply_mask_rows_are_queries(s, i0, cw, g);
+        if (cls != kSkip) {
+            O::scores(s, Qt, kop);   // rows: queries (registers), lanes: keys
+            if (cls == kPartial) apply_mask_rows_are_queries(s, i0, cw, g);
+            if constexpr (kDK) O::scores(da, dOt, vop);
+        }
+        if constexpr (kDma) {
+            if constexpr (PART == 2 && sizeof(T) == 2) rpv.store16(reinterpret_cast<uint16_t*>(pvt), fs.q);
+            __syncthreads();
+            if (e + 1 < n) issue(e + 1);
+        }
+        if (cls == kSkip) continue;
         const bool on[2] = {true, true};
         if constexpr (kDV) {
             // 4A (dd^2 with dd = 2g at alpha = 1.5), into dV
@@ -804,7 +842,6 @@ __global__ __launch_bounds__(kNT, PART == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdPar
             pv_w<T, D, NBK>(dva, dOPVt, a4, on, fs.a);
         }
         if constexpr (kDK) {
-            O::scores(da, dOt, vop);
             // 2 dS = dd (dA - delta) in place of S, into dK
             by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
