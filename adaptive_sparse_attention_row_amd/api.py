@@ -62,6 +62,12 @@ def lib() -> ctypes.CDLL:
     L.entmax_attn_bwd.restype = i32
     L.entmax_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, f32, f32,
                                   i32, i32, i32, P, sz, P]
+    L.entmax_attn_fwd_gv.restype = i32
+    L.entmax_attn_fwd_gv.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, i32,
+                                     i32, i32, P, sz, P]
+    L.entmax_attn_bwd_gv.restype = i32
+    L.entmax_attn_bwd_gv.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, f32, f32,
+                                     i32, i32, i32, P, sz, P]
     L.entmax_attn_threshold.restype = i32
     L.entmax_attn_threshold.argtypes = [P, P, P, P, i32, i32, i32, i32, f32, f32, i32, i32, i32, P, sz, P]
     L.entmax_attn_threshold_workspace.restype = sz
@@ -247,6 +253,56 @@ def attn_bwd(q, k, v, do, tau, block_mask, scale: Optional[float] = None,
                                dk.data_ptr(), dv.data_ptr(), B, H, L, d, float(scale), float(alpha),
                                dt, mask, window, _dev_ptr(ws), ws_bytes, _stream(q.device))
     _check("entmax_attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_fwd_gv(q, k, v, scale: Optional[float] = None, mask: int = MASK_NONE, window: int = 0,
+                alpha: float = 1.5):
+    """Forward for training (bf16, L <= 16384): returns (O, tau, block_mask,
+    GV fp32 [B, H, L, d], gsum fp32 [B, H, L]) for attn_bwd_gv."""
+    import torch
+    B, H, L, d = q.shape
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous CUDA tensors of one shape and dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = torch.empty(B, H, L, d, device=q.device, dtype=torch.float32)
+    gv = torch.empty_like(O)
+    tau = torch.empty(B, H, L, device=q.device, dtype=torch.float32)
+    gsum = torch.empty_like(tau)
+    bm = torch.empty(mask_shape(B, H, L, d, dt), device=q.device, dtype=torch.int32)
+    ws_bytes = lib().entmax_attn_fwd_workspace(B, H, L, d, dt, mask, window)
+    ws = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    st = lib().entmax_attn_fwd_gv(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(), tau.data_ptr(),
+                                  bm.data_ptr(), gv.data_ptr(), gsum.data_ptr(), B, H, L, d, float(scale),
+                                  float(alpha), dt, mask, window, ws.data_ptr(), ws_bytes, _stream(q.device))
+    _check("entmax_attn_fwd_gv", st)
+    return O, tau, bm, gv, gsum
+
+
+def attn_bwd_gv(q, k, v, do, tau, block_mask, gv, gsum, scale: Optional[float] = None,
+                mask: int = MASK_NONE, window: int = 0, alpha: float = 1.5):
+    """Backward of attn_fwd_gv.  Returns (dQ, dK, dV), fp32 [B, H, L, d]."""
+    import torch
+    B, H, L, d = q.shape
+    for t in (q, k, v, do):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, do must be contiguous CUDA tensors of one shape and dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty(B, H, L, d, device=q.device, dtype=torch.float32)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    ws_bytes = lib().entmax_attn_bwd_workspace(B, H, L, d, dt, mask, window)
+    ws = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    st = lib().entmax_attn_bwd_gv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), tau.data_ptr(),
+                                  block_mask.data_ptr(), gv.data_ptr(), gsum.data_ptr(), dq.data_ptr(),
+                                  dk.data_ptr(), dv.data_ptr(), B, H, L, d, float(scale), float(alpha), dt,
+                                  mask, window, ws.data_ptr(), ws_bytes, _stream(q.device))
+    _check("entmax_attn_bwd_gv", st)
     return dq, dk, dv
 
 

@@ -55,6 +55,8 @@ struct BwdParams {
     float* dk;
     float* dv;
     float* delta;  // workspace [BH][L]
+    const float* gv;    // [BH][L][d] sum_j g V_j from the forward (null: delta from a pass over the keys)
+    const float* gsum;  // [BH][L] sum_j g
     const uint32_t* range;  // workspace [kRangeBlocks][4]: max |Q|, |K|, |V|, |dO| bits per block (bf16)
     int BH, L, mode, W, nQ, nKB, Tc, Tr64, Wd;
     float scale;
@@ -338,6 +340,43 @@ struct DqCfg {
     static constexpr int kTps = (sizeof(T) == 4 && D == 128) ? 1 : 2;
     static constexpr int kBlk = Ops<T, D>::kKTile > Ops<T, D>::kVTile ? Ops<T, D>::kKTile : Ops<T, D>::kVTile;
 };
+
+// ------------------------------------------------------------ delta from G.V
+// delta_i = sum_j g_ij dA_ij / sum_j g_ij = dO_i . (sum_j g_ij V_j) / sum_j g_ij:
+// with G.V and sum g from the forward, one dot product per row.  D / 8 lanes
+// per row (an aligned group of a wave), each with 8 elements of d (one
+// 16-byte load of dO); the grid strides over the rows.
+template <typename T, int D>
+__global__ __launch_bounds__(kNT) void bwd_delta_kernel(BwdParams p) {
+    constexpr int kLpr = D / 8;  // lanes per row
+    const size_t rows = (size_t)p.BH * p.L;
+    const size_t stride = (size_t)gridDim.x * (kNT / kLpr);
+    const int part = threadIdx.x % kLpr;
+    for (size_t row = (size_t)blockIdx.x * (kNT / kLpr) + threadIdx.x / kLpr; row < rows; row += stride) {
+        float acc = 0.0f;
+        const T* dO = reinterpret_cast<const T*>(p.dout) + row * D + part * 8;
+        const float* gv = p.gv + row * D + part * 8;
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gv), g1 = *reinterpret_cast<const f32x4*>(gv + 4);
+        if constexpr (sizeof(T) == 2) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(dO);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float o = __builtin_bit_cast(float, ((x[e >> 1] >> ((e & 1) * 16)) & 0xffffu) << 16);
+                acc = fmaf(o, e < 4 ? g0[e] : g1[e - 4], acc);
+            }
+        } else {
+            const f32x4 o0 = *reinterpret_cast<const f32x4*>(dO), o1 = *reinterpret_cast<const f32x4*>(dO + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(o0[e], g0[e], fmaf(o1[e], g1[e], acc));
+        }
+#pragma unroll
+        for (int o = kLpr / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+        if (part == 0) {
+            const float den = p.gsum[row];
+            p.delta[row] = den > 0.0f ? acc / den : 0.0f;
+        }
+    }
+}
 
 // ------------------------------------------------------------ dQ kernel
 template <typename T, int D, bool GEN>
@@ -631,24 +670,30 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq32_kernel(BwdParams p) {
         O::template scores<1>(da, vbuf, dop);
     };
 
-    // ---- pass 1: delta_i = sum g dA / sum g
-    float num = 0.f, den = 0.f;
-    walk(std::false_type{}, score_products, [&](int, int, f32x16(&s)[2][1], f32x16(&da)[2][1]) {
-        by_alpha<GEN>([&](auto gen_c) {
+    // ---- pass 1: delta_i = sum g dA / sum g (given by bwd_delta_kernel when
+    // the forward wrote G.V and sum g)
+    float dl;
+    if (p.gv != nullptr) {
+        dl = row < p.L ? p.delta[(size_t)bh * p.L + row] : 0.f;
+    } else {
+        float num = 0.f, den = 0.f;
+        walk(std::false_type{}, score_products, [&](int, int, f32x16(&s)[2][1], f32x16(&da)[2][1]) {
+            by_alpha<GEN>([&](auto gen_c) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float dd = dd_of(gen_c, s[kb][0][r] * p.scale);
-                    num += dd * da[kb][0][r];
-                    den += dd;
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const float dd = dd_of(gen_c, s[kb][0][r] * p.scale);
+                        num += dd * da[kb][0][r];
+                        den += dd;
+                    }
+            });
         });
-    });
-    num += __shfl_xor(num, 32, kWave);
-    den += __shfl_xor(den, 32, kWave);
-    const float dl = den > 0.f ? num / den : 0.f;
-    if (h == 0 && row < p.L) p.delta[(size_t)bh * p.L + row] = dl;
+        num += __shfl_xor(num, 32, kWave);
+        den += __shfl_xor(den, 32, kWave);
+        dl = den > 0.f ? num / den : 0.f;
+        if (h == 0 && row < p.L) p.delta[(size_t)bh * p.L + row] = dl;
+    }
 
     // ---- pass 2: dQ^T += K^T (2 dS)^T
     typename O::template OAcc<1> oa;
@@ -894,6 +939,13 @@ hipError_t launch_bwd_class(const BwdParams& bp, hipStream_t stream) {
         hipError_t e0 = hipGetLastError();
         if (e0 != hipSuccess) return e0;
     }
+    if (bp.gv != nullptr) {
+        const size_t blocks = ((size_t)bp.BH * bp.L * (D / 8) + kNT - 1) / kNT;
+        hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)(blocks < (1u << 20) ? blocks : (1u << 20))),
+                           dim3(kNT), 0, stream, bp);
+        hipError_t e1 = hipGetLastError();
+        if (e1 != hipSuccess) return e1;
+    }
     if constexpr (sizeof(T) == 2)
         hipLaunchKernelGGL((bwd_dq32_kernel<D, GEN>), dim3(bp.nQ * bp.BH), dim3(kNT), 0, stream, bp);
     else
@@ -932,6 +984,8 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t stream) {
     bp.tau = a.tau; bp.mask = a.block_mask;
     bp.dq = a.dq; bp.dk = a.dk; bp.dv = a.dv;
     bp.delta = reinterpret_cast<float*>(a.workspace);
+    bp.gv = a.gv;
+    bp.gsum = a.gsum;
     bp.range = reinterpret_cast<const uint32_t*>(reinterpret_cast<char*>(a.workspace) +
                                                  (((size_t)a.B * a.H * a.L * sizeof(float) + 255) & ~(size_t)255));
     bp.BH = a.B * a.H; bp.L = a.L; bp.mode = a.mask;

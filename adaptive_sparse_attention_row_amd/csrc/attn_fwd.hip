@@ -70,6 +70,8 @@ struct FwdParams {
     float* umax;      // workspace [BH][Tr64][Tc]: largest raw score per (64-row block, tile)
     u32x2* clist;     // workspace [BH * nQ][kCandCap][128]: candidates (score bits, key index), slot-major per row block
     int* ostate;      // workspace [BH * nQ]: 1 where the solve kernel wrote O itself (null: the output kernel writes all)
+    float* gv;        // [BH][L][d]: sum_j g_ij V_j, g = dA/dS (null: not requested; fused kernel only)
+    float* gsum;      // [BH][L]: sum_j g_ij
     int gather;       // the solve kernel writes O from the candidate lists where it can
     int BH, L, mode, W, nQ, Tc, Tr64, Wd;
     float scale;
@@ -775,9 +777,11 @@ __global__ __launch_bounds__(kNT, kStatsOcc) void fwd_stats_kernel(FwdParams p) 
 // products and sums in list order.  D / 32 lanes per row, each with 32
 // elements of d; the lanes of a row load each entry's V row piece by
 // 16-byte loads, kB entries in flight.
+// wk = 1: the same sums with the derivatives g = dA/dS as weights, into
+// p.gv, and their row sums into p.gsum.
 template <typename T, int D>
 __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, const u32x2* clist,
-                                            const uint16_t (&cntq)[4][kBR], const float* row_tau) {
+                                            const uint16_t (&cntq)[4][kBR], const float* row_tau, int wk) {
     constexpr int kLpr = D / 32;              // lanes per row
     constexpr int kRpp = kNT / kLpr;          // rows per pass
     constexpr int kVec = 16 / (int)sizeof(T); // elements per 16-byte load
@@ -790,7 +794,7 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
         if (r0 + row >= p.L) continue;
         const float tau = row_tau[row];
         const int n0 = cntq[0][row], n1 = n0 + cntq[1][row], n2 = n1 + cntq[2][row], n = n2 + cntq[3][row];
-        float acc[32];
+        float acc[32], gs = 0.0f;
 #pragma unroll
         for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
         for (int i0 = 0; i0 < n; i0 += kB) {
@@ -805,12 +809,13 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
                 const float sv = __builtin_bit_cast(float, e[0]);
                 float w;
                 if (p.gen) {
-                    w = p.am.p(sv, tau);
+                    w = wk ? p.am.g(sv, tau) : p.am.p(sv, tau);
                 } else {
                     const float dd = 0.5f * fmaxf(sv - tau, 0.0f);
-                    w = dd * dd;
+                    w = wk ? dd : dd * dd;
                 }
                 a[u] = (i0 + u < n) ? w : 0.0f;
+                gs += a[u];
                 key[u] = e[1];
             }
             u32x4 v[kB][kLd];
@@ -833,7 +838,7 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
                         acc[j * kVec + e] = fmaf(a[u], x, acc[j * kVec + e]);
                     }
         }
-        float* orow = p.o + ((size_t)bh * p.L + r0 + row) * D + part * 32;
+        float* orow = (wk ? p.gv : p.o) + ((size_t)bh * p.L + r0 + row) * D + part * 32;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             f32x4 o4;
@@ -841,6 +846,7 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
             for (int e = 0; e < 4; ++e) o4[e] = acc[4 * j + e];
             *reinterpret_cast<f32x4*>(orow + 4 * j) = o4;
         }
+        if (wk && part == 0) p.gsum[(size_t)bh * p.L + r0 + row] = gs;
     }
 }
 
@@ -1328,7 +1334,10 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
             __syncthreads();
             gathered = ss.gwork_s < 0;
         }
-        if (gathered) gather_rows<T, D>(p, bh, r0, clist, cntq, row_tau);
+        if (gathered) {
+            gather_rows<T, D>(p, bh, r0, clist, cntq, row_tau, 0);
+            if (p.gv != nullptr) gather_rows<T, D>(p, bh, r0, clist, cntq, row_tau, 1);
+        }
         if (t == 0 && p.ostate != nullptr) p.ostate[blk] = gathered ? 1 : 0;
     }
 
@@ -1493,11 +1502,12 @@ struct OutLds {
 };
 
 // The block's rows from the tiles whose bits are set in mw0 / mw1 (its two
-// 64-row blocks' mask words).
+// 64-row blocks' mask words).  wk = 1: the derivatives g = dA/dS as weights
+// (<= 1 like A), into p.gv, and their row sums into p.gsum.
 template <int D, bool GEN>
 __device__ __forceinline__ void out_phase_bf16(const FwdParams& p, int bh, int r0, OutLds<D>& ol,
                                                const uint32_t* mw0, const uint32_t* mw1, uint16_t* list,
-                                               int& nlist_s, int& vover_s, const float* tau_lds) {
+                                               int& nlist_s, int& vover_s, const float* tau_lds, int wk = 0) {
     using O = Ops<__bf16, D>;
     constexpr int kVRow = O::kVRow;
     constexpr int kKPer = O::kChunks / kNT;  // K chunks per thread per tile
@@ -1570,7 +1580,9 @@ __device__ __forceinline__ void out_phase_bf16(const FwdParams& p, int bh, int r
     };
 
     typename O::template OAcc<1> oa;
+    float gs = 0.0f;
     auto run = [&](bool f16) {
+        gs = 0.0f;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -1596,15 +1608,24 @@ __device__ __forceinline__ void out_phase_bf16(const FwdParams& p, int bh, int r
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) acc[kb][0][r] = p.am.p(acc[kb][0][r] * p.scale, tq);
+                            for (int r = 0; r < 16; ++r) {
+                                const float sv = acc[kb][0][r] * p.scale;
+                                acc[kb][0][r] = wk ? p.am.g(sv, tq) : p.am.p(sv, tq);
+                            }
                     } else {
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const float dd = 0.5f * fmaxf(acc[kb][0][r] * p.scale - tq, 0.0f);
-                                acc[kb][0][r] = dd * dd;
+                                acc[kb][0][r] = wk ? dd : dd * dd;
                             }
+                    }
+                    if (wk) {
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) gs += acc[kb][0][r];
                     }
                     if (f16) {
                         const uint16_t* Vt = vbuf[e & 1];
@@ -1641,8 +1662,10 @@ __device__ __forceinline__ void out_phase_bf16(const FwdParams& p, int bh, int r
     if (vover_s) run(false);  // a V entry beyond fp16 range somewhere in this block's tiles
 
     // O = sum A V; register r of a lane holds d = db*32 + 8(r/4) + 4h + r%4
+    if (wk) gs += __shfl_xor(gs, 32, kWave);
     if (R0 + m < p.L) {
-        float* orow = p.o + ((size_t)bh * p.L + R0 + m) * D;
+        if (wk && h == 0) p.gsum[(size_t)bh * p.L + R0 + m] = gs;
+        float* orow = (wk ? p.gv : p.o) + ((size_t)bh * p.L + R0 + m) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -1712,12 +1735,16 @@ __global__ __launch_bounds__(kNT, (FusedCfg<D, TCMAX>::kOcc)) void fwd_fused_ker
     }
     if (p.o == nullptr) return;
     __syncthreads();
-    if (p.gen)
-        out_phase_bf16<D, true>(p, bh, r0, wk.out, bl.maskw[0], bl.maskw[1], bl.list, bl.nlist_s, bl.vover_s,
-                                bl.row_tau);
-    else
-        out_phase_bf16<D, false>(p, bh, r0, wk.out, bl.maskw[0], bl.maskw[1], bl.list, bl.nlist_s, bl.vover_s,
-                                 bl.row_tau);
+    // O, then (when requested) G.V and sum g over the same tiles
+    for (int what = 0; what < (p.gv != nullptr ? 2 : 1); ++what) {
+        if (what) __syncthreads();
+        if (p.gen)
+            out_phase_bf16<D, true>(p, bh, r0, wk.out, bl.maskw[0], bl.maskw[1], bl.list, bl.nlist_s, bl.vover_s,
+                                    bl.row_tau, what);
+        else
+            out_phase_bf16<D, false>(p, bh, r0, wk.out, bl.maskw[0], bl.maskw[1], bl.list, bl.nlist_s,
+                                     bl.vover_s, bl.row_tau, what);
+    }
 }
 
 template <typename T, int D, int TCMAX>
@@ -1818,6 +1845,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int phase, hipStream_t stream) {
     if (a.L > kMaxL) return hipErrorInvalidValue;
     FwdParams fp;
     fp.q = a.q; fp.k = a.k; fp.v = a.v; fp.o = a.o; fp.tau = a.tau;
+    fp.gv = a.gv; fp.gsum = a.gsum;
     char* ws = reinterpret_cast<char*>(a.workspace);
     fp.rowstat = reinterpret_cast<float*>(ws);
     size_t off = round256(rowstat_bytes(a.B, a.H, a.L));

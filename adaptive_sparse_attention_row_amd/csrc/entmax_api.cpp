@@ -27,6 +27,9 @@ int read_options(const entmax_options* o, int* cand_cap, int* row_hist) {
 }
 
 // Shared checks of the attention entry points (everything except pointers).
+// Longest sequence of the fused forward kernel, the only one that writes G.V.
+constexpr int kGvMaxL = 16384;
+
 int check_attn_shape(int B, int H, int L, int d, float alpha, int dtype, int mask, int window) {
     if (!(alpha > 1.0f && alpha <= 2.0f)) return ENTMAX_ERR_ALPHA;
     if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return ENTMAX_ERR_DTYPE;
@@ -104,10 +107,16 @@ size_t entmax_attn_fwd_workspace(int B, int H, int L, int d, int dtype, int mask
     return entmax::attn_fwd_workspace_bytes(B, H, L, d, dtype);
 }
 
-int entmax_attn_fwd_ex(const void* Q, const void* K, const void* V, float* O, float* tau,
-                       uint32_t* block_mask, int B, int H, int L, int d, float scale, float alpha,
-                       int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
-                       const entmax_options* options, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward, with G.V and sum g as well when gv is not null (bf16, the
+// fused kernel's range of L only).
+int attn_fwd_impl(const void* Q, const void* K, const void* V, float* O, float* tau,
+                  uint32_t* block_mask, float* gv, float* gsum, int B, int H, int L, int d, float scale,
+                  float alpha, int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
+                  const entmax_options* options, void* stream) {
     if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr || tau == nullptr)
         return ENTMAX_ERR_NULL;
     int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
@@ -129,8 +138,42 @@ int entmax_attn_fwd_ex(const void* Q, const void* K, const void* V, float* O, fl
     const int maxcap = entmax::attn_max_candidate_cap(d, dtype);
     a.cand_cap = (cap > 0 && cap < maxcap) ? cap : maxcap;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.gv = gv; a.gsum = gsum;
     (void)hipGetLastError();
     return hip_status(entmax::launch_attn_fwd(a, 7, (hipStream_t)stream));
+}
+
+// The backward; with gv and gsum from the forward, delta comes from them
+// instead of a pass over the keys (bf16 only).
+int attn_bwd_impl(const void* Q, const void* K, const void* V, const void* dO, const float* tau,
+                  const uint32_t* block_mask, const float* gv, const float* gsum, float* dQ, float* dK,
+                  float* dV, int B, int H, int L, int d, float scale, float alpha, int dtype, int mask,
+                  int window, void* workspace, size_t workspace_bytes, void* stream);
+
+}  // namespace
+
+extern "C" {
+
+int entmax_attn_fwd_ex(const void* Q, const void* K, const void* V, float* O, float* tau,
+                       uint32_t* block_mask, int B, int H, int L, int d, float scale, float alpha,
+                       int dtype, int mask, int window, void* workspace, size_t workspace_bytes,
+                       const entmax_options* options, void* stream) {
+    return attn_fwd_impl(Q, K, V, O, tau, block_mask, nullptr, nullptr, B, H, L, d, scale, alpha, dtype,
+                         mask, window, workspace, workspace_bytes, options, stream);
+}
+
+int entmax_attn_fwd_gv(const void* Q, const void* K, const void* V, float* O, float* tau,
+                       uint32_t* block_mask, float* GV, float* gsum, int B, int H, int L, int d,
+                       float scale, float alpha, int dtype, int mask, int window, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (GV == nullptr || gsum == nullptr) return ENTMAX_ERR_NULL;
+    int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
+    if (st != ENTMAX_OK) return st;
+    if (dtype != ENTMAX_BF16) return ENTMAX_ERR_DTYPE;
+    if (L > kGvMaxL) return ENTMAX_ERR_SHAPE;
+    if (!aligned16(GV) || ((uintptr_t)gsum & 3u)) return ENTMAX_ERR_ALIGN;
+    return attn_fwd_impl(Q, K, V, O, tau, block_mask, GV, gsum, B, H, L, d, scale, alpha, dtype, mask,
+                         window, workspace, workspace_bytes, nullptr, stream);
 }
 
 int entmax_attn_fwd(const void* Q, const void* K, const void* V, float* O, float* tau,
@@ -228,6 +271,33 @@ int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
                     float* dV, int B, int H, int L, int d, float scale, float alpha, int dtype,
                     int mask, int window, void* workspace, size_t workspace_bytes,
                     void* stream) {
+    return attn_bwd_impl(Q, K, V, dO, tau, block_mask, nullptr, nullptr, dQ, dK, dV, B, H, L, d, scale, alpha,
+                         dtype, mask, window, workspace, workspace_bytes, stream);
+}
+
+int entmax_attn_bwd_gv(const void* Q, const void* K, const void* V, const void* dO,
+                       const float* tau, const uint32_t* block_mask, const float* GV,
+                       const float* gsum, float* dQ, float* dK, float* dV, int B, int H, int L,
+                       int d, float scale, float alpha, int dtype, int mask, int window,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (GV == nullptr || gsum == nullptr) return ENTMAX_ERR_NULL;
+    int st = check_attn_shape(B, H, L, d, alpha, dtype, mask, window);
+    if (st != ENTMAX_OK) return st;
+    if (dtype != ENTMAX_BF16) return ENTMAX_ERR_DTYPE;
+    if (L > kGvMaxL) return ENTMAX_ERR_SHAPE;
+    if (!aligned16(GV) || ((uintptr_t)gsum & 3u)) return ENTMAX_ERR_ALIGN;
+    return attn_bwd_impl(Q, K, V, dO, tau, block_mask, GV, gsum, dQ, dK, dV, B, H, L, d, scale, alpha, dtype,
+                         mask, window, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int attn_bwd_impl(const void* Q, const void* K, const void* V, const void* dO, const float* tau,
+                  const uint32_t* block_mask, const float* gv, const float* gsum, float* dQ, float* dK,
+                  float* dV, int B, int H, int L, int d, float scale, float alpha, int dtype, int mask,
+                  int window, void* workspace, size_t workspace_bytes, void* stream) {
     if (Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || tau == nullptr ||
         block_mask == nullptr || dQ == nullptr || dK == nullptr || dV == nullptr)
         return ENTMAX_ERR_NULL;
@@ -245,6 +315,7 @@ int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
     a.q = Q; a.k = K; a.v = V; a.dout = dO; a.tau = const_cast<float*>(tau);
     a.block_mask = const_cast<uint32_t*>(block_mask);
     a.dq = dQ; a.dk = dK; a.dv = dV;
+    a.gv = const_cast<float*>(gv); a.gsum = const_cast<float*>(gsum);
     a.B = B; a.H = H; a.L = L; a.d = d; a.scale = scale; a.alpha = alpha; a.dtype = dtype;
     a.mask = mask; a.window = mask == ENTMAX_MASK_CAUSAL_WINDOW_SINK ? window : 0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
@@ -252,7 +323,7 @@ int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
     return hip_status(entmax::launch_attn_bwd(a, (hipStream_t)stream));
 }
 
-}  // extern "C"
+}  // namespace
 
 namespace {
 constexpr int kMaxDecodeLen = 1 << 24;

@@ -23,6 +23,8 @@ struct AttnArgs {
     float* dq;
     float* dk;
     float* dv;
+    float* gv;    // forward writes (may be null), backward reads (null: delta pass)
+    float* gsum;  // same
     int B, H, L, d;
     float scale;
     float alpha;  // in (1, 2]

@@ -300,6 +300,32 @@ def bench_attn(api, torch, timer, cfg, steps, warmup, with_bwd=False, alpha=1.5,
         res["bwd_dense_equiv_tflops"] = round(10 * d * pairs / (t_bwd * 1e-3) / 1e12, 3)
         res["bwd_12dp_tflops"] = round(12 * d * pairs / (t_bwd * 1e-3) / 1e12, 3)
         res["bwd_frac_of_peak_12dp"] = round(12 * d * pairs / (t_bwd * 1e-3) / 1e12 / peak, 4)
+        if cfg.dtype == "bf16" and L <= 16384:
+            # the training pair: the forward also writes G.V and sum g, and the
+            # backward takes delta from them instead of a pass over the keys
+            gvb = torch.empty_like(O)
+            gsb = torch.empty_like(tau)
+
+            def fwd_gv():
+                r = lib.entmax_attn_fwd_gv(q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(),
+                                           tau.data_ptr(), bm.data_ptr(), gvb.data_ptr(), gsb.data_ptr(), B, H, L,
+                                           d, sc, alpha, dt, cfg.mask, cfg.window, ws.data_ptr(), wsb, st)
+                assert r == 0, api.status_str(r)
+
+            def bwd_gv():
+                r = lib.entmax_attn_bwd_gv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                           tau.data_ptr(), bm.data_ptr(), gvb.data_ptr(), gsb.data_ptr(),
+                                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d, sc, alpha,
+                                           dt, cfg.mask, cfg.window, bws.data_ptr(), bwsb, st)
+                assert r == 0, api.status_str(r)
+
+            t_fg = timer(fwd_gv, bwd_steps, 2)
+            res["train_fwd_gv_ms"] = round(t_fg, 5)
+            t_bg = timer(bwd_gv, bwd_steps, 2)
+            res["train_bwd_gv_ms"] = round(t_bg, 5)
+            res["train_bwd_gv_min_ms"] = timer.last["min_ms"]
+            res["train_bwd_gv_frac_of_peak_12dp"] = round(12 * d * pairs / (t_bg * 1e-3) / 1e12 / peak, 4)
+            res["train_step_ms"] = round(t_fg + t_bg, 5)
     del q, k, v, O
     torch.cuda.empty_cache()
     return res, (t_fwd, t_stats, t_out)

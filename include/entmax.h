@@ -214,6 +214,38 @@ int entmax_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * Forward and backward for training, without the backward's delta pass.
+ *
+ * delta_i = sum_j g_ij dA_ij / sum_j g_ij (g_ij = dA_ij/dS_ij, the derivative
+ * of the weights in the scores: [(S_ij - tau_i)/2]_+ at alpha = 1.5, and
+ * [(alpha-1)(S_ij - tau_i)]_+^(1/(alpha-1) - 1) otherwise; dA_ij = dO_i . V_j)
+ * equals dO_i . GV_i / gsum_i with GV_i = sum_j g_ij V_j and
+ * gsum_i = sum_j g_ij.  The threshold's implicit derivative on the support
+ * ("AdaSplash-2: Faster Differentiable Sparse Attention", sec. 3.3 "Backward
+ * pass") needs delta; entmax_attn_bwd gets it from an extra pass over every
+ * row's non-null tiles, which these two calls replace by one more product in
+ * the forward's output phase and a dot product per row.
+ *
+ * entmax_attn_fwd_gv: entmax_attn_fwd (same arguments, workspace and
+ *   results: O, tau and the mask are bit-identical) that also writes
+ *     GV    [B][H][L][d] fp32, 16-byte aligned (overwritten)
+ *     gsum  [B][H][L] fp32 (overwritten)
+ * entmax_attn_bwd_gv: entmax_attn_bwd (same arguments and workspace) that
+ *   takes GV and gsum from entmax_attn_fwd_gv on the same inputs.
+ * Both need bf16 inputs (ENTMAX_ERR_DTYPE otherwise) and L <= 16384
+ * (ENTMAX_ERR_SHAPE otherwise); NULL GV or gsum is ENTMAX_ERR_NULL.
+ */
+int entmax_attn_fwd_gv(const void* Q, const void* K, const void* V, float* O, float* tau,
+                       uint32_t* block_mask, float* GV, float* gsum, int B, int H, int L, int d,
+                       float scale, float alpha, int dtype, int mask, int window, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int entmax_attn_bwd_gv(const void* Q, const void* K, const void* V, const void* dO,
+                       const float* tau, const uint32_t* block_mask, const float* GV,
+                       const float* gsum, float* dQ, float* dK, float* dV, int B, int H, int L,
+                       int d, float scale, float alpha, int dtype, int mask, int window,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode step: the newest query of every (batch, head), at position
  * L - 1, against the first L rows of its KV cache.  Exactly the last query
  * row of entmax_attn_fwd for the same mask mode (mode 0 and mode 1 both

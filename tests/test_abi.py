@@ -138,6 +138,39 @@ def test_attn_bwd_validation(api):
     assert call(6, FAKE + 4) == api.ERR_ALIGN
 
 
+def test_gv_validation(api):
+    """The training pair: bf16 and L <= 16384 only; GV and gsum required."""
+    L = api.lib()
+    # a caller-held mask: the threshold workspace suffices
+    need = L.entmax_attn_threshold_workspace(1, 2, 100, 64, 1, 1, 0)
+    f = L.entmax_attn_fwd_gv
+    base = [FAKE] * 8 + [1, 2, 100, 64, 0.125, 1.5, 1, 1, 0, FAKE, need, None]
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(6, None) == api.ERR_NULL      # GV
+    assert call(7, None) == api.ERR_NULL      # gsum
+    assert call(14, 0) == api.ERR_DTYPE       # fp32
+    assert call(10, 16448) == api.ERR_SHAPE   # L above the fused kernel's range
+    assert call(6, FAKE + 4) == api.ERR_ALIGN
+    assert call(0, None) == api.ERR_NULL      # Q, as in entmax_attn_fwd
+    assert call(18, need - 1) == api.ERR_WORKSPACE
+    bneed = L.entmax_attn_bwd_workspace(1, 2, 100, 64, 1, 1, 0)
+    b = L.entmax_attn_bwd_gv
+    bbase = [FAKE] * 11 + [1, 2, 100, 64, 0.125, 1.5, 1, 1, 0, FAKE, bneed, None]
+    def bcall(i, v):
+        a = list(bbase)
+        a[i] = v
+        return b(*a)
+    assert bcall(6, None) == api.ERR_NULL     # GV
+    assert bcall(7, None) == api.ERR_NULL     # gsum
+    assert bcall(17, 0) == api.ERR_DTYPE
+    assert bcall(13, 16448) == api.ERR_SHAPE
+    assert bcall(10, None) == api.ERR_NULL    # dV
+    assert bcall(21, bneed - 1) == api.ERR_WORKSPACE
+
+
 def test_options_validation(api):
     """Per-call options: out-of-range values are rejected before any launch."""
     import ctypes as C

@@ -195,3 +195,62 @@ def test_operand_ranges(env, orc, case):
     for g in (dq, dk, dv):
         assert np.all(np.isfinite(g))
     check_heads(orc, inp, 0.125, 1, 0, dq, dk, dv, [0, 1], case)
+
+
+GV_SHAPES = [
+    # (B, H, L, d, mode, W)
+    (1, 2, 300, 64, 1, 0),
+    (1, 2, 256, 128, 0, 0),
+    (2, 1, 200, 64, 2, 32),
+    (1, 2, 1024, 64, 1, 0),
+    (1, 1, 2048, 128, 1, 0),
+]
+
+
+@pytest.mark.parametrize("shape", GV_SHAPES, ids=lambda s: "B{}H{}L{}d{}m{}W{}".format(*s))
+@pytest.mark.parametrize("alpha", [1.5, 1.25])
+def test_gv_path(env, orc, shape, alpha):
+    """entmax_attn_fwd_gv: O, tau and the mask bit-identical to entmax_attn_fwd;
+    sum g against the oracle's; delta = dO . GV / sum g against the oracle's
+    delta; entmax_attn_bwd_gv's gradients against the oracle."""
+    api, torch = env
+    B, H, L, d, mode, W = shape
+    scale = 1.0 / math.sqrt(d)
+    inp = gen(B, H, L, d, "bf16", seed=71 + L + d)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    O, tau, bm = api.attn_fwd(q, k, v, scale=scale, mask=mode, window=W, alpha=alpha)
+    O2, tau2, bm2, gv, gsum = api.attn_fwd_gv(q, k, v, scale=scale, mask=mode, window=W, alpha=alpha)
+    dq, dk, dv = api.attn_bwd_gv(q, k, v, do, tau2, bm2, gv, gsum, scale=scale, mask=mode, window=W,
+                                 alpha=alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(tau, tau2) and torch.equal(bm, bm2)
+    Qn, Kn, Vn, dOn = (inp[n].float().numpy() for n in ("q", "k", "v", "do"))
+    _, _, _, gs_ref = orc.attn_fwd(Qn, Kn, Vn, scale, mode, W, alpha=alpha)
+    gs = gsum.cpu().numpy().reshape(-1)
+    assert np.abs(gs - gs_ref).max() <= 2e-3 * max(1.0, np.abs(gs_ref).max()), "gsum"
+    delta = (do.float() * gv).sum(-1).cpu().numpy().reshape(-1) / gs
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        rq, rk, rv, _, dref = orc.attn_bwd_head(Qn[b, h], Kn[b, h], Vn[b, h], dOn[b, h], scale, mode, W,
+                                                alpha=alpha)
+        dd = delta[bh * L:(bh + 1) * L]
+        assert np.abs(dd - dref).max() <= GRAD_TOL * max(np.abs(dref).max(), 1e-30), f"delta head {bh}"
+        for name, g, r in (("dQ", dq[b, h], rq), ("dK", dk[b, h], rk), ("dV", dv[b, h], rv)):
+            mx, fro = rel(g.cpu().numpy(), r)
+            assert mx <= GRAD_TOL, f"{shape} alpha {alpha} head {bh} {name}: max rel {mx:.3e} (fro {fro:.3e})"
+
+
+def test_gv_c5_two_heads(env, orc):
+    """The training pair at the L = 16384, d = 128 causal shape (two heads):
+    gradients against the oracle's full backward of each head."""
+    api, torch = env
+    from adaptive_sparse_attention_row_amd.workloads import C5, gen_config
+    inp = gen_config(C5, H=2)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    O, tau, bm, gv, gsum = api.attn_fwd_gv(q, k, v, scale=C5.scale, mask=C5.mask, window=C5.window)
+    dq, dk, dv = api.attn_bwd_gv(q, k, v, do, tau, bm, gv, gsum, scale=C5.scale, mask=C5.mask,
+                                 window=C5.window)
+    torch.cuda.synchronize()
+    w = check_heads(orc, inp, C5.scale, C5.mask, C5.window, dq.cpu().numpy(), dk.cpu().numpy(),
+                    dv.cpu().numpy(), [0, 1], "c5 gv")
+    print(f"c5 gv bwd worst max-rel {w:.3e}")
