@@ -777,11 +777,11 @@ __global__ __launch_bounds__(kNT, kStatsOcc) void fwd_stats_kernel(FwdParams p) 
 // products and sums in list order.  D / 32 lanes per row, each with 32
 // elements of d; the lanes of a row load each entry's V row piece by
 // 16-byte loads, kB entries in flight.
-// wk = 1: the same sums with the derivatives g = dA/dS as weights, into
-// p.gv, and their row sums into p.gsum.
-template <typename T, int D>
+// GV: in the same pass, G.V (the derivatives g = dA/dS as weights) into
+// p.gv and their row sums into p.gsum; each V row is read once for both.
+template <typename T, int D, bool GV>
 __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, const u32x2* clist,
-                                            const uint16_t (&cntq)[4][kBR], const float* row_tau, int wk) {
+                                            const uint16_t (&cntq)[4][kBR], const float* row_tau) {
     constexpr int kLpr = D / 32;              // lanes per row
     constexpr int kRpp = kNT / kLpr;          // rows per pass
     constexpr int kVec = 16 / (int)sizeof(T); // elements per 16-byte load
@@ -794,11 +794,15 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
         if (r0 + row >= p.L) continue;
         const float tau = row_tau[row];
         const int n0 = cntq[0][row], n1 = n0 + cntq[1][row], n2 = n1 + cntq[2][row], n = n2 + cntq[3][row];
-        float acc[32], gs = 0.0f;
+        float acc[32], accg[GV ? 32 : 1], gs = 0.0f;
 #pragma unroll
         for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+        if constexpr (GV) {
+#pragma unroll
+            for (int j = 0; j < 32; ++j) accg[j] = 0.0f;
+        }
         for (int i0 = 0; i0 < n; i0 += kB) {
-            float a[kB];
+            float a[kB], gw[kB];
             uint32_t key[kB];
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
@@ -807,15 +811,16 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
                 const int c = i - (qq == 0 ? 0 : qq == 1 ? n0 : qq == 2 ? n1 : n2);
                 const u32x2 e = clist[(size_t)(4 * c + qq) * kBR + row];
                 const float sv = __builtin_bit_cast(float, e[0]);
-                float w;
+                const bool live = i0 + u < n;
                 if (p.gen) {
-                    w = wk ? p.am.g(sv, tau) : p.am.p(sv, tau);
+                    a[u] = live ? p.am.p(sv, tau) : 0.0f;
+                    if constexpr (GV) gw[u] = live ? p.am.g(sv, tau) : 0.0f;
                 } else {
-                    const float dd = 0.5f * fmaxf(sv - tau, 0.0f);
-                    w = wk ? dd : dd * dd;
+                    const float dd = live ? 0.5f * fmaxf(sv - tau, 0.0f) : 0.0f;
+                    a[u] = dd * dd;
+                    if constexpr (GV) gw[u] = dd;
                 }
-                a[u] = (i0 + u < n) ? w : 0.0f;
-                gs += a[u];
+                if constexpr (GV) gs += gw[u];
                 key[u] = e[1];
             }
             u32x4 v[kB][kLd];
@@ -836,17 +841,27 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
                         const float x = sizeof(T) == 2 ? __builtin_bit_cast(float, (bits >> ((e & 1) * 16)) << 16)
                                                        : __builtin_bit_cast(float, bits);
                         acc[j * kVec + e] = fmaf(a[u], x, acc[j * kVec + e]);
+                        if constexpr (GV) accg[j * kVec + e] = fmaf(gw[u], x, accg[j * kVec + e]);
                     }
         }
-        float* orow = (wk ? p.gv : p.o) + ((size_t)bh * p.L + r0 + row) * D + part * 32;
+        const size_t off = ((size_t)bh * p.L + r0 + row) * D + part * 32;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             f32x4 o4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o4[e] = acc[4 * j + e];
-            *reinterpret_cast<f32x4*>(orow + 4 * j) = o4;
+            *reinterpret_cast<f32x4*>(p.o + off + 4 * j) = o4;
         }
-        if (wk && part == 0) p.gsum[(size_t)bh * p.L + r0 + row] = gs;
+        if constexpr (GV) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                f32x4 g4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) g4[e] = accg[4 * j + e];
+                *reinterpret_cast<f32x4*>(p.gv + off + 4 * j) = g4;
+            }
+            if (part == 0) p.gsum[(size_t)bh * p.L + r0 + row] = gs;
+        }
     }
 }
 
@@ -1335,8 +1350,8 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
             gathered = ss.gwork_s < 0;
         }
         if (gathered) {
-            gather_rows<T, D>(p, bh, r0, clist, cntq, row_tau, 0);
-            if (p.gv != nullptr) gather_rows<T, D>(p, bh, r0, clist, cntq, row_tau, 1);
+            if (p.gv != nullptr) gather_rows<T, D, true>(p, bh, r0, clist, cntq, row_tau);
+            else gather_rows<T, D, false>(p, bh, r0, clist, cntq, row_tau);
         }
         if (t == 0 && p.ostate != nullptr) p.ostate[blk] = gathered ? 1 : 0;
     }
