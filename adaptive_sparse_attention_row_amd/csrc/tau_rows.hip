@@ -22,13 +22,16 @@
 //   5. P from the register copy, so HBM sees one read and one write per
 //      element; the loads of the wave's next row are issued into the
 //      registers as they free up.
-// Wider rows take a 256-thread streaming kernel that reads the row three
-// times (maximum, candidates above m - 2, output).  While it compacts the
-// candidates it also bins them (the histogram initialisation of AdaSplash-2
-// sec. 3.1, 64 left-edge bins): the histogram threshold tau_h brackets tau
-// within one bin width, so the refinement starts from [tau_h, tau_h + h]
-// instead of the whole [m - 2, m - 2/sqrt(n)].  That matters when a dense row
-// overflows the LDS list and every refinement step re-reads the row.
+// Rows up to 32768 wide (float4 access): a 256-thread workgroup holds the
+// row in registers instead (tau_rows_block), so the refinement steps of a
+// dense row never re-read it.  Wider rows take a 256-thread streaming kernel
+// that reads the row three times (maximum, candidates above m - 2, output).
+// While it compacts the candidates it also bins them (the histogram
+// initialisation of AdaSplash-2 sec. 3.1, 64 left-edge bins): the histogram
+// threshold tau_h brackets tau within one bin width, so the refinement starts
+// from [tau_h, tau_h + h] instead of the whole [m - 2, m - 2/sqrt(n)].  That
+// matters when a dense row overflows the LDS list and every refinement step
+// re-reads the row.
 //
 // Other alpha in (1, 2] (AdaSplash-2 sec. 2.3; see AlphaMap) take the same
 // structure with p = [(alpha-1)(s - tau)]_+^(1/(alpha-1)): the lower bound is
@@ -222,6 +225,97 @@ __global__ __launch_bounds__(kWave, 3) void tau_rows_wave(const float* __restric
     }
 }
 
+// Rows of 64 VPT < cols <= 256 VPT (float4 access): a 256-thread workgroup
+// holds the row in registers, VPT values per thread, so HBM sees one read and
+// one write per element however many refinement steps the row needs (a dense
+// row's candidates overflow any LDS list).  Every Halley-bisection step
+// visits the registers, from the plain bracket: a step over registers costs
+// less than the histogram's LDS atomic per score (measured on dense rows of
+// 32768: 0.196 ms for 2048 rows from the plain bracket, 0.259 ms with the
+// histogram first).  Three rows per CU in flight at VPT = 64, two at 128
+// (256 KB per CU, more than HBM needs in flight).
+// FULL: cols == 256 VPT, no bounds on the accesses.
+template <int VPT, bool FULL, bool GEN>
+__global__ __launch_bounds__(kThreads, (VPT <= 64 ? 3 : 2)) void tau_rows_block(const float* __restrict__ S,
+                                                             float* __restrict__ P,
+                                                             float* __restrict__ tau_out, int cols,
+                                                             int64_t ld, AlphaMap am) {
+    static_assert(VPT % 4 == 0, "float4 chunks");
+    __shared__ float red[2][kWaves][6];
+    __shared__ float mbuf[kWaves];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const float* src = S + row * ld;
+    constexpr int kCh = VPT / 4;
+    // chunk k of the thread is the float4 at column (256 k + t) * 4; chunks
+    // past the end re-read the last chunk that starts inside the row
+    const int last = ((cols - 1) / 4) * 4;
+    float v[VPT];
+#pragma unroll
+    for (int k = 0; k < kCh; ++k) {
+        const int pos = (k * kThreads + t) * 4;
+        const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (FULL ? pos : min(pos, last))));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * k + e] = (FULL || pos + e < cols) ? q[e] : neg_inf();
+    }
+    float mx = neg_inf();
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) mx = fmaxf(mx, v[k]);
+    const float m = block_max(mx, mbuf);
+
+    float tau;
+    if (m == neg_inf()) {
+        tau = neg_inf();
+    } else {
+        // (cols bounds the active count from above, which keeps the upper
+        // bracket end m - 2/sqrt(n) valid).  Each step reads the registers
+        // through an opaque copy: otherwise the compiler hoists the
+        // step-invariant part of every term (x - m) out of the loop and keeps
+        // a second copy of the row, which spills.
+        if constexpr (GEN) {
+            tau = refine_tau_gen(m, (float)cols, am, [&](float tt, RowSums& s) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    float x = v[k];
+                    asm volatile("" : "+v"(x));
+                    accumulate_gen(s, x, tt, am);
+                }
+            }, red);
+        } else {
+            tau = refine_tau(m, (float)cols, [&](float tt, RowSums& s) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    float x = v[k];
+                    asm volatile("" : "+v"(x));
+                    accumulate(s, x, tt, m);
+                }
+            }, red);
+        }
+    }
+    if (t == 0) tau_out[row] = tau;
+    if (P == nullptr) return;
+    float* dst = P + row * ld;
+    const float h = -0.5f * tau;
+    // an opaque copy of the thread index: the bounds below are not the
+    // loads' bounds kept alive through the refinement (one mask per chunk)
+    int ti = t;
+    asm volatile("" : "+v"(ti));
+#pragma unroll
+    for (int k = 0; k < kCh; ++k) {
+        const int pos = (k * kThreads + ti) * 4;
+        f32x4 q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = GEN ? am.p(v[4 * k + e], tau) : prob_h(v[4 * k + e], h);
+        if (FULL || pos + 3 < cols) {
+            __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(dst + pos));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (pos + e < cols) dst[pos + e] = q[e];
+        }
+    }
+}
+
 // Any width: the row is streamed from global memory (L2-resident after the
 // first pass for moderate widths).
 template <bool GEN>
@@ -365,6 +459,22 @@ hipError_t launch_rows(const float* S, float* P, float* tau, int64_t rows, int64
         if (cols <= 32 * kWave) return launch_wave<32, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
         if (cols <= 64 * kWave) return launch_wave<64, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
         if (cols <= 128 * kWave) return launch_wave<128, true, GEN>(S, P, tau, rows, cols, ld, am, stream);
+        if (cols <= 128 * kThreads) {
+            const dim3 grid((unsigned)rows), block(kThreads);
+            if (cols == 64 * kThreads)
+                hipLaunchKernelGGL((tau_rows_block<64, true, GEN>), grid, block, 0, stream, S, P, tau, (int)cols, ld,
+                                   am);
+            else if (cols < 64 * kThreads)
+                hipLaunchKernelGGL((tau_rows_block<64, false, GEN>), grid, block, 0, stream, S, P, tau, (int)cols,
+                                   ld, am);
+            else if (cols == 128 * kThreads)
+                hipLaunchKernelGGL((tau_rows_block<128, true, GEN>), grid, block, 0, stream, S, P, tau, (int)cols,
+                                   ld, am);
+            else
+                hipLaunchKernelGGL((tau_rows_block<128, false, GEN>), grid, block, 0, stream, S, P, tau, (int)cols,
+                                   ld, am);
+            return hipGetLastError();
+        }
     } else {
         if (cols <= 8 * kWave) return launch_wave<8, false, GEN>(S, P, tau, rows, cols, ld, am, stream);
         if (cols <= 16 * kWave) return launch_wave<16, false, GEN>(S, P, tau, rows, cols, ld, am, stream);

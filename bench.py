@@ -425,29 +425,36 @@ def bench_decode(api, torch, timer, steps, warmup):
 
 def bench_wide_rows(api, torch, timer, steps, warmup):
     """Rows wider than 8192 that are dense (every score within reach of the
-    maximum, so the candidates overflow the LDS list and each refinement
-    step re-reads the row): the streaming row kernel with and without the
-    histogram-initialised bracket (AdaSplash-2 sec. 3.1)."""
-    rows, cols = 2048, 32768
-    g = torch.Generator("cpu").manual_seed(61)
-    S = (0.02 * torch.randn(rows, cols, generator=g)).cuda()
-    P = torch.empty_like(S)
-    tau = torch.empty(rows, device="cuda")
+    maximum, so the candidates overflow any LDS list): 2048 rows of 32768,
+    which a workgroup holds in registers (one read, one write per element),
+    and 1024 rows of 65536, which are streamed and re-read by every
+    refinement step, with and without the histogram-initialised bracket
+    (AdaSplash-2 sec. 3.1)."""
+    out = {}
     lib = api.lib()
-    st = api._stream(S.device)
+    for rows, cols, hists in ((2048, 32768, (1,)), (1024, 65536, (1, 0))):
+        g = torch.Generator("cpu").manual_seed(61)
+        S = (0.02 * torch.randn(rows, cols, generator=g)).cuda()
+        P = torch.empty_like(S)
+        tau = torch.empty(rows, device="cuda")
+        st = api._stream(S.device)
+        rec = {"workload": f"rows{rows}x{cols}_f32_dense (0.02 N(0, 1))"}
+        for hist in hists:
+            opts = api._opts(0, row_plain_bracket=not hist)
 
-    out = {"workload": f"rows{rows}x{cols}_f32_dense (0.02 N(0, 1))"}
-    for hist in (1, 0):
-        opts = api._opts(0, row_plain_bracket=not hist)
+            def run():
+                r = lib.entmax_tau_rows_ex(S.data_ptr(), P.data_ptr(), tau.data_ptr(), rows, cols, cols, 1.5,
+                                           opts, st)
+                assert r == 0, api.status_str(r)
 
-        def run():
-            r = lib.entmax_tau_rows_ex(S.data_ptr(), P.data_ptr(), tau.data_ptr(), rows, cols, cols, 1.5, opts, st)
-            assert r == 0, api.status_str(r)
-
-        t = timer(run, max(steps // 2, 5), 2)
-        out["histogram_ms" if hist else "bracket_only_ms"] = round(t, 5)
-    del S, P
-    torch.cuda.empty_cache()
+            t = timer(run, max(steps // 2, 5), 2)
+            key = "ms" if len(hists) == 1 else ("histogram_ms" if hist else "bracket_only_ms")
+            rec[key] = round(t, 5)
+            if len(hists) == 1 or hist:
+                rec["GB_per_s"] = round(8 * rows * cols / (timer.last["mean_ms"] * 1e-3) / 1e9, 1)
+        out[f"rows{cols}"] = rec
+        del S, P
+        torch.cuda.empty_cache()
     return out
 
 

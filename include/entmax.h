@@ -301,11 +301,15 @@ int entmax_attn_decode_noalloc(const void* q, const void* K, const void* V, floa
  *    histogram-initialised sweeps (AdaSplash-2 sec. 3.1 and sec. 3.3 phases
  *    2-3); tests use a tiny cap to force that path.  Results agree either way
  *    within the tolerances.  Values outside 0 .. 128 give ENTMAX_ERR_ARG.
- *  row_plain_bracket: entmax_tau_rows on rows wider than 8192 starts its
- *    refinement from the histogram bracket [tau_h, tau_h + 1/(64 (alpha-1))]
- *    of AdaSplash-2 sec. 3.1 and Proposition 3.1 (0, the default), or from the
- *    plain bracket [m - 1/(alpha-1), m - n^(1-alpha)/(alpha-1)] (1).  Other
- *    values give ENTMAX_ERR_ARG.
+ *  row_plain_bracket: entmax_tau_rows on rows that it streams from memory
+ *    (wider than 32768, or wider than 8192 without 16-byte row alignment)
+ *    starts its refinement from the histogram bracket
+ *    [tau_h, tau_h + 1/(64 (alpha-1))] of AdaSplash-2 sec. 3.1 and
+ *    Proposition 3.1 (0, the default), or from the plain bracket
+ *    [m - 1/(alpha-1), m - n^(1-alpha)/(alpha-1)] (1).  Rows it holds in
+ *    registers always start from the plain bracket (a refinement step over
+ *    registers costs less than building the histogram).  Other values give
+ *    ENTMAX_ERR_ARG.
  */
 typedef struct entmax_options {
     int candidate_cap;

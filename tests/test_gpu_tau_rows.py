@@ -69,7 +69,7 @@ def env():
 
 
 @pytest.mark.parametrize("cols", [1, 2, 3, 63, 64, 65, 257, 1000, 1024, 1025, 4096, 8191,
-                                  8192, 8193, 20000])
+                                  8192, 8193, 16384, 20000, 32768, 40000])
 def test_widths(env, orc, cols):
     api, torch = env
     rng = np.random.default_rng(cols)
@@ -180,7 +180,7 @@ ALPHAS = [1.1, 1.25, 1.75, 2.0]
 
 
 @pytest.mark.parametrize("alpha", ALPHAS)
-@pytest.mark.parametrize("cols", [1, 65, 1000, 8192, 8193, 20000])
+@pytest.mark.parametrize("cols", [1, 65, 1000, 8192, 8193, 20000, 32768])
 def test_alpha_widths(env, orc, cols, alpha):
     api, torch = env
     a = float(np.float32(alpha))
@@ -238,20 +238,21 @@ def test_alpha_out_of_range_rejected(env):
 
 @pytest.mark.parametrize("alpha", [1.5, 1.25, 2.0])
 @pytest.mark.parametrize("hist", [1, 0], ids=["hist", "nohist"])
-def test_wide_rows_histogram_bracket(env, orc, alpha, hist):
-    """Rows wider than 8192 (the streaming kernel), with and without the
-    histogram-initialised bracket: sparse rows, dense rows that overflow the
-    LDS list, near-constant and one-hot rows; same results either way."""
+@pytest.mark.parametrize("cols", [20000, 32768, 40000])
+def test_wide_rows_histogram_bracket(env, orc, alpha, hist, cols):
+    """Rows wider than 8192 (held in a workgroup's registers up to 32768,
+    streamed beyond), with and without the histogram-initialised bracket:
+    sparse rows, dense rows that overflow any LDS list, near-constant and
+    one-hot rows; same results either way."""
     api, torch = env
     a = float(np.float32(alpha))
     rng = np.random.default_rng(70 + hist)
-    cols = 20000
     S = rng.normal(size=(8, cols)).astype(np.float32)
     S[1] *= 0.02                       # dense: every score near the max
     S[2] = 3.0; S[2, ::7] = 2.9        # near-constant
     S[3] = -5.0; S[3, 1234] = 5.0      # one-hot
     S[4] *= 4.0
-    S[5, :10000] = -np.inf             # half masked
+    S[5, :cols // 2] = -np.inf         # half masked
     S[6] = np.linspace(-0.5, 0.5, cols)
     S[7] *= 0.3
     tau, P = _run(api, torch, S, alpha=a, row_plain_bracket=not hist)
