@@ -985,8 +985,10 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
     const int srow = qh * 64 + kh * 32 + m;  // the row this lane solves (with lane l ^ 32)
 
     // ---- collect the scores above each collecting row's bound
-    auto collect = [&]() {
-        float lr[2];
+    // bin: scores past a sub-list's capacity go to the row's histogram over
+    // [bound, max] (the overflow path adds the listed ones after the solve)
+    auto collect = [&](bool bin) {
+        float lr[2], hlo[2], hinv[2];
         int cc[2] = {0, 0};
         bool coll[2];
 #pragma unroll
@@ -994,6 +996,8 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
             const int row = qh * 64 + qb * 32 + m;
             coll[qb] = rstate[row] == kRowCollect;
             lr[qb] = coll[qb] ? raw_threshold(row_lo[row], p.scale) : __builtin_inff();
+            hlo[qb] = row_lo[row];
+            hinv[qb] = coll[qb] ? (float)kHistBins / (row_m[row] - row_lo[row]) : 0.0f;
         }
         ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
 #pragma unroll
@@ -1020,6 +1024,10 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                                 e[0] = __builtin_bit_cast(uint32_t, x * p.scale);
                                 e[1] = (uint32_t)(J * kBC + kb * 32 + key_of_reg(r, h));
                                 clist[(size_t)(4 * c + q) * kBR + row] = e;
+                            } else if (bin) {
+                                // (x * scale > bound, so the bin index is >= 0)
+                                const int k = min((int)((x * p.scale - hlo[qb]) * hinv[qb]), kHistBins - 1);
+                                atomicAdd(&hist[k * kBR + row], 1);
                             }
                             cc[qb] = c + 1;
                         }
@@ -1089,46 +1097,29 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
         return flag_s != 0;
     };
 
-    collect();
+    // the histogram of the overflow path is built during the first collect
+    // (the ring sweep's first barrier orders the clearing before its atomics)
+    for (int i = t; i < kHistBins * kBR; i += kNT) hist[i] = 0;
+    collect(true);
     solve();
 
     // (no row overflowed: no row can be in the sweep state below)
     const bool overflowed = (ss.state_s >> kRowOver) & 1;
     if (overflowed) {
-        // ---- histogram of the scores above the bound of each overflowing row
-        for (int i = t; i < kHistBins * kBR; i += kNT) hist[i] = 0;
-        float lr[2], hlo[2], hinv[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int row = qh * 64 + qb * 32 + m;
-            const bool over = rstate[row] == kRowOver;
-            hlo[qb] = row_lo[row];
-            hinv[qb] = over ? (float)kHistBins / (row_m[row] - row_lo[row]) : 0.0f;
-            lr[qb] = over ? raw_threshold(row_lo[row], p.scale) : __builtin_inff();
+        // ---- histogram of the scores above the bound of each overflowing
+        // row: the collect binned the scores past the lists' capacity; add
+        // the listed ones (entry i of sub-list qq of a row sits at
+        // (4 i + qq) kBR + row, so the threads walk the lists in order)
+        for (int e = t; e < 4 * capq * kBR; e += kNT) {
+            const int row = e % kBR, qq = (e / kBR) & 3, i = e / (4 * kBR);
+            if (rstate[row] == kRowOver && i < (int)cntq[qq][row]) {
+                const float sv = __builtin_bit_cast(float, clist[e][0]);
+                const int k = min((int)((sv - row_lo[row]) * ((float)kHistBins / (row_m[row] - row_lo[row]))),
+                                  kHistBins - 1);
+                atomicAdd(&hist[k * kBR + row], 1);
+            }
         }
         __syncthreads();
-        ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int row = qh * 64 + qb * 32 + m;
-                float mx = neg_inf();
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][qb][r]);
-                if (__builtin_amdgcn_ballot_w64(mx > lr[qb]) == 0) continue;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float x = acc[kb][qb][r];
-                        if (x > lr[qb]) {
-                            const int k = min((int)((x * p.scale - hlo[qb]) * hinv[qb]), kHistBins - 1);
-                            atomicAdd(&hist[k * kBR + row], 1);
-                        }
-                    }
-            }
-        });
         // tau_h from the bin counts (one thread per row), the bracket
         // [tau_h, tau_h + w], and whether the scores above tau_h fit the lists
         if (t < kBR && rstate[t] == kRowOver) {
@@ -1180,7 +1171,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
         }
         __syncthreads();
         if (any_row(kRowCollect)) {
-            collect();
+            collect(false);
             solve();
             // rows still overflowing keep the histogram bracket
             if (t < kBR && rstate[t] == kRowOver) rstate[t] = kRowSweep;
@@ -1188,7 +1179,11 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
         }
     }
 
-    // ---- Halley-bisection sweeps for rows whose lists overflowed
+    // ---- refinement sweeps for rows whose lists overflowed: Newton steps
+    // from below on F^(alpha-1) - 1 (newton_or_bisect), from the two sums F =
+    // sum p and F1 = sum p/u; at alpha = 1.5 that is sqrt(F) - 1, the 2-norm
+    // of the g_i less 1, which is exactly linear in tau while the support
+    // stays fixed, so the steps land on tau once the support is found.
     const bool swept = overflowed && any_row(kRowSweep);
     if (swept) {
         float* const fb_t = ss.fb.t;
@@ -1207,8 +1202,9 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                 tq[qb] = fb_t[row];
                 lr[qb] = fb_active[row] != 0 ? raw_threshold(tq[qb], p.scale) : __builtin_inff();
             }
-            float sc[2] = {0.f, 0.f}, sf[2] = {0.f, 0.f}, sf1[2] = {0.f, 0.f};
-            float smn[2] = {__builtin_inff(), __builtin_inff()};
+            float sf[2] = {0.f, 0.f}, sf1[2] = {0.f, 0.f};
+            const float hs = 0.5f * p.scale;
+            const float hc[2] = {-0.5f * tq[0], -0.5f * tq[1]};
             ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int, int, f32x16(&acc)[2][2]) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
@@ -1218,89 +1214,60 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
 #pragma unroll
                         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][qb][r]);
                     if (__builtin_amdgcn_ballot_w64(mx > lr[qb]) == 0) continue;
+                    if (p.gen) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float x = acc[kb][qb][r];
-                            if (x > lr[qb]) {
-                                const float sv = x * p.scale;
-                                sc[qb] += 1.f;
-                                smn[qb] = fminf(smn[qb], sv);
-                                if (p.gen) {
-                                    // F = sum p, F1 = sum p/u (Newton)
-                                    const float u = p.am.am1 * (sv - tq[qb]);
+                            for (int r = 0; r < 16; ++r) {
+                                const float x = acc[kb][qb][r];
+                                if (x > lr[qb]) {
+                                    // F = sum p, F1 = sum p/u
+                                    const float u = p.am.am1 * (x * p.scale - tq[qb]);
                                     const float pu = p.am.pw1(u);  // p / u
                                     sf[qb] = fmaf(pu, u, sf[qb]);
                                     sf1[qb] += pu;
-                                } else {
-                                    const float gg = 0.5f * (sv - tq[qb]);
-                                    sf[qb] = fmaf(gg, gg, sf[qb]);
-                                    sf1[qb] += gg;
                                 }
                             }
-                        }
+                    } else {
+                        // g = [(s - t)/2]_+, F = sum g^2, F1 = sum g: three
+                        // operations per score, no branch
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const float gg = fmaxf(fmaf(acc[kb][qb][r], hs, hc[qb]), 0.0f);
+                                sf[qb] = fmaf(gg, gg, sf[qb]);
+                                sf1[qb] += gg;
+                            }
+                    }
                 }
             });
             // combine the two lane halves, then the two key parities
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                sc[qb] += __shfl_xor(sc[qb], 32, kWave);
                 sf[qb] += __shfl_xor(sf[qb], 32, kWave);
                 sf1[qb] += __shfl_xor(sf1[qb], 32, kWave);
-                smn[qb] = fminf(smn[qb], __shfl_xor(smn[qb], 32, kWave));
                 if (h == 0) {
                     const int row = qh * 64 + qb * 32 + m;
-                    fb_part[row][kh][0] = sc[qb];
-                    fb_part[row][kh][1] = sf[qb];
-                    fb_part[row][kh][2] = sf1[qb];
-                    fb_part[row][kh][3] = smn[qb];
+                    fb_part[row][kh][0] = sf[qb];
+                    fb_part[row][kh][1] = sf1[qb];
                 }
             }
             if (t == 0) flag_s = 0;
             __syncthreads();
             if (h == 0 && fb_active[srow]) {
-                const float C = fb_part[srow][0][0] + fb_part[srow][1][0];
-                const float F = fb_part[srow][0][1] + fb_part[srow][1][1];
-                const float F1 = fb_part[srow][0][2] + fb_part[srow][1][2];
-                const float mn = fminf(fb_part[srow][0][3], fb_part[srow][1][3]);
+                const float F = fb_part[srow][0][0] + fb_part[srow][1][0];
+                const float F1 = fb_part[srow][0][1] + fb_part[srow][1][1];
                 float lo = row_lo[srow], hi = row_hi[srow], tc = fb_t[srow];
-                if (p.gen) {
-                    bool fin;
-                    const float tn = newton_or_bisect(tc, F, F1, lo, hi, &fin, p.am);
-                    if (fin || hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
-                        fb_active[srow] = 0;
-                        row_tau[srow] = fin ? tn : 0.5f * (lo + hi);
-                    } else {
-                        fb_t[srow] = tn;
-                        atomicOr(&flag_s, 1);
-                    }
+                // (at alpha = 1.5, F1 = sum g is sum p/u of the general map)
+                bool fin;
+                const float tn = newton_or_bisect(tc, F, F1, lo, hi, &fin, p.am);
+                if (fin || hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
+                    fb_active[srow] = 0;
+                    row_tau[srow] = fin ? tn : 0.5f * (lo + hi);
                 } else {
-                    const bool below = F - 1.0f >= 0.0f;
-                    if (below) lo = tc; else hi = tc;
-                    // exact finish: the normaliser over the scores above tc is
-                    // the quadratic (C/4) u^2 - F1 u + F - 1 in u = tau - tc;
-                    // when its smaller root stays below all of those scores,
-                    // they are the support and tc + u is tau
-                    const float disc = fmaxf(F1 * F1 - C * (F - 1.0f), 0.0f);
-                    const float te = tc + (F1 - sqrtf(disc)) / (0.5f * C);
-                    const float tn = halley_or_bisect(tc, F, F1, C, lo, hi);
-                    if (below && C > 0.0f && te < mn) {
-                        fb_active[srow] = 0;
-                        row_tau[srow] = fmaxf(te, tc);
-                    } else if (below && fabsf(tn - tc) <= 1e-6f * fmaxf(1.0f, fabsf(tc))) {
-                        // Halley steps from below approach tau from one side, so
-                        // the bracket need not close: a step under 1e-6
-                        // relative (the fp32 sums round near 1e-7) ends it
-                        fb_active[srow] = 0;
-                        row_tau[srow] = tn;
-                    } else if (hi - lo <= 4e-7f * fmaxf(1.0f, fabsf(tc))) {
-                        fb_active[srow] = 0;
-                        row_tau[srow] = 0.5f * (lo + hi);
-                    } else {
-                        fb_t[srow] = tn;
-                        atomicOr(&flag_s, 1);
-                    }
+                    fb_t[srow] = tn;
+                    atomicOr(&flag_s, 1);
                 }
                 row_lo[srow] = lo;
                 row_hi[srow] = hi;

@@ -157,6 +157,10 @@ inline AlphaMap make_alpha_map(float alpha) {
 // is above tau), where F - 1 grows like a power e of the distance and
 // Newton on it closes only 1 - 1/e of the gap per step far from the root.
 // The step is e (F - F^(2-alpha)) / F1 (the plain Newton step at alpha = 2).
+// From a point above the root (reached through the rounding of the sums) the
+// same tangent lands at or below the root, again by convexity, so the step
+// is taken from there too: a bisection from above would need a halving per
+// bit of the gap left to the last point below.
 // Steps that leave (lo, hi) fall back to bisection.  Returns the next point
 // and updates the bracket; *done is set once the step is below 1e-6 relative
 // (tau is then the returned point, one Newton step further, so its error is
@@ -166,18 +170,28 @@ inline AlphaMap make_alpha_map(float alpha) {
 __device__ __forceinline__ float newton_or_bisect(float t, float F, float F1, float& lo, float& hi,
                                                   bool* done, const AlphaMap& am) {
     *done = false;
+    const float tol = 1e-6f * fmaxf(1.0f, fabsf(t));
     if (F - 1.0f >= 0.0f) {
         lo = t;
         const float Fq = am.lin ? 1.0f : exp2f((1.0f - am.am1) * log2f(F));  // F^(2-alpha)
         const float step = am.e * (F - Fq) / F1;
         const float tn = t + step;
-        if (!(step > 1e-6f * fmaxf(1.0f, fabsf(t)))) {
+        if (!(step > tol)) {
             *done = true;
             return fminf(fmaxf(tn, lo), hi);
         }
         return (tn < hi) ? tn : 0.5f * (lo + hi);
     }
     hi = t;
+    if (F > 0.0f && F1 > 0.0f) {
+        const float Fq = am.lin ? 1.0f : exp2f((1.0f - am.am1) * log2f(F));
+        const float step = am.e * (F - Fq) / F1;  // < 0
+        const float tn = t + step;
+        if (tn > lo) {
+            if (!(-step > tol)) *done = true;
+            return tn;
+        }
+    }
     return 0.5f * (lo + hi);
 }
 
