@@ -507,10 +507,10 @@ __device__ __forceinline__ float raw_threshold(float lo, float scale) {
 
 // Threshold of a row from its candidates: every entry is above `lo`, and
 // none of the row's other scores is.  Two lanes share a row (sums are
-// combined with lane l ^ 32).  Newton steps from below: f(t) = sum
-// [(x - t)/2]_+^2 - 1 is convex and decreasing, so a step from a point with
-// f >= 0 stays at or below the root (bisection takes over if rounding lands
-// above it).  Exact finish: when the closed-form root of {x > t} lies below
+// combined with lane l ^ 32).  Newton steps from below on sqrt(F) - 1, F(t) =
+// sum [(x - t)/2]_+^2 (the norm of a vector of convex non-negative functions
+// of t, so convex and decreasing): a step from a point with F >= 1 stays at or
+// below the root (bisection takes over if rounding lands above it).  Exact finish: when the closed-form root of {x > t} lies below
 // the set's smallest member, that set is the support and the root is tau.
 // Sums in fp64.  A step from a point above the root (rounding) is a Newton
 // step too: the tangent of a convex decreasing function meets zero at or
@@ -555,7 +555,12 @@ __device__ __forceinline__ double solve_candidates(const Src& src, double mx, do
                 done = true;
                 continue;
             }
-            double tn = t + f / F1;
+            // Newton step on sqrt(F) - 1 (F = f + 1 = |g|^2, g = [(x - t)/2]_+):
+            // the norm of g is convex and decreasing in t too, closer to
+            // linear than F, so the step from below is longer (by up to 2x
+            // while F >> 1) and still stays at or below the root
+            const double rF = sqrt(f + 1.0);
+            double tn = t + 2.0 * rF * (rF - 1.0) / F1;
             if (!(tn > lo && tn < hi)) tn = 0.5 * (lo + hi);
             t = tn;
         } else {
