@@ -906,32 +906,43 @@ constexpr int kGatherTileCost = 32;
 enum { kRowNone = 0, kRowCollect = 1, kRowSweep = 2, kRowDone = 3, kRowOver = 4 };
 
 // LDS of the solve phase alone: per-row state, and the scratch of the
-// overflow path (the histogram, then the sweep sums).
+// overflow path (the histogram, then the sweep sums).  PACK: two 16-bit bin
+// counts per word (bin 2i in the low half of word i, bin 2i + 1 in the high
+// half), for rows of at most 65535 scores (the fused kernel: L <= 16384).
+template <bool PACK>
 struct SolveScratch {
+    static constexpr int kPer = PACK ? 2 : 1;  // bins per word
     float row_hi[kBR];
     int rstate[kBR];
     uint16_t cntq[4][kBR];  // entries met per candidate sub-list
     int state_s;            // bit s set: some row of the block is in state s after the last solve
     int gwork_s;            // list entries of the block (the gather decision)
     union {
-        int hist[kHistBins * kBR];  // counts [bin][row]
+        uint32_t hist[kHistBins / kPer * kBR];  // counts [bin / kPer][row]
         struct {
             float t[kBR];
             int active[kBR];
             float part[kBR][2][4];
         } fb;
     };
+    static constexpr int kHistWords = kHistBins / kPer * kBR;
+    __device__ __forceinline__ void hist_add(int k, int row) {
+        atomicAdd(&hist[(k / kPer) * kBR + row], PACK ? 1u << (16 * (k & 1)) : 1u);
+    }
+    __device__ __forceinline__ int hist_get(int k, int row) const {
+        const uint32_t w = hist[(k / kPer) * kBR + row];
+        return PACK ? (int)((w >> (16 * (k & 1))) & 0xffffu) : (int)w;
+    }
 };
 
 // from_stats: the block's row statistics and raw tile maxima are already in
 // bl (the score sweep ran in this workgroup); otherwise they are read from
 // the workspace.  Returns whether it wrote O from the candidate lists.
-template <typename T, int D, int TCMAX, int S>
+template <typename T, int D, int TCMAX, int S, bool PACK>
 __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                                             const typename Ops<T, D>::template QOp<2>& qop, T* ring,
-                                            SolveScratch& ss, BlockLds<TCMAX>& bl, bool from_stats) {
+                                            SolveScratch<PACK>& ss, BlockLds<TCMAX>& bl, bool from_stats) {
     constexpr int WD = TCMAX / 32;
-    int* const hist = ss.hist;
     uint16_t* const list = bl.list;
     float(&um_s)[2][TCMAX] = bl.um_s;
     uint16_t(&cntq)[4][kBR] = ss.cntq;
@@ -1032,7 +1043,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                             } else if (bin) {
                                 // (x * scale > bound, so the bin index is >= 0)
                                 const int k = min((int)((x * p.scale - hlo[qb]) * hinv[qb]), kHistBins - 1);
-                                atomicAdd(&hist[k * kBR + row], 1);
+                                ss.hist_add(k, row);
                             }
                             cc[qb] = c + 1;
                         }
@@ -1104,7 +1115,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
 
     // the histogram of the overflow path is built during the first collect
     // (the ring sweep's first barrier orders the clearing before its atomics)
-    for (int i = t; i < kHistBins * kBR; i += kNT) hist[i] = 0;
+    for (int i = t; i < ss.kHistWords; i += kNT) ss.hist[i] = 0u;
     collect(true);
     solve();
 
@@ -1121,7 +1132,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                 const float sv = __builtin_bit_cast(float, clist[e][0]);
                 const int k = min((int)((sv - row_lo[row]) * ((float)kHistBins / (row_m[row] - row_lo[row]))),
                                   kHistBins - 1);
-                atomicAdd(&hist[k * kBR + row], 1);
+                ss.hist_add(k, row);
             }
         }
         __syncthreads();
@@ -1136,7 +1147,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                 // scores stand at its left edge)
                 double S0 = 0.0, S1 = 0.0, S2 = 0.0, best = -2.0;
                 for (int k = kHistBins - 1; k >= 0; --k) {
-                    const double H = (double)hist[k * kBR + t];
+                    const double H = (double)ss.hist_get(k, t);
                     if (H == 0.0) continue;
                     const double y = lo + k * wd - mx;
                     S0 += H;
@@ -1155,7 +1166,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                     const double mid = 0.5 * (a + b);
                     double F = 0.0;
                     for (int k = 0; k < kHistBins; ++k) {
-                        const int H = hist[k * kBR + t];
+                        const int H = ss.hist_get(k, t);
                         const double u = (double)p.am.am1 * (lo + k * wd - mid);
                         if (H > 0 && u > 0.0) F += H * (p.am.lin ? u : pow(u, (double)p.am.e));
                     }
@@ -1169,7 +1180,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
             const float thi = (float)fmin(th + wd + mg, mx);
             int above = 0;
             const int k0 = max((int)floor((tlo - lo) / wd) - 1, 0);
-            for (int k = k0; k < kHistBins; ++k) above += hist[k * kBR + t];
+            for (int k = k0; k < kHistBins; ++k) above += ss.hist_get(k, t);
             row_lo[t] = fmaxf(row_lo[t], tlo);
             row_hi[t] = thi;
             rstate[t] = (above <= 3 * capq) ? kRowCollect : kRowSweep;
@@ -1342,7 +1353,7 @@ template <typename T, int D, int TCMAX>
 __global__ __launch_bounds__(kNT, (CollectCfg<T, D>::kOcc)) void fwd_solve_kernel(FwdParams p) {
     using O = Ops<T, D>;
     __shared__ __attribute__((aligned(16))) T ring[CollectCfg<T, D>::kS * 2 * 64 * D];
-    __shared__ SolveScratch ss;
+    __shared__ SolveScratch<false> ss;
     __shared__ BlockLds<TCMAX> bl;
     int bh, r0;
     decode_item(blockIdx.x, p.BH, p.nQ, p.mode != 0, bh, r0);
@@ -1695,6 +1706,10 @@ struct FusedCfg {
     // three workgroups per CU fit (<= 168 VGPRs, <= 53 KB LDS) at d = 64 with
     // tables for up to 128 key tiles
     static constexpr int kOcc = (D == 64 && TCMAX <= 128) ? 3 : 2;
+    // ring stages of the candidate sweeps: two at d = 64 (the next pair of
+    // tiles loads while the current one is swept), one at d = 128 (two stages
+    // and the solve scratch would not fit beside the second workgroup)
+    static constexpr int kSolveS = (D == 64) ? 2 : 1;
 };
 
 template <int D, int TCMAX, bool CAUSAL>
@@ -1705,8 +1720,8 @@ __global__ __launch_bounds__(kNT, (FusedCfg<D, TCMAX>::kOcc)) void fwd_fused_ker
     union Work {
         T sring[StatsCfg<T, D>::kS * 2 * 64 * D];
         struct {
-            T ring[2 * 64 * D];  // one stage
-            SolveScratch ss;
+            T ring[FusedCfg<D, TCMAX>::kSolveS * 2 * 64 * D];
+            SolveScratch<true> ss;  // (L <= 16384: a bin count fits 16 bits)
         } solve;
         OutLds<D> out;
     };
@@ -1718,7 +1733,8 @@ __global__ __launch_bounds__(kNT, (FusedCfg<D, TCMAX>::kOcc)) void fwd_fused_ker
         O::load_q(qop, reinterpret_cast<const T*>(p.q) + (size_t)bh * p.L * D, r0 + 64 * (wave_id() & 1), p.L);
         stats_phase<T, D, TCMAX, CAUSAL>(p, bh, r0, qop, wk.sring, bl, true);
         __syncthreads();
-        if (solve_phase<T, D, TCMAX, 1>(p, bh, r0, qop, wk.solve.ring, wk.solve.ss, bl, true)) return;
+        if (solve_phase<T, D, TCMAX, FusedCfg<D, TCMAX>::kSolveS>(p, bh, r0, qop, wk.solve.ring, wk.solve.ss, bl, true))
+            return;
     }
     if (p.o == nullptr) return;
     __syncthreads();
