@@ -420,3 +420,34 @@ def test_query_variance_sweep_sampled(env, orc, sd):
     check_mask(orc, inp, cfg.scale, cfg.mask, cfg.window, bm, [0], label=cfg.name)
     nnz = sum(bin(int(x)).count("1") for x in bm.reshape(-1))
     print(f"{cfg.name}: max |dO| = {err:.3e}, block sparsity {1 - nnz / (2 * 128 * 128):.4f}")
+
+
+@pytest.mark.parametrize("cap", [0, 1])
+def test_constant_rows_longest_fused(env, cap):
+    """Rows of 16384 equal scores, the longest the fused kernel takes: the
+    threshold is the bracket end m - 2/sqrt(n) ("AdaSplash-2: Faster
+    Differentiable Sparse Attention" sec. 2.4) and O is the mean of the n
+    active V rows.  cap = 1 sends every row through the overflow path, whose
+    histogram then holds all of a row's scores in its top bin (up to 16384
+    counts in one 16-bit half word)."""
+    api, torch = env
+    import torch as T
+    B, H, L, d = 1, 1, 16384, 64
+    inp = gen(B, H, L, d, "bf16", seed=61)
+    inp["q"].zero_()
+    V = inp["v"][0, 0].double().numpy()
+    Tc = L // 64
+    for mode in (0, 1):
+        O, tau, bm = run_gpu(api, torch, inp, 0.125, mode, 0, candidate_cap=cap)
+        n = np.full(L, L, dtype=np.float64) if mode == 0 else np.arange(1, L + 1, dtype=np.float64)
+        tau_ref = -2.0 / np.sqrt(n)
+        dt = np.abs(tau.reshape(L) - tau_ref)
+        assert np.all(dt <= 1e-4 * np.maximum(1.0, np.abs(tau_ref))), f"mode {mode}: tau err {dt.max():.3e}"
+        O_ref = (np.broadcast_to(V.mean(axis=0), (L, d)) if mode == 0
+                 else np.cumsum(V, axis=0) / n[:, None])
+        err = np.abs(O.reshape(L, d) - O_ref).max()
+        assert err <= O_TOL["bf16"], f"mode {mode} cap {cap}: O err {err:.3e}"
+        # every tile with an active key is non-null (all active scores exceed tau)
+        bits = np.unpackbits(bm.reshape(L // 64, -1).view(np.uint8), axis=1, bitorder="little")[:, :Tc]
+        want = np.ones((L // 64, Tc), dtype=np.uint8) if mode == 0 else np.tril(np.ones((L // 64, Tc), dtype=np.uint8))
+        assert np.array_equal(bits, want), f"mode {mode} cap {cap}: mask"
