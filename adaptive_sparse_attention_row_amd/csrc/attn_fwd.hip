@@ -462,28 +462,53 @@ struct CandSrc {
     __device__ __forceinline__ void each(F f) const { each_from(0, f); }
 };
 
-// The same entries with the first KR held in registers; missing entries
-// read -inf, which no threshold test passes.
-template <int KR>
+// The same entries: the first KR scores in registers (missing entries read
+// -inf, which no threshold test passes), their keys and the next KL scores
+// in a column of LDS that only this thread touches (col[k * kNT]: keys for
+// k < KR, scores for KR <= k < KR + KL), any further ones read from the
+// workspace on each pass.  Every pass visits the entries in list order.  The
+// slots of the first KR + KL entries lie inside the block's lists (slot(i) <
+// 4 (KR + KL) <= kCandCap), so they are loaded unconditionally, all at once.
+template <int KR, int KL>
 struct RegSrc {
+    static_assert(4 * (KR + KL) <= kCandCap, "entries' slots inside the lists");
     float v[KR];
-    uint32_t key[KR];
     CandSrc src;
-    __device__ __forceinline__ void load(const CandSrc& s) {
+    uint32_t* col;
+    int nl;
+    __device__ __forceinline__ void load(const CandSrc& s, uint32_t* lds_col) {
         src = s;
+        col = lds_col;
         const int n = s.n();
+        // (the LDS scores only in waves where some lane's list is longer than
+        // the registers: a wave-uniform branch)
+        const bool longer = __builtin_amdgcn_ballot_w64(n > KR) != 0;
+        u32x2 e[KR];
+        uint32_t x[KL > 0 ? KL : 1];
+#pragma unroll
+        for (int k = 0; k < KR; ++k) e[k] = s.entry(k);
+        if (longer) {
+#pragma unroll
+            for (int k = 0; k < KL; ++k) x[k] = __builtin_bit_cast(uint32_t, s.at(KR + k));
+        }
 #pragma unroll
         for (int k = 0; k < KR; ++k) {
-            const u32x2 e = (k < n) ? s.entry(k) : u32x2{__builtin_bit_cast(uint32_t, neg_inf()), 0u};
-            v[k] = __builtin_bit_cast(float, e[0]);
-            key[k] = e[1];
+            v[k] = (k < n) ? __builtin_bit_cast(float, e[k][0]) : neg_inf();
+            col[k * kNT] = e[k][1];
         }
+        if (longer) {
+#pragma unroll
+            for (int k = 0; k < KL; ++k) col[(KR + k) * kNT] = x[k];
+        }
+        nl = min(max(n - KR, 0), KL);
     }
+    __device__ __forceinline__ uint32_t key(int k) const { return col[k * kNT]; }
     template <class F>
     __device__ __forceinline__ void each(F f) const {
 #pragma unroll
         for (int k = 0; k < KR; ++k) f(v[k]);
-        src.each_from(KR, f);
+        for (int k = 0; k < nl; ++k) f(__builtin_bit_cast(float, col[(KR + k) * kNT]));
+        src.each_from(KR + nl, f);
     }
 };
 
@@ -893,6 +918,13 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
 //           last sweep sets its tiles in the mask.
 template <int D>
 constexpr int kSolveRegs = D == 128 ? 8 : 16;  // candidates per lane held in registers
+// and the next ones per lane in LDS: the score ring every caller of the solve
+// passes holds at least 2 x 64 x D elements of T per stage, S stages, read as
+// words over kNT threads (the keys of the register entries take kSolveRegs)
+template <typename T, int D, int S>
+constexpr int kSolveLds = (S * 2 * 64 * D * (int)sizeof(T) / (4 * kNT) - kSolveRegs<D>) < 16
+                              ? S * 2 * 64 * D * (int)sizeof(T) / (4 * kNT) - kSolveRegs<D>
+                              : 16;
 constexpr int kHistBins = 32;
 
 // The solve kernel writes O itself from the candidate lists when
@@ -1067,8 +1099,9 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
         const int b0 = cntq[h ^ 1][srow], b1 = cntq[2 + (h ^ 1)][srow];
         const bool act = open && max(max(a0, a1), max(b0, b1)) <= capq;
         const int n = act ? a0 + a1 + b0 + b1 : 1;
-        RegSrc<kSolveRegs<D>> src;
-        src.load(CandSrc{clist + srow, act ? a0 : 0, act ? a1 : 0, h});
+        // (the score ring is idle between sweeps)
+        RegSrc<kSolveRegs<D>, kSolveLds<T, D, S>> src;
+        src.load(CandSrc{clist + srow, act ? a0 : 0, act ? a1 : 0, h}, reinterpret_cast<uint32_t*>(ring) + t);
         const double mx = row_m[srow];
         const float tr = p.gen ? solve_candidates_gen(src, row_lo[srow], p.am.hi(row_m[srow], (float)n), act, p.am)
                                : (float)solve_candidates(src, mx, row_lo[srow], mx - 2.0 / sqrt((double)n), act);
@@ -1084,7 +1117,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                 }
             };
 #pragma unroll
-            for (int k = 0; k < kSolveRegs<D>; ++k) mark(src.v[k], src.key[k]);
+            for (int k = 0; k < kSolveRegs<D>; ++k) mark(src.v[k], src.key(k));
             for (int i = kSolveRegs<D>; i < na; ++i) {
                 const u32x2 e = src.src.entry(i);
                 mark(__builtin_bit_cast(float, e[0]), e[1]);
