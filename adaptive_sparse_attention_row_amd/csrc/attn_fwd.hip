@@ -449,14 +449,24 @@ struct CandSrc {
     __device__ __forceinline__ int slot(int i) const { return i < n0 ? 4 * i + h : 4 * (i - n0) + 2 + h; }
     __device__ __forceinline__ u32x2 entry(int i) const { return glob[(size_t)slot(i) * kBR]; }
     __device__ __forceinline__ float at(int i) const { return __builtin_bit_cast(float, entry(i)[0]); }
-    // f(x) for entries i0, i0 + 1, ... in order
+    // f(x) for entries i0, i0 + 1, ... in order.  Four entries per step are
+    // loaded at once from clamped slots (every slot of i in [0, n) lies inside
+    // the lists); entries past a lane's list read -inf, which every caller's
+    // f ignores (no threshold test passes).  The step count is wave-uniform.
     template <class F>
     __device__ __forceinline__ void each_from(int i0, F f) const {
-#pragma unroll 4
-        for (int c = i0; c < n0; ++c) f(__builtin_bit_cast(float, glob[(size_t)(4 * c + h) * kBR][0]));
-#pragma unroll 4
-        for (int c = i0 > n0 ? i0 - n0 : 0; c < n1; ++c)
-            f(__builtin_bit_cast(float, glob[(size_t)(4 * c + 2 + h) * kBR][0]));
+        const int n = n0 + n1;
+        for (int k = i0; __builtin_amdgcn_ballot_w64(k < n) != 0; k += 4) {
+            float x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = k + u;
+                const float y = at(max(min(i, n - 1), 0));
+                x[u] = (i < n) ? y : neg_inf();
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) f(x[u]);
+        }
     }
     template <class F>
     __device__ __forceinline__ void each(F f) const { each_from(0, f); }
@@ -1118,9 +1128,15 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
             };
 #pragma unroll
             for (int k = 0; k < kSolveRegs<D>; ++k) mark(src.v[k], src.key(k));
-            for (int i = kSolveRegs<D>; i < na; ++i) {
-                const u32x2 e = src.src.entry(i);
-                mark(__builtin_bit_cast(float, e[0]), e[1]);
+            // the rest from the workspace, four entries loaded at once from
+            // clamped slots (inside the lists)
+            for (int i = kSolveRegs<D>; __builtin_amdgcn_ballot_w64(i < na) != 0; i += 4) {
+                u32x2 e[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) e[u] = src.src.entry(max(min(i + u, na - 1), 0));
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (i + u < na) mark(__builtin_bit_cast(float, e[u][0]), e[u][1]);
             }
             if (h == 0) {
                 row_tau[srow] = tr;
