@@ -841,15 +841,28 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
 #pragma unroll
             for (int j = 0; j < 32; ++j) accg[j] = 0.0f;
         }
+        // entry i of the row in list order (i < n)
+        auto entry = [&](int i) -> u32x2 {
+            const int qq = (i >= n0) + (i >= n1) + (i >= n2);
+            const int c = i - (qq == 0 ? 0 : qq == 1 ? n0 : qq == 2 ? n1 : n2);
+            return clist[(size_t)(4 * c + qq) * kBR + row];
+        };
+        // the entries of the next step are loaded while this step's V rows
+        // are in flight, so a step waits for one round trip, not two
+        u32x2 en[kB];
+        if (n > 0) {
+#pragma unroll
+            for (int u = 0; u < kB; ++u) en[u] = entry(min(u, n - 1));
+        }
         for (int i0 = 0; i0 < n; i0 += kB) {
             float a[kB], gw[kB];
             uint32_t key[kB];
+            u32x2 ec[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) ec[u] = en[u];
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
-                const int i = min(i0 + u, n - 1);
-                const int qq = (i >= n0) + (i >= n1) + (i >= n2);
-                const int c = i - (qq == 0 ? 0 : qq == 1 ? n0 : qq == 2 ? n1 : n2);
-                const u32x2 e = clist[(size_t)(4 * c + qq) * kBR + row];
+                const u32x2 e = ec[u];
                 const float sv = __builtin_bit_cast(float, e[0]);
                 const bool live = i0 + u < n;
                 if (p.gen) {
@@ -869,6 +882,10 @@ __device__ __forceinline__ void gather_rows(const FwdParams& p, int bh, int r0, 
 #pragma unroll
                 for (int j = 0; j < kLd; ++j)
                     v[u][j] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key[u] * D + part * 32 + j * kVec);
+            if (i0 + kB < n) {
+#pragma unroll
+                for (int u = 0; u < kB; ++u) en[u] = entry(min(i0 + kB + u, n - 1));
+            }
 #pragma unroll
             for (int u = 0; u < kB; ++u)
 #pragma unroll
