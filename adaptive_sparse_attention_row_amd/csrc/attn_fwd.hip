@@ -1074,16 +1074,7 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
             hlo[qb] = row_lo[row];
             hinv[qb] = coll[qb] ? (float)kHistBins / (row_m[row] - row_lo[row]) : 0.0f;
         }
-        // entry c of this lane's sub-list of row `row` sits (c * 4 kBR + q kBR
-        // + row) slots into the block's lists: a byte offset from one base
-        // pointer (kept in scalar registers) that fits 32 bits
-        char* const cbase = reinterpret_cast<char*>(clist);
-        constexpr uint32_t kSlotStep = 4 * kBR * sizeof(u32x2);  // bytes from entry c to c + 1
-        uint32_t loff[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) loff[qb] = (uint32_t)((q * kBR + qh * 64 + qb * 32 + m) * sizeof(u32x2));
         ring_sweep<T, D, S>(list, nlist_s, Kh, ring, qop, R0, g, [&](int J, int, f32x16(&acc)[2][2]) {
-            const uint32_t kbase = (uint32_t)(J * kBC + 4 * h);  // key of register 0 (key_of_reg less 8(r/4) + r%4)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const int row = qh * 64 + qb * 32 + m;
@@ -1103,14 +1094,11 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
                             // past the capacity only the count goes on: it shows
                             // the overflow, and the list is not used
                             const int c = cc[qb];
-                            u32x2 e;
-                            e[0] = __builtin_bit_cast(uint32_t, x * p.scale);
-                            e[1] = kbase + (uint32_t)(kb * 32 + 8 * (r >> 2) + (r & 3));
-                            u32x2* const slot = reinterpret_cast<u32x2*>(cbase + (loff[qb] + (uint32_t)c * kSlotStep));
-                            if (__builtin_amdgcn_ballot_w64(c >= capq) == 0) {
-                                *slot = e;  // no active lane is at its capacity
-                            } else if (c < capq) {
-                                *slot = e;
+                            if (c < capq) {
+                                u32x2 e;
+                                e[0] = __builtin_bit_cast(uint32_t, x * p.scale);
+                                e[1] = (uint32_t)(J * kBC + kb * 32 + key_of_reg(r, h));
+                                clist[(size_t)(4 * c + q) * kBR + row] = e;
                             } else if (bin) {
                                 // (x * scale > bound, so the bin index is >= 0)
                                 const int k = min((int)((x * p.scale - hlo[qb]) * hinv[qb]), kHistBins - 1);
