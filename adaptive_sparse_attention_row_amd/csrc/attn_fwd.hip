@@ -1192,13 +1192,26 @@ __device__ __forceinline__ bool solve_phase(const FwdParams& p, int bh, int r0,
         // row: the collect binned the scores past the lists' capacity; add
         // the listed ones (entry i of sub-list qq of a row sits at
         // (4 i + qq) kBR + row, so the threads walk the lists in order)
-        for (int e = t; e < 4 * capq * kBR; e += kNT) {
-            const int row = e % kBR, qq = (e / kBR) & 3, i = e / (4 * kBR);
-            if (rstate[row] == kRowOver && i < (int)cntq[qq][row]) {
-                const float sv = __builtin_bit_cast(float, clist[e][0]);
-                const int k = min((int)((sv - row_lo[row]) * ((float)kHistBins / (row_m[row] - row_lo[row]))),
-                                  kHistBins - 1);
-                ss.hist_add(k, row);
+        // (kNT is a multiple of kBR, so a thread keeps its row; every slot
+        // read lies inside the lists, so four loads go out at once)
+        static_assert(kNT % kBR == 0, "one row per thread");
+        {
+            const int row = t % kBR;
+            const bool over = rstate[row] == kRowOver;
+            const float rlo = row_lo[row], rinv = (float)kHistBins / (row_m[row] - row_lo[row]);
+            const int nE = 4 * capq * kBR;
+            for (int e0 = t; e0 < nE; e0 += 4 * kNT) {
+                float sv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sv[u] = __builtin_bit_cast(float, clist[min(e0 + u * kNT, nE - 1)][0]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = e0 + u * kNT, qq = (e / kBR) & 3, i = e / (4 * kBR);
+                    if (e < nE && over && i < (int)cntq[qq][row]) {
+                        const int k = min((int)((sv[u] - rlo) * rinv), kHistBins - 1);
+                        ss.hist_add(k, row);
+                    }
+                }
             }
         }
         __syncthreads();
