@@ -122,7 +122,10 @@ struct AlphaMap {
         if (!(u > 0.0f)) return 0.0f;
         return lin ? u : exp2f(e * log2f(u));
     }
-    __device__ __forceinline__ float p(float s, float tau) const { return pw(am1 * (s - tau)); }
+    // (s > tau is tested before the difference is formed: a masked score
+    // against the threshold of a row with no active key, -inf - -inf, would
+    // give a NaN, and the build assumes no NaN reaches a comparison)
+    __device__ __forceinline__ float p(float s, float tau) const { return s > tau ? pw(am1 * (s - tau)) : 0.0f; }
     // u^(e-1) for u > 0 (1 for sparsemax), 0 otherwise: p = u * pw1(u) and
     // p/u = pw1(u), so a Newton step needs one power and no division
     __device__ __forceinline__ float pw1(float u) const {
@@ -131,6 +134,7 @@ struct AlphaMap {
     }
     // dp/ds = u^(e-1) on the support (1 for sparsemax), 0 off it
     __device__ __forceinline__ float g(float s, float tau) const {
+        if (!(s > tau)) return 0.0f;
         const float u = am1 * (s - tau);
         if (!(u > 0.0f)) return 0.0f;
         return lin ? 1.0f : exp2f((e - 1.0f) * log2f(u));
